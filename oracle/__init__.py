@@ -1,0 +1,169 @@
+"""fp64 CPU oracle for the Momentum-Mamba selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The product library (``selective_state_space_msm_amd``) never imports it,
+and it imports nothing from the product.  It shares no code with the HIP path.
+
+The arithmetic lives in ``msm_oracle.c`` (plain double-precision loops; its header gives the
+equations and the pages they follow).  This module only builds that file with gcc, loads it
+with ctypes and widens numpy inputs to float64 (exact for fp32 and bf16 values).
+
+Pinned by ``tests/test_oracle_pins.py``: worked examples printed on the pages, closed forms,
+the materialised matrix form, the convolution form, finite differences and scaling identities.
+``tests/test_oracle_mutants.py`` compiles deliberately broken copies of the C file and checks
+that the pins reject each of them.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "msm_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libmsm_oracle.so")
+
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+             "-std=c11", "-Wall"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C file into a shared library with the oracle's fixed gcc flags."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    """Compile msm_oracle.c (always).  Returns the .so path."""
+    return compile_source(SOURCE, _LIB_PATH)
+
+
+def _f64(a):
+    """Widen to a C-contiguous float64 array (exact for fp32 / bf16-valued inputs)."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shapes(x, A, B):
+    Bt, L, D = x.shape
+    D2, N = A.shape
+    if D2 != D or B.shape != (Bt, L, N):
+        raise ValueError("inconsistent shapes: x %s A %s B %s" % (x.shape, A.shape, B.shape))
+    return Bt, L, D, N
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P, I64, Dbl, Int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
+        lib.msm_oracle_fwd.argtypes = [P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64, I64, P, P, P, Int]
+        lib.msm_oracle_fwd.restype = Int
+        lib.msm_oracle_fwd_plain.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, P, Int]
+        lib.msm_oracle_fwd_plain.restype = Int
+        lib.msm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64, I64,
+                                       P, P, P, P, P, P, Int]
+        lib.msm_oracle_bwd.restype = Int
+        lib.msm_oracle_max_threads.argtypes = []
+        lib.msm_oracle_max_threads.restype = Int
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return int(self.lib.msm_oracle_max_threads())
+
+    def fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, threads=0):
+        """Momentum recurrence forward in fp64.  Returns (y, last_h, last_v) as float64.
+
+        x, delta: (Bt, L, D); A: (D, N); B, C: (Bt, L, N); Dskip: (D,) or None.
+        """
+        x, delta, A, B, C = (_f64(a) for a in (x, delta, A, B, C))
+        Ds = None if Dskip is None else _f64(Dskip)
+        Bt, L, D, N = _shapes(x, A, B)
+        if delta.shape != x.shape or C.shape != B.shape or (Ds is not None and Ds.shape != (D,)):
+            raise ValueError("inconsistent shapes")
+        y = np.empty((Bt, L, D), np.float64)
+        last_h = np.empty((Bt, D, N), np.float64)
+        last_v = np.empty((Bt, D, N), np.float64)
+        rc = self.lib.msm_oracle_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds),
+                                     float(beta), float(alpha), Bt, L, D, N, _ptr(y),
+                                     _ptr(last_h), _ptr(last_v), int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_fwd failed (%d)" % rc)
+        return y, last_h, last_v
+
+    def fwd_plain(self, x, delta, A, B, C, Dskip=None, threads=0):
+        """Standard (velocity-free) Mamba recurrence in fp64.  Returns (y, last_h)."""
+        x, delta, A, B, C = (_f64(a) for a in (x, delta, A, B, C))
+        Ds = None if Dskip is None else _f64(Dskip)
+        Bt, L, D, N = _shapes(x, A, B)
+        y = np.empty((Bt, L, D), np.float64)
+        last_h = np.empty((Bt, D, N), np.float64)
+        rc = self.lib.msm_oracle_fwd_plain(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(Ds), Bt, L, D, N, _ptr(y), _ptr(last_h),
+                                           int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_fwd_plain failed (%d)" % rc)
+        return y, last_h
+
+    def bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, threads=0):
+        """Gradients of sum(dy * y) in fp64.
+
+        Returns a dict with dx, ddelta (Bt, L, D), dA (D, N), dB, dC (Bt, L, N) and dDskip
+        (D,) (None when Dskip is None).
+        """
+        x, delta, A, B, C, dy = (_f64(a) for a in (x, delta, A, B, C, dy))
+        Ds = None if Dskip is None else _f64(Dskip)
+        Bt, L, D, N = _shapes(x, A, B)
+        if dy.shape != x.shape:
+            raise ValueError("dy shape")
+        out = dict(dx=np.empty((Bt, L, D)), ddelta=np.empty((Bt, L, D)), dA=np.empty((D, N)),
+                   dB=np.empty((Bt, L, N)), dC=np.empty((Bt, L, N)),
+                   dDskip=None if Ds is None else np.empty((D,)))
+        rc = self.lib.msm_oracle_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds),
+                                     _ptr(dy), float(beta), float(alpha), Bt, L, D, N,
+                                     _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                                     _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dDskip"]),
+                                     int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_bwd failed (%d)" % rc)
+        return out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from msm_oracle.c (compiled on first use if no library is present)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def fwd(*args, **kw):
+    return default().fwd(*args, **kw)
+
+
+def fwd_plain(*args, **kw):
+    return default().fwd_plain(*args, **kw)
+
+
+def bwd(*args, **kw):
+    return default().bwd(*args, **kw)
+
+
+def max_threads() -> int:
+    return default().max_threads()

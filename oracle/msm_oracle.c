@@ -1,0 +1,218 @@
+/*
+ * msm_oracle.c -- plain, slow fp64 CPU oracle for the Momentum-Mamba selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call this file:
+ * only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.  It shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * What it computes (all in double precision, inputs widened exactly from their stored dtype):
+ *
+ *   Momentum Mamba README, "Momentum Mamba Recurrence": per batch row b, channel d, state n
+ *     v_t = beta * v_{t-1} + alpha * (delta_t * B_t * x_t)
+ *     h_t = exp(delta_t * A) * h_{t-1} + v_t
+ *     y_t = C_t . h_t                 (sum over the N states)
+ *   with v and h starting at zero (the README states this for v; h is read the same way).
+ *   Layout of the arrays follows the selection semantics of "Mamba: Choosing What to Remember
+ *   Based on the Input" (section "From input features to update coefficients"): B_t and C_t
+ *   hold N values per position shared across channels, delta one value per channel, A fixed
+ *   per (channel, state).  Row-major shapes:
+ *     x, delta, y, dy, dx, ddelta : (Bt, L, D)
+ *     A, dA                       : (D, N)
+ *     B, C, dB, dC                : (Bt, L, N)
+ *     Dskip, dDskip               : (D,)          (the per-channel skip weight of the Mamba block)
+ *     last_h, last_v              : (Bt, D, N)
+ *   The optional skip adds Dskip[d] * x to y ("Where the state computation sits in a Mamba
+ *   block": a learned per-channel weight times the current input).  alpha does not scale it.
+ *
+ *   Backward (Momentum Mamba README, "Gradient Flow" and "Gradient Formulas"), for the loss
+ *   l = sum(dy * y), read as follows (the page's listing reuses one variable for two adjoints):
+ *     gh_t = C_t * dy_t + a_{t+1} * gh_{t+1}          adjoint of h_t
+ *     gv_t = gh_t + beta * gv_{t+1}                   adjoint of v_t (v_t also feeds h_t)
+ *     dx_t     += alpha * delta_t * B_t * gv_t
+ *     ddelta_t += alpha * B_t * x_t * gv_t + A * a_t * h_{t-1} * gh_t
+ *     dA       += delta_t * a_t * h_{t-1} * gh_t      (summed over b and t)
+ *     dB_t     += alpha * delta_t * x_t * gv_t        (summed over channels d)
+ *     dC_t     += dy_t * h_t                          (summed over channels d; from y = C.h)
+ *     dx       += Dskip * dy,  dDskip = sum_{b,t} dy * x      (only when Dskip is given)
+ *   The page writes the velocity adjoint as a pure beta-decay; the velocity also enters h_t
+ *   directly, so its adjoint carries gh_t as well (checked by finite differences in tests).
+ *
+ * Threads: the forward is split over (b, d) channel pairs, which are independent.  The
+ * backward is split over batch rows b; dA and dDskip are first summed per row and the rows are
+ * then added in order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+int msm_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Momentum recurrence, forward.  last_h / last_v may be NULL; Dskip may be NULL. */
+int msm_oracle_fwd(const double* x, const double* delta, const double* A, const double* B,
+                   const double* C, const double* Dskip, double beta, double alpha, int64_t Bt,
+                   int64_t L, int64_t D, int64_t N, double* y, double* last_h, double* last_v,
+                   int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  set_threads(nthreads);
+  int64_t nchan = Bt * D;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t bd = 0; bd < nchan; ++bd) {
+    int64_t b = bd / D, d = bd % D;
+    for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double v = 0.0, h = 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        double dt = delta[(b * L + t) * D + d];
+        double xt = x[(b * L + t) * D + d];
+        double a = exp(dt * A[d * N + n]);
+        double w = alpha * (dt * B[(b * L + t) * N + n] * xt);
+        v = beta * v + w;
+        h = a * h + v;
+        y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * h;
+      }
+      if (last_h) last_h[(b * D + d) * N + n] = h;
+      if (last_v) last_v[(b * D + d) * N + n] = v;
+    }
+    if (Dskip)
+      for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] += Dskip[d] * x[(b * L + t) * D + d];
+  }
+  return 0;
+}
+
+/* Standard Mamba recurrence without a velocity state (Momentum Mamba README, "Standard Mamba
+ * Recurrence"): h_t = exp(delta_t A) h_{t-1} + delta_t B_t x_t, y_t = C_t . h_t.
+ * Kept separate from the momentum loop on purpose: the tests check that beta = 0, alpha = 1
+ * of the momentum recurrence reproduces it. */
+int msm_oracle_fwd_plain(const double* x, const double* delta, const double* A, const double* B,
+                         const double* C, const double* Dskip, int64_t Bt, int64_t L, int64_t D,
+                         int64_t N, double* y, double* last_h, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  set_threads(nthreads);
+  int64_t nchan = Bt * D;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t bd = 0; bd < nchan; ++bd) {
+    int64_t b = bd / D, d = bd % D;
+    for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double h = 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        double dt = delta[(b * L + t) * D + d];
+        double xt = x[(b * L + t) * D + d];
+        h = exp(dt * A[d * N + n]) * h + dt * B[(b * L + t) * N + n] * xt;
+        y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * h;
+      }
+      if (last_h) last_h[(b * D + d) * N + n] = h;
+    }
+    if (Dskip)
+      for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] += Dskip[d] * x[(b * L + t) * D + d];
+  }
+  return 0;
+}
+
+/* Backward of l = sum(dy * y) for the momentum recurrence.  All outputs are overwritten.
+ * dDskip must be non-NULL when Dskip is non-NULL and is ignored otherwise. */
+int msm_oracle_bwd(const double* x, const double* delta, const double* A, const double* B,
+                   const double* C, const double* Dskip, const double* dy, double beta,
+                   double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
+                   double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
+                   int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  if (Dskip && !dDskip) return 1;
+  set_threads(nthreads);
+  memset(dx, 0, sizeof(double) * (size_t)(Bt * L * D));
+  memset(ddelta, 0, sizeof(double) * (size_t)(Bt * L * D));
+  memset(dB, 0, sizeof(double) * (size_t)(Bt * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(Bt * L * N));
+  /* per-batch-row partial sums for the parameters shared across b */
+  double* dA_rows = (double*)calloc((size_t)(Bt * D * N) + 1, sizeof(double));
+  double* dD_rows = (double*)calloc((size_t)(Bt * D) + 1, sizeof(double));
+  if (!dA_rows || !dD_rows) { free(dA_rows); free(dD_rows); return 2; }
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bt; ++b) {
+    double* hs = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+    if (!hs) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t n = 0; n < N; ++n) {
+        double An = A[d * N + n];
+        /* forward, keeping every h_t: hs[t+1] = h_t, hs[0] = h_{-1} = 0 */
+        double v = 0.0, h = 0.0;
+        hs[0] = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+          double dt = delta[(b * L + t) * D + d];
+          double xt = x[(b * L + t) * D + d];
+          double a = exp(dt * An);
+          v = beta * v + alpha * (dt * B[(b * L + t) * N + n] * xt);
+          h = a * h + v;
+          hs[t + 1] = h;
+        }
+        /* reverse sweep */
+        double gh_next = 0.0, gv_next = 0.0, a_next = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          int64_t i = (b * L + t) * D + d;
+          int64_t j = (b * L + t) * N + n;
+          double dt = delta[i], xt = x[i], dyt = dy[i];
+          double a = exp(dt * An);
+          double gh = C[j] * dyt + a_next * gh_next;
+          double gv = gh + beta * gv_next;
+          double hprev = hs[t]; /* h_{t-1} */
+          dx[i] += alpha * dt * B[j] * gv;
+          ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gh;
+          dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh;
+          dB[j] += alpha * dt * xt * gv;
+          dC[j] += dyt * hs[t + 1];
+          gh_next = gh;
+          gv_next = gv;
+          a_next = a;
+        }
+      }
+      if (Dskip) {
+        for (int64_t t = 0; t < L; ++t) {
+          int64_t i = (b * L + t) * D + d;
+          dx[i] += Dskip[d] * dy[i];
+          dD_rows[b * D + d] += dy[i] * x[i];
+        }
+      }
+    }
+    free(hs);
+  }
+  if (failed) { free(dA_rows); free(dD_rows); return 2; }
+  for (int64_t k = 0; k < D * N; ++k) {
+    double s = 0.0;
+    for (int64_t b = 0; b < Bt; ++b) s += dA_rows[b * D * N + k];
+    dA[k] = s;
+  }
+  if (Dskip) {
+    for (int64_t d = 0; d < D; ++d) {
+      double s = 0.0;
+      for (int64_t b = 0; b < Bt; ++b) s += dD_rows[b * D + d];
+      dDskip[d] = s;
+    }
+  }
+  free(dA_rows);
+  free(dD_rows);
+  return 0;
+}

@@ -1,0 +1,387 @@
+"""Checks that pin the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees.  ``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+runs them on deliberately broken copies and expects at least one pin to fail for each.
+
+None of these checks calls the oracle's own formula a second time: they compare it with values
+printed on the pages (``tests/golden``), closed forms, a materialised matrix form, a library
+convolution / IIR filter, finite differences, or exact invariances of the recurrence.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.signal
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def num(v):
+    """Golden values are numbers or strings "lnX" meaning log(X)."""
+    if isinstance(v, str):
+        assert v.startswith("ln")
+        return math.log(float(v[2:]))
+    return float(v)
+
+
+def close(a, b, rtol=1e-12, atol=1e-12, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.abs(a - b)
+    bad = err > atol + rtol * np.abs(b)
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(err - rtol * np.abs(b)), err.shape) if err.ndim else ()
+        raise AssertionError("%s mismatch: got %r want %r (max err %.3e at %s)"
+                             % (what, a[i] if err.ndim else a, b[i] if err.ndim else b,
+                                float(err.max()), i))
+
+
+def seq(values):
+    """(L,) list -> (1, L, 1) array for a single channel."""
+    return np.asarray(values, np.float64).reshape(1, -1, 1)
+
+
+def seqn(rows):
+    """(L, N) nested list -> (1, L, N)."""
+    a = np.asarray(rows, np.float64)
+    return a.reshape(1, a.shape[0], a.shape[1])
+
+
+def run_single(orc, deltas, xs, A_row, B_rows, C_rows, beta=0.0, alpha=1.0, plain=False):
+    """One batch row, one channel: returns (y (L,), last_h (N,), last_v (N,) or None)."""
+    x = seq(xs)
+    delta = seq(deltas)
+    A = np.asarray(A_row, np.float64).reshape(1, -1)
+    B = seqn(B_rows)
+    C = seqn(C_rows)
+    if plain:
+        y, lh = orc.fwd_plain(x, delta, A, B, C)
+        return y[0, :, 0], lh[0, 0], None
+    y, lh, lv = orc.fwd(x, delta, A, B, C, beta, alpha)
+    return y[0, :, 0], lh[0, 0], lv[0, 0]
+
+
+# ---------------------------------------------------------------------------------------------
+# Worked examples printed on the pages
+# ---------------------------------------------------------------------------------------------
+
+def pin_retention_fig2(orc):
+    """A = ln 0.5: state 2 retained to 1 (Delta=1) or 0.5 (Delta=2); writes 2 and 4."""
+    g = golden("retention_fig2.json")
+    A = num(g["A"])
+    prev = g["prev_state"]
+    for plain in (False, True):
+        for case in g["retention"]:
+            # step 0 writes the previous state from zero (Delta=1, B=1, x=prev); step 1 writes
+            # nothing (B=0, x=0) so only the retained part is left.
+            y, lh, _ = run_single(orc, [1.0, case["delta"]], [prev, 0.0], [A], [[1.0], [0.0]],
+                                  [[1.0], [1.0]], plain=plain)
+            close(y[0], prev, what="primed state")
+            close(y[1], case["state"], what="Fig.2 retention")
+            close(lh[0], case["state"], what="Fig.2 last state")
+        for case in g["write"]["cases"]:
+            y, lh, _ = run_single(orc, [case["delta"]], [g["write"]["u"]], [A],
+                                  [[g["write"]["B"]]], [[1.0]], plain=plain)
+            close(lh[0], case["write"], what="Fig.2 write")
+
+
+def pin_write_ratio_fig3(orc):
+    g = golden("write_ratio_fig3.json")
+    for case in g["cases"]:
+        y, lh, lv = run_single(orc, [case["delta"]], [g["u"]], [math.log(0.5), math.log(0.8)],
+                               [g["B"]], [[1.0, 1.0]])
+        close(lh, case["write"], what="Fig.3 write ratio")
+        close(lv, case["write"], what="Fig.3 velocity equals the write at the first step")
+
+
+def pin_two_updates_fig5(orc):
+    g = golden("two_updates_fig5.json")
+    A = [num(a) for a in g["A"]]
+    for plain in (False, True):
+        for case in g["cases"]:
+            # step 0 writes the start state from zero: Delta=1, x=1, B=start_state
+            y, lh, _ = run_single(orc, [1.0, case["delta"]], [1.0, g["u"]], A,
+                                  [g["start_state"], case["B"]], [[1.0, 1.0], case["C"]],
+                                  plain=plain)
+            close(y[0], sum(g["start_state"]), what="Fig.5 primed read")
+            close(lh, case["state"], what="Fig.5 %s state" % case["name"])
+            close(y[1], case["y"], what="Fig.5 %s read" % case["name"])
+
+
+def pin_retention_gate_table(orc):
+    """Scalar ZOH gate written through the first-order recurrence with B = (1-e^-D)/D."""
+    g = golden("retention_gate_table.json")
+    A = g["A"]
+    for case in g["cases"]:
+        dlt = num(case["delta"])
+        B1 = (1.0 - math.exp(A * dlt)) / dlt
+        close(math.exp(A * dlt), case["old_weight"], what="gate old-state weight")
+        close(dlt * B1, case["input_weight"], what="gate input weight")
+        y, lh, _ = run_single(orc, [1.0, dlt], [g["prev_state"], g["held_input"]], [A],
+                              [[1.0], [B1]], [[1.0], [1.0]])
+        close(lh[0], case["state"], what="retention gate table state")
+
+
+# ---------------------------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------------------------
+
+def _const_run(orc, L, a, beta, w):
+    """Constant coefficients: delta=1, A=ln a, B=1, x=w (alpha=1), C=1 -> y_t = h_t."""
+    y, lh, lv = run_single(orc, [1.0] * L, [w] * L, [math.log(a)], [[1.0]] * L, [[1.0]] * L,
+                           beta=beta, alpha=1.0)
+    return y, lv
+
+
+def closed_form_h(t, a, beta, w):
+    if beta == 0.0:
+        return w * (1.0 - a ** (t + 1)) / (1.0 - a)
+    geo = (1.0 - a ** (t + 1)) / (1.0 - a)
+    if abs(a - beta) < 1e-15:
+        cross = (t + 1) * beta ** (t + 1)
+    else:
+        cross = beta * (a ** (t + 1) - beta ** (t + 1)) / (a - beta)
+    return w / (1.0 - beta) * (geo - cross)
+
+
+def pin_closed_form(orc):
+    # hand-computed: beta = a = 0.5, w = 2 -> h = 2, 4, 5.5
+    y, _ = _const_run(orc, 3, 0.5, 0.5, 2.0)
+    close(y, [2.0, 4.0, 5.5], what="hand-computed momentum steps")
+    for (a, beta, w) in [(0.8, 0.9, 0.3), (0.95, 0.5, -1.25), (0.6, 0.0, 0.7), (0.7, 0.7, 1.0)]:
+        L = 120
+        y, _ = _const_run(orc, L, a, beta, w)
+        want = [closed_form_h(t, a, beta, w) for t in range(L)]
+        close(y, want, rtol=1e-11, atol=1e-13, what="closed form a=%g beta=%g" % (a, beta))
+        for Lv in (1, 2, 5, 17):
+            _, lv = _const_run(orc, Lv, a, beta, w)
+            close(lv[0], w * (1.0 - beta ** Lv) / (1.0 - beta), rtol=1e-12,
+                  what="velocity geometric sum")
+
+
+# ---------------------------------------------------------------------------------------------
+# Materialised matrix form (lower-triangular L_ij of the Mamba-2 page, extended to momentum)
+# ---------------------------------------------------------------------------------------------
+
+def matrix_form_y(x, delta, A, B, C, beta, alpha, Dskip=None):
+    """y_i = sum_{m<=i} sum_n C_{i,n} K_{i,m,n} w_{m,n} + Dskip x_i, with
+    K_{i,m,n} = sum_{j=m..i} (prod_{k=j+1..i} a_{k,n}) beta^(j-m) and w = alpha delta B x.
+    For beta = 0 only j = m survives: K = prod_{k=m+1..i} a_k (the semiseparable L_ij)."""
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    y = np.zeros((Bt, L, D))
+    for b in range(Bt):
+        for d in range(D):
+            a = np.exp(delta[b, :, d, None] * A[d][None, :])
+            w = alpha * delta[b, :, d, None] * B[b] * x[b, :, d, None]
+            for i in range(L):
+                acc = 0.0
+                for m in range(i + 1):
+                    K = np.zeros(N)
+                    for j in range(m, i + 1):
+                        K += np.prod(a[j + 1:i + 1], axis=0) * beta ** (j - m)
+                    acc += float(np.sum(C[b, i] * K * w[m]))
+                y[b, i, d] = acc + (0.0 if Dskip is None else Dskip[d] * x[b, i, d])
+    return y
+
+
+def semiseparable_y(x, delta, A, B, C):
+    """beta = 0 reading straight from L_ij = C_i^T (A_i ... A_{j+1}) Bbar_j, y = L x."""
+    Bt, L, D = x.shape
+    y = np.zeros((Bt, L, D))
+    for b in range(Bt):
+        for d in range(D):
+            Abar = np.exp(delta[b, :, d, None] * A[d][None, :])        # (L, N)
+            Bbar = delta[b, :, d, None] * B[b]                         # (L, N)
+            Lmat = np.zeros((L, L))
+            for i in range(L):
+                for j in range(i + 1):
+                    Lmat[i, j] = np.sum(C[b, i] * np.prod(Abar[j + 1:i + 1], axis=0) * Bbar[j])
+            y[b, :, d] = Lmat @ x[b, :, d]
+    return y
+
+
+def _rand_problem(rng, Bt, L, D, N, dskip):
+    x = rng.standard_normal((Bt, L, D))
+    delta = np.exp(rng.uniform(np.log(1e-2), np.log(0.5), size=(Bt, L, D)))
+    A = -np.exp(rng.uniform(np.log(0.3), np.log(3.0), size=(D, N)))
+    B = rng.standard_normal((Bt, L, N))
+    C = rng.standard_normal((Bt, L, N))
+    Ds = rng.standard_normal(D) if dskip else None
+    return x, delta, A, B, C, Ds
+
+
+def pin_matrix_form(orc):
+    rng = np.random.default_rng(7)
+    x, delta, A, B, C, Ds = _rand_problem(rng, 2, 12, 3, 3, True)
+    y0, _, _ = orc.fwd(x, delta, A, B, C, 0.0, 1.0)
+    close(y0, semiseparable_y(x, delta, A, B, C), rtol=1e-11, atol=1e-12,
+          what="beta=0 semiseparable matrix form")
+    for beta, alpha in [(0.9, 1.0), (0.5, 0.7), (0.99, 2.0)]:
+        y, _, _ = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds)
+        close(y, matrix_form_y(x, delta, A, B, C, beta, alpha, Ds), rtol=1e-11, atol=1e-12,
+              what="momentum matrix form beta=%g" % beta)
+
+
+# ---------------------------------------------------------------------------------------------
+# Time-invariant special case: convolution / IIR filter (library routines)
+# ---------------------------------------------------------------------------------------------
+
+def pin_convolution(orc):
+    rng = np.random.default_rng(11)
+    L, N = 50, 3
+    xs = rng.standard_normal(L)
+    dlt = 0.3
+    A = np.array([-0.5, -1.3, -2.2])
+    Bv = rng.standard_normal(N)
+    Cv = rng.standard_normal(N)
+    for beta, alpha in [(0.0, 1.0), (0.8, 0.6)]:
+        a = np.exp(dlt * A)
+        K = np.zeros(L)
+        for l in range(L):
+            inner = sum(a ** (l - j) * beta ** j for j in range(l + 1))
+            K[l] = np.sum(Cv * alpha * dlt * Bv * inner)
+        want = np.convolve(xs, K)[:L]
+        y, _, _ = orc.fwd(xs.reshape(1, L, 1), np.full((1, L, 1), dlt), A.reshape(1, N),
+                          np.tile(Bv, (1, L, 1)), np.tile(Cv, (1, L, 1)), beta, alpha)
+        close(y[0, :, 0], want, rtol=1e-11, atol=1e-12, what="LTI convolution beta=%g" % beta)
+    # A = 0 (no decay): beta = 0 gives a running sum; beta > 0 gives an IIR-filtered velocity
+    # integrated by the running sum.
+    dl = np.exp(rng.uniform(-3, -1, size=L))
+    Bs = rng.standard_normal((L, 1))
+    wseq = 0.4 * dl * Bs[:, 0] * xs
+    for beta in (0.0, 0.7):
+        v = scipy.signal.lfilter([1.0], [1.0, -beta], wseq)
+        want = np.cumsum(v)
+        y, lh, lv = orc.fwd(xs.reshape(1, L, 1), dl.reshape(1, L, 1), np.zeros((1, 1)),
+                            Bs.reshape(1, L, 1), np.ones((1, L, 1)), beta, 0.4)
+        close(y[0, :, 0], want, rtol=1e-12, atol=1e-13, what="A=0 filter beta=%g" % beta)
+        close(lv[0, 0, 0], v[-1], rtol=1e-12, atol=1e-13, what="A=0 last velocity")
+
+
+# ---------------------------------------------------------------------------------------------
+# beta = 0 reduces to the standard recurrence
+# ---------------------------------------------------------------------------------------------
+
+def pin_beta0_equivalence(orc):
+    rng = np.random.default_rng(3)
+    x, delta, A, B, C, Ds = _rand_problem(rng, 2, 40, 5, 4, True)
+    y, lh, lv = orc.fwd(x, delta, A, B, C, 0.0, 1.0, Dskip=Ds)
+    yp, lhp = orc.fwd_plain(x, delta, A, B, C, Dskip=Ds)
+    assert np.array_equal(y, yp), "beta=0, alpha=1 must equal the standard recurrence bitwise"
+    assert np.array_equal(lh, lhp)
+    # with beta = 0 the velocity is just the last write alpha*delta*B*x
+    close(lv, 1.0 * delta[:, -1, :, None] * B[:, -1, None, :] * x[:, -1, :, None], rtol=1e-15,
+          what="beta=0 velocity")
+
+
+# ---------------------------------------------------------------------------------------------
+# Structure: linearity, causality, alpha-homogeneity
+# ---------------------------------------------------------------------------------------------
+
+def pin_structure(orc):
+    rng = np.random.default_rng(5)
+    x, delta, A, B, C, Ds = _rand_problem(rng, 2, 30, 4, 3, True)
+    x2 = rng.standard_normal(x.shape)
+    beta, alpha = 0.85, 1.3
+    y1, _, _ = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds)
+    y2, _, _ = orc.fwd(x2, delta, A, B, C, beta, alpha, Dskip=Ds)
+    y12, _, _ = orc.fwd(x + x2, delta, A, B, C, beta, alpha, Dskip=Ds)
+    close(y12, y1 + y2, rtol=1e-11, atol=1e-12, what="linearity in x")
+    # causality: a change at t' leaves every earlier output bitwise unchanged
+    tp = 17
+    xp = x.copy()
+    xp[:, tp, :] += 1.0
+    yp, _, _ = orc.fwd(xp, delta, A, B, C, beta, alpha, Dskip=Ds)
+    assert np.array_equal(yp[:, :tp], y1[:, :tp]), "causality"
+    assert not np.allclose(yp[:, tp:], y1[:, tp:]), "a change must reach later outputs"
+    # alpha enters only the write: y(alpha) - Dx = alpha * (y(1) - Dx)
+    ya, _, _ = orc.fwd(x, delta, A, B, C, beta, 1.0, Dskip=Ds)
+    close(y1 - Ds * x, alpha * (ya - Ds * x), rtol=1e-11, atol=1e-12, what="alpha homogeneity")
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward: central finite differences and scaling identities
+# ---------------------------------------------------------------------------------------------
+
+def _loss(orc, p, dy, beta, alpha):
+    y, _, _ = orc.fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], beta, alpha, Dskip=p["Dskip"])
+    return float(np.sum(dy * y))
+
+
+def pin_finite_differences(orc, shape=(2, 7, 3, 2), beta=0.9, alpha=0.7, dskip=True, seed=13,
+                           max_per_input=None):
+    rng = np.random.default_rng(seed)
+    Bt, L, D, N = shape
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, dskip)
+    dy = rng.standard_normal((Bt, L, D))
+    p = dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Ds)
+    g = orc.bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds)
+    names = [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC")]
+    if dskip:
+        names.append(("Dskip", "dDskip"))
+    eps = 1e-6
+    for pname, gname in names:
+        arr = p[pname]
+        idx = list(np.ndindex(arr.shape))
+        if max_per_input is not None and len(idx) > max_per_input:
+            sel = rng.choice(len(idx), max_per_input, replace=False)
+            idx = [idx[i] for i in sel]
+        for i in idx:
+            orig = arr[i]
+            arr[i] = orig + eps
+            lp = _loss(orc, p, dy, beta, alpha)
+            arr[i] = orig - eps
+            lm = _loss(orc, p, dy, beta, alpha)
+            arr[i] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname][i]
+            if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                raise AssertionError("finite difference mismatch for %s%s: fd %.9g analytic %.9g"
+                                     % (gname, i, fd, an))
+
+
+def pin_scaling_identities(orc):
+    rng = np.random.default_rng(17)
+    x, delta, A, B, C, Ds = _rand_problem(rng, 2, 48, 5, 3, True)
+    dy = rng.standard_normal(x.shape)
+    beta, alpha = 0.9, 0.8
+    y, _, _ = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds)
+    g = orc.bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds)
+    lp = float(np.sum(dy * (y - Ds * x)))            # loss without the skip term
+    ip = lambda a, b: float(np.sum(a * b))
+    close(ip(g["dx"] - Ds * dy, x), lp, rtol=1e-10, what="<dx - D dy, x>")
+    close(ip(g["dB"], B), lp, rtol=1e-10, what="<dB, B>")
+    close(ip(g["dC"], C), lp, rtol=1e-10, what="<dC, C>")
+    close(ip(g["ddelta"], delta) - ip(g["dA"], A), lp, rtol=1e-10, what="<ddelta,delta>-<dA,A>")
+    close(ip(g["dx"], x), float(np.sum(dy * y)), rtol=1e-10, what="<dx, x>")
+    close(ip(g["dDskip"], Ds), float(np.sum(dy * Ds * x)), rtol=1e-12, what="<dDskip, Dskip>")
+
+
+def pin_bwd_beta0_alpha0(orc):
+    """alpha = 0 writes nothing: the state stays zero, y is the skip term, and every gradient
+    except dx (= Dskip * dy) is zero."""
+    rng = np.random.default_rng(19)
+    x, delta, A, B, C, Ds = _rand_problem(rng, 1, 9, 2, 2, True)
+    dy = rng.standard_normal(x.shape)
+    y, lh, lv = orc.fwd(x, delta, A, B, C, 0.5, 0.0, Dskip=Ds)
+    close(y, Ds * x, rtol=0, atol=0, what="alpha=0 output")
+    g = orc.bwd(x, delta, A, B, C, dy, 0.5, 0.0, Dskip=Ds)
+    for k in ("ddelta", "dA", "dB", "dC"):
+        close(g[k], 0.0, rtol=0, atol=0, what="alpha=0 %s" % k)
+    close(g["dx"], Ds * dy, rtol=1e-15, atol=0, what="alpha=0 dx")
+
+
+ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
+            pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
+            pin_beta0_equivalence, pin_structure, pin_finite_differences,
+            pin_scaling_identities, pin_bwd_beta0_alpha0]

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in copies of the C oracle (on the CPU) and check the pins catch each.
+
+Every mutant is one textual change to ``oracle/msm_oracle.c`` -- a dropped term, a wrong sign,
+an off-by-one index, a swapped adjoint -- compiled with the oracle's own flags into a temporary
+directory.  A mutant that passes every pin would mean the pins cannot tell it from the oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+# (name, original text, replacement, occurrence index to replace (0 = first))
+MUTANTS = [
+    ("fwd_velocity_reads_h", "v = beta * v + w;", "v = beta * h + w;", 0),
+    ("fwd_h_skips_velocity", "h = a * h + v;", "h = a * h + w;", 0),
+    ("fwd_exp_sign", "double a = exp(dt * A[d * N + n]);", "double a = exp(-dt * A[d * N + n]);", 0),
+    ("fwd_write_drops_delta", "double w = alpha * (dt * B[(b * L + t) * N + n] * xt);",
+     "double w = alpha * (B[(b * L + t) * N + n] * xt);", 0),
+    ("fwd_reads_velocity", "y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * h;",
+     "y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * v;", 0),
+    ("fwd_skip_uses_delta",
+     "y[(b * L + t) * D + d] += Dskip[d] * x[(b * L + t) * D + d];",
+     "y[(b * L + t) * D + d] += Dskip[d] * delta[(b * L + t) * D + d];", 0),
+    ("fwd_alpha_scales_velocity", "v = beta * v + w;", "v = alpha * beta * v + w;", 0),
+    ("plain_write_drops_delta",
+     "h = exp(dt * A[d * N + n]) * h + dt * B[(b * L + t) * N + n] * xt;",
+     "h = exp(dt * A[d * N + n]) * h + B[(b * L + t) * N + n] * xt;", 0),
+    ("bwd_velocity_adjoint_pure_decay", "double gv = gh + beta * gv_next;",
+     "double gv = C[j] * dyt + beta * gv_next;", 0),
+    ("bwd_exp_path_uses_gv", "ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gh;",
+     "ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gv;", 0),
+    ("bwd_dC_off_by_one", "dC[j] += dyt * hs[t + 1];", "dC[j] += dyt * hs[t];", 0),
+    ("bwd_hprev_off_by_one", "double hprev = hs[t];", "double hprev = hs[t + 1];", 0),
+    ("bwd_dA_drops_a", "dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh;",
+     "dA_rows[(b * D + d) * N + n] += dt * hprev * gh;", 0),
+    ("bwd_gh_uses_a_t", "double gh = C[j] * dyt + a_next * gh_next;",
+     "double gh = C[j] * dyt + a * gh_next;", 0),
+    ("bwd_skip_dx_uses_x", "dx[i] += Dskip[d] * dy[i];", "dx[i] += Dskip[d] * x[i];", 0),
+    ("bwd_dB_uses_gh", "dB[j] += alpha * dt * xt * gv;", "dB[j] += alpha * dt * xt * gh;", 0),
+    ("bwd_dx_drops_alpha", "dx[i] += alpha * dt * B[j] * gv;", "dx[i] += dt * B[j] * gv;", 0),
+    ("bwd_dDskip_uses_y", "dD_rows[b * D + d] += dy[i] * x[i];", "dD_rows[b * D + d] += dy[i];", 0),
+]
+
+
+def _mutate(src, old, new, occ):
+    pos = -1
+    for _ in range(occ + 1):
+        pos = src.find(old, pos + 1)
+        assert pos >= 0, "mutation site not found: %r" % old
+    return src[:pos] + new + src[pos + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new, occ):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    mutated = _mutate(src, old, new, occ)
+    assert mutated != src
+    cpath = os.path.join(str(tmp_path), "mutant_%s.c" % name)
+    with open(cpath, "w") as f:
+        f.write(mutated)
+    so = oracle.compile_source(cpath, os.path.join(str(tmp_path), "libmutant_%s.so" % name))
+    orc = oracle.Oracle(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError as e:
+            caught.append((pin.__name__, str(e)[:120]))
+    assert caught, "no pin caught mutant %s" % name
