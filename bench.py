@@ -1,0 +1,291 @@
+"""Benchmark of the Momentum-Mamba selective scan on one MI355X.
+
+One step = one msm_scan_fwd call over the Mamba-1.4B layer shape (Bt=4, L=4096, D=4096, N=16,
+bf16 I/O with fp32 state, beta=0.9, alpha=1) with inputs already resident in HBM.  The line
+also reports the backward on its own workload (Bt=4, L=2048, D=2048, N=16, fp32) timed the
+same way, the ALU roofline of the forward's single kernel, the algorithmic HBM rate, and the
+fp64 oracle timed on the host cores on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload m1p4b] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "fwd/bwd selective-scan state-updates/sec (Bt·L·D·N) + achieved HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+# VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (packed FP32 is not used)
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Issue slots the recurrence needs per state update: exp2 (v_exp_f32, half rate: 2 slots) plus
+# delta*A, the write c*B, the velocity FMA, the hidden-state FMA and the readout FMA; the
+# velocity FMA disappears when beta = 0.
+SLOTS_PER_UPDATE = {True: 6, False: 7}
+
+
+def alg_bytes_fwd(w: workloads.Workload, last_state: bool = False) -> int:
+    s = 2 if w.io == "bf16" else 4
+    b = w.Bt * w.L * (3 * w.D * s + 2 * w.N * s) + 4 * w.D * w.N
+    if w.dskip:
+        b += 4 * w.D
+    if last_state:
+        b += 8 * w.Bt * w.D * w.N
+    return b
+
+
+def alg_bytes_bwd(w: workloads.Workload) -> int:
+    s = 2 if w.io == "bf16" else 4
+    b = w.Bt * w.L * (5 * w.D * s + 4 * w.N * s) + 8 * w.D * w.N
+    if w.dskip:
+        b += 8 * w.D
+    return b
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_msm_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from the committed rocprof counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed(fn, stream, steps, warmup):
+    """Run fn warmup times, then time `steps` calls with HIP events on `stream`.  Returns the
+    mean duration per call in ms and the list of per-call durations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(steps):
+            fn()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total = evs[0].elapsed_time(evs[-1])
+    return total / steps, per
+
+
+def to_dev(inp):
+    import torch
+    dt = torch.float32 if inp["io"] == "f32" else torch.bfloat16
+    d = {}
+    for k in ("x", "delta", "B", "C", "dy"):
+        if inp.get(k) is not None:
+            d[k] = torch.from_numpy(inp[k]).to("cuda").to(dt)
+    d["A"] = torch.from_numpy(inp["A"]).to("cuda")
+    d["Dskip"] = None if inp["Dskip"] is None else torch.from_numpy(inp["Dskip"]).to("cuda")
+    return d
+
+
+def bench_fwd(w, steps, warmup, stream):
+    import torch
+    import selective_state_space_msm_amd as msm
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp)
+    y = torch.empty_like(g["x"])
+    nbytes = msm.msm_scan_fwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    plan = msm.msm_scan_fwd_plan(w.Bt, w.L, w.D, w.N, w.io, w.beta)
+
+    def step():
+        msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta, w.alpha, g["Dskip"],
+                         y=y, workspace=ws, stream=stream)
+
+    ms, per = timed(step, stream, steps, warmup)
+    return ms, per, plan
+
+
+def bench_bwd(w, steps, warmup, stream):
+    import torch
+    import selective_state_space_msm_amd as msm
+    inp = workloads.make_inputs(w)
+    g = to_dev(inp)
+    nbytes = msm.msm_scan_bwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    out = {"dx": torch.empty_like(g["x"]), "ddelta": torch.empty_like(g["x"]),
+           "dA": torch.empty_like(g["A"]), "dB": torch.empty_like(g["B"]),
+           "dC": torch.empty_like(g["C"])}
+    plan = msm.msm_scan_bwd_plan(w.Bt, w.L, w.D, w.N, w.io, w.beta)
+
+    def step():
+        msm.msm_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], w.beta, w.alpha,
+                         g["Dskip"], out=out, workspace=ws, stream=stream)
+
+    ms, per = timed(step, stream, steps, warmup)
+    return ms, per, plan
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded slice of the workload: every batch row and
+    every step of a block of channels sized for roughly target_s seconds on the host cores."""
+    import oracle
+    threads = oracle.max_threads()
+    inp = workloads.make_inputs(w.replace(D=64, L=min(w.L, 1024)), seed=w.seed + 7)
+    t0 = time.perf_counter()
+    oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], w.beta, w.alpha,
+               Dskip=inp["Dskip"], threads=threads)
+    probe_rate = w.Bt * inp["x"].shape[1] * 64 * w.N / (time.perf_counter() - t0)
+    # channels so that the timed sample takes about target_s
+    dsel = int(max(threads, min(w.D, target_s * probe_rate / (w.Bt * w.L * w.N))))
+    sw = w.replace(D=dsel)
+    inp = workloads.make_inputs(sw, seed=w.seed + 8)
+    t0 = time.perf_counter()
+    oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], w.beta, w.alpha,
+               Dskip=inp["Dskip"], threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": sw.updates / dt, "unit": "state-updates/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 C oracle forward, Bt=%d L=%d N=%d over %d of the %d channels "
+                      "(%.3g state updates in %.1f s, OpenMP over channels)"
+                      % (sw.Bt, sw.L, sw.N, dsel, w.D, sw.updates, dt)}
+
+
+def pmc_summary(fetch_csv, write_csv, kernel_substr, name, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --calib-copy` into profiles/traffic_<name>.json.  Each counter is scaled by what
+    it reads for the plain 256 MiB device copy of the same run (known bytes / counter)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if kernel_substr in r["Kernel_Name"]:
+                vals.append(v)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+        return vals, copy
+
+    fk, fcopy = per_kernel(fetch_csv, "FETCH_SIZE")
+    wk, wcopy = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = (256 << 20) / 1024.0
+    fscale = copy_kib / (sum(fcopy) / len(fcopy))
+    wscale = copy_kib / (sum(wcopy) / len(wcopy))
+    fetch = sum(fk) / len(fk) * fscale * 1024
+    write = sum(wk) / len(wk) * wscale * 1024
+    rec = {"kernel": kernel_substr, "source_hash": source_hash(),
+           "fetch_KiB_per_dispatch": sum(fk) / len(fk), "write_KiB_per_dispatch": sum(wk) / len(wk),
+           "fetch_scale": fscale, "write_scale": wscale, "hbm_bytes_per_launch": fetch + write,
+           "dispatches": [len(fk), len(wk)], "command": command}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % name), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="m1p4b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--bwd-workload", default="bwd", choices=sorted(workloads.WORKLOADS) + ["none"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "NAME",
+                                                       "COMMAND"),
+                    help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
+    args = ap.parse_args(argv)
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(*args.pmc_summary), indent=1))
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stream = torch.cuda.current_stream()
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.direction != "fwd":
+        raise SystemExit("--workload must be a forward workload")
+    ms, per, plan = bench_fwd(w, args.steps, args.warmup, stream)
+    sec = ms / 1e3
+    beta0 = w.beta == 0.0
+    slots = w.updates * SLOTS_PER_UPDATE[beta0]
+    achieved_slots = slots / sec / 1e12
+    abytes = alg_bytes_fwd(w)
+    kname = "fwd_%s" % w.name
+    rec = {
+        "metric": METRIC,
+        "value": w.updates / sec,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; distributions of the workload recipe)",
+        "config": {"workload": "%s: forward scan, Mamba-1.4B layer shape" % w.name if w.name == "m1p4b"
+                   else "%s: forward scan" % w.name,
+                   "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io, "beta": w.beta,
+                   "alpha": w.alpha, "dskip": w.dskip, "plan": plan},
+        "roofline": {"bound": "alu", "achieved": achieved_slots, "peak": VALU_PEAK_TSLOTS,
+                     "unit": "T VALU slots/s", "frac": achieved_slots / VALU_PEAK_TSLOTS,
+                     "traffic": measured_traffic(kname),
+                     "slots_per_update": SLOTS_PER_UPDATE[beta0],
+                     "kernel_ms_mean": ms, "kernel_ms_min": min(per)},
+        "hbm": {"algorithmic_bytes": abytes, "achieved_GBs": abytes / sec / 1e9,
+                "peak_GBs": HBM_PEAK_GBS, "frac": abytes / sec / 1e9 / HBM_PEAK_GBS},
+    }
+    if args.bwd_workload != "none":
+        wb = workloads.WORKLOADS[args.bwd_workload]
+        bms, bper, bplan = bench_bwd(wb, max(3, args.steps // 2), max(1, args.warmup // 2), stream)
+        bbytes = alg_bytes_bwd(wb)
+        rec["bwd"] = {"workload": "%s: backward, Bt=%d L=%d D=%d N=%d io=%s beta=%g"
+                                  % (wb.name, wb.Bt, wb.L, wb.D, wb.N, wb.io, wb.beta),
+                      "ms_per_call": bms, "state_updates_per_s": wb.updates / (bms / 1e3),
+                      "algorithmic_GBs": bbytes / (bms / 1e3) / 1e9,
+                      "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": bplan}
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["calib_copy_bytes"] = 2 * src.numel()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,130 @@
+/*
+ * msm.h -- C ABI of the Momentum-Mamba selective scan for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Momentum Mamba README, "Momentum Mamba Recurrence"; its plain-Mamba special
+ * case beta = 0, alpha = 1 is "Standard Mamba Recurrence" on the same page).  For every batch
+ * row b, channel d and state n, starting from v = h = 0:
+ *
+ *     a_t = exp(delta[b,t,d] * A[d,n])                               (exact Abar, first-order Bbar:
+ *     v_t = beta * v_{t-1} + alpha * delta[b,t,d] * B[b,t,n] * x[b,t,d]   "Discretization Note")
+ *     h_t = a_t * h_{t-1} + v_t
+ *     y[b,t,d] = sum_n C[b,t,n] * h_t  (+ Dskip[d] * x[b,t,d] when Dskip is given)
+ *
+ * B and C carry N values per position shared by all channels, delta one value per channel and
+ * A one value per (channel, state) -- the selection layout of "Mamba: Choosing What to Remember
+ * Based on the Input", section "From input features to update coefficients".  The skip term is
+ * the per-channel D weight of the Mamba block ("Where the state computation sits in a Mamba
+ * block" on the same page); alpha does not scale it.
+ *
+ * The backward returns the gradients of sum(dy * y) with respect to every input (README,
+ * "Gradient Flow" / "Gradient Formulas"; the velocity adjoint also receives the hidden-state
+ * adjoint because v_t enters h_t directly).  dB, dC sum over channels, dA over batch and time.
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE pointers to contiguous row-major buffers owned by the
+ *     caller.  The library allocates no memory and keeps no mutable global state.
+ *   - Shapes: x, delta, y, dy, dx, ddelta: (Bt, L, D).  A, dA: (D, N) fp32.
+ *             B, C, dB, dC: (Bt, L, N).  Dskip, dDskip: (D,) fp32.  last_h, last_v: (Bt, D, N) fp32.
+ *   - io selects the element type of x, delta, B, C, y, dy, dx, ddelta, dB, dC:
+ *     MSM_F32 (IEEE binary32) or MSM_BF16 (bfloat16, outputs rounded to nearest even).
+ *     A, Dskip, dA, dDskip, last_h, last_v are always fp32.  All arithmetic and every state
+ *     is fp32 inside the kernels.  A is in natural-log units (the kernels rescale it to base 2).
+ *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued asynchronously; the
+ *     function returns once it is enqueued.
+ *   - workspace is caller-owned device scratch of at least the size returned by the matching
+ *     *_workspace_bytes query for the same shape and io (may be NULL when that size is 0).
+ *     Its contents on entry do not matter and are undefined on exit.  Two calls in flight at
+ *     the same time must not share a workspace.
+ *   - Argument errors are detected before anything is enqueued and reported as a status; no
+ *     exception crosses the ABI and nothing is printed.  A launch failure reported by the HIP
+ *     runtime is returned as MSM_ERR_LAUNCH.  Non-finite inputs are not checked: NaN/Inf
+ *     propagate to the outputs.
+ */
+#ifndef MSM_H_
+#define MSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSM_OK = 0,
+  MSM_ERR_INVALID_ARG = 1, /* null required pointer, bad size, beta outside [0,1), alpha not
+                              finite or negative, an output overlapping an input */
+  MSM_ERR_UNSUPPORTED = 2, /* valid by the method but outside this build (N > 64, io value) */
+  MSM_ERR_WORKSPACE = 3,   /* workspace smaller than the query result */
+  MSM_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch */
+} msm_status;
+
+typedef enum { MSM_F32 = 0, MSM_BF16 = 1 } msm_dtype;
+
+/* Optional launch plan.  0 in a field means "choose automatically".
+ *   states_per_wave : 1, 2, 4, 8 or 16 -- how many of the N states one 64-lane wavefront keeps
+ *                     in registers (a workgroup holds ceil(N / states_per_wave) wavefronts).
+ *   chunks          : number of time chunks the sequence is cut into (1..64); chunks > 1 adds
+ *                     a pass that summarises each chunk as an affine map of its start state.
+ * A plan never changes results beyond fp32 rounding order. */
+typedef struct {
+  int32_t states_per_wave;
+  int32_t chunks;
+} msm_plan;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t msm_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* msm_status_string(msm_status s);
+
+/* Workspace sizes in bytes.  Valid for every plan the library may choose (automatic or
+ * explicit).  Return 0 for invalid sizes. */
+size_t msm_scan_fwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io);
+size_t msm_scan_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io);
+
+/* The plan msm_scan_fwd / msm_scan_bwd would use for this shape (written to *plan). */
+msm_status msm_scan_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
+                             float beta, msm_plan* plan);
+msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
+                             float beta, msm_plan* plan);
+
+/* Forward scan.  y is overwritten.  last_h / last_v (the states after the final step) are
+ * written when non-NULL.  Dskip may be NULL.  Requirements: Bt, L, D >= 1; 1 <= N <= 64;
+ * 0 <= beta < 1; alpha finite and >= 0.  Outputs must not overlap any input. */
+msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* Dskip, void* y, float* last_h,
+                        float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                        float alpha, msm_dtype io, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Forward scan with an explicit plan (NULL plan = automatic, identical to msm_scan_fwd). */
+msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, void* y,
+                                  float* last_h, float* last_v, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan);
+
+/* Backward scan: gradients of sum(dy * y).  dx, ddelta, dB, dC, dA are overwritten (not
+ * accumulated).  dDskip is required exactly when Dskip is non-NULL.  The forward is recomputed
+ * inside; no saved activations are needed.  Same requirements as msm_scan_fwd. */
+msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* Dskip, const void* dy, void* dx,
+                        void* ddelta, float* dA, void* dB, void* dC, float* dDskip, int64_t Bt,
+                        int64_t L, int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip,
+                                  const void* dy, void* dx, void* ddelta, float* dA, void* dB,
+                                  void* dC, float* dDskip, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSM_H_ */

@@ -1,0 +1,269 @@
+"""Momentum-Mamba selective scan on AMD MI355X (gfx950): thin Python binding of libmsm.so.
+
+The functions here have the names of the C entry points declared in ``include/msm.h`` and do
+argument marshalling only: every step of the scan runs in the library's HIP kernels.  PyTorch
+provides device memory and the current HIP stream.  If ``libmsm.so`` has not been built (see
+``selective_state_space_msm_amd.build``) every call raises ``MsmLibraryMissing``; there is no
+fallback implementation.
+
+    y = msm_scan_fwd(x, delta, A, B, C, beta=0.9, alpha=1.0)             # (Bt, L, D)
+    y, last_h, last_v = msm_scan_fwd(..., return_last_state=True)
+    grads = msm_scan_bwd(x, delta, A, B, C, dy, beta=0.9, alpha=1.0)     # dict of tensors
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MsmError", "MsmLibraryMissing", "MSM_F32", "MSM_BF16", "library_path", "load_library",
+    "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
+    "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
+    "msm_scan_bwd", "EXPORTED_SYMBOLS",
+]
+
+MSM_F32 = 0
+MSM_BF16 = 1
+_STATUS = {0: "MSM_OK", 1: "MSM_ERR_INVALID_ARG", 2: "MSM_ERR_UNSUPPORTED",
+           3: "MSM_ERR_WORKSPACE", 4: "MSM_ERR_LAUNCH"}
+EXPORTED_SYMBOLS = [
+    "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
+    "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
+    "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmsm.so")
+_lib = None
+
+
+class MsmError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s" % (what, _STATUS.get(status, "status %d" % status)))
+
+
+class MsmLibraryMissing(RuntimeError):
+    pass
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("states_per_wave", ctypes.c_int32), ("chunks", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmsm.so (once).  Raises MsmLibraryMissing when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MsmLibraryMissing(
+            "libmsm.so not found at %s; build it with `python -m selective_state_space_msm_amd.build`"
+            " (or __graft_entry__.build())" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, F, I32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                          ctypes.c_size_t)
+    lib.msm_version.argtypes = []
+    lib.msm_version.restype = I32
+    lib.msm_status_string.argtypes = [ctypes.c_int]
+    lib.msm_status_string.restype = ctypes.c_char_p
+    for name in ("msm_scan_fwd_workspace_bytes", "msm_scan_bwd_workspace_bytes"):
+        fn = getattr(lib, name)
+        fn.argtypes = [I64, I64, I64, I64, ctypes.c_int]
+        fn.restype = SZ
+    for name in ("msm_scan_fwd_plan", "msm_scan_bwd_plan"):
+        fn = getattr(lib, name)
+        fn.argtypes = [I64, I64, I64, I64, ctypes.c_int, F, ctypes.POINTER(_Plan)]
+        fn.restype = ctypes.c_int
+    fwd = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P]
+    lib.msm_scan_fwd.argtypes = fwd
+    lib.msm_scan_fwd.restype = ctypes.c_int
+    lib.msm_scan_fwd_with_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
+    lib.msm_scan_fwd_with_plan.restype = ctypes.c_int
+    bwd = [P, P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P]
+    lib.msm_scan_bwd.argtypes = bwd
+    lib.msm_scan_bwd.restype = ctypes.c_int
+    lib.msm_scan_bwd_with_plan.argtypes = bwd + [ctypes.POINTER(_Plan)]
+    lib.msm_scan_bwd_with_plan.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def msm_version() -> int:
+    return int(load_library().msm_version())
+
+
+def msm_status_string(status: int) -> str:
+    return load_library().msm_status_string(int(status)).decode()
+
+
+def _io_code(io) -> int:
+    if io in (MSM_F32, "f32", "fp32", "float32"):
+        return MSM_F32
+    if io in (MSM_BF16, "bf16", "bfloat16"):
+        return MSM_BF16
+    import torch
+    if io == torch.float32:
+        return MSM_F32
+    if io == torch.bfloat16:
+        return MSM_BF16
+    raise ValueError("unsupported io dtype %r" % (io,))
+
+
+def msm_scan_fwd_workspace_bytes(Bt, L, D, N, io) -> int:
+    return int(load_library().msm_scan_fwd_workspace_bytes(Bt, L, D, N, _io_code(io)))
+
+
+def msm_scan_bwd_workspace_bytes(Bt, L, D, N, io) -> int:
+    return int(load_library().msm_scan_bwd_workspace_bytes(Bt, L, D, N, _io_code(io)))
+
+
+def _plan_call(fn, Bt, L, D, N, io, beta):
+    pl = _Plan()
+    st = fn(Bt, L, D, N, _io_code(io), float(beta), ctypes.byref(pl))
+    if st != 0:
+        raise MsmError(st, fn.__name__)
+    return {"states_per_wave": pl.states_per_wave, "chunks": pl.chunks}
+
+
+def msm_scan_fwd_plan(Bt, L, D, N, io, beta) -> dict:
+    return _plan_call(load_library().msm_scan_fwd_plan, Bt, L, D, N, io, beta)
+
+
+def msm_scan_bwd_plan(Bt, L, D, N, io, beta) -> dict:
+    return _plan_call(load_library().msm_scan_bwd_plan, Bt, L, D, N, io, beta)
+
+
+# ----------------------------------------------------------------------------------------------
+# tensor marshalling
+# ----------------------------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, workspace, device):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise MsmError(3, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _plan_arg(plan):
+    if plan is None:
+        return None
+    return ctypes.byref(_Plan(int(plan.get("states_per_wave", 0)), int(plan.get("chunks", 0))))
+
+
+def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=None,
+                 last_v=None, return_last_state=False, workspace=None, stream=None, plan=None):
+    """Forward scan.  x, delta: (Bt, L, D); A: (D, N) fp32; B, C: (Bt, L, N); Dskip: (D,) fp32.
+
+    x, delta, B, C share one dtype (float32 or bfloat16), which is also the dtype of y.
+    Returns y, or (y, last_h, last_v) when return_last_state is true.
+    """
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    _check(x, "x", (Bt, L, D), x.dtype, dev)
+    _check(delta, "delta", (Bt, L, D), x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(B, "B", (Bt, L, N), x.dtype, dev)
+    _check(C, "C", (Bt, L, N), x.dtype, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+    _check(y, "y", (Bt, L, D), x.dtype, dev)
+    if return_last_state:
+        if last_h is None:
+            last_h = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+        if last_v is None:
+            last_v = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+    for t, nm in ((last_h, "last_h"), (last_v, "last_v")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N), torch.float32, dev)
+    nbytes = int(lib.msm_scan_fwd_workspace_bytes(Bt, L, D, N, io))
+    ws, wsb = _workspace(nbytes, workspace, dev)
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(y), _ptr(last_h),
+            _ptr(last_v), Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb,
+            _stream_handle(stream, dev))
+    if plan is None:
+        st = lib.msm_scan_fwd(*args)
+    else:
+        st = lib.msm_scan_fwd_with_plan(*args, _plan_arg(plan))
+    if st != 0:
+        raise MsmError(st, "msm_scan_fwd")
+    if return_last_state:
+        return y, last_h, last_v
+    return y
+
+
+def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, workspace=None,
+                 stream=None, plan=None):
+    """Gradients of sum(dy * y).  Returns a dict: dx, ddelta (Bt, L, D) and dB, dC (Bt, L, N)
+    in the I/O dtype; dA (D, N) and dDskip (D,) (None without Dskip) in float32."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for t, nm, shp in ((x, "x", (Bt, L, D)), (delta, "delta", (Bt, L, D)), (B, "B", (Bt, L, N)),
+                       (C, "C", (Bt, L, N)), (dy, "dy", (Bt, L, D))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty((Bt, L, D), dtype=x.dtype, device=dev))
+    o.setdefault("ddelta", torch.empty((Bt, L, D), dtype=x.dtype, device=dev))
+    o.setdefault("dA", torch.empty((D, N), dtype=torch.float32, device=dev))
+    o.setdefault("dB", torch.empty((Bt, L, N), dtype=x.dtype, device=dev))
+    o.setdefault("dC", torch.empty((Bt, L, N), dtype=x.dtype, device=dev))
+    if Dskip is not None:
+        o.setdefault("dDskip", torch.empty((D,), dtype=torch.float32, device=dev))
+    else:
+        o["dDskip"] = None
+    nbytes = int(lib.msm_scan_bwd_workspace_bytes(Bt, L, D, N, io))
+    ws, wsb = _workspace(nbytes, workspace, dev)
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy), _ptr(o["dx"]),
+            _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]),
+            Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
+    if plan is None:
+        st = lib.msm_scan_bwd(*args)
+    else:
+        st = lib.msm_scan_bwd_with_plan(*args, _plan_arg(plan))
+    if st != 0:
+        raise MsmError(st, "msm_scan_bwd")
+    return o

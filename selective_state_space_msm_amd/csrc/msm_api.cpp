@@ -1,0 +1,375 @@
+// C ABI of the Momentum-Mamba selective scan: argument checks, launch planning, workspace
+// layout.  Every check happens before anything is enqueued; nothing here allocates memory.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/msm.h"
+#include "msm_internal.h"
+
+namespace {
+
+using msm::kMaxChunks;
+using msm::kTile;
+using msm::kWave;
+
+constexpr int64_t kTargetWaves = 1024;  // one wavefront per SIMD on 256 CUs x 4 SIMDs
+constexpr int64_t kMaxWorkgroups = 4096;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int padded_states(int64_t N) { return N <= 4 ? 4 : (N <= 16 ? 16 : 64); }
+
+bool shape_ok(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  if (Bt < 1 || L < 1 || D < 1 || N < 1) return false;
+  const int64_t lim = (int64_t)1 << 40;
+  if (Bt > lim || L > lim || D > lim) return false;
+  // tile row offsets are 32-bit byte offsets: kTile rows of D fp32 values must fit
+  if (D > ((int64_t)1 << 24)) return false;
+  // element counts must stay far inside int64 and the grid inside 2^31 workgroups
+  if (Bt * L > lim || Bt * L * D > ((int64_t)1 << 50)) return false;
+  if (ceil_div(D, kWave) * Bt * kMaxChunks > ((int64_t)1 << 31) - 1) return false;
+  return true;
+}
+
+msm_status check_common(int64_t Bt, int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                        msm_dtype io) {
+  if (io != MSM_F32 && io != MSM_BF16) return MSM_ERR_UNSUPPORTED;
+  if (Bt < 1 || L < 1 || D < 1 || N < 1) return MSM_ERR_INVALID_ARG;
+  if (N > msm::kMaxN) return MSM_ERR_UNSUPPORTED;
+  if (!shape_ok(Bt, L, D, N)) return MSM_ERR_INVALID_ARG;
+  if (!(beta >= 0.0f && beta < 1.0f)) return MSM_ERR_INVALID_ARG;  // also rejects NaN
+  if (!(alpha >= 0.0f) || !isfinite(alpha)) return MSM_ERR_INVALID_ARG;
+  return MSM_OK;
+}
+
+// ---- forward planning ----
+int64_t fwd_max_chunks(int64_t Bt, int64_t L, int64_t D) {
+  const int64_t wg_per_chunk = Bt * ceil_div(D, kWave);
+  int64_t g = ceil_div(kMaxWorkgroups, wg_per_chunk);
+  if (g > kMaxChunks) g = kMaxChunks;
+  const int64_t tiles = ceil_div(L, kTile);
+  if (g > tiles) g = tiles;
+  return g < 1 ? 1 : g;
+}
+
+bool allowed_k(int NP, int K) {
+  switch (NP) {
+    case 4: return K == 1 || K == 2 || K == 4;
+    case 16: return K == 1 || K == 2 || K == 4 || K == 8 || K == 16;
+    case 64: return K == 4 || K == 8 || K == 16;
+    default: return false;
+  }
+}
+
+// Launch plan.  Measured on MI355X: the scan is VALU-bound, and two wavefronts per SIMD hide
+// each other's LDS, memory and scalar instructions, so the preferred plan keeps S = NP/K
+// wavefronts of few states each per 64-channel block when the channels alone give at least
+// one wavefront per SIMD.  Otherwise the sequence is cut into chunks of wavefronts with more
+// states each, until there are about two wavefronts per SIMD.
+msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int NP = padded_states(N);
+  const int64_t chan_blocks = Bt * ceil_div(D, kWave);
+  msm_plan pl{0, 1};
+  const int kpref = NP == 4 ? 1 : (NP == 16 ? 2 : 8);
+  if (chan_blocks * (NP / kpref) >= kTargetWaves) {
+    pl.states_per_wave = kpref;
+    return pl;
+  }
+  const int kchunk = NP == 4 ? 2 : (NP == 16 ? 4 : 8);
+  const int64_t waves = chan_blocks * (NP / kchunk);
+  int64_t G = ceil_div(2 * kTargetWaves, waves);
+  const int64_t gmax = fwd_max_chunks(Bt, L, D);
+  if (G > gmax) G = gmax;
+  if (G < 1) G = 1;
+  pl.states_per_wave = kchunk;
+  pl.chunks = (int32_t)G;
+  return pl;
+}
+
+struct FwdLayout {
+  size_t off_bv, off_bh, off_q, off_sd, total;
+};
+
+FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int64_t G = fwd_max_chunks(Bt, L, D);
+  FwdLayout l{};
+  if (G <= 1) return l;
+  const size_t per = align_up(sizeof(float) * (size_t)(Bt * G * N * D));
+  l.off_bv = 0;
+  l.off_bh = per;
+  l.off_q = 2 * per;
+  l.off_sd = 3 * per;
+  l.total = 3 * per + align_up(sizeof(float) * (size_t)(Bt * G * D));
+  return l;
+}
+
+// ---- backward planning ----
+msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int NP = padded_states(N);
+  const int64_t chan_blocks = Bt * ceil_div(D, kWave);
+  msm_plan pl{0, 1};
+  const int kmin = NP == 64 ? 4 : 1;
+  for (int K = 4; K >= kmin; K /= 2) {
+    if (!allowed_k(NP, K)) continue;
+    pl.states_per_wave = K;
+    if (chan_blocks * (NP / K) >= kTargetWaves) return pl;
+  }
+  return pl;  // smallest allowed K: most parallelism available without chunking
+}
+
+bool bwd_allowed_k(int NP, int K) {
+  switch (NP) {
+    case 4: return K == 1 || K == 2 || K == 4;
+    case 16: return K == 1 || K == 2 || K == 4;
+    case 64: return K == 4;
+    default: return false;
+  }
+}
+
+struct BwdLayout {
+  size_t off_ckpt, off_dbc, off_dA, off_dD, total;
+};
+
+BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int64_t NT = ceil_div(L, msm::kBwdTile);
+  const int64_t ncb = ceil_div(D, kWave);
+  const int NP = padded_states(N);
+  BwdLayout l{};
+  l.off_ckpt = 0;
+  l.off_dbc = align_up(sizeof(float) * (size_t)(Bt * NT * 2 * N * D));
+  l.off_dA = l.off_dbc + align_up(sizeof(float) * (size_t)(Bt * ncb * L * 2 * NP));
+  l.off_dD = l.off_dA + align_up(sizeof(float) * (size_t)(Bt * N * D));
+  l.total = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  return l;
+}
+
+// ---- overlap checks ----
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, size_t bytes) {
+  Range r{(uintptr_t)p, (uintptr_t)p + bytes};
+  return r;
+}
+bool overlaps(Range a, Range b) {
+  if (a.lo == 0 || b.lo == 0 || a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+bool any_overlap(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msm_version(void) { return 10000; }
+
+const char* msm_status_string(msm_status s) {
+  switch (s) {
+    case MSM_OK: return "MSM_OK";
+    case MSM_ERR_INVALID_ARG: return "MSM_ERR_INVALID_ARG: invalid argument";
+    case MSM_ERR_UNSUPPORTED: return "MSM_ERR_UNSUPPORTED: unsupported by this build";
+    case MSM_ERR_WORKSPACE: return "MSM_ERR_WORKSPACE: workspace too small";
+    case MSM_ERR_LAUNCH: return "MSM_ERR_LAUNCH: kernel launch failed";
+    default: return "MSM_ERR_UNKNOWN";
+  }
+}
+
+size_t msm_scan_fwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io) {
+  if (check_common(Bt, L, D, N, 0.f, 1.f, io) != MSM_OK) return 0;
+  return fwd_layout(Bt, L, D, N).total;
+}
+
+size_t msm_scan_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io) {
+  if (check_common(Bt, L, D, N, 0.f, 1.f, io) != MSM_OK) return 0;
+  return bwd_layout(Bt, L, D, N).total;
+}
+
+msm_status msm_scan_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
+                             float beta, msm_plan* plan) {
+  msm_status st = check_common(Bt, L, D, N, beta, 1.f, io);
+  if (st != MSM_OK) return st;
+  if (!plan) return MSM_ERR_INVALID_ARG;
+  *plan = auto_fwd_plan(Bt, L, D, N);
+  return MSM_OK;
+}
+
+msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
+                             float beta, msm_plan* plan) {
+  msm_status st = check_common(Bt, L, D, N, beta, 1.f, io);
+  if (st != MSM_OK) return st;
+  if (!plan) return MSM_ERR_INVALID_ARG;
+  *plan = auto_bwd_plan(Bt, L, D, N);
+  return MSM_OK;
+}
+
+msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, void* y,
+                                  float* last_h, float* last_v, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan) {
+  msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
+
+  msm_plan pl = auto_fwd_plan(Bt, L, D, N);
+  const int NP = padded_states(N);
+  if (plan) {
+    if (plan->states_per_wave != 0) {
+      if (!allowed_k(NP, plan->states_per_wave)) return MSM_ERR_UNSUPPORTED;
+      pl.states_per_wave = plan->states_per_wave;
+    }
+    if (plan->chunks != 0) {
+      if (plan->chunks < 1 || plan->chunks > fwd_max_chunks(Bt, L, D)) return MSM_ERR_INVALID_ARG;
+      pl.chunks = plan->chunks;
+    }
+  }
+
+  const size_t es = io == MSM_BF16 ? 2 : 4;
+  const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
+  const FwdLayout lay = fwd_layout(Bt, L, D, N);
+  if (workspace_bytes < lay.total || (lay.total > 0 && !workspace)) return MSM_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, nxd * es), rng(delta, nxd * es), rng(A, (size_t)(D * N) * 4),
+                       rng(B, nbc * es), rng(C, nbc * es), rng(Dskip, Dskip ? (size_t)D * 4 : 0)};
+  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? (size_t)(Bt * D * N) * 4 : 0),
+                        rng(last_v, last_v ? (size_t)(Bt * D * N) * 4 : 0),
+                        rng(workspace, lay.total)};
+  if (any_overlap(outs, 4, ins, 6)) return MSM_ERR_INVALID_ARG;
+
+  // chunk length: a multiple of the tile, so only the final chunk can end mid-tile
+  int64_t G = pl.chunks;
+  int64_t Tc = ceil_div(ceil_div(L, G), kTile) * kTile;
+  G = ceil_div(L, Tc);  // rounding Tc up can leave fewer non-empty chunks
+
+  msm::FwdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.y = y;
+  a.last_h = last_h;
+  a.last_v = last_v;
+  char* ws = static_cast<char*>(workspace);
+  a.s_bv = G > 1 ? reinterpret_cast<float*>(ws + lay.off_bv) : nullptr;
+  a.s_bh = G > 1 ? reinterpret_cast<float*>(ws + lay.off_bh) : nullptr;
+  a.s_q = G > 1 ? reinterpret_cast<float*>(ws + lay.off_q) : nullptr;
+  a.s_sd = G > 1 ? reinterpret_cast<float*>(ws + lay.off_sd) : nullptr;
+  a.Bt = Bt;
+  a.L = L;
+  a.D = D;
+  a.N = N;
+  a.Tc = Tc;
+  a.G = (int32_t)G;
+  a.ncb = (int32_t)ceil_div(D, kWave);
+  a.beta = beta;
+  a.alpha = alpha;
+  a.beta_pow_tc = (float)pow((double)beta, (double)Tc);
+
+  hipError_t e = msm::launch_fwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* Dskip, void* y, float* last_h,
+                        float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                        float alpha, msm_dtype io, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return msm_scan_fwd_with_plan(x, delta, A, B, C, Dskip, y, last_h, last_v, Bt, L, D, N, beta,
+                                alpha, io, workspace, workspace_bytes, stream, nullptr);
+}
+
+msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip,
+                                  const void* dy, void* dx, void* ddelta, float* dA, void* dB,
+                                  void* dC, float* dDskip, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan) {
+  msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC)
+    return MSM_ERR_INVALID_ARG;
+  if ((Dskip != nullptr) != (dDskip != nullptr)) return MSM_ERR_INVALID_ARG;
+
+  msm_plan pl = auto_bwd_plan(Bt, L, D, N);
+  const int NP = padded_states(N);
+  if (plan) {
+    if (plan->states_per_wave != 0) {
+      if (!bwd_allowed_k(NP, plan->states_per_wave)) return MSM_ERR_UNSUPPORTED;
+      pl.states_per_wave = plan->states_per_wave;
+    }
+    if (plan->chunks != 0 && plan->chunks != 1) return MSM_ERR_UNSUPPORTED;
+  }
+
+  const size_t es = io == MSM_BF16 ? 2 : 4;
+  const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
+  const BwdLayout lay = bwd_layout(Bt, L, D, N);
+  if (workspace_bytes < lay.total || !workspace) return MSM_ERR_WORKSPACE;
+  const Range ins[] = {rng(x, nxd * es), rng(delta, nxd * es), rng(A, (size_t)(D * N) * 4),
+                       rng(B, nbc * es), rng(C, nbc * es), rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(dy, nxd * es)};
+  const Range outs[] = {rng(dx, nxd * es),           rng(ddelta, nxd * es),
+                        rng(dA, (size_t)(D * N) * 4), rng(dB, nbc * es),
+                        rng(dC, nbc * es),           rng(dDskip, dDskip ? (size_t)D * 4 : 0),
+                        rng(workspace, lay.total)};
+  if (any_overlap(outs, 7, ins, 7)) return MSM_ERR_INVALID_ARG;
+
+  msm::BwdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.dy = dy;
+  a.dx = dx;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dDskip = dDskip;
+  char* ws = static_cast<char*>(workspace);
+  a.ckpt = reinterpret_cast<float*>(ws + lay.off_ckpt);
+  a.dbc_part = reinterpret_cast<float*>(ws + lay.off_dbc);
+  a.dA_part = reinterpret_cast<float*>(ws + lay.off_dA);
+  a.dD_part = reinterpret_cast<float*>(ws + lay.off_dD);
+  a.Bt = Bt;
+  a.L = L;
+  a.D = D;
+  a.N = N;
+  a.NT = ceil_div(L, msm::kBwdTile);
+  a.ncb = (int32_t)ceil_div(D, kWave);
+  a.NP = NP;
+  a.beta = beta;
+  a.alpha = alpha;
+  hipError_t e = msm::launch_bwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* Dskip, const void* dy, void* dx,
+                        void* ddelta, float* dA, void* dB, void* dC, float* dDskip, int64_t Bt,
+                        int64_t L, int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return msm_scan_bwd_with_plan(x, delta, A, B, C, Dskip, dy, dx, ddelta, dA, dB, dC, dDskip, Bt,
+                                L, D, N, beta, alpha, io, workspace, workspace_bytes, stream,
+                                nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the forward and backward kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msm {
+
+constexpr float kLog2e = 1.4426950408889634f;  // A is rescaled once so that a = 2^(delta*A2)
+
+// 2^x on the transcendental unit (v_exp_f32, half rate on gfx950).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct bf16_storage {
+  uint16_t bits;
+};
+
+// Raw buffer resource over `bytes` bytes starting at `base` (gfx9-family descriptor word 3).
+// A load whose per-lane offset is at or past the extent returns 0 without touching memory and
+// a store there is dropped; the kernels use this for rows past the end of a chunk.  Extents
+// are clamped to [0, 2^31 - 1]; every offset a kernel uses stays far below that bound.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// I/O element access.  "raw" is what sits in a register between the load and its first use.
+template <typename IO>
+struct io;
+
+template <>
+struct io<float> {
+  using raw = float;
+  static constexpr int es = 4;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  // element `lane` of the row starting at element `row` (row is wavefront-uniform, so the
+  // address is a scalar base plus a 32-bit per-lane offset)
+  static __device__ __forceinline__ raw load_row(const void* p, int64_t row, uint32_t lane) {
+    return (static_cast<const float*>(p) + row)[lane];
+  }
+  static __device__ __forceinline__ void store_row(void* p, int64_t row, uint32_t lane, float v) {
+    (static_cast<float*>(p) + row)[lane] = v;
+  }
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ float widen(raw r) { return r; }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+
+template <>
+struct io<bf16_storage> {
+  using raw = uint32_t;  // the 16 bf16 bits, zero-extended
+  static constexpr int es = 2;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return static_cast<const uint16_t*>(p)[i];
+  }
+  static __device__ __forceinline__ raw load_row(const void* p, int64_t row, uint32_t lane) {
+    return (static_cast<const uint16_t*>(p) + row)[lane];
+  }
+  static __device__ __forceinline__ void store_row(void* p, int64_t row, uint32_t lane, float v) {
+    (static_cast<__bf16*>(p) + row)[lane] = static_cast<__bf16>(v);
+  }
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff, float v) {
+    const __bf16 hv = static_cast<__bf16>(v);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hv), r, voff, soff, 0);
+  }
+  // bf16 -> fp32 is exact: the bf16 bits are the upper half of the fp32 pattern.
+  static __device__ __forceinline__ float widen(raw r) { return __uint_as_float(r << 16); }
+  // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);
+  }
+};
+
+}  // namespace msm

@@ -1,0 +1,346 @@
+// Forward selective scan with momentum (gfx950).
+//
+// Recurrence (Momentum Mamba README, "Momentum Mamba Recurrence"), per (b, d, n):
+//   v_t = beta v_{t-1} + alpha delta_t B_t x_t,  h_t = exp(delta_t A) h_{t-1} + v_t,
+//   y_t = sum_n C_t h_t (+ Dskip x_t).
+// Each step is the affine map (v, h) -> ([[beta, 0], [beta, a_t]] (v, h) + (w_t, w_t)); maps
+// compose associatively, which is what lets the sequence be cut into chunks (the chunked
+// scan with a running prefix of the README's kernel notes; the inter-chunk scan over chunk
+// states of the Mamba-2 page's four-step algorithm).
+//
+// Work decomposition (one 64-lane wavefront = 64 consecutive channels x K states):
+//   * lane = channel d, so every x/delta/y access of a wavefront is one contiguous row;
+//   * the K states of a channel live in registers; a workgroup holds S = NP/K wavefronts that
+//     own disjoint state groups of the same 64 channels (NP = padded state count);
+//   * B_t and C_t are the same for all channels, so each workgroup stages a tile of kTile steps
+//     of them in LDS (fp32, B pre-multiplied by alpha) and every lane reads them as broadcasts;
+//   * the per-wavefront partial sums of y_t = C_t . h_t are added across the S wavefronts in
+//     LDS in a fixed order (deterministic), one barrier per tile, double-buffered;
+//   * time runs sequentially inside a lane.  When the channel count alone cannot fill the
+//     GPU the sequence is cut into G chunks: a summary pass maps every chunk but the last to
+//     its affine map from a zero start (bv, bh, q and the sum of delta), and the main pass
+//     composes the maps of the preceding chunks in its prologue to get its exact start state.
+//
+// The y reduction never needs MFMA: the scan is a per-element recurrence bound by VALU issue
+// (one v_exp_f32 plus five fp32 multiply/FMA per state update), not a dense contraction.
+#include "msm_device.hpp"
+#include "msm_internal.h"
+
+namespace msm {
+namespace {
+
+// Occupancy hint: the launch plans put one or two wavefronts on a SIMD, so the scheduler may
+// spend registers on hiding LDS and transcendental latency instead of on more wavefronts.
+template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP>
+__global__ __launch_bounds__(S* kWave) __attribute__((amdgpu_waves_per_eu(1, K >= 8 ? 1 : 2)))
+void fwd_kernel(const FwdArgs p) {
+  using T = io<IO>;
+  using raw = typename T::raw;
+  constexpr int TT = kTile;
+  constexpr int BCW = 2 * K;                    // floats per (tile row, wave): B then C
+  constexpr int BC_PER_TILE = TT * S * BCW;
+  constexpr int NTHR = S * kWave;
+  constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
+  constexpr bool YPART = !SUMMARY && S > 1;
+
+  __shared__ float bcs[2][TT][S][BCW];
+  __shared__ float ypart[YPART ? 2 : 1][YPART ? S : 1][TT][kWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int g = tid / kWave;
+  int64_t blk = blockIdx.x;
+  const int cb = (int)(blk % p.ncb);
+  blk /= p.ncb;
+  const int64_t b = blk % p.Bt;
+  const int k = (int)(blk / p.Bt);
+  const int64_t L = p.L, D = p.D, N = p.N;
+  const int64_t t0 = (int64_t)k * p.Tc;
+  const int64_t t1 = (t0 + p.Tc < L) ? t0 + p.Tc : L;
+  const int d = cb * kWave + lane;
+  const bool dvalid = d < D;
+  const int dl = dvalid ? d : (int)D - 1;
+  const float beta = p.beta;
+
+  float A2[K], v[K], h[K], q[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t n = (int64_t)g * K + j;
+    A2[j] = n < N ? p.A[dl * N + n] * kLog2e : 0.f;
+    v[j] = 0.f;
+    h[j] = 0.f;
+    q[j] = 0.f;
+  }
+  float sd = 0.f, bpow = 1.f;
+  const float dsk = (HAS_DSKIP && g == 0) ? p.Dskip[dl] : 0.f;
+
+  if (!SUMMARY && k > 0) {
+    // Exact start state of this chunk: apply the maps of chunks 0..k-1 in order.
+    for (int kk = 0; kk < k; ++kk) {
+      const int64_t base = b * p.G + kk;
+      const float sdv = p.s_sd[base * D + dl];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t n = (int64_t)g * K + j;
+        if (n < N) {
+          const int64_t idx = (base * N + n) * D + dl;
+          const float r = exp2_fast(A2[j] * sdv);     // product of a_t over the chunk
+          float hn = fmaf(r, h[j], p.s_bh[idx]);
+          if (!BETA0) {
+            hn = fmaf(p.s_q[idx], v[j], hn);
+            v[j] = fmaf(p.beta_pow_tc, v[j], p.s_bv[idx]);
+          }
+          h[j] = hn;
+        }
+      }
+    }
+  }
+
+  // ---- addressing ----
+  // Every global access of a tile goes through a buffer resource whose base is the tile's first
+  // row and whose extent ends at the last row of this chunk.  Offsets are per-lane constants
+  // (row * row_bytes + lane_bytes), so the loads need no address arithmetic, and rows past the
+  // chunk end fall outside the resource: they read as zero and touch no memory.  That is what
+  // makes the prefetch unconditional (an uneven number of loads on different paths would make
+  // the in-order vmcnt waits of the current tile drain the prefetch of the next one).
+  const uint32_t lane_off = (uint32_t)dl * T::es;
+  const int64_t row_bytes = D * T::es;
+  uint32_t voff_row[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) voff_row[tt] = (uint32_t)(tt * row_bytes) + lane_off;
+  auto rsrc_tile = [&](const void* base, int64_t ts, int64_t elem_per_row) {
+    const int64_t ebytes = elem_per_row * T::es;
+    return make_rsrc(static_cast<const char*>(base) + (b * L + ts) * ebytes, (t1 - ts) * ebytes);
+  };
+
+  // ---- B/C staging: global (I/O dtype) -> registers -> LDS (fp32) ----
+  // Element (tt, n) of a tile; both B and C are loaded for it.
+  constexpr int BCE = TT * S * K;                       // (tt, n) elements per tile
+  constexpr int NPE = (BCE + NTHR - 1) / NTHR;
+  uint32_t bc_voff[NPE];
+  bool bc_nok[NPE];
+#pragma unroll
+  for (int r = 0; r < NPE; ++r) {
+    const int i = tid + r * NTHR;
+    const int ic = i < BCE ? i : BCE - 1;
+    const int n = ic % (S * K);
+    bc_nok[r] = n < N;
+    bc_voff[r] = (uint32_t)(((ic / (S * K)) * N + (n < N ? n : 0)) * T::es);
+  }
+  raw bre[NPE], cre[NPE];
+  auto stage_load = [&](int64_t ts) {
+    const auto rb = rsrc_tile(p.B, ts, N);
+    const auto rc = rsrc_tile(p.C, ts, N);
+#pragma unroll
+    for (int r = 0; r < NPE; ++r) {
+      bre[r] = T::bload(rb, bc_voff[r], 0u);
+      cre[r] = T::bload(rc, bc_voff[r], 0u);
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NPE; ++r) {
+      const int i = tid + r * NTHR;
+      if (i < BCE) {
+        const int tt = i / (S * K);
+        const int n = i % (S * K);
+        float* dst = &bcs[buf][tt][n / K][0];
+        dst[n % K] = bc_nok[r] ? T::widen(bre[r]) * p.alpha : 0.f;
+        dst[K + n % K] = bc_nok[r] ? T::widen(cre[r]) : 0.f;
+      }
+    }
+  };
+  auto load_xd = [&](raw(&xr)[TT], raw(&dr)[TT], int64_t ts) {
+    const auto rx = rsrc_tile(p.x, ts, D);
+    const auto rd = rsrc_tile(p.delta, ts, D);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      xr[tt] = T::bload(rx, voff_row[tt], 0u);
+      dr[tt] = T::bload(rd, voff_row[tt], 0u);
+    }
+  };
+
+  // One time step for the K states of this lane.  bc holds [B(K) | C(K)] of that step.
+  auto step = [&](float xv, float dv, const float* bc) -> float {
+    const float c = dv * xv;
+    float ysum = HAS_DSKIP ? dsk * xv : 0.f;
+    if (SUMMARY) bpow *= beta;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float a = exp2_fast(dv * A2[j]);
+      const float w = c * bc[j];
+      if (BETA0)
+        v[j] = w;
+      else
+        v[j] = fmaf(beta, v[j], w);
+      h[j] = fmaf(a, h[j], v[j]);
+      if (SUMMARY) {
+        if (!BETA0) q[j] = fmaf(a, q[j], bpow);
+      } else {
+        ysum = fmaf(bc[K + j], h[j], ysum);
+      }
+    }
+    if (SUMMARY) sd += dv;
+    return ysum;
+  };
+  auto emit = [&](int buf, int tt, int64_t t, float ysum) {
+    if (SUMMARY) return;
+    if (S == 1) {
+      if (dvalid) T::bstore(rsrc_tile(p.y, t, D), lane_off, 0u, ysum);
+    } else {
+      ypart[YPART ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
+    }
+  };
+  // Full tile.  The B/C broadcasts of the next batch of RB steps are read from LDS into
+  // registers before the current batch is computed; the scheduling barrier keeps the compiler
+  // from sinking those reads next to their uses, where their latency would be exposed (one
+  // wavefront per SIMD has nothing else to issue meanwhile).
+  constexpr int RB = (32 / K) < TT ? (32 / K) : TT;
+  constexpr int NB = TT / RB;
+  auto compute_tile = [&](const raw(&xr)[TT], const raw(&dr)[TT], int buf, int64_t ts) {
+    float bcv[2][RB][BCW];
+    auto read_batch = [&](float(&dst)[RB][BCW], int jb) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const float* src = &bcs[buf][jb * RB + i][g][0];
+#pragma unroll
+        for (int e = 0; e < BCW; ++e) dst[i][e] = src[e];
+      }
+    };
+    read_batch(bcv[0], 0);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      if (jb + 1 < NB) read_batch(bcv[(jb + 1) & 1], jb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int tt = jb * RB + i;
+        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), bcv[jb & 1][i]);
+        emit(buf, tt, ts + tt, ysum);
+      }
+    }
+  };
+  auto compute_tail = [&](int buf, int64_t ts, int nv) {
+    for (int tt = 0; tt < nv; ++tt) {
+      const int64_t row = (b * L + ts + tt) * D;
+      const float ysum = step(T::widen(T::load_row(p.x, row, dl)),
+                              T::widen(T::load_row(p.delta, row, dl)), &bcs[buf][tt][g][0]);
+      emit(buf, tt, ts + tt, ysum);
+    }
+  };
+  auto finalize = [&](int buf, int64_t ts, int nv) {
+    if (!YPART) return;
+    const auto ry = rsrc_tile(p.y, ts, D);
+    for (int tt = g; tt < nv; tt += S) {
+      float s = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < S; ++gg) s += ypart[YPART ? buf : 0][YPART ? gg : 0][tt][lane];
+      if (dvalid) T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off, 0u, s);
+    }
+  };
+
+  raw xa[TT], da[TT], xb[TT], db[TT];
+  int64_t ts = t0;
+  int buf = 0;
+  stage_load(ts);
+  stage_store(0);
+  load_xd(xa, da, ts);
+  __syncthreads();
+
+  // One tile: compute the tile at ts from (xc, dc) while the next tile's inputs are in flight.
+  auto half = [&](raw(&xc)[TT], raw(&dc)[TT], raw(&xn)[TT], raw(&dn)[TT]) -> bool {
+    const int nv = (int)((t1 - ts < TT) ? t1 - ts : TT);
+    const int64_t tn = ts + TT;
+    const bool has_next = tn < t1;
+    stage_load(tn);  // unconditional; past the chunk end these read nothing
+    load_xd(xn, dn, tn);
+    if (nv == TT)
+      compute_tile(xc, dc, buf, ts);
+    else
+      compute_tail(buf, ts, nv);
+    if (has_next) stage_store(buf ^ 1);
+    __syncthreads();
+    finalize(buf, ts, nv);
+    ts = tn;
+    buf ^= 1;
+    return has_next;
+  };
+  while (half(xa, da, xb, db) && half(xb, db, xa, da)) {
+  }
+
+  if (SUMMARY) {
+    if (dvalid) {
+      const int64_t base = b * p.G + k;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t n = (int64_t)g * K + j;
+        if (n < N) {
+          const int64_t idx = (base * N + n) * D + d;
+          p.s_bh[idx] = h[j];
+          if (!BETA0) {
+            p.s_bv[idx] = v[j];
+            p.s_q[idx] = q[j];
+          }
+        }
+      }
+      if (g == 0) p.s_sd[base * D + d] = sd;
+    }
+  } else if (k == p.G - 1 && dvalid) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)g * K + j;
+      if (n < N) {
+        if (p.last_h) p.last_h[(b * D + d) * N + n] = h[j];
+        if (p.last_v) p.last_v[(b * D + d) * N + n] = v[j];
+      }
+    }
+  }
+}
+
+template <typename IO, int K, int S, bool BETA0>
+hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
+  const dim3 block(S * kWave);
+  if (a.G > 1) {
+    const dim3 grid((unsigned)(a.ncb * a.Bt * (a.G - 1)));
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(a.ncb * a.Bt * a.G));
+  if (a.Dskip)
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename IO, bool BETA0>
+hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
+  // padded state count NP = K * S is 4, 16 or 64
+  const int NP = a.N <= 4 ? 4 : (a.N <= 16 ? 16 : 64);
+  switch (NP * 100 + K) {
+    case 401: return launch_ks<IO, 1, 4, BETA0>(a, s);
+    case 402: return launch_ks<IO, 2, 2, BETA0>(a, s);
+    case 404: return launch_ks<IO, 4, 1, BETA0>(a, s);
+    case 1601: return launch_ks<IO, 1, 16, BETA0>(a, s);
+    case 1602: return launch_ks<IO, 2, 8, BETA0>(a, s);
+    case 1604: return launch_ks<IO, 4, 4, BETA0>(a, s);
+    case 1608: return launch_ks<IO, 8, 2, BETA0>(a, s);
+    case 1616: return launch_ks<IO, 16, 1, BETA0>(a, s);
+    case 6404: return launch_ks<IO, 4, 16, BETA0>(a, s);
+    case 6408: return launch_ks<IO, 8, 8, BETA0>(a, s);
+    case 6416: return launch_ks<IO, 16, 4, BETA0>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s) {
+  if (io_bf16) {
+    return beta0 ? launch_io<bf16_storage, true>(a, K, s) : launch_io<bf16_storage, false>(a, K, s);
+  }
+  return beta0 ? launch_io<float, true>(a, K, s) : launch_io<float, false>(a, K, s);
+}
+
+}  // namespace msm

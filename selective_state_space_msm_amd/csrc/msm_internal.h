@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI layer (msm_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msm {
+
+constexpr int kWave = 64;        // wavefront width on CDNA
+constexpr int kTile = 16;        // time steps staged per LDS tile in the forward
+constexpr int kMaxChunks = 64;   // upper bound on time chunks (sizes the workspace)
+constexpr int kMaxN = 64;        // states supported per channel
+constexpr int kBwdTile = 16;     // time steps recomputed per register tile in the backward
+
+struct FwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  void* y;
+  float* last_h;
+  float* last_v;
+  // chunk summaries, [Bt][G][N][D] (sd: [Bt][G][D]); unused when G == 1
+  float* s_bv;
+  float* s_bh;
+  float* s_q;
+  float* s_sd;
+  int64_t Bt, L, D, N;
+  int64_t Tc;        // chunk length, a multiple of kTile
+  int32_t G;         // number of chunks
+  int32_t ncb;       // channel blocks of 64
+  float beta, alpha;
+  float beta_pow_tc;  // beta^Tc, the velocity decay across one full chunk
+};
+
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* dy;
+  void* dx;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dDskip;
+  // workspace
+  float* ckpt;       // [Bt][NT][2][N][D]  (v, h) before each tile of kBwdTile steps
+  float* dbc_part;   // [Bt][ncb][L][2][NP] per channel-block partial sums of dB/alpha and dC
+  float* dA_part;    // [Bt][N][D]
+  float* dD_part;    // [Bt][D]
+  int64_t Bt, L, D, N;
+  int64_t NT;        // tiles = ceil(L / kBwdTile)
+  int32_t ncb;
+  int32_t NP;        // padded states = states_per_wave * waves
+  float beta, alpha;
+};
+
+// Both return hipSuccess or the first launch error.
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
+
+}  // namespace msm

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function msm.h declares,
+and rejects bad arguments before anything reaches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import selective_state_space_msm_amd as msm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msm.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msm.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(msm.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", msm.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code, word in [(0, "MSM_OK"), (1, "INVALID_ARG"), (2, "UNSUPPORTED"), (3, "WORKSPACE"),
+                       (4, "LAUNCH"), (99, "UNKNOWN")]:
+        assert word in msm.msm_status_string(code)
+    assert msm.msm_version() >= 10000
+
+
+def test_workspace_queries(lib):
+    assert msm.msm_scan_fwd_workspace_bytes(0, 10, 10, 4, "f32") == 0
+    assert msm.msm_scan_fwd_workspace_bytes(1, 10, 10, 65, "f32") == 0
+    assert msm.msm_scan_bwd_workspace_bytes(1, -1, 10, 4, "bf16") == 0
+    # the large-batch headline shape needs no chunk summaries; the long sequence does
+    plan = msm.msm_scan_fwd_plan(4, 4096, 4096, 16, "bf16", 0.9)
+    assert plan["chunks"] == 1
+    plan = msm.msm_scan_fwd_plan(1, 65536, 2048, 16, "bf16", 0.95)
+    assert plan["chunks"] > 1
+    assert msm.msm_scan_fwd_workspace_bytes(1, 65536, 2048, 16, "bf16") > 0
+    assert msm.msm_scan_bwd_workspace_bytes(4, 2048, 2048, 16, "f32") > 0
+
+
+def _fwd(lib, *, x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, y=0x100000,
+         lh=None, lv=None, Bt=1, L=8, D=4, N=4, beta=0.5, alpha=1.0, io=0, ws=None, wsb=0,
+         plan=None):
+    P = ctypes.c_void_p
+    args = [P(x), P(delta), P(A), P(B), P(C), P(Dskip), P(y), P(lh), P(lv), Bt, L, D, N,
+            ctypes.c_float(beta), ctypes.c_float(alpha), io, P(ws), wsb, None]
+    if plan is None:
+        return lib.msm_scan_fwd(*args)
+    return lib.msm_scan_fwd_with_plan(*args, ctypes.byref(plan))
+
+
+def test_fwd_argument_validation_never_launches(lib):
+    # every call below must be rejected by the host checks (no GPU in this container)
+    assert _fwd(lib, x=None) == INVALID
+    assert _fwd(lib, y=None) == INVALID
+    assert _fwd(lib, Bt=0) == INVALID
+    assert _fwd(lib, L=0) == INVALID
+    assert _fwd(lib, D=-3) == INVALID
+    assert _fwd(lib, N=0) == INVALID
+    assert _fwd(lib, N=65) == UNSUPPORTED
+    assert _fwd(lib, io=7) == UNSUPPORTED
+    assert _fwd(lib, beta=1.0) == INVALID
+    assert _fwd(lib, beta=-0.1) == INVALID
+    assert _fwd(lib, beta=float("nan")) == INVALID
+    assert _fwd(lib, alpha=-1.0) == INVALID
+    assert _fwd(lib, alpha=float("inf")) == INVALID
+    assert _fwd(lib, alpha=float("nan")) == INVALID
+    # output overlapping an input
+    assert _fwd(lib, y=0x1000 + 16) == INVALID
+    assert _fwd(lib, lh=0x4000) == INVALID
+    # chunked shape without the workspace it needs
+    need = lib.msm_scan_fwd_workspace_bytes(1, 65536, 64, 16, 0)
+    assert need > 0
+    big = dict(x=0x10000000, delta=0x20000000, A=0x30000000, B=0x40000000, C=0x50000000,
+               y=0x60000000, Bt=1, L=65536, D=64, N=16)
+    assert _fwd(lib, **big) == WORKSPACE
+    assert _fwd(lib, ws=0x70000000, wsb=need - 1, **big) == WORKSPACE
+    # workspace overlapping an input
+    assert _fwd(lib, ws=0x10000000, wsb=need, **big) == INVALID
+    # explicit plans outside what the build supports
+    bad = msm._Plan(3, 1)
+    assert _fwd(lib, plan=bad) == UNSUPPORTED
+    bad = msm._Plan(4, 1000)
+    assert _fwd(lib, plan=bad) == INVALID
+
+
+def test_bwd_argument_validation_never_launches(lib):
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, dy=0x6000,
+                 dx=0x100000, ddelta=0x200000, dA=0x300000, dB=0x400000, dC=0x500000,
+                 dDskip=None, Bt=1, L=8, D=4, N=4, beta=0.5, alpha=1.0, io=0, ws=0x900000,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.msm_scan_bwd(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
+                                P(a["Dskip"]), P(a["dy"]), P(a["dx"]), P(a["ddelta"]), P(a["dA"]),
+                                P(a["dB"]), P(a["dC"]), P(a["dDskip"]), a["Bt"], a["L"], a["D"],
+                                a["N"], ctypes.c_float(a["beta"]), ctypes.c_float(a["alpha"]),
+                                a["io"], P(a["ws"]), a["wsb"], None)
+
+    assert call(dy=None) == INVALID
+    assert call(dA=None) == INVALID
+    assert call(Dskip=0x7000) == INVALID          # Dskip without dDskip
+    assert call(dDskip=0x700000) == INVALID       # dDskip without Dskip
+    assert call(beta=1.5) == INVALID
+    assert call(N=100) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(dx=0x6000) == INVALID             # gradient aliasing dy
+    assert call(dB=0x100000 + 4) == INVALID       # two outputs overlapping
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(msm, "_lib", None)
+    monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(msm.MsmLibraryMissing):
+        msm.load_library()

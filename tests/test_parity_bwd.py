@@ -1,0 +1,109 @@
+"""Backward parity: gradients from the HIP library (through the C ABI) against the fp64
+oracle, plus the scaling identities of the backward at full size."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (assert_close, host, inputs_to_device, log, run_bwd, run_fwd,
+                      sample_channels, sub_problem)
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+NAMES = ("dx", "ddelta", "dA", "dB", "dC", "dDskip")
+
+
+def oracle_bwd(inp):
+    return oracle.bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["dy"],
+                      inp["beta"], inp["alpha"], Dskip=inp["Dskip"])
+
+
+def check_full(inp, plan=None, tag=""):
+    io = inp["io"]
+    log("bwd %s shape=%s io=%s beta=%g alpha=%g plan=%s" % (tag, inp["x"].shape, io, inp["beta"],
+                                                           inp["alpha"], plan))
+    got = run_bwd(inp, plan=plan)
+    want = oracle_bwd(inp)
+    for k in NAMES:
+        if want[k] is None:
+            assert got[k] is None
+            continue
+        # dA and dDskip are fp32 outputs in every I/O mode
+        assert_close(host(got[k]), want[k], "f32" if k in ("dA", "dDskip") and io == "f32" else io,
+                     "%s %s" % (k, tag))
+
+
+@pytest.mark.parametrize("beta", [0.9, 0.0])
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_tiny_workload(beta, K):
+    inp = workloads.make_inputs(W["tiny"].replace(beta=beta), with_dy=True)
+    check_full(inp, plan={"states_per_wave": K}, tag="tiny")
+
+
+SMALL = W["bwd"].replace(Bt=2, L=100, D=70, N=16)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 4])
+@pytest.mark.parametrize("beta,alpha,dskip", [(0.9, 1.0, False), (0.0, 1.0, True),
+                                              (0.6, 0.7, True)])
+def test_small_ragged(io, K, beta, alpha, dskip):
+    inp = workloads.make_inputs(SMALL.replace(io=io, beta=beta, alpha=alpha, dskip=dskip),
+                                a_kind="random", seed=31)
+    check_full(inp, plan={"states_per_wave": K}, tag="small")
+
+
+@pytest.mark.parametrize("N", [1, 3, 5, 17])
+def test_state_counts(N):
+    inp = workloads.make_inputs(SMALL.replace(L=40, D=33, N=N, dskip=True), a_kind="random",
+                                seed=40 + N)
+    check_full(inp, tag="N=%d" % N)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 16), (2, 17, 1, 4), (1, 16, 64, 16), (3, 5, 65, 2)])
+def test_degenerate_shapes(shape):
+    Bt, L, D, N = shape
+    inp = workloads.make_inputs(SMALL.replace(Bt=Bt, L=L, D=D, N=N, dskip=True), seed=3)
+    check_full(inp, tag="shape=%s" % (shape,))
+
+
+def test_deterministic_across_runs():
+    inp = workloads.make_inputs(SMALL.replace(dskip=True), seed=4)
+    g = inputs_to_device(inp)
+    a = run_bwd(inp, g)
+    b = run_bwd(inp, g)
+    for k in NAMES:
+        assert np.array_equal(host(a[k]), host(b[k])), k
+
+
+def test_full_size_backward():
+    w = W["bwd"]
+    log("full-size bwd: drawing inputs")
+    inp = workloads.make_inputs(w)
+    g = inputs_to_device(inp)
+    got = {k: (None if v is None else host(v)) for k, v in run_bwd(inp, g).items()}
+    # (1) batch row 0 in full: every output of that row, including dB and dC (sums over all d)
+    log("  oracle on batch row 0 (all channels)")
+    sub0 = sub_problem(inp, bsel=slice(0, 1))
+    o0 = oracle_bwd(sub0)
+    for k in ("dx", "ddelta", "dB", "dC"):
+        assert_close(got[k][0:1], o0[k], w.io, "%s row 0" % k)
+    # (2) sampled channels over every batch row: dx, ddelta and dA (dA sums over b and t)
+    dsel = sample_channels(w.D, 16, seed=w.seed)
+    log("  oracle on %d sampled channels x all rows" % len(dsel))
+    od = oracle_bwd(sub_problem(inp, dsel=dsel))
+    assert_close(got["dx"][:, :, dsel], od["dx"], w.io, "dx sampled")
+    assert_close(got["ddelta"][:, :, dsel], od["ddelta"], w.io, "ddelta sampled")
+    assert_close(got["dA"][dsel], od["dA"], w.io, "dA sampled")
+    # (3) scaling identities on the whole output (fp64 inner products on the host):
+    #     <dB,B> = <dC,C> = <dx,x> = <ddelta,delta> - <dA,A> = <dy,y>  (no skip term here)
+    y = host(run_fwd(inp, g)[0])
+    ip = lambda a, b: float(np.sum(np.asarray(a, np.float64) * np.asarray(b, np.float64)))
+    ref = ip(inp["dy"], y)
+    vals = {"<dB,B>": ip(got["dB"], inp["B"]), "<dC,C>": ip(got["dC"], inp["C"]),
+            "<dx,x>": ip(got["dx"], inp["x"]),
+            "<dd,d>-<dA,A>": ip(got["ddelta"], inp["delta"]) - ip(got["dA"], inp["A"])}
+    log("  <dy,y> = %.9g; %s" % (ref, vals))
+    for k, v in vals.items():
+        assert abs(v - ref) <= 1e-4 * abs(ref) + 1e-2, (k, v, ref)
