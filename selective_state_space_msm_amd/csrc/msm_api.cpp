@@ -248,8 +248,12 @@ msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float*
                         rng(workspace, lay.total)};
   if (any_overlap(outs, 4, ins, 6)) return MSM_ERR_INVALID_ARG;
 
-  // chunk length: a multiple of the tile, so only the final chunk can end mid-tile
+  // chunk length: a multiple of the tile, so only the final chunk can end mid-tile.  The
+  // kernels address a chunk with 32-bit byte offsets: keep every chunk of every (Bt,L,D)
+  // array below 2^31 bytes.
   int64_t G = pl.chunks;
+  const int64_t max_rows = (((int64_t)1 << 31) - 1) / (D * (int64_t)es);
+  if (ceil_div(L, G) > max_rows) G = ceil_div(L, max_rows - kTile);
   int64_t Tc = ceil_div(ceil_div(L, G), kTile) * kTile;
   G = ceil_div(L, Tc);  // rounding Tc up can leave fewer non-empty chunks
 

@@ -19,6 +19,9 @@ struct bf16_storage {
 // A load whose per-lane offset is at or past the extent returns 0 without touching memory and
 // a store there is dropped; the kernels use this for rows past the end of a chunk.  Extents
 // are clamped to [0, 2^31 - 1]; every offset a kernel uses stays far below that bound.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u32(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
@@ -32,6 +35,8 @@ template <>
 struct io<float> {
   using raw = float;
   static constexpr int es = 4;
+  // delta * x from the raw values
+  static __device__ __forceinline__ float mul_raw(raw a, raw b) { return a * b; }
   static __device__ __forceinline__ raw load(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
@@ -60,6 +65,10 @@ template <>
 struct io<bf16_storage> {
   using raw = uint32_t;  // the 16 bf16 bits, zero-extended
   static constexpr int es = 2;
+  // delta * x from the raw bits: widen both (exact) and multiply
+  static __device__ __forceinline__ float mul_raw(raw a, raw b) {
+    return __uint_as_float(a << 16) * __uint_as_float(b << 16);
+  }
   static __device__ __forceinline__ raw load(const void* p, int64_t i) {
     return static_cast<const uint16_t*>(p)[i];
   }

@@ -49,11 +49,10 @@ void fwd_kernel(const FwdArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int g = tid / kWave;
-  int64_t blk = blockIdx.x;
-  const int cb = (int)(blk % p.ncb);
-  blk /= p.ncb;
-  const int64_t b = blk % p.Bt;
-  const int k = (int)(blk / p.Bt);
+  const uint32_t blk = blockIdx.x / (uint32_t)p.ncb;
+  const int cb = (int)(blockIdx.x - blk * (uint32_t)p.ncb);
+  const int64_t b = blk % (uint32_t)p.Bt;
+  const int k = (int)(blk / (uint32_t)p.Bt);
   const int64_t L = p.L, D = p.D, N = p.N;
   const int64_t t0 = (int64_t)k * p.Tc;
   const int64_t t1 = (t0 + p.Tc < L) ? t0 + p.Tc : L;
@@ -103,14 +102,33 @@ void fwd_kernel(const FwdArgs p) {
   // chunk end fall outside the resource: they read as zero and touch no memory.  That is what
   // makes the prefetch unconditional (an uneven number of loads on different paths would make
   // the in-order vmcnt waits of the current tile drain the prefetch of the next one).
+  // Resource bases and extents are carried as byte offsets from the chunk start; the host keeps
+  // every chunk below 2^31 bytes per array.
   const uint32_t lane_off = (uint32_t)dl * T::es;
-  const int64_t row_bytes = D * T::es;
+  const uint32_t row_bytes = (uint32_t)(D * T::es);
+  const uint32_t bc_row_bytes = (uint32_t)(N * T::es);
+  const uint32_t chunk_rows = (uint32_t)(t1 - t0);
+  const uint32_t ext_d = chunk_rows * row_bytes, ext_n = chunk_rows * bc_row_bytes;
+  const char* x0 = static_cast<const char*>(p.x) + (b * L + t0) * D * T::es;
+  const char* dl0 = static_cast<const char*>(p.delta) + (b * L + t0) * D * T::es;
+  char* y0 = static_cast<char*>(p.y) + (b * L + t0) * D * T::es;
+  const char* B0 = static_cast<const char*>(p.B) + (b * L + t0) * N * T::es;
+  const char* C0 = static_cast<const char*>(p.C) + (b * L + t0) * N * T::es;
   uint32_t voff_row[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) voff_row[tt] = (uint32_t)(tt * row_bytes) + lane_off;
-  auto rsrc_tile = [&](const void* base, int64_t ts, int64_t elem_per_row) {
-    const int64_t ebytes = elem_per_row * T::es;
-    return make_rsrc(static_cast<const char*>(base) + (b * L + ts) * ebytes, (t1 - ts) * ebytes);
+  for (int tt = 0; tt < TT; ++tt) voff_row[tt] = (uint32_t)tt * row_bytes + lane_off;
+  // resource for the rows starting at chunk row r (r may lie past the chunk end)
+  // (extents in signed 64-bit so that they stay scalar: an unsigned saturating subtract is
+  // lowered to a vector instruction, which turns every load into a waterfall loop)
+  auto rs_d = [&](const char* base, uint32_t r) {
+    const uint32_t off = r * row_bytes;
+    const int64_t e = (int64_t)ext_d - (int64_t)off;
+    return make_rsrc_u32(base + off, e > 0 ? (uint32_t)e : 0u);
+  };
+  auto rs_n = [&](const char* base, uint32_t r) {
+    const uint32_t off = r * bc_row_bytes;
+    const int64_t e = (int64_t)ext_n - (int64_t)off;
+    return make_rsrc_u32(base + off, e > 0 ? (uint32_t)e : 0u);
   };
 
   // ---- B/C staging: global (I/O dtype) -> registers -> LDS (fp32) ----
@@ -129,8 +147,8 @@ void fwd_kernel(const FwdArgs p) {
   }
   raw bre[NPE], cre[NPE];
   auto stage_load = [&](int64_t ts) {
-    const auto rb = rsrc_tile(p.B, ts, N);
-    const auto rc = rsrc_tile(p.C, ts, N);
+    const auto rb = rs_n(B0, (uint32_t)(ts - t0));
+    const auto rc = rs_n(C0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int r = 0; r < NPE; ++r) {
       bre[r] = T::bload(rb, bc_voff[r], 0u);
@@ -151,8 +169,8 @@ void fwd_kernel(const FwdArgs p) {
     }
   };
   auto load_xd = [&](raw(&xr)[TT], raw(&dr)[TT], int64_t ts) {
-    const auto rx = rsrc_tile(p.x, ts, D);
-    const auto rd = rsrc_tile(p.delta, ts, D);
+    const auto rx = rs_d(x0, (uint32_t)(ts - t0));
+    const auto rd = rs_d(dl0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       xr[tt] = T::bload(rx, voff_row[tt], 0u);
@@ -161,8 +179,7 @@ void fwd_kernel(const FwdArgs p) {
   };
 
   // One time step for the K states of this lane.  bc holds [B(K) | C(K)] of that step.
-  auto step = [&](float xv, float dv, const float* bc) -> float {
-    const float c = dv * xv;
+  auto step = [&](float xv, float dv, float c, const float* bc) -> float {
     float ysum = HAS_DSKIP ? dsk * xv : 0.f;
     if (SUMMARY) bpow *= beta;
 #pragma unroll
@@ -183,10 +200,11 @@ void fwd_kernel(const FwdArgs p) {
     if (SUMMARY) sd += dv;
     return ysum;
   };
-  auto emit = [&](int buf, int tt, int64_t t, float ysum) {
+  // ry: resource of the tile being computed (only used when S == 1)
+  auto emit = [&](int buf, int tt, __amdgpu_buffer_rsrc_t ry, float ysum) {
     if (SUMMARY) return;
     if (S == 1) {
-      if (dvalid) T::bstore(rsrc_tile(p.y, t, D), lane_off, 0u, ysum);
+      if (dvalid) T::bstore(ry, (uint32_t)tt * row_bytes + lane_off, 0u, ysum);
     } else {
       ypart[YPART ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
     }
@@ -198,6 +216,7 @@ void fwd_kernel(const FwdArgs p) {
   constexpr int RB = (32 / K) < TT ? (32 / K) : TT;
   constexpr int NB = TT / RB;
   auto compute_tile = [&](const raw(&xr)[TT], const raw(&dr)[TT], int buf, int64_t ts) {
+    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     float bcv[2][RB][BCW];
     auto read_batch = [&](float(&dst)[RB][BCW], int jb) {
 #pragma unroll
@@ -215,22 +234,24 @@ void fwd_kernel(const FwdArgs p) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int tt = jb * RB + i;
-        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), bcv[jb & 1][i]);
-        emit(buf, tt, ts + tt, ysum);
+        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), T::mul_raw(dr[tt], xr[tt]),
+                                bcv[jb & 1][i]);
+        emit(buf, tt, ry, ysum);
       }
     }
   };
   auto compute_tail = [&](int buf, int64_t ts, int nv) {
+    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     for (int tt = 0; tt < nv; ++tt) {
       const int64_t row = (b * L + ts + tt) * D;
-      const float ysum = step(T::widen(T::load_row(p.x, row, dl)),
-                              T::widen(T::load_row(p.delta, row, dl)), &bcs[buf][tt][g][0]);
-      emit(buf, tt, ts + tt, ysum);
+      const raw xr = T::load_row(p.x, row, dl), dr = T::load_row(p.delta, row, dl);
+      const float ysum = step(T::widen(xr), T::widen(dr), T::mul_raw(dr, xr), &bcs[buf][tt][g][0]);
+      emit(buf, tt, ry, ysum);
     }
   };
   auto finalize = [&](int buf, int64_t ts, int nv) {
     if (!YPART) return;
-    const auto ry = rsrc_tile(p.y, ts, D);
+    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     for (int tt = g; tt < nv; tt += S) {
       float s = 0.f;
 #pragma unroll
