@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsm.so")
-SOURCES = ["msm_api.cpp", "msm_fwd.hip", "msm_bwd.hip"]
+SOURCES = ["msm_api.cpp", "msm_fwd.hip", "msm_bwd.hip", "msm_bwd_wide.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

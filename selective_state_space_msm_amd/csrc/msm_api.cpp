@@ -108,26 +108,31 @@ FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
 }
 
 // ---- backward planning ----
-msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
-  const int NP = padded_states(N);
-  const int64_t chan_blocks = Bt * ceil_div(D, kWave);
-  msm_plan pl{0, 1};
-  const int kmin = NP == 64 ? 4 : 1;
-  for (int K = 4; K >= kmin; K /= 2) {
-    if (!allowed_k(NP, K)) continue;
-    pl.states_per_wave = K;
-    if (chan_blocks * (NP / K) >= kTargetWaves) return pl;
-  }
-  return pl;  // smallest allowed K: most parallelism available without chunking
-}
+// channels per backward workgroup
+int64_t bwd_chans(int NP) { return NP == 64 ? kWave : msm::kBwdChans; }
 
 bool bwd_allowed_k(int NP, int K) {
   switch (NP) {
-    case 4: return K == 1 || K == 2 || K == 4;
+    case 4: return K == 1 || K == 2;
     case 16: return K == 1 || K == 2 || K == 4;
-    case 64: return K == 4;
+    case 64: return K == 4;  // the full-wavefront backward: 16 wavefronts of 4 states
     default: return false;
   }
+}
+
+// For 4 or 16 padded states a backward workgroup holds 2K states of kBwdChans channels per
+// wavefront and NP / (2K) wavefronts.  The largest K that still gives a wavefront per SIMD wins;
+// otherwise the smallest allowed K (most wavefronts).  64 padded states always take K = 4.
+msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int NP = padded_states(N);
+  const int64_t chan_blocks = Bt * ceil_div(D, bwd_chans(NP));
+  msm_plan pl{0, 1};
+  for (int K = 4; K >= 1; K /= 2) {
+    if (!bwd_allowed_k(NP, K)) continue;
+    pl.states_per_wave = K;
+    if (chan_blocks * (NP / (bwd_chans(NP) == kWave ? K : 2 * K)) >= kTargetWaves) return pl;
+  }
+  return pl;
 }
 
 struct BwdLayout {
@@ -136,7 +141,8 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int64_t NT = ceil_div(L, msm::kBwdTile);
-  const int64_t ncb = ceil_div(D, kWave);
+  // sized for the narrower channel blocks, which have the most partial sums
+  const int64_t ncb = ceil_div(D, msm::kBwdChans);
   const int NP = padded_states(N);
   BwdLayout l{};
   l.off_ckpt = 0;
@@ -357,7 +363,7 @@ msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float*
   a.D = D;
   a.N = N;
   a.NT = ceil_div(L, msm::kBwdTile);
-  a.ncb = (int32_t)ceil_div(D, kWave);
+  a.ncb = (int32_t)ceil_div(D, bwd_chans(NP));
   a.NP = NP;
   a.beta = beta;
   a.alpha = alpha;

@@ -7,87 +7,127 @@
 //   dA   += delta_t a_t h_{t-1} gh_t        dB_t += alpha delta_t x_t gv_t  (sum over d)
 //   dC_t += dy_t h_t  (sum over d)          dx += Dskip dy, dDskip = sum dy x
 //
-// Work decomposition mirrors the forward: lane = channel, a wavefront keeps K states, a
-// workgroup holds S wavefronts with disjoint state groups of the same 64 channels.
+// Work decomposition.  A workgroup owns kBwdChans = 32 channels of one batch row; lane l of a
+// wavefront serves channel l % 32 and the two 32-lane halves hold different states, so a
+// wavefront keeps 2K states of 32 channels and a workgroup of S wavefronts covers all NP = 2SK
+// (padded) states.  Half-width channel blocks double the number of workgroups, which is what
+// fills the 256 CUs at the usual training shapes (Bt * D / 32 workgroups).
 //   phase 1: forward over the whole sequence, writing the (v, h) state before every tile of
 //            kBwdTile steps to a checkpoint buffer (the recompute strategy of the README's
 //            backward notes: reconstruct the forward instead of storing it);
 //   phase 2: tiles in reverse order; each tile is recomputed from its checkpoint into
 //            registers (h_t and a_t for every step), then swept backwards.
-// Reductions: the sums over n for dx/ddelta go across the S wavefronts through LDS (fixed
-// order); the sums over channels d for dB/dC go across the 64 lanes with a butterfly
-// reduce-scatter, then across channel blocks in a small finalize kernel (fixed order, so the
-// result does not depend on scheduling).
+// x, delta, dy and B, C are staged once per workgroup into LDS, one tile ahead (the loads for
+// the next tile are issued before the current tile's arithmetic and written to the other LDS
+// buffer after it).  The adjoint state and the sums behind dx / ddelta / dA are fp64: ddelta
+// is a difference of two large sums, and fp32 adjoints lose too many bits over long sequences.
+// Reductions, all in a fixed order so results do not depend on scheduling:
+//   over n for dx / ddelta: in-lane over K, across the two halves with v_permlane32_swap,
+//     across the S wavefronts through LDS;
+//   over d for dB / dC: across the 32 lanes of a half with a reduce-scatter (v_permlane16_swap
+//     then DPP), then across channel blocks in a small finalize kernel.
+// This kernel serves 4 and 16 padded states; 64 padded states use the full-wavefront
+// backward in msm_bwd_wide.hip.
 #include "msm_device.hpp"
 #include "msm_internal.h"
 
 namespace msm {
 namespace {
 
-// Butterfly reduce-scatter of M values over the 64 lanes of a wavefront.  Stage SMASK
-// exchanges with lane ^ SMASK: lanes with that bit set keep the upper half of the remaining
-// values, the others the lower half, and each adds what its partner sent.  Once one value is
-// left, the remaining stages are a plain all-reduce.  On return lane l holds in v[0] the sum
-// over all 64 lanes of value (l >> (6 - log2 M)).
-template <int CNT, int SMASK, int M>
-__device__ __forceinline__ void rs_stage(float (&v)[M], int lane) {
-  if constexpr (SMASK >= 1) {
-    if constexpr (CNT > 1) {
-      constexpr int HALF = CNT / 2;
-      const bool up = (lane & SMASK) != 0;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// One reduce-scatter stage inside a 16-lane row: lanes are paired by the DPP pattern CTRL,
+// partners differ in lane bit MASK; the lane with the bit set keeps the upper half.
+template <int CTRL, int MASK, int H, int M>
+__device__ __forceinline__ void rs_dpp(float (&v)[M], int lane) {
+  const bool up = (lane & MASK) != 0;
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) {
-        const float keep = up ? v[i + HALF] : v[i];
-        const float send = up ? v[i] : v[i + HALF];
-        v[i] = keep + __shfl_xor(send, SMASK);
-      }
-      rs_stage<HALF, SMASK / 2, M>(v, lane);
-    } else {
-      v[0] += __shfl_xor(v[0], SMASK);
-      rs_stage<1, SMASK / 2, M>(v, lane);
-    }
+  for (int i = 0; i < H; ++i) {
+    const float lo = v[i] + dpp<CTRL>(v[i]);
+    const float hi = v[i + H] + dpp<CTRL>(v[i + H]);
+    v[i] = up ? hi : lo;
   }
 }
 
-template <int M>
-__device__ __forceinline__ void reduce_scatter64(float (&v)[M], int lane) {
-  static_assert(M >= 1 && M <= 64 && (M & (M - 1)) == 0, "M must be a power of two <= 64");
-  rs_stage<M, 32, M>(v, lane);
+// Reduce-scatter of 32 values over each 32-lane half of a wavefront.  The pairings are
+// lane^16 (permlane16 swap), lane^15 (row mirror), lane^7 within 8 (half-row mirror), lane^2
+// and lane^1 (quad permutes); each pairs lanes that agree on the bits decided so far and
+// differ in the next one (16, 8, 4, 2, 1), and together they cover all 32 lanes.  On return
+// lane l holds in v[0] the sum over its half of value (l & 31).
+__device__ __forceinline__ void reduce_scatter32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // after the swap, lanes 0-15 of each 32 hold (their v[i], partner's v[i]) and lanes 16-31
+    // hold (partner's v[i+16], their v[i+16])
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + 16]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  rs_dpp<0x140, 8, 8>(v, lane);  // row_mirror
+  rs_dpp<0x141, 4, 4>(v, lane);  // row_half_mirror
+  rs_dpp<0x4E, 2, 2>(v, lane);   // quad_perm [2,3,0,1]
+  rs_dpp<0xB1, 1, 1>(v, lane);   // quad_perm [1,0,3,2]
 }
 
-constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+// Adds a across the two halves of the wavefront for lanes 0-31 and b for lanes 32-63 (the
+// same pairing trick as above, with v_permlane32_swap on both 32-bit words of each double).
+__device__ __forceinline__ double swap_add32(double a, double b) {
+  const uint64_t ua = __double_as_longlong(a), ub = __double_as_longlong(b);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
+                                                   false, false);
+  const double e0 = __longlong_as_double((int64_t)(((uint64_t)hi[0] << 32) | lo[0]));
+  const double e1 = __longlong_as_double((int64_t)(((uint64_t)hi[1] << 32) | lo[1]));
+  return e0 + e1;
+}
+
+// Buffer resource for the rows of a (L, row_bytes) slab starting at row r; rows at or past
+// the end read as zero and are never written.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t r,
+                                                             int64_t row_bytes, int64_t total) {
+  const int64_t off = r * row_bytes;
+  return make_rsrc(static_cast<const char*>(base) + off, total - off);
+}
 
 template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP>
 __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
+  constexpr int CB = kBwdChans;          // channels per workgroup
+  constexpr int P = kWave / CB;          // state groups per wavefront (2)
   constexpr int TB = kBwdTile;
-  constexpr int BCW = 2 * K;
-  constexpr int BC_PER_TILE = TB * S * BCW;
   constexpr int NTHR = S * kWave;
-  constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
-  // rows whose per-wavefront partials sit in LDS at once (fp64, so fewer rows for big S)
-  constexpr int SR = S >= 16 ? 8 : TB;
+  constexpr int NPB = S * P * K;         // padded states of the workgroup
+  constexpr int GS = S * P;              // state groups of the workgroup
+  // rows whose per-wavefront dx / ddelta partials sit in LDS at once
+  constexpr int SR = (S * TB * kWave * 8 <= 65536) ? TB : TB / 2;
   constexpr int NSR = TB / SR;
-  // steps per lane-reduce block of dB/dC values (at most 64 values per block)
-  constexpr int RB = (64 / (2 * K)) < SR ? (64 / (2 * K)) : SR;
-  constexpr int M = 2 * K * RB;
+  constexpr int M = 32;                  // values per lane in one dB/dC reduce-scatter
+  constexpr int RB = M / (2 * K);        // rows per reduce-scatter
   constexpr int NRB = SR / RB;
-  static_assert(TB % SR == 0 && SR % RB == 0, "tile must split into rounds and reduce blocks");
+  static_assert(P == 2, "the lane pairing below assumes two 32-lane halves");
+  static_assert(RB >= 1 && SR % RB == 0 && TB % SR == 0, "tile must split into reduce blocks");
 
-  __shared__ float bcs[TB][S][BCW];       // fp32 B (alpha-scaled) | C, for the recompute
-  __shared__ double bcs64[TB][S][BCW];    // the same values widened, for the adjoint sweep
-  __shared__ double spart[2][S][SR][kWave];
+  __shared__ float4 xs[2][TB][CB];            // x, delta, dy, delta * x
+  __shared__ float bcs[2][TB][GS][2 * K];     // alpha B | C, for the recompute
+  __shared__ double bcs64[2][TB][GS][2 * K];  // the same values widened, for the adjoint
+  __shared__ double spart[S][SR][kWave];      // per wavefront: dx (lanes < 32) | ddelta
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int g = tid / kWave;
-  const int cb = (int)(blockIdx.x % p.ncb);
-  const int64_t b = blockIdx.x / p.ncb;
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ch = lane & (CB - 1);
+  const int gs = g * P + lane / CB;  // state group of this lane
+  const uint32_t bq = blockIdx.x / (uint32_t)p.ncb;
+  const int cb = (int)(blockIdx.x - bq * (uint32_t)p.ncb);
+  const int64_t b = bq;
   const int64_t L = p.L, D = p.D, N = p.N, NT = p.NT;
-  const int64_t d = (int64_t)cb * kWave + lane;
+  const int d = cb * CB + ch;
   const bool dvalid = d < D;
-  const int64_t dl = dvalid ? d : D - 1;
+  const int dl = dvalid ? d : (int)D - 1;
   const float beta = p.beta;
   const double beta64 = p.beta;
 
@@ -95,7 +135,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   double A64[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int64_t n = (int64_t)g * K + j;
+    const int64_t n = (int64_t)gs * K + j;
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     A64[j] = an;
@@ -103,23 +143,85 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     h[j] = 0.f;
   }
 
-  auto stage = [&](int64_t ts, int64_t nv) {
+  // ---- staging addresses (per-tile buffer resources, constant per-thread offsets) ----
+  const int64_t row_bytes = D * T::es, bc_row_bytes = N * T::es;
+  const int64_t tot_d = L * row_bytes, tot_n = L * bc_row_bytes;
+  const char* x0 = static_cast<const char*>(p.x) + b * tot_d;
+  const char* dl0 = static_cast<const char*>(p.delta) + b * tot_d;
+  const char* dy0 = static_cast<const char*>(p.dy) + b * tot_d;
+  const char* B0 = static_cast<const char*>(p.B) + b * tot_n;
+  const char* C0 = static_cast<const char*>(p.C) + b * tot_n;
+
+  constexpr int XE = TB * CB;  // elements of one array in one tile
+  constexpr int NX = (XE + NTHR - 1) / NTHR;
+  uint32_t x_voff[NX];
 #pragma unroll
-    for (int r = 0; r < NPER; ++r) {
+  for (int r = 0; r < NX; ++r) {
+    const int i = tid + r * NTHR;
+    const int ic = i < XE ? i : XE - 1;
+    const int dch = cb * CB + ic % CB;
+    x_voff[r] = (uint32_t)((ic / CB) * row_bytes + (dch < D ? dch : D - 1) * T::es);
+  }
+  raw xr[NX], dr[NX], gr[NX];
+  auto x_load = [&](int64_t ts, bool with_dy) {
+    const auto rx = rows_rsrc(x0, ts, row_bytes, tot_d);
+    const auto rd = rows_rsrc(dl0, ts, row_bytes, tot_d);
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      xr[r] = T::bload(rx, x_voff[r], 0u);
+      dr[r] = T::bload(rd, x_voff[r], 0u);
+    }
+    if (with_dy) {
+      const auto rg = rows_rsrc(dy0, ts, row_bytes, tot_d);
+#pragma unroll
+      for (int r = 0; r < NX; ++r) gr[r] = T::bload(rg, x_voff[r], 0u);
+    }
+  };
+  auto x_store = [&](int buf, bool with_dy) {
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
       const int i = tid + r * NTHR;
-      if (i < BC_PER_TILE) {
-        const int tt = i / (S * BCW);
-        const int rem = i % (S * BCW);
-        const int gg = rem / BCW;
-        const int r2 = rem % BCW;
-        const int64_t n = (int64_t)gg * K + (r2 % K);
-        float val = 0.f;
-        if (tt < nv && n < N) {
-          const int64_t idx = (b * L + ts + tt) * N + n;
-          val = (r2 >= K) ? T::widen(T::load(p.C, idx)) : T::widen(T::load(p.B, idx)) * p.alpha;
-        }
-        (&bcs[0][0][0])[i] = val;
-        (&bcs64[0][0][0])[i] = val;
+      if (NX * NTHR == XE || i < XE) {
+        const float xv = T::widen(xr[r]), dv = T::widen(dr[r]);
+        xs[buf][i / CB][i % CB] = make_float4(xv, dv, with_dy ? T::widen(gr[r]) : 0.f, dv * xv);
+      }
+    }
+  };
+
+  constexpr int BCE = TB * NPB;  // (row, state) pairs of one tile
+  constexpr int NPE = (BCE + NTHR - 1) / NTHR;
+  uint32_t bc_voff[NPE];
+  bool bc_nok[NPE];
+#pragma unroll
+  for (int r = 0; r < NPE; ++r) {
+    const int i = tid + r * NTHR;
+    const int ic = i < BCE ? i : BCE - 1;
+    const int n = ic % NPB;
+    bc_nok[r] = n < N;
+    bc_voff[r] = (uint32_t)(((ic / NPB) * N + (n < N ? n : 0)) * T::es);
+  }
+  raw bre[NPE], cre[NPE];
+  auto bc_load = [&](int64_t ts) {
+    const auto rb = rows_rsrc(B0, ts, bc_row_bytes, tot_n);
+    const auto rc = rows_rsrc(C0, ts, bc_row_bytes, tot_n);
+#pragma unroll
+    for (int r = 0; r < NPE; ++r) {
+      bre[r] = T::bload(rb, bc_voff[r], 0u);
+      cre[r] = T::bload(rc, bc_voff[r], 0u);
+    }
+  };
+  auto bc_store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NPE; ++r) {
+      const int i = tid + r * NTHR;
+      if (NPE * NTHR == BCE || i < BCE) {
+        const int tt = i / NPB, n = i % NPB;
+        const float bv = bc_nok[r] ? T::widen(bre[r]) * p.alpha : 0.f;
+        const float cv = bc_nok[r] ? T::widen(cre[r]) : 0.f;
+        bcs[buf][tt][n / K][n % K] = bv;
+        bcs[buf][tt][n / K][K + n % K] = cv;
+        bcs64[buf][tt][n / K][n % K] = bv;
+        bcs64[buf][tt][n / K][K + n % K] = cv;
       }
     }
   };
@@ -127,50 +229,57 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     return (((b * NT + tile) * 2 + which) * N + n) * D + dl;
   };
 
-  // ---------------- phase 1: forward with checkpoints ----------------
-  for (int64_t tile = 0; tile < NT; ++tile) {
-    const int64_t ts = tile * TB;
-    const int64_t nv = (L - ts < TB) ? L - ts : TB;
-    if (dvalid) {
+  // one forward step of the K states (recurrence only); c = delta * x
+  auto fstep = [&](float dv, float c, const float* bb, float* a_out, float* h_out) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int64_t n = (int64_t)g * K + j;
-        if (n < N) {
-          p.ckpt[ckpt_index(tile, 0, n)] = v[j];
-          p.ckpt[ckpt_index(tile, 1, n)] = h[j];
-        }
-      }
+    for (int j = 0; j < K; ++j) {
+      const float a = exp2_fast(dv * A2[j]);
+      const float w = c * bb[j];
+      v[j] = BETA0 ? w : fmaf(beta, v[j], w);
+      h[j] = fmaf(a, h[j], v[j]);
+      if (a_out) a_out[j] = a;
+      if (h_out) h_out[j] = h[j];
     }
-    raw xr[TB], dr[TB];
-#pragma unroll
-    for (int tt = 0; tt < TB; ++tt) {
-      const int64_t t = ts + (tt < nv ? tt : nv - 1);
-      xr[tt] = T::load(p.x, (b * L + t) * D + dl);
-      dr[tt] = T::load(p.delta, (b * L + t) * D + dl);
-    }
+  };
+
+  // ---------------- phase 1: forward over the whole sequence, checkpoint every tile ----
+  {
+    int buf = 0;
+    bc_load(0);
+    x_load(0, false);
+    bc_store(0);
+    x_store(0, false);
     __syncthreads();
-    stage(ts, nv);
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < TB; ++tt) {
-      if (tt < nv) {
-        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
-        const float c = dv * xv;
-        const float* bc = &bcs[tt][g][0];
+    for (int64_t tile = 0; tile < NT; ++tile) {
+      const int64_t ts = tile * TB;
+      if (dvalid) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          const float a = exp2_fast(dv * A2[j]);
-          const float w = c * bc[j];
-          v[j] = BETA0 ? w : fmaf(beta, v[j], w);
-          h[j] = fmaf(a, h[j], v[j]);
+          const int64_t n = (int64_t)gs * K + j;
+          if (n < N) {
+            p.ckpt[ckpt_index(tile, 0, n)] = v[j];
+            p.ckpt[ckpt_index(tile, 1, n)] = h[j];
+          }
         }
       }
+      // next tile, unconditionally (past the end the resources read zeros)
+      bc_load(ts + TB);
+      x_load(ts + TB, false);
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const float4 r = xs[buf][tt][ch];
+        fstep(r.y, r.w, &bcs[buf][tt][gs][0], nullptr, nullptr);
+      }
+      if (tile + 1 < NT) {
+        bc_store(buf ^ 1);
+        x_store(buf ^ 1, false);
+      }
+      __syncthreads();
+      buf ^= 1;
     }
   }
 
   // ---------------- phase 2: reverse sweep ----------------
-  // The adjoint state and the sums that feed ddelta are kept in fp64: ddelta is a difference
-  // of two large terms (x * sum B gv and sum A a h gh), and fp32 adjoints lose too many bits.
   double ghn[K], gvn[K], dAacc[K];  // ghn = a_{t+1} gh_{t+1}, gvn = beta gv_{t+1}
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -178,61 +287,55 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     gvn[j] = 0.0;
     dAacc[j] = 0.0;
   }
-  float dDacc = 0.f;
-  const float dsk = HAS_DSKIP ? p.Dskip[dl] : 0.f;
-  float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * p.NP;
+  double dDacc = 0.0;
+  const double dsk = (HAS_DSKIP && gs == 0) ? (double)p.Dskip[dl] : 0.0;
+  float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
+  char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
+  char* ddl0 = static_cast<char*>(p.ddelta) + b * tot_d;
+  const uint32_t lane_off = (uint32_t)dl * T::es;
 
+  float cv[K], chh[K];  // checkpoint (v, h) before the current tile
+  auto load_ckpt = [&](float(&ov)[K], float(&oh)[K], int64_t tile) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)gs * K + j;
+      const int64_t nc = n < N ? n : N - 1;
+      ov[j] = n < N ? p.ckpt[ckpt_index(tile, 0, nc)] : 0.f;
+      oh[j] = n < N ? p.ckpt[ckpt_index(tile, 1, nc)] : 0.f;
+    }
+  };
+  int buf = 0;
+  load_ckpt(cv, chh, NT - 1);
+  bc_load((NT - 1) * TB);
+  x_load((NT - 1) * TB, true);
+  bc_store(0);
+  x_store(0, true);
+  __syncthreads();
   for (int64_t tile = NT - 1; tile >= 0; --tile) {
     const int64_t ts = tile * TB;
     const int nv = (int)((L - ts < TB) ? L - ts : TB);
-    raw xr[TB], dr[TB], gr[TB];
-#pragma unroll
-    for (int tt = 0; tt < TB; ++tt) {
-      const int64_t t = ts + (tt < nv ? tt : nv - 1);
-      const int64_t idx = (b * L + t) * D + dl;
-      xr[tt] = T::load(p.x, idx);
-      dr[tt] = T::load(p.delta, idx);
-      gr[tt] = T::load(p.dy, idx);
-    }
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)g * K + j;
-      v[j] = n < N ? p.ckpt[ckpt_index(tile, 0, n)] : 0.f;
-      h[j] = n < N ? p.ckpt[ckpt_index(tile, 1, n)] : 0.f;
-    }
-    __syncthreads();  // previous tile's readers of bcs / spart are done
-    stage(ts, nv);
-    __syncthreads();
+    const int64_t tp = tile > 0 ? tile - 1 : 0;  // prefetch (tile 0 again at the end)
+    float cvn[K], chn[K];
+    load_ckpt(cvn, chn, tp);
+    bc_load(tp * TB);
+    x_load(tp * TB, true);
 
-    // recompute the tile: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt}
+    // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt}
     float hs[TB + 1][K], av[TB][K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) hs[0][j] = h[j];
+    for (int j = 0; j < K; ++j) {
+      v[j] = cv[j];
+      h[j] = chh[j];
+      hs[0][j] = h[j];
+    }
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
-      if (tt < nv) {
-        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
-        const float c = dv * xv;
-        const float* bc = &bcs[tt][g][0];
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-          const float a = exp2_fast(dv * A2[j]);
-          const float w = c * bc[j];
-          v[j] = BETA0 ? w : fmaf(beta, v[j], w);
-          h[j] = fmaf(a, h[j], v[j]);
-          av[tt][j] = a;
-          hs[tt + 1][j] = h[j];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-          av[tt][j] = 0.f;
-          hs[tt + 1][j] = 0.f;
-        }
-      }
+      const float4 r = xs[buf][tt][ch];
+      fstep(r.y, r.w, &bcs[buf][tt][gs][0], av[tt], hs[tt + 1]);
     }
 
-    // reverse sweep over the tile in rounds of SR rows, each split into reduce blocks of RB
+    const auto rdx = rows_rsrc(dx0, ts, row_bytes, tot_d);
+    const auto rdd = rows_rsrc(ddl0, ts, row_bytes, tot_d);
 #pragma unroll
     for (int sr = NSR - 1; sr >= 0; --sr) {
 #pragma unroll
@@ -242,82 +345,77 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         for (int tb = RB - 1; tb >= 0; --tb) {
           const int tr = rb * RB + tb;  // row within the round
           const int tt = sr * SR + tr;  // row within the tile
-          if (tt < nv) {
-            const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]), gy = T::widen(gr[tt]);
-            const float c = dv * xv;
-            const double gy64 = gy, dv64 = dv;
-            const double* bc = &bcs64[tt][g][0];
-            double s1 = 0.0, s2 = 0.0;
+          const float4 r = xs[buf][tt][ch];
+          const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
+          const double gy64 = gy, dv64 = dv;
+          const double* bc = &bcs64[buf][tt][gs][0];
+          double s1 = 0.0, s2 = 0.0;
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-              const double a64 = av[tt][j];
-              const double gh = fma(bc[K + j], gy64, ghn[j]);
-              const double gv = BETA0 ? gh : gh + gvn[j];
-              s1 = fma(bc[j], gv, s1);
-              const double gg = a64 * (double)hs[tt][j] * gh;
-              s2 = fma(A64[j], gg, s2);
-              dAacc[j] = fma(dv64, gg, dAacc[j]);
-              vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
-              vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
-              ghn[j] = a64 * gh;
-              if (!BETA0) gvn[j] = beta64 * gv;
-            }
-            spart[0][g][tr][lane] = s1;
-            spart[1][g][tr][lane] = s2;
-            if (HAS_DSKIP) dDacc = fmaf(gy, xv, dDacc);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 2 * K; ++j) vals[tb * 2 * K + j] = 0.f;
+          for (int j = 0; j < K; ++j) {
+            const double a64 = av[tt][j];
+            const double gh = fma(bc[K + j], gy64, ghn[j]);
+            const double gv = BETA0 ? gh : gh + gvn[j];
+            s1 = fma(bc[j], gv, s1);
+            ghn[j] = a64 * gh;
+            const double gg = ghn[j] * (double)hs[tt][j];  // a_t h_{t-1} gh_t
+            s2 = fma(A64[j], gg, s2);
+            dAacc[j] = fma(dv64, gg, dAacc[j]);
+            if (!BETA0) gvn[j] = beta64 * gv;
+            vals[(tb * 2 + 0) * K + j] = dvalid ? c * (float)gv : 0.f;       // dB / alpha
+            vals[(tb * 2 + 1) * K + j] = dvalid ? gy * hs[tt + 1][j] : 0.f;  // dC
           }
+          const double qx = fma(dsk, gy64, dv64 * s1);
+          const double qd = fma((double)xv, s1, s2);
+          spart[g][tr][lane] = swap_add32(qx, qd);
+          if (HAS_DSKIP) dDacc = fma(gy64, (double)xv, dDacc);
         }
-        if (!dvalid) {
-#pragma unroll
-          for (int i = 0; i < M; ++i) vals[i] = 0.f;
-        }
-        reduce_scatter64<M>(vals, lane);
-        constexpr int SH = 6 - ilog2(M);
-        const int idx = lane >> SH;
-        if ((lane & ((1 << SH) - 1)) == 0) {
-          const int tb = idx / (2 * K);
-          const int which = (idx / K) % 2;
-          const int j = idx % K;
-          const int tt = sr * SR + rb * RB + tb;
-          const int64_t n = (int64_t)g * K + j;
-          if (tt < nv && n < N) dbc[(ts + tt) * 2 * p.NP + which * p.NP + n] = vals[0];
-        }
+        reduce_scatter32(vals, lane);
+        const int m = lane & 31;
+        const int tt = sr * SR + rb * RB + m / (2 * K);
+        const int n = gs * K + m % K;
+        if (tt < nv) dbc[(ts + tt) * 2 * NPB + ((m / K) & 1) * NPB + n] = vals[0];
       }
       __syncthreads();
-      // dx / ddelta for the rows of this round owned by this wavefront: add the S partials
-      // in a fixed order, then combine in fp64 (the ddelta cancellation happens here)
-      for (int tr = g; tr < SR; tr += S) {
-        const int tt = sr * SR + tr;
-        if (tt >= nv) break;
-        double s1 = 0.0, s2 = 0.0;
+      // dx / ddelta of this round's rows: each wavefront takes every S-th row and adds the S
+      // partials of its lane in a fixed order (fp64), rounding once to the I/O type
 #pragma unroll
-        for (int gg = 0; gg < S; ++gg) {
-          s1 += spart[0][gg][tr][lane];
-          s2 += spart[1][gg][tr][lane];
-        }
-        if (dvalid) {
-          const int64_t idx = (b * L + ts + tt) * D + d;
-          const double xv = T::widen(T::load(p.x, idx)), dv = T::widen(T::load(p.delta, idx));
-          double dxv = dv * s1;
-          if (HAS_DSKIP) dxv = fma((double)dsk, (double)T::widen(T::load(p.dy, idx)), dxv);
-          T::store(p.dx, idx, (float)dxv);
-          T::store(p.ddelta, idx, (float)fma(xv, s1, s2));
+      for (int tr0 = 0; tr0 < SR; tr0 += S) {
+        const int tr = tr0 + g;
+        const int tt = sr * SR + tr;
+        if (tr < SR && tt < nv) {
+          double q = 0.0;
+#pragma unroll
+          for (int w = 0; w < S; ++w) q += spart[w][tr][lane];
+          if (dvalid) {
+            if (lane < CB)
+              T::bstore(rdx, lane_off, (uint32_t)(tt * row_bytes), (float)q);
+            else
+              T::bstore(rdd, lane_off, (uint32_t)(tt * row_bytes), (float)q);
+          }
         }
       }
-      if (NSR > 1) __syncthreads();  // spart is reused by the next round of this tile
+      if (sr > 0) __syncthreads();  // spart is reused by the next round of this tile
+    }
+    if (tile > 0) {
+      bc_store(buf ^ 1);
+      x_store(buf ^ 1, true);
+    }
+    __syncthreads();
+    buf ^= 1;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      cv[j] = cvn[j];
+      chh[j] = chn[j];
     }
   }
 
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)g * K + j;
+      const int64_t n = (int64_t)gs * K + j;
       if (n < N) p.dA_part[(b * N + n) * D + d] = (float)dAacc[j];
     }
-    if (HAS_DSKIP && g == 0) p.dD_part[b * D + d] = dDacc;
+    if (HAS_DSKIP && gs == 0) p.dD_part[b * D + d] = (float)dDacc;
   }
 }
 
@@ -362,35 +460,42 @@ hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false>), grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = a.Bt * a.L * 2 * a.N + a.D * a.N + (a.Dskip ? a.D : 0);
-  hipLaunchKernelGGL((bwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256),
-                     0, s, a);
   return hipGetLastError();
 }
 
 template <typename IO, bool BETA0>
 hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
   switch (a.NP * 100 + K) {
-    case 401: return launch_ks<IO, 1, 4, BETA0>(a, s);
-    case 402: return launch_ks<IO, 2, 2, BETA0>(a, s);
-    case 404: return launch_ks<IO, 4, 1, BETA0>(a, s);
-    case 1601: return launch_ks<IO, 1, 16, BETA0>(a, s);
-    case 1602: return launch_ks<IO, 2, 8, BETA0>(a, s);
-    case 1604: return launch_ks<IO, 4, 4, BETA0>(a, s);
-    case 6404: return launch_ks<IO, 4, 16, BETA0>(a, s);
+    // S = NP / (2K) wavefronts per workgroup
+    case 401: return launch_ks<IO, 1, 2, BETA0>(a, s);
+    case 402: return launch_ks<IO, 2, 1, BETA0>(a, s);
+    case 1601: return launch_ks<IO, 1, 8, BETA0>(a, s);
+    case 1602: return launch_ks<IO, 2, 4, BETA0>(a, s);
+    case 1604: return launch_ks<IO, 4, 2, BETA0>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename IO>
+hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
+  const int64_t total = a.Bt * a.L * 2 * a.N + a.D * a.N + (a.Dskip ? a.D : 0);
+  hipLaunchKernelGGL((bwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s) {
-  if (io_bf16) {
-    return beta0 ? launch_io<bf16_storage, true>(a, K, s) : launch_io<bf16_storage, false>(a, K, s);
-  }
-  return beta0 ? launch_io<float, true>(a, K, s) : launch_io<float, false>(a, K, s);
+  hipError_t e;
+  if (a.NP == 64)
+    e = launch_bwd_wide(a, io_bf16, beta0, s);
+  else if (io_bf16)
+    e = beta0 ? launch_io<bf16_storage, true>(a, K, s) : launch_io<bf16_storage, false>(a, K, s);
+  else
+    e = beta0 ? launch_io<float, true>(a, K, s) : launch_io<float, false>(a, K, s);
+  if (e != hipSuccess) return e;
+  return io_bf16 ? launch_finalize<bf16_storage>(a, s) : launch_finalize<float>(a, s);
 }
 
 }  // namespace msm

@@ -1,0 +1,329 @@
+// Backward of the momentum selective scan for 64 padded states (17 <= N <= 64), gfx950.
+//
+// Same adjoints and the same two phases as the half-wavefront backward (msm_bwd.hip), with
+// full-wavefront channel blocks: lane = channel (64 per workgroup), a wavefront keeps K = 4
+// states and a workgroup of 16 wavefronts covers the 64 states.  The sums over channels for
+// dB / dC use a butterfly reduce-scatter over the 64 lanes; dx / ddelta sum the 16 wavefront
+// partials through LDS in a fixed order.  Partials go through the shared finalize kernel.
+#include "msm_device.hpp"
+#include "msm_internal.h"
+
+namespace msm {
+namespace {
+
+// Butterfly reduce-scatter of M values over the 64 lanes of a wavefront.  Stage SMASK
+// exchanges with lane ^ SMASK: lanes with that bit set keep the upper half of the remaining
+// values, the others the lower half, and each adds what its partner sent.  Once one value is
+// left, the remaining stages are a plain all-reduce.  On return lane l holds in v[0] the sum
+// over all 64 lanes of value (l >> (6 - log2 M)).
+template <int CNT, int SMASK, int M>
+__device__ __forceinline__ void rs_stage(float (&v)[M], int lane) {
+  if constexpr (SMASK >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int HALF = CNT / 2;
+      const bool up = (lane & SMASK) != 0;
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) {
+        const float keep = up ? v[i + HALF] : v[i];
+        const float send = up ? v[i] : v[i + HALF];
+        v[i] = keep + __shfl_xor(send, SMASK);
+      }
+      rs_stage<HALF, SMASK / 2, M>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], SMASK);
+      rs_stage<1, SMASK / 2, M>(v, lane);
+    }
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void reduce_scatter64(float (&v)[M], int lane) {
+  static_assert(M >= 1 && M <= 64 && (M & (M - 1)) == 0, "M must be a power of two <= 64");
+  rs_stage<M, 32, M>(v, lane);
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP>
+__global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
+  using T = io<IO>;
+  using raw = typename T::raw;
+  constexpr int TB = kBwdTile;
+  constexpr int BCW = 2 * K;
+  constexpr int BC_PER_TILE = TB * S * BCW;
+  constexpr int NTHR = S * kWave;
+  constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
+  // rows whose per-wavefront partials sit in LDS at once (fp64, so fewer rows for big S)
+  constexpr int SR = S >= 16 ? 8 : TB;
+  constexpr int NSR = TB / SR;
+  // steps per lane-reduce block of dB/dC values (at most 64 values per block)
+  constexpr int RB = (64 / (2 * K)) < SR ? (64 / (2 * K)) : SR;
+  constexpr int M = 2 * K * RB;
+  constexpr int NRB = SR / RB;
+  static_assert(TB % SR == 0 && SR % RB == 0, "tile must split into rounds and reduce blocks");
+
+  __shared__ float bcs[TB][S][BCW];       // fp32 B (alpha-scaled) | C, for the recompute
+  __shared__ double bcs64[TB][S][BCW];    // the same values widened, for the adjoint sweep
+  __shared__ double spart[2][S][SR][kWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int g = tid / kWave;
+  const int cb = (int)(blockIdx.x % p.ncb);
+  const int64_t b = blockIdx.x / p.ncb;
+  const int64_t L = p.L, D = p.D, N = p.N, NT = p.NT;
+  const int64_t d = (int64_t)cb * kWave + lane;
+  const bool dvalid = d < D;
+  const int64_t dl = dvalid ? d : D - 1;
+  const float beta = p.beta;
+  const double beta64 = p.beta;
+
+  float A2[K], v[K], h[K];
+  double A64[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t n = (int64_t)g * K + j;
+    const float an = n < N ? p.A[dl * N + n] : 0.f;
+    A2[j] = an * kLog2e;
+    A64[j] = an;
+    v[j] = 0.f;
+    h[j] = 0.f;
+  }
+
+  auto stage = [&](int64_t ts, int64_t nv) {
+#pragma unroll
+    for (int r = 0; r < NPER; ++r) {
+      const int i = tid + r * NTHR;
+      if (i < BC_PER_TILE) {
+        const int tt = i / (S * BCW);
+        const int rem = i % (S * BCW);
+        const int gg = rem / BCW;
+        const int r2 = rem % BCW;
+        const int64_t n = (int64_t)gg * K + (r2 % K);
+        float val = 0.f;
+        if (tt < nv && n < N) {
+          const int64_t idx = (b * L + ts + tt) * N + n;
+          val = (r2 >= K) ? T::widen(T::load(p.C, idx)) : T::widen(T::load(p.B, idx)) * p.alpha;
+        }
+        (&bcs[0][0][0])[i] = val;
+        (&bcs64[0][0][0])[i] = val;
+      }
+    }
+  };
+  auto ckpt_index = [&](int64_t tile, int which, int64_t n) {
+    return (((b * NT + tile) * 2 + which) * N + n) * D + dl;
+  };
+
+  // ---------------- phase 1: forward with checkpoints ----------------
+  for (int64_t tile = 0; tile < NT; ++tile) {
+    const int64_t ts = tile * TB;
+    const int64_t nv = (L - ts < TB) ? L - ts : TB;
+    if (dvalid) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t n = (int64_t)g * K + j;
+        if (n < N) {
+          p.ckpt[ckpt_index(tile, 0, n)] = v[j];
+          p.ckpt[ckpt_index(tile, 1, n)] = h[j];
+        }
+      }
+    }
+    raw xr[TB], dr[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      const int64_t t = ts + (tt < nv ? tt : nv - 1);
+      xr[tt] = T::load(p.x, (b * L + t) * D + dl);
+      dr[tt] = T::load(p.delta, (b * L + t) * D + dl);
+    }
+    __syncthreads();
+    stage(ts, nv);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      if (tt < nv) {
+        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
+        const float c = dv * xv;
+        const float* bc = &bcs[tt][g][0];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float a = exp2_fast(dv * A2[j]);
+          const float w = c * bc[j];
+          v[j] = BETA0 ? w : fmaf(beta, v[j], w);
+          h[j] = fmaf(a, h[j], v[j]);
+        }
+      }
+    }
+  }
+
+  // ---------------- phase 2: reverse sweep ----------------
+  // The adjoint state and the sums that feed ddelta are kept in fp64: ddelta is a difference
+  // of two large terms (x * sum B gv and sum A a h gh), and fp32 adjoints lose too many bits.
+  double ghn[K], gvn[K], dAacc[K];  // ghn = a_{t+1} gh_{t+1}, gvn = beta gv_{t+1}
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    ghn[j] = 0.0;
+    gvn[j] = 0.0;
+    dAacc[j] = 0.0;
+  }
+  float dDacc = 0.f;
+  const float dsk = HAS_DSKIP ? p.Dskip[dl] : 0.f;
+  float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * p.NP;
+
+  for (int64_t tile = NT - 1; tile >= 0; --tile) {
+    const int64_t ts = tile * TB;
+    const int nv = (int)((L - ts < TB) ? L - ts : TB);
+    raw xr[TB], dr[TB], gr[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      const int64_t t = ts + (tt < nv ? tt : nv - 1);
+      const int64_t idx = (b * L + t) * D + dl;
+      xr[tt] = T::load(p.x, idx);
+      dr[tt] = T::load(p.delta, idx);
+      gr[tt] = T::load(p.dy, idx);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)g * K + j;
+      v[j] = n < N ? p.ckpt[ckpt_index(tile, 0, n)] : 0.f;
+      h[j] = n < N ? p.ckpt[ckpt_index(tile, 1, n)] : 0.f;
+    }
+    __syncthreads();  // previous tile's readers of bcs / spart are done
+    stage(ts, nv);
+    __syncthreads();
+
+    // recompute the tile: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt}
+    float hs[TB + 1][K], av[TB][K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) hs[0][j] = h[j];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      if (tt < nv) {
+        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
+        const float c = dv * xv;
+        const float* bc = &bcs[tt][g][0];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float a = exp2_fast(dv * A2[j]);
+          const float w = c * bc[j];
+          v[j] = BETA0 ? w : fmaf(beta, v[j], w);
+          h[j] = fmaf(a, h[j], v[j]);
+          av[tt][j] = a;
+          hs[tt + 1][j] = h[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          av[tt][j] = 0.f;
+          hs[tt + 1][j] = 0.f;
+        }
+      }
+    }
+
+    // reverse sweep over the tile in rounds of SR rows, each split into reduce blocks of RB
+#pragma unroll
+    for (int sr = NSR - 1; sr >= 0; --sr) {
+#pragma unroll
+      for (int rb = NRB - 1; rb >= 0; --rb) {
+        float vals[M];
+#pragma unroll
+        for (int tb = RB - 1; tb >= 0; --tb) {
+          const int tr = rb * RB + tb;  // row within the round
+          const int tt = sr * SR + tr;  // row within the tile
+          if (tt < nv) {
+            const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]), gy = T::widen(gr[tt]);
+            const float c = dv * xv;
+            const double gy64 = gy, dv64 = dv;
+            const double* bc = &bcs64[tt][g][0];
+            double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+              const double a64 = av[tt][j];
+              const double gh = fma(bc[K + j], gy64, ghn[j]);
+              const double gv = BETA0 ? gh : gh + gvn[j];
+              s1 = fma(bc[j], gv, s1);
+              const double gg = a64 * (double)hs[tt][j] * gh;
+              s2 = fma(A64[j], gg, s2);
+              dAacc[j] = fma(dv64, gg, dAacc[j]);
+              vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
+              vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
+              ghn[j] = a64 * gh;
+              if (!BETA0) gvn[j] = beta64 * gv;
+            }
+            spart[0][g][tr][lane] = s1;
+            spart[1][g][tr][lane] = s2;
+            if (HAS_DSKIP) dDacc = fmaf(gy, xv, dDacc);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2 * K; ++j) vals[tb * 2 * K + j] = 0.f;
+          }
+        }
+        if (!dvalid) {
+#pragma unroll
+          for (int i = 0; i < M; ++i) vals[i] = 0.f;
+        }
+        reduce_scatter64<M>(vals, lane);
+        constexpr int SH = 6 - ilog2(M);
+        const int idx = lane >> SH;
+        if ((lane & ((1 << SH) - 1)) == 0) {
+          const int tb = idx / (2 * K);
+          const int which = (idx / K) % 2;
+          const int j = idx % K;
+          const int tt = sr * SR + rb * RB + tb;
+          const int64_t n = (int64_t)g * K + j;
+          if (tt < nv && n < N) dbc[(ts + tt) * 2 * p.NP + which * p.NP + n] = vals[0];
+        }
+      }
+      __syncthreads();
+      // dx / ddelta for the rows of this round owned by this wavefront: add the S partials
+      // in a fixed order, then combine in fp64 (the ddelta cancellation happens here)
+      for (int tr = g; tr < SR; tr += S) {
+        const int tt = sr * SR + tr;
+        if (tt >= nv) break;
+        double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+        for (int gg = 0; gg < S; ++gg) {
+          s1 += spart[0][gg][tr][lane];
+          s2 += spart[1][gg][tr][lane];
+        }
+        if (dvalid) {
+          const int64_t idx = (b * L + ts + tt) * D + d;
+          const double xv = T::widen(T::load(p.x, idx)), dv = T::widen(T::load(p.delta, idx));
+          double dxv = dv * s1;
+          if (HAS_DSKIP) dxv = fma((double)dsk, (double)T::widen(T::load(p.dy, idx)), dxv);
+          T::store(p.dx, idx, (float)dxv);
+          T::store(p.ddelta, idx, (float)fma(xv, s1, s2));
+        }
+      }
+      if (NSR > 1) __syncthreads();  // spart is reused by the next round of this tile
+    }
+  }
+
+  if (dvalid) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)g * K + j;
+      if (n < N) p.dA_part[(b * N + n) * D + d] = (float)dAacc[j];
+    }
+    if (HAS_DSKIP && g == 0) p.dD_part[b * D + d] = dDacc;
+  }
+}
+
+template <typename IO, bool BETA0>
+hipError_t launch_wide(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.ncb * a.Bt)), block(16 * kWave);
+  if (a.Dskip)
+    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, hipStream_t s) {
+  if (a.NP != 64) return hipErrorInvalidValue;
+  if (io_bf16) return beta0 ? launch_wide<bf16_storage, true>(a, s) : launch_wide<bf16_storage, false>(a, s);
+  return beta0 ? launch_wide<float, true>(a, s) : launch_wide<float, false>(a, s);
+}
+
+}  // namespace msm

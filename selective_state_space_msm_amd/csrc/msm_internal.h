@@ -12,6 +12,7 @@ constexpr int kTile = 16;        // time steps staged per LDS tile in the forwar
 constexpr int kMaxChunks = 64;   // upper bound on time chunks (sizes the workspace)
 constexpr int kMaxN = 64;        // states supported per channel
 constexpr int kBwdTile = 16;     // time steps recomputed per register tile in the backward
+constexpr int kBwdChans = 32;    // channels per workgroup in the backward (half a wavefront)
 
 struct FwdArgs {
   const void* x;
@@ -52,18 +53,21 @@ struct BwdArgs {
   float* dDskip;
   // workspace
   float* ckpt;       // [Bt][NT][2][N][D]  (v, h) before each tile of kBwdTile steps
-  float* dbc_part;   // [Bt][ncb][L][2][NP] per channel-block partial sums of dB/alpha and dC
+  float* dbc_part;   // [Bt][ncb][L][2][NP] per channel-block (kBwdChans) partial sums
+                     // of dB/alpha and dC
   float* dA_part;    // [Bt][N][D]
   float* dD_part;    // [Bt][D]
   int64_t Bt, L, D, N;
   int64_t NT;        // tiles = ceil(L / kBwdTile)
-  int32_t ncb;
-  int32_t NP;        // padded states = states_per_wave * waves
+  int32_t ncb;       // channel blocks: kBwdChans channels, or 64 when NP == 64
+  int32_t NP;        // padded states
   float beta, alpha;
 };
 
 // Both return hipSuccess or the first launch error.
 hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
+// The 64-state backward (channel blocks of 64, K = 4); launch_bwd calls it for NP == 64.
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, hipStream_t s);
 
 }  // namespace msm

@@ -114,12 +114,15 @@ def test_bwd_argument_validation_never_launches(lib):
                  dx=0x100000, ddelta=0x200000, dA=0x300000, dB=0x400000, dC=0x500000,
                  dDskip=None, Bt=1, L=8, D=4, N=4, beta=0.5, alpha=1.0, io=0, ws=0x900000,
                  wsb=1 << 30)
+        plan = kw.pop("plan", None)
         a.update(kw)
-        return lib.msm_scan_bwd(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
-                                P(a["Dskip"]), P(a["dy"]), P(a["dx"]), P(a["ddelta"]), P(a["dA"]),
-                                P(a["dB"]), P(a["dC"]), P(a["dDskip"]), a["Bt"], a["L"], a["D"],
-                                a["N"], ctypes.c_float(a["beta"]), ctypes.c_float(a["alpha"]),
-                                a["io"], P(a["ws"]), a["wsb"], None)
+        args = [P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]),
+                P(a["dy"]), P(a["dx"]), P(a["ddelta"]), P(a["dA"]), P(a["dB"]), P(a["dC"]),
+                P(a["dDskip"]), a["Bt"], a["L"], a["D"], a["N"], ctypes.c_float(a["beta"]),
+                ctypes.c_float(a["alpha"]), a["io"], P(a["ws"]), a["wsb"], None]
+        if plan is None:
+            return lib.msm_scan_bwd(*args)
+        return lib.msm_scan_bwd_with_plan(*args, ctypes.byref(plan))
 
     assert call(dy=None) == INVALID
     assert call(dA=None) == INVALID
@@ -131,6 +134,10 @@ def test_bwd_argument_validation_never_launches(lib):
     assert call(wsb=16) == WORKSPACE
     assert call(dx=0x6000) == INVALID             # gradient aliasing dy
     assert call(dB=0x100000 + 4) == INVALID       # two outputs overlapping
+    # explicit plans: N=4 pads to 4 states, two per wavefront half at most
+    assert call(plan=msm._Plan(4, 1)) == UNSUPPORTED
+    assert call(plan=msm._Plan(3, 1)) == UNSUPPORTED
+    assert call(plan=msm._Plan(2, 2)) == UNSUPPORTED  # the backward is never chunked
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -138,3 +145,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(msm.MsmLibraryMissing):
         msm.load_library()
+
+
+def test_bwd_plan_choice():
+    # Bt * D / 32 workgroups; the largest states-per-lane that still gives 1024 wavefronts
+    assert msm.msm_scan_bwd_plan(4, 2048, 2048, 16, "f32", 0.9) == {"states_per_wave": 2,
+                                                                     "chunks": 1}
+    # few channel blocks: the smallest K (most wavefronts)
+    assert msm.msm_scan_bwd_plan(1, 64, 64, 16, "f32", 0.9)["states_per_wave"] == 1
+    # 64 padded states: the full-wavefront backward, 4 states per lane
+    assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 4
