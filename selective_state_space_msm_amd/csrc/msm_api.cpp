@@ -121,17 +121,20 @@ bool bwd_allowed_k(int NP, int K) {
 }
 
 // For 4 or 16 padded states a backward workgroup holds 2K states of kBwdChans channels per
-// wavefront and NP / (2K) wavefronts.  The largest K that still gives a wavefront per SIMD wins;
-// otherwise the smallest allowed K (most wavefronts).  64 padded states always take K = 4.
+// wavefront and NP / (2K) wavefronts.  A wavefront alone on its SIMD stalls on every non-VALU
+// instruction and on LDS and fp64 latencies, so the plan asks for two wavefronts per SIMD: the
+// largest K (at most 2: K = 4 needs more registers than two wavefronts leave) that still gives
+// 2 * 1024 wavefronts, else K = 1.  64 padded states always take K = 4 (full-wavefront kernel).
 msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int NP = padded_states(N);
-  const int64_t chan_blocks = Bt * ceil_div(D, bwd_chans(NP));
   msm_plan pl{0, 1};
-  for (int K = 4; K >= 1; K /= 2) {
-    if (!bwd_allowed_k(NP, K)) continue;
-    pl.states_per_wave = K;
-    if (chan_blocks * (NP / (bwd_chans(NP) == kWave ? K : 2 * K)) >= kTargetWaves) return pl;
+  if (NP == 64) {
+    pl.states_per_wave = 4;
+    return pl;
   }
+  const int64_t chan_blocks = Bt * ceil_div(D, msm::kBwdChans);
+  pl.states_per_wave = 1;
+  if (bwd_allowed_k(NP, 2) && chan_blocks * (NP / 4) >= 2 * kTargetWaves) pl.states_per_wave = 2;
   return pl;
 }
 

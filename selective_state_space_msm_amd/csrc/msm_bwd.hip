@@ -73,15 +73,11 @@ __device__ __forceinline__ void reduce_scatter32(float (&v)[32], int lane) {
 }
 
 // Adds a across the two halves of the wavefront for lanes 0-31 and b for lanes 32-63 (the
-// same pairing trick as above, with v_permlane32_swap on both 32-bit words of each double).
-__device__ __forceinline__ double swap_add32(double a, double b) {
-  const uint64_t ua = __double_as_longlong(a), ub = __double_as_longlong(b);
-  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
-  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
-                                                   false, false);
-  const double e0 = __longlong_as_double((int64_t)(((uint64_t)hi[0] << 32) | lo[0]));
-  const double e1 = __longlong_as_double((int64_t)(((uint64_t)hi[1] << 32) | lo[1]));
-  return e0 + e1;
+// same pairing trick as above, with v_permlane32_swap).
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Buffer resource for the rows of a (L, row_bytes) slab starting at row r; rows at or past
@@ -102,19 +98,16 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   constexpr int NTHR = S * kWave;
   constexpr int NPB = S * P * K;         // padded states of the workgroup
   constexpr int GS = S * P;              // state groups of the workgroup
-  // rows whose per-wavefront dx / ddelta partials sit in LDS at once
-  constexpr int SR = (S * TB * kWave * 8 <= 65536) ? TB : TB / 2;
-  constexpr int NSR = TB / SR;
   constexpr int M = 32;                  // values per lane in one dB/dC reduce-scatter
   constexpr int RB = M / (2 * K);        // rows per reduce-scatter
-  constexpr int NRB = SR / RB;
+  constexpr int NRB = TB / RB;
   static_assert(P == 2, "the lane pairing below assumes two 32-lane halves");
-  static_assert(RB >= 1 && SR % RB == 0 && TB % SR == 0, "tile must split into reduce blocks");
+  static_assert(RB >= 1 && TB % RB == 0, "tile must split into reduce blocks");
 
-  __shared__ float4 xs[2][TB][CB];            // x, delta, dy, delta * x
-  __shared__ float bcs[2][TB][GS][2 * K];     // alpha B | C, for the recompute
-  __shared__ double bcs64[2][TB][GS][2 * K];  // the same values widened, for the adjoint
-  __shared__ double spart[S][SR][kWave];      // per wavefront: dx (lanes < 32) | ddelta
+  __shared__ float4 xs[2][TB][CB];          // x, delta, dy, delta * x
+  __shared__ float bs[2][TB][GS][K];        // alpha B
+  __shared__ double cs64[2][TB][GS][K];     // C, widened for the adjoint recurrence
+  __shared__ float spart[2][S][TB][kWave];  // per wavefront: dx (lanes < 32) | ddelta partials
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -131,14 +124,13 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const float beta = p.beta;
   const double beta64 = p.beta;
 
-  float A2[K], v[K], h[K];
-  double A64[K];
+  float A2[K], Af[K], v[K], h[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int64_t n = (int64_t)gs * K + j;
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
-    A64[j] = an;
+    Af[j] = an;
     v[j] = 0.f;
     h[j] = 0.f;
   }
@@ -152,6 +144,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const char* B0 = static_cast<const char*>(p.B) + b * tot_n;
   const char* C0 = static_cast<const char*>(p.C) + b * tot_n;
 
+  // x, delta, dy of channels past D are staged as zeros (their offset is past every extent),
+  // so those lanes carry zero gradients without further masking
   constexpr int XE = TB * CB;  // elements of one array in one tile
   constexpr int NX = (XE + NTHR - 1) / NTHR;
   uint32_t x_voff[NX];
@@ -160,7 +154,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     const int i = tid + r * NTHR;
     const int ic = i < XE ? i : XE - 1;
     const int dch = cb * CB + ic % CB;
-    x_voff[r] = (uint32_t)((ic / CB) * row_bytes + (dch < D ? dch : D - 1) * T::es);
+    x_voff[r] = dch < D ? (uint32_t)((ic / CB) * row_bytes + dch * T::es) : 0x80000000u;
   }
   raw xr[NX], dr[NX], gr[NX];
   auto x_load = [&](int64_t ts, bool with_dy) {
@@ -191,42 +185,50 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   constexpr int BCE = TB * NPB;  // (row, state) pairs of one tile
   constexpr int NPE = (BCE + NTHR - 1) / NTHR;
   uint32_t bc_voff[NPE];
-  bool bc_nok[NPE];
 #pragma unroll
   for (int r = 0; r < NPE; ++r) {
     const int i = tid + r * NTHR;
     const int ic = i < BCE ? i : BCE - 1;
     const int n = ic % NPB;
-    bc_nok[r] = n < N;
-    bc_voff[r] = (uint32_t)(((ic / NPB) * N + (n < N ? n : 0)) * T::es);
+    bc_voff[r] = n < N ? (uint32_t)(((ic / NPB) * N + n) * T::es) : 0x80000000u;
   }
   raw bre[NPE], cre[NPE];
-  auto bc_load = [&](int64_t ts) {
+  auto bc_load = [&](int64_t ts, bool with_c) {
     const auto rb = rows_rsrc(B0, ts, bc_row_bytes, tot_n);
-    const auto rc = rows_rsrc(C0, ts, bc_row_bytes, tot_n);
 #pragma unroll
-    for (int r = 0; r < NPE; ++r) {
-      bre[r] = T::bload(rb, bc_voff[r], 0u);
-      cre[r] = T::bload(rc, bc_voff[r], 0u);
+    for (int r = 0; r < NPE; ++r) bre[r] = T::bload(rb, bc_voff[r], 0u);
+    if (with_c) {
+      const auto rc = rows_rsrc(C0, ts, bc_row_bytes, tot_n);
+#pragma unroll
+      for (int r = 0; r < NPE; ++r) cre[r] = T::bload(rc, bc_voff[r], 0u);
     }
   };
-  auto bc_store = [&](int buf) {
+  auto bc_store = [&](int buf, bool with_c) {
 #pragma unroll
     for (int r = 0; r < NPE; ++r) {
       const int i = tid + r * NTHR;
       if (NPE * NTHR == BCE || i < BCE) {
         const int tt = i / NPB, n = i % NPB;
-        const float bv = bc_nok[r] ? T::widen(bre[r]) * p.alpha : 0.f;
-        const float cv = bc_nok[r] ? T::widen(cre[r]) : 0.f;
-        bcs[buf][tt][n / K][n % K] = bv;
-        bcs[buf][tt][n / K][K + n % K] = cv;
-        bcs64[buf][tt][n / K][n % K] = bv;
-        bcs64[buf][tt][n / K][K + n % K] = cv;
+        bs[buf][tt][n / K][n % K] = T::widen(bre[r]) * p.alpha;
+        if (with_c) cs64[buf][tt][n / K][n % K] = T::widen(cre[r]);
       }
     }
   };
-  auto ckpt_index = [&](int64_t tile, int which, int64_t n) {
-    return (((b * NT + tile) * 2 + which) * N + n) * D + dl;
+  // checkpoints, [Bt][NT][2][N][D] fp32: one buffer resource per (b, tile) and constant
+  // per-lane offsets; lanes without a state (channel past D, padded n) get an offset past
+  // the extent, so their stores are dropped and their loads read zero
+  const int64_t ck_tile_bytes = 2 * N * D * 4;
+  uint32_t ck_voff[2][K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t n = (int64_t)gs * K + j;
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+      ck_voff[w][j] = (dvalid && n < N) ? (uint32_t)(((w * N + n) * D + d) * 4) : 0x80000000u;
+  }
+  auto ck_rsrc = [&](int64_t tile) {
+    return make_rsrc(reinterpret_cast<const char*>(p.ckpt) + (b * NT + tile) * ck_tile_bytes,
+                     ck_tile_bytes);
   };
 
   // one forward step of the K states (recurrence only); c = delta * x
@@ -243,83 +245,169 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   };
 
   // ---------------- phase 1: forward over the whole sequence, checkpoint every tile ----
+  // A tile's arithmetic here is short next to the latency of its loads, so the loads run four
+  // tiles ahead through a ring of register sets: tile k is loaded into set k % 4 during tile
+  // k - 4 and staged into LDS at the end of tile k - 1.  The loop starts at tile -4 (steps
+  // with a negative tile only load and stage), so every step has the same memory pattern.
   {
-    int buf = 0;
-    bc_load(0);
-    x_load(0, false);
-    bc_store(0);
-    x_store(0, false);
-    __syncthreads();
-    for (int64_t tile = 0; tile < NT; ++tile) {
+    struct Set {
+      raw x[NX], d[NX], b[NPE];
+    };
+    Set s0{}, s1{}, s2{}, s3{};
+    auto load1 = [&](Set& st, int64_t tile) {
       const int64_t ts = tile * TB;
-      if (dvalid) {
+      const auto rx = rows_rsrc(x0, ts, row_bytes, tot_d);
+      const auto rd = rows_rsrc(dl0, ts, row_bytes, tot_d);
+      const auto rb = rows_rsrc(B0, ts, bc_row_bytes, tot_n);
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-          const int64_t n = (int64_t)gs * K + j;
-          if (n < N) {
-            p.ckpt[ckpt_index(tile, 0, n)] = v[j];
-            p.ckpt[ckpt_index(tile, 1, n)] = h[j];
-          }
+      for (int r = 0; r < NX; ++r) {
+        st.x[r] = T::bload(rx, x_voff[r], 0u);
+        st.d[r] = T::bload(rd, x_voff[r], 0u);
+      }
+#pragma unroll
+      for (int r = 0; r < NPE; ++r) st.b[r] = T::bload(rb, bc_voff[r], 0u);
+    };
+    auto store1 = [&](const Set& st, int buf) {
+#pragma unroll
+      for (int r = 0; r < NX; ++r) {
+        const int i = tid + r * NTHR;
+        if (NX * NTHR == XE || i < XE) {
+          const float xv = T::widen(st.x[r]), dv = T::widen(st.d[r]);
+          xs[buf][i / CB][i % CB] = make_float4(xv, dv, 0.f, dv * xv);
         }
       }
-      // next tile, unconditionally (past the end the resources read zeros)
-      bc_load(ts + TB);
-      x_load(ts + TB, false);
 #pragma unroll
-      for (int tt = 0; tt < TB; ++tt) {
-        const float4 r = xs[buf][tt][ch];
-        fstep(r.y, r.w, &bcs[buf][tt][gs][0], nullptr, nullptr);
+      for (int r = 0; r < NPE; ++r) {
+        const int i = tid + r * NTHR;
+        if (NPE * NTHR == BCE || i < BCE)
+          bs[buf][i / NPB][(i % NPB) / K][(i % NPB) % K] = T::widen(st.b[r]) * p.alpha;
       }
-      if (tile + 1 < NT) {
-        bc_store(buf ^ 1);
-        x_store(buf ^ 1, false);
+    };
+    // one step: checkpoint and compute `tile` (if it exists), refill `mine` with tile + 4,
+    // stage `next` (tile + 1) into the other LDS buffer.  Loads and stores are unconditional
+    // (past the end the resources read zeros and the staged buffer goes unused).
+    auto step1 = [&](int64_t tile, Set& mine, const Set& next) {
+      const bool live = tile >= 0 && tile < NT;
+      {
+        // a step without a tile stores through an empty resource (dropped): a store under a
+        // branch would not be counted in the wait for this step's loads, three steps later
+        const auto rc = live ? ck_rsrc(tile) : make_rsrc(p.ckpt, 0);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          io<float>::bstore(rc, ck_voff[0][j], 0u, v[j]);
+          io<float>::bstore(rc, ck_voff[1][j], 0u, h[j]);
+        }
       }
+      load1(mine, tile + 4);
+      if (live) {
+        const int buf = (int)(tile & 1);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) {
+          const float4 r = xs[buf][tt][ch];
+          fstep(r.y, r.w, &bs[buf][tt][gs][0], nullptr, nullptr);
+        }
+      }
+      store1(next, (int)((tile + 1) & 1));
       __syncthreads();
-      buf ^= 1;
+    };
+    // whole groups of four steps (up to three idle steps at the end): a single loop exit
+    // keeps the compiler's count of loads in flight exact at the loop head
+    for (int64_t t0 = -4; t0 < NT; t0 += 4) {
+      step1(t0, s0, s1);
+      step1(t0 + 1, s1, s2);
+      step1(t0 + 2, s2, s3);
+      step1(t0 + 3, s3, s0);
     }
   }
 
   // ---------------- phase 2: reverse sweep ----------------
-  double ghn[K], gvn[K], dAacc[K];  // ghn = a_{t+1} gh_{t+1}, gvn = beta gv_{t+1}
+  // The adjoint recurrence (gh, gv) runs in fp64: fp32 adjoints lose too many bits over long
+  // sequences for ddelta, a difference of two large sums.  Products that leave the
+  // recurrence are rounded to fp32; dA is summed in fp32 within a tile and in fp64 across.
+  double ghn[K], gvp[K], dA64[K];  // ghn = a_{t+1} gh_{t+1}, gvp = gv_{t+1}
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     ghn[j] = 0.0;
-    gvn[j] = 0.0;
-    dAacc[j] = 0.0;
+    gvp[j] = 0.0;
+    dA64[j] = 0.0;
   }
-  double dDacc = 0.0;
-  const double dsk = (HAS_DSKIP && gs == 0) ? (double)p.Dskip[dl] : 0.0;
-  float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
+  double dD64 = 0.0;
+  const float dsk = (HAS_DSKIP && gs == 0) ? p.Dskip[dl] : 0.f;
+  const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
   char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
   char* ddl0 = static_cast<char*>(p.ddelta) + b * tot_d;
   const uint32_t lane_off = (uint32_t)dl * T::es;
 
-  float cv[K], chh[K];  // checkpoint (v, h) before the current tile
-  auto load_ckpt = [&](float(&ov)[K], float(&oh)[K], int64_t tile) {
+  // dx / ddelta of the rows of `tile`, whose partials sit in spart[pb]: each wavefront takes
+  // every S-th row and adds the S partials of its lane in a fixed order (fp64), rounding once.
+  // Lanes 0-31 hold dx and lanes 32-63 ddelta; both stores are issued by every lane, and the
+  // lanes that must not write (other half, channels past D) carry an offset past every
+  // extent, which the buffer unit drops.  (A per-lane choice of buffer would make the
+  // compiler loop over the distinct descriptors.)
+  const uint32_t vo_dx = (dvalid && lane < CB) ? lane_off : 0x80000000u;
+  const uint32_t vo_dd = (dvalid && lane >= CB) ? lane_off : 0x80000000u;
+  auto finalize = [&](int64_t tile, int pb, bool valid) {
+    const int64_t ts = tile * TB;
+    // an invalid tile gets empty resources: every store below is then dropped
+    const auto rdx = valid ? rows_rsrc(dx0, ts, row_bytes, tot_d) : make_rsrc(dx0, 0);
+    const auto rdd = valid ? rows_rsrc(ddl0, ts, row_bytes, tot_d) : make_rsrc(ddl0, 0);
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)gs * K + j;
-      const int64_t nc = n < N ? n : N - 1;
-      ov[j] = n < N ? p.ckpt[ckpt_index(tile, 0, nc)] : 0.f;
-      oh[j] = n < N ? p.ckpt[ckpt_index(tile, 1, nc)] : 0.f;
+    for (int tr0 = 0; tr0 < TB; tr0 += S) {
+      const int tt = tr0 + g;
+      if (tr0 + S <= TB || tt < TB) {
+        double q = (double)spart[pb][0][tt][lane];
+#pragma unroll
+        for (int w = 1; w < S; ++w) q += (double)spart[pb][w][tt][lane];
+        // rows past the end of the sequence are past the extent: dropped
+        const uint32_t ro = (uint32_t)(tt * row_bytes);
+        T::bstore(rdx, vo_dx + ro, 0u, (float)q);
+        T::bstore(rdd, vo_dd + ro, 0u, (float)q);
+      }
     }
   };
-  int buf = 0;
-  load_ckpt(cv, chh, NT - 1);
-  bc_load((NT - 1) * TB);
-  x_load((NT - 1) * TB, true);
-  bc_store(0);
-  x_store(0, true);
-  __syncthreads();
-  for (int64_t tile = NT - 1; tile >= 0; --tile) {
-    const int64_t ts = tile * TB;
-    const int nv = (int)((L - ts < TB) ? L - ts : TB);
-    const int64_t tp = tile > 0 ? tile - 1 : 0;  // prefetch (tile 0 again at the end)
-    float cvn[K], chn[K];
-    load_ckpt(cvn, chn, tp);
-    bc_load(tp * TB);
-    x_load(tp * TB, true);
 
+  // dB / dC partials of this workgroup, [L][2][NPB] fp32 at dbc: a resource per tile and a
+  // constant offset per lane and reduce block (lane l of a half holds value l & 31)
+  const int64_t dbc_row_bytes = 2 * NPB * 4, dbc_tot = L * dbc_row_bytes;
+  uint32_t dbc_voff[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int m = lane & 31;
+    const int tt = rb * RB + m / (2 * K);
+    const int n = gs * K + m % K;
+    dbc_voff[rb] = (uint32_t)((tt * 2 * NPB + ((m / K) & 1) * NPB + n) * 4);
+  }
+
+  auto load_ckpt = [&](float(&ov)[K], float(&oh)[K], int64_t tile) {
+    const auto rc = ck_rsrc(tile);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ov[j] = io<float>::bload(rc, ck_voff[0][j], 0u);
+      oh[j] = io<float>::bload(rc, ck_voff[1][j], 0u);
+    }
+  };
+
+  // one step of the reverse sweep: prefetch tile - 1 (its checkpoint into `nv_`/`nh_`, its
+  // inputs into registers), recompute and sweep `tile` (if it exists) from LDS, finish the
+  // dx / ddelta of tile + 1, stage tile - 1 into the other LDS buffer.  Loads, stores and the
+  // barrier are unconditional, so every step has the same memory pattern.
+  auto step2 = [&](int64_t tile, const float(&cv)[K], const float(&chh)[K], float(&nv_)[K],
+                   float(&nh_)[K]) {
+    const bool live = tile >= 0;
+    const int buf = (int)((NT - 1 - tile) & 1);
+    const int pb = (int)(tile & 1);
+    const int64_t tp = tile > 0 ? tile - 1 : 0;  // prefetch (tile 0 again at the end)
+    load_ckpt(nv_, nh_, tp);
+    bc_load(tp * TB, true);
+    x_load(tp * TB, true);
+    // tile + 1's partials were completed before the last barrier
+    finalize(tile + 1, pb ^ 1, tile + 1 < NT && tile + 1 >= 0);
+
+    // The sweep runs in every step (a step past tile 0 sweeps stale LDS data): its stores are
+    // dropped through an empty resource and its sums are not kept.  No memory operation
+    // depends on a branch, so the compiler can count the loads still in flight exactly.
+    const int64_t ts = tile * TB;
+    const auto rdbc = live ? rows_rsrc(dbc, ts, dbc_row_bytes, dbc_tot) : make_rsrc(dbc, 0);
     // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt}
     float hs[TB + 1][K], av[TB][K];
 #pragma unroll
@@ -331,91 +419,80 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       const float4 r = xs[buf][tt][ch];
-      fstep(r.y, r.w, &bcs[buf][tt][gs][0], av[tt], hs[tt + 1]);
+      fstep(r.y, r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1]);
     }
 
-    const auto rdx = rows_rsrc(dx0, ts, row_bytes, tot_d);
-    const auto rdd = rows_rsrc(ddl0, ts, row_bytes, tot_d);
+    float dAt[K];
 #pragma unroll
-    for (int sr = NSR - 1; sr >= 0; --sr) {
+    for (int j = 0; j < K; ++j) dAt[j] = 0.f;
+    float dDt = 0.f;
 #pragma unroll
-      for (int rb = NRB - 1; rb >= 0; --rb) {
-        float vals[M];
+    for (int rb = NRB - 1; rb >= 0; --rb) {
+      float vals[M];
 #pragma unroll
-        for (int tb = RB - 1; tb >= 0; --tb) {
-          const int tr = rb * RB + tb;  // row within the round
-          const int tt = sr * SR + tr;  // row within the tile
-          const float4 r = xs[buf][tt][ch];
-          const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
-          const double gy64 = gy, dv64 = dv;
-          const double* bc = &bcs64[buf][tt][gs][0];
-          double s1 = 0.0, s2 = 0.0;
+      for (int tb = RB - 1; tb >= 0; --tb) {
+        const int tt = rb * RB + tb;
+        const float4 r = xs[buf][tt][ch];
+        const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
+        const double gy64 = gy;
+        float p1 = 0.f, p2 = 0.f;
 #pragma unroll
-          for (int j = 0; j < K; ++j) {
-            const double a64 = av[tt][j];
-            const double gh = fma(bc[K + j], gy64, ghn[j]);
-            const double gv = BETA0 ? gh : gh + gvn[j];
-            s1 = fma(bc[j], gv, s1);
-            ghn[j] = a64 * gh;
-            const double gg = ghn[j] * (double)hs[tt][j];  // a_t h_{t-1} gh_t
-            s2 = fma(A64[j], gg, s2);
-            dAacc[j] = fma(dv64, gg, dAacc[j]);
-            if (!BETA0) gvn[j] = beta64 * gv;
-            vals[(tb * 2 + 0) * K + j] = dvalid ? c * (float)gv : 0.f;       // dB / alpha
-            vals[(tb * 2 + 1) * K + j] = dvalid ? gy * hs[tt + 1][j] : 0.f;  // dC
-          }
-          const double qx = fma(dsk, gy64, dv64 * s1);
-          const double qd = fma((double)xv, s1, s2);
-          spart[g][tr][lane] = swap_add32(qx, qd);
-          if (HAS_DSKIP) dDacc = fma(gy64, (double)xv, dDacc);
+        for (int j = 0; j < K; ++j) {
+          const double gh = fma(cs64[buf][tt][gs][j], gy64, ghn[j]);
+          const double gv = BETA0 ? gh : fma(beta64, gvp[j], gh);
+          ghn[j] = (double)av[tt][j] * gh;
+          if (!BETA0) gvp[j] = gv;
+          const float gvf = (float)gv;
+          const float gg = (float)ghn[j] * hs[tt][j];  // a_t h_{t-1} gh_t
+          p1 = j == 0 ? bs[buf][tt][gs][j] * gvf : fmaf(bs[buf][tt][gs][j], gvf, p1);
+          p2 = j == 0 ? Af[j] * gg : fmaf(Af[j], gg, p2);
+          dAt[j] = fmaf(dv, gg, dAt[j]);
+          vals[(tb * 2 + 0) * K + j] = c * gvf;             // dB / alpha
+          vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
         }
-        reduce_scatter32(vals, lane);
-        const int m = lane & 31;
-        const int tt = sr * SR + rb * RB + m / (2 * K);
-        const int n = gs * K + m % K;
-        if (tt < nv) dbc[(ts + tt) * 2 * NPB + ((m / K) & 1) * NPB + n] = vals[0];
-      }
-      __syncthreads();
-      // dx / ddelta of this round's rows: each wavefront takes every S-th row and adds the S
-      // partials of its lane in a fixed order (fp64), rounding once to the I/O type
-#pragma unroll
-      for (int tr0 = 0; tr0 < SR; tr0 += S) {
-        const int tr = tr0 + g;
-        const int tt = sr * SR + tr;
-        if (tr < SR && tt < nv) {
-          double q = 0.0;
-#pragma unroll
-          for (int w = 0; w < S; ++w) q += spart[w][tr][lane];
-          if (dvalid) {
-            if (lane < CB)
-              T::bstore(rdx, lane_off, (uint32_t)(tt * row_bytes), (float)q);
-            else
-              T::bstore(rdd, lane_off, (uint32_t)(tt * row_bytes), (float)q);
-          }
+        float qx = dv * p1;
+        if (HAS_DSKIP) {
+          qx = fmaf(dsk, gy, qx);
+          dDt = fmaf(gy, xv, dDt);
         }
+        const float qd = fmaf(xv, p1, p2);
+        spart[pb][g][tt][lane] = swap_add32(qx, qd);
       }
-      if (sr > 0) __syncthreads();  // spart is reused by the next round of this tile
+      reduce_scatter32(vals, lane);
+      // rows past the end of the sequence are past the extent: dropped
+      io<float>::bstore(rdbc, dbc_voff[rb], 0u, vals[0]);
     }
-    if (tile > 0) {
-      bc_store(buf ^ 1);
-      x_store(buf ^ 1, true);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dA64[j] += (double)dAt[j];
+      if (HAS_DSKIP) dD64 += (double)dDt;
     }
+    bc_store(buf ^ 1, true);
+    x_store(buf ^ 1, true);
     __syncthreads();
-    buf ^= 1;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      cv[j] = cvn[j];
-      chh[j] = chn[j];
-    }
+  };
+
+  float ckv0[K], ckh0[K], ckv1[K], ckh1[K];
+  load_ckpt(ckv0, ckh0, NT - 1);
+  bc_load((NT - 1) * TB, true);
+  x_load((NT - 1) * TB, true);
+  bc_store(0, true);
+  x_store(0, true);
+  __syncthreads();
+  // tiles NT-1 .. 0, then tile -1 (finishes tile 0), in pairs so the checkpoint registers
+  // alternate instead of being copied; a possible extra step (tile -2) does nothing but load
+  for (int64_t t = NT - 1; t >= -1; t -= 2) {
+    step2(t, ckv0, ckh0, ckv1, ckh1);
+    step2(t - 1, ckv1, ckh1, ckv0, ckh0);
   }
 
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int64_t n = (int64_t)gs * K + j;
-      if (n < N) p.dA_part[(b * N + n) * D + d] = (float)dAacc[j];
+      if (n < N) p.dA_part[(b * N + n) * D + d] = (float)dA64[j];
     }
-    if (HAS_DSKIP && gs == 0) p.dD_part[b * D + d] = (float)dDacc;
+    if (HAS_DSKIP && gs == 0) p.dD_part[b * D + d] = (float)dD64;
   }
 }
 

@@ -148,10 +148,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def test_bwd_plan_choice():
-    # Bt * D / 32 workgroups; the largest states-per-lane that still gives 1024 wavefronts
-    assert msm.msm_scan_bwd_plan(4, 2048, 2048, 16, "f32", 0.9) == {"states_per_wave": 2,
+    # Bt * D / 32 workgroups; two states per lane only once that still gives 2048 wavefronts
+    assert msm.msm_scan_bwd_plan(4, 2048, 2048, 16, "f32", 0.9) == {"states_per_wave": 1,
                                                                      "chunks": 1}
-    # few channel blocks: the smallest K (most wavefronts)
+    assert msm.msm_scan_bwd_plan(8, 2048, 4096, 16, "f32", 0.9)["states_per_wave"] == 2
     assert msm.msm_scan_bwd_plan(1, 64, 64, 16, "f32", 0.9)["states_per_wave"] == 1
+    assert msm.msm_scan_bwd_plan(1, 64, 64, 4, "f32", 0.9)["states_per_wave"] == 1
     # 64 padded states: the full-wavefront backward, 4 states per lane
     assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 4

@@ -93,7 +93,8 @@ def make_inputs(w: Workload, *, a_kind: str = "s4d", with_dy: bool | None = None
     a_kind: "s4d"    -> A[d, n] = -(n+1)  (the configs' S4D-real initialisation)
             "random" -> A[d, n] = -exp(U(ln 0.5, ln 16))  (no structure across n or d)
     Returns a dict of float32 numpy arrays: x, delta, A, B, C, Dskip (or None), dy (or None),
-    plus the scalars beta, alpha and the io string.
+    plus the scalars beta, alpha and the io string.  beta and alpha are rounded to float32,
+    the precision in which the library receives them, so both sides see the same values.
     """
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     Bt, L, D, N = w.Bt, w.L, w.D, w.N
@@ -122,5 +123,5 @@ def make_inputs(w: Workload, *, a_kind: str = "s4d", with_dy: bool | None = None
         x, delta, B, C = (round_to_bf16(a) for a in (x, delta, B, C))
         if dy is not None:
             dy = round_to_bf16(dy)
-    return dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Dskip, dy=dy, beta=w.beta,
-                alpha=w.alpha, io=w.io)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Dskip, dy=dy,
+                beta=float(np.float32(w.beta)), alpha=float(np.float32(w.alpha)), io=w.io)
