@@ -200,11 +200,16 @@ void fwd_kernel(const FwdArgs p) {
     if (SUMMARY) sd += dv;
     return ysum;
   };
+  // y stores are never under a branch (a store the compiler cannot count makes its waits for
+  // the prefetched inputs drain more than they need): channels past D carry an offset past
+  // every extent, and rows past the chunk end lie past the tile resource's extent, so the
+  // buffer unit drops both.
+  const uint32_t lane_off_y = dvalid ? lane_off : 0x80000000u;
   // ry: resource of the tile being computed (only used when S == 1)
   auto emit = [&](int buf, int tt, __amdgpu_buffer_rsrc_t ry, float ysum) {
     if (SUMMARY) return;
     if (S == 1) {
-      if (dvalid) T::bstore(ry, (uint32_t)tt * row_bytes + lane_off, 0u, ysum);
+      T::bstore(ry, (uint32_t)tt * row_bytes + lane_off_y, 0u, ysum);
     } else {
       ypart[YPART ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
     }
@@ -240,53 +245,77 @@ void fwd_kernel(const FwdArgs p) {
       }
     }
   };
-  auto compute_tail = [&](int buf, int64_t ts, int nv) {
+  // The ragged last tile of a chunk (nv < TT rows), once per chunk after the main loop: rows
+  // past nv must leave the state alone, so each row is guarded (a uniform branch).
+  auto compute_tail = [&](const raw(&xr)[TT], const raw(&dr)[TT], int buf, int64_t ts, int nv) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
-    for (int tt = 0; tt < nv; ++tt) {
-      const int64_t row = (b * L + ts + tt) * D;
-      const raw xr = T::load_row(p.x, row, dl), dr = T::load_row(p.delta, row, dl);
-      const float ysum = step(T::widen(xr), T::widen(dr), T::mul_raw(dr, xr), &bcs[buf][tt][g][0]);
-      emit(buf, tt, ry, ysum);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < nv) {
+        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), T::mul_raw(dr[tt], xr[tt]),
+                                &bcs[buf][tt][g][0]);
+        emit(buf, tt, ry, ysum);
+      }
     }
   };
-  auto finalize = [&](int buf, int64_t ts, int nv) {
+  // y of the tile whose partials are in ypart[buf]: each wavefront takes rows g, g + S, ...,
+  // adds the S partials in a fixed order and stores, a fixed number of stores per wavefront.
+  auto finalize = [&](int buf, int64_t ts) {
     if (!YPART) return;
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
-    for (int tt = g; tt < nv; tt += S) {
+#pragma unroll
+    for (int r = 0; r < TT / S; ++r) {
+      const int tt = r * S + g;
       float s = 0.f;
 #pragma unroll
       for (int gg = 0; gg < S; ++gg) s += ypart[YPART ? buf : 0][YPART ? gg : 0][tt][lane];
-      if (dvalid) T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off, 0u, s);
+      T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, s);
     }
   };
 
+  // ---- main loop over the full tiles of the chunk, then the ragged tail ----
+  const int64_t nfull = (t1 - t0) / TT;
+  const int nrem = (int)((t1 - t0) - nfull * TT);
   raw xa[TT], da[TT], xb[TT], db[TT];
-  int64_t ts = t0;
   int buf = 0;
-  stage_load(ts);
+  stage_load(t0);
   stage_store(0);
-  load_xd(xa, da, ts);
+  load_xd(xa, da, t0);
   __syncthreads();
 
-  // One tile: compute the tile at ts from (xc, dc) while the next tile's inputs are in flight.
-  auto half = [&](raw(&xc)[TT], raw(&dc)[TT], raw(&xn)[TT], raw(&dn)[TT]) -> bool {
-    const int nv = (int)((t1 - ts < TT) ? t1 - ts : TT);
-    const int64_t tn = ts + TT;
-    const bool has_next = tn < t1;
-    stage_load(tn);  // unconditional; past the chunk end these read nothing
-    load_xd(xn, dn, tn);
-    if (nv == TT)
-      compute_tile(xc, dc, buf, ts);
-    else
-      compute_tail(buf, ts, nv);
-    if (has_next) stage_store(buf ^ 1);
+  // One full tile: issue the next tile's loads, compute this one from (xc, dc) while they are in
+  // flight, stage the next B/C, one barrier, store this tile's y.  Nothing here depends on a
+  // branch: past the chunk end the loads read zeros and the staged buffer goes unused.
+  auto full = [&](int64_t ts, const raw(&xc)[TT], const raw(&dc)[TT], raw(&xn)[TT],
+                  raw(&dn)[TT]) {
+    stage_load(ts + TT);
+    load_xd(xn, dn, ts + TT);
+    compute_tile(xc, dc, buf, ts);
+    stage_store(buf ^ 1);
     __syncthreads();
-    finalize(buf, ts, nv);
-    ts = tn;
+    finalize(buf, ts);
     buf ^= 1;
-    return has_next;
   };
-  while (half(xa, da, xb, db) && half(xb, db, xa, da)) {
+  int64_t ts = t0;
+  // pairs of tiles, so the two register sets alternate without copies; one loop exit
+  for (int64_t i = 0; i + 1 < nfull; i += 2) {
+    full(ts, xa, da, xb, db);
+    full(ts + TT, xb, db, xa, da);
+    ts += 2 * TT;
+  }
+  auto tail = [&](const raw(&xc)[TT], const raw(&dc)[TT]) {
+    if (nrem > 0) {
+      compute_tail(xc, dc, buf, ts, nrem);
+      __syncthreads();
+      finalize(buf, ts);
+    }
+  };
+  if (nfull & 1) {
+    full(ts, xa, da, xb, db);
+    ts += TT;
+    tail(xb, db);
+  } else {
+    tail(xa, da);
   }
 
   if (SUMMARY) {
