@@ -42,9 +42,15 @@ void fwd_kernel(const FwdArgs p) {
   constexpr int NTHR = S * kWave;
   constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
   constexpr bool YPART = !SUMMARY && S > 1;
+  // y partials are double-buffered (one barrier per tile) except with 16 wavefronts, where
+  // two buffers would not fit in LDS next to the staged tiles; those take a second barrier
+  constexpr int YB = S >= 16 ? 1 : 2;
 
   __shared__ float bcs[2][TT][S][BCW];
-  __shared__ float ypart[YPART ? 2 : 1][YPART ? S : 1][TT][kWave];
+  __shared__ float ypart[YPART ? YB : 1][YPART ? S : 1][TT][kWave];
+  // (delta, delta * x) of the tile, widened once per workgroup: the S wavefronts share them
+  __shared__ float2 xdl[2][TT][kWave];
+  __shared__ float xxl[HAS_DSKIP ? 2 : 1][HAS_DSKIP ? TT : 1][kWave];  // x, for the skip term
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -114,9 +120,6 @@ void fwd_kernel(const FwdArgs p) {
   char* y0 = static_cast<char*>(p.y) + (b * L + t0) * D * T::es;
   const char* B0 = static_cast<const char*>(p.B) + (b * L + t0) * N * T::es;
   const char* C0 = static_cast<const char*>(p.C) + (b * L + t0) * N * T::es;
-  uint32_t voff_row[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) voff_row[tt] = (uint32_t)tt * row_bytes + lane_off;
   // resource for the rows starting at chunk row r (r may lie past the chunk end)
   // (extents in signed 64-bit so that they stay scalar: an unsigned saturating subtract is
   // lowered to a vector instruction, which turns every load into a waterfall loop)
@@ -168,13 +171,38 @@ void fwd_kernel(const FwdArgs p) {
       }
     }
   };
-  auto load_xd = [&](raw(&xr)[TT], raw(&dr)[TT], int64_t ts) {
+  // x / delta staging: element (row, channel) i of a tile goes through thread i mod NTHR; the
+  // values are widened and delta * x formed once here, then every wavefront reads them from
+  // LDS.  Channels past D carry an offset past every extent and read as zero.
+  constexpr int XE = TT * kWave;
+  constexpr int NX = (XE + NTHR - 1) / NTHR;
+  uint32_t x_voff[NX];
+#pragma unroll
+  for (int r = 0; r < NX; ++r) {
+    const int i = tid + r * NTHR;
+    const int ic = i < XE ? i : XE - 1;
+    const int dch = cb * kWave + ic % kWave;
+    x_voff[r] = dch < D ? (uint32_t)((ic / kWave) * row_bytes + dch * T::es) : 0x80000000u;
+  }
+  raw xr[NX], dr[NX];
+  auto load_xd = [&](int64_t ts) {
     const auto rx = rs_d(x0, (uint32_t)(ts - t0));
     const auto rd = rs_d(dl0, (uint32_t)(ts - t0));
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      xr[tt] = T::bload(rx, voff_row[tt], 0u);
-      dr[tt] = T::bload(rd, voff_row[tt], 0u);
+    for (int r = 0; r < NX; ++r) {
+      xr[r] = T::bload(rx, x_voff[r], 0u);
+      dr[r] = T::bload(rd, x_voff[r], 0u);
+    }
+  };
+  auto store_xd = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int i = tid + r * NTHR;
+      if (NX * NTHR == XE || i < XE) {
+        const float xv = T::widen(xr[r]), dv = T::widen(dr[r]);
+        xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(dr[r], xr[r]));
+        if (HAS_DSKIP) xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? i / kWave : 0][i % kWave] = xv;
+      }
     }
   };
 
@@ -211,7 +239,7 @@ void fwd_kernel(const FwdArgs p) {
     if (S == 1) {
       T::bstore(ry, (uint32_t)tt * row_bytes + lane_off_y, 0u, ysum);
     } else {
-      ypart[YPART ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
+      ypart[YPART && YB == 2 ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
     }
   };
   // Full tile.  The B/C broadcasts of the next batch of RB steps are read from LDS into
@@ -220,40 +248,43 @@ void fwd_kernel(const FwdArgs p) {
   // wavefront per SIMD has nothing else to issue meanwhile).
   constexpr int RB = (32 / K) < TT ? (32 / K) : TT;
   constexpr int NB = TT / RB;
-  auto compute_tile = [&](const raw(&xr)[TT], const raw(&dr)[TT], int buf, int64_t ts) {
+  auto compute_tile = [&](int buf, int64_t ts) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     float bcv[2][RB][BCW];
-    auto read_batch = [&](float(&dst)[RB][BCW], int jb) {
+    float2 dcv[2][RB];
+    auto read_batch = [&](float(&dst)[RB][BCW], float2(&dd)[RB], int jb) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const float* src = &bcs[buf][jb * RB + i][g][0];
 #pragma unroll
         for (int e = 0; e < BCW; ++e) dst[i][e] = src[e];
+        dd[i] = xdl[buf][jb * RB + i][lane];
       }
     };
-    read_batch(bcv[0], 0);
+    read_batch(bcv[0], dcv[0], 0);
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
-      if (jb + 1 < NB) read_batch(bcv[(jb + 1) & 1], jb + 1);
+      if (jb + 1 < NB) read_batch(bcv[(jb + 1) & 1], dcv[(jb + 1) & 1], jb + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int tt = jb * RB + i;
-        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), T::mul_raw(dr[tt], xr[tt]),
-                                bcv[jb & 1][i]);
+        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
+        const float ysum = step(xv, dcv[jb & 1][i].x, dcv[jb & 1][i].y, bcv[jb & 1][i]);
         emit(buf, tt, ry, ysum);
       }
     }
   };
   // The ragged last tile of a chunk (nv < TT rows), once per chunk after the main loop: rows
   // past nv must leave the state alone, so each row is guarded (a uniform branch).
-  auto compute_tail = [&](const raw(&xr)[TT], const raw(&dr)[TT], int buf, int64_t ts, int nv) {
+  auto compute_tail = [&](int buf, int64_t ts, int nv) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       if (tt < nv) {
-        const float ysum = step(T::widen(xr[tt]), T::widen(dr[tt]), T::mul_raw(dr[tt], xr[tt]),
-                                &bcs[buf][tt][g][0]);
+        const float2 dc = xdl[buf][tt][lane];
+        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
+        const float ysum = step(xv, dc.x, dc.y, &bcs[buf][tt][g][0]);
         emit(buf, tt, ry, ysum);
       }
     }
@@ -268,7 +299,7 @@ void fwd_kernel(const FwdArgs p) {
       const int tt = r * S + g;
       float s = 0.f;
 #pragma unroll
-      for (int gg = 0; gg < S; ++gg) s += ypart[YPART ? buf : 0][YPART ? gg : 0][tt][lane];
+      for (int gg = 0; gg < S; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][lane];
       T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, s);
     }
   };
@@ -276,46 +307,34 @@ void fwd_kernel(const FwdArgs p) {
   // ---- main loop over the full tiles of the chunk, then the ragged tail ----
   const int64_t nfull = (t1 - t0) / TT;
   const int nrem = (int)((t1 - t0) - nfull * TT);
-  raw xa[TT], da[TT], xb[TT], db[TT];
   int buf = 0;
   stage_load(t0);
+  load_xd(t0);
   stage_store(0);
-  load_xd(xa, da, t0);
+  store_xd(0);
   __syncthreads();
 
-  // One full tile: issue the next tile's loads, compute this one from (xc, dc) while they are in
-  // flight, stage the next B/C, one barrier, store this tile's y.  Nothing here depends on a
-  // branch: past the chunk end the loads read zeros and the staged buffer goes unused.
-  auto full = [&](int64_t ts, const raw(&xc)[TT], const raw(&dc)[TT], raw(&xn)[TT],
-                  raw(&dn)[TT]) {
+  // One full tile: issue the next tile's loads, compute this one from LDS while they are in
+  // flight, stage the next tile into the other LDS buffer, one barrier, store this tile's y.
+  // Nothing here depends on a branch: past the chunk end the loads read zeros and the staged
+  // buffer goes unused.
+  int64_t ts = t0;
+  for (int64_t i = 0; i < nfull; ++i) {
     stage_load(ts + TT);
-    load_xd(xn, dn, ts + TT);
-    compute_tile(xc, dc, buf, ts);
+    load_xd(ts + TT);
+    compute_tile(buf, ts);
     stage_store(buf ^ 1);
+    store_xd(buf ^ 1);
     __syncthreads();
     finalize(buf, ts);
+    if (YPART && YB == 1) __syncthreads();  // partials read before the next tile rewrites them
     buf ^= 1;
-  };
-  int64_t ts = t0;
-  // pairs of tiles, so the two register sets alternate without copies; one loop exit
-  for (int64_t i = 0; i + 1 < nfull; i += 2) {
-    full(ts, xa, da, xb, db);
-    full(ts + TT, xb, db, xa, da);
-    ts += 2 * TT;
-  }
-  auto tail = [&](const raw(&xc)[TT], const raw(&dc)[TT]) {
-    if (nrem > 0) {
-      compute_tail(xc, dc, buf, ts, nrem);
-      __syncthreads();
-      finalize(buf, ts);
-    }
-  };
-  if (nfull & 1) {
-    full(ts, xa, da, xb, db);
     ts += TT;
-    tail(xb, db);
-  } else {
-    tail(xa, da);
+  }
+  if (nrem > 0) {
+    compute_tail(buf, ts, nrem);
+    __syncthreads();
+    finalize(buf, ts);
   }
 
   if (SUMMARY) {
