@@ -208,7 +208,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="m1p4b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--bwd-workload", default="bwd", choices=sorted(workloads.WORKLOADS) + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -148,17 +148,23 @@ void fwd_kernel(const FwdArgs p) {
     bc_nok[r] = n < N;
     bc_voff[r] = (uint32_t)(((ic / (S * K)) * N + (n < N ? n : 0)) * T::es);
   }
-  raw bre[NPE], cre[NPE];
-  auto stage_load = [&](int64_t ts) {
+  // The inputs of one tile as this thread stages them (a few elements of B, C, x and delta).
+  // Loads run two tiles ahead of the arithmetic through a ring of three such sets.
+  constexpr int XE = TT * kWave;
+  constexpr int NX = (XE + NTHR - 1) / NTHR;
+  struct Set {
+    raw b[NPE], c[NPE], x[NX], d[NX];
+  };
+  auto stage_load = [&](Set& st, int64_t ts) {
     const auto rb = rs_n(B0, (uint32_t)(ts - t0));
     const auto rc = rs_n(C0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int r = 0; r < NPE; ++r) {
-      bre[r] = T::bload(rb, bc_voff[r], 0u);
-      cre[r] = T::bload(rc, bc_voff[r], 0u);
+      st.b[r] = T::bload(rb, bc_voff[r], 0u);
+      st.c[r] = T::bload(rc, bc_voff[r], 0u);
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](const Set& st, int buf) {
 #pragma unroll
     for (int r = 0; r < NPE; ++r) {
       const int i = tid + r * NTHR;
@@ -166,16 +172,14 @@ void fwd_kernel(const FwdArgs p) {
         const int tt = i / (S * K);
         const int n = i % (S * K);
         float* dst = &bcs[buf][tt][n / K][0];
-        dst[n % K] = bc_nok[r] ? T::widen(bre[r]) * p.alpha : 0.f;
-        dst[K + n % K] = bc_nok[r] ? T::widen(cre[r]) : 0.f;
+        dst[n % K] = bc_nok[r] ? T::widen(st.b[r]) * p.alpha : 0.f;
+        dst[K + n % K] = bc_nok[r] ? T::widen(st.c[r]) : 0.f;
       }
     }
   };
   // x / delta staging: element (row, channel) i of a tile goes through thread i mod NTHR; the
   // values are widened and delta * x formed once here, then every wavefront reads them from
   // LDS.  Channels past D carry an offset past every extent and read as zero.
-  constexpr int XE = TT * kWave;
-  constexpr int NX = (XE + NTHR - 1) / NTHR;
   uint32_t x_voff[NX];
 #pragma unroll
   for (int r = 0; r < NX; ++r) {
@@ -184,26 +188,33 @@ void fwd_kernel(const FwdArgs p) {
     const int dch = cb * kWave + ic % kWave;
     x_voff[r] = dch < D ? (uint32_t)((ic / kWave) * row_bytes + dch * T::es) : 0x80000000u;
   }
-  raw xr[NX], dr[NX];
-  auto load_xd = [&](int64_t ts) {
+  auto load_xd = [&](Set& st, int64_t ts) {
     const auto rx = rs_d(x0, (uint32_t)(ts - t0));
     const auto rd = rs_d(dl0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
-      xr[r] = T::bload(rx, x_voff[r], 0u);
-      dr[r] = T::bload(rd, x_voff[r], 0u);
+      st.x[r] = T::bload(rx, x_voff[r], 0u);
+      st.d[r] = T::bload(rd, x_voff[r], 0u);
     }
   };
-  auto store_xd = [&](int buf) {
+  auto store_xd = [&](const Set& st, int buf) {
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       const int i = tid + r * NTHR;
       if (NX * NTHR == XE || i < XE) {
-        const float xv = T::widen(xr[r]), dv = T::widen(dr[r]);
-        xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(dr[r], xr[r]));
+        const float xv = T::widen(st.x[r]), dv = T::widen(st.d[r]);
+        xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
         if (HAS_DSKIP) xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? i / kWave : 0][i % kWave] = xv;
       }
     }
+  };
+  auto load_set = [&](Set& st, int64_t ts) {
+    stage_load(st, ts);
+    load_xd(st, ts);
+  };
+  auto store_set = [&](const Set& st, int buf) {
+    stage_store(st, buf);
+    store_xd(st, buf);
   };
 
   // One time step for the K states of this lane.  bc holds [B(K) | C(K)] of that step.
@@ -304,37 +315,38 @@ void fwd_kernel(const FwdArgs p) {
     }
   };
 
-  // ---- main loop over the full tiles of the chunk, then the ragged tail ----
+  // ---- main loop: the full tiles of the chunk, then the ragged tail, in steps of three ----
   const int64_t nfull = (t1 - t0) / TT;
   const int nrem = (int)((t1 - t0) - nfull * TT);
-  int buf = 0;
-  stage_load(t0);
-  load_xd(t0);
-  stage_store(0);
-  store_xd(0);
+  const int64_t ntile = nfull + (nrem > 0 ? 1 : 0);
+  Set sa, sb, sc;
+  load_set(sa, t0);
+  load_set(sb, t0 + TT);
+  store_set(sa, 0);
   __syncthreads();
 
-  // One full tile: issue the next tile's loads, compute this one from LDS while they are in
-  // flight, stage the next tile into the other LDS buffer, one barrier, store this tile's y.
-  // Nothing here depends on a branch: past the chunk end the loads read zeros and the staged
-  // buffer goes unused.
-  int64_t ts = t0;
-  for (int64_t i = 0; i < nfull; ++i) {
-    stage_load(ts + TT);
-    load_xd(ts + TT);
-    compute_tile(buf, ts);
-    stage_store(buf ^ 1);
-    store_xd(buf ^ 1);
+  // One step: issue the loads of tile k + 2, compute tile k (if it exists) from LDS, stage
+  // tile k + 1 into the other LDS buffer, one barrier, store tile k's y.  No memory operation
+  // depends on a branch (the compute issues none when there are y partials): past the chunk
+  // end the loads read zeros, the staged buffer goes unused and the y stores are dropped.
+  auto stepk = [&](int64_t k, Set& ld, const Set& st) {
+    const int64_t ts = t0 + k * TT;
+    const int buf = (int)(k & 1);
+    load_set(ld, ts + 2 * TT);
+    if (k < nfull)
+      compute_tile(buf, ts);
+    else if (k == nfull && nrem > 0)
+      compute_tail(buf, ts, nrem);
+    store_set(st, buf ^ 1);
     __syncthreads();
     finalize(buf, ts);
     if (YPART && YB == 1) __syncthreads();  // partials read before the next tile rewrites them
-    buf ^= 1;
-    ts += TT;
-  }
-  if (nrem > 0) {
-    compute_tail(buf, ts, nrem);
-    __syncthreads();
-    finalize(buf, ts);
+  };
+  // groups of three steps so the three register sets rotate without copies; one loop exit
+  for (int64_t k = 0; k < ntile; k += 3) {
+    stepk(k, sc, sb);
+    stepk(k + 1, sa, sc);
+    stepk(k + 2, sb, sa);
   }
 
   if (SUMMARY) {
