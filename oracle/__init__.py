@@ -67,12 +67,13 @@ class Oracle:
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         P, I64, Dbl, Int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
-        lib.msm_oracle_fwd.argtypes = [P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64, I64, P, P, P, Int]
+        lib.msm_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64, I64, P, P, P,
+                                       Int]
         lib.msm_oracle_fwd.restype = Int
         lib.msm_oracle_fwd_plain.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, P, Int]
         lib.msm_oracle_fwd_plain.restype = Int
-        lib.msm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64, I64,
-                                       P, P, P, P, P, P, Int]
+        lib.msm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64,
+                                       I64, P, P, P, P, P, P, P, P, Int]
         lib.msm_oracle_bwd.restype = Int
         lib.msm_oracle_max_threads.argtypes = []
         lib.msm_oracle_max_threads.restype = Int
@@ -82,22 +83,27 @@ class Oracle:
     def max_threads(self) -> int:
         return int(self.lib.msm_oracle_max_threads())
 
-    def fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, threads=0):
+    def fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, threads=0, h0=None, v0=None):
         """Momentum recurrence forward in fp64.  Returns (y, last_h, last_v) as float64.
 
-        x, delta: (Bt, L, D); A: (D, N); B, C: (Bt, L, N); Dskip: (D,) or None.
+        x, delta: (Bt, L, D); A: (D, N); B, C: (Bt, L, N); Dskip: (D,) or None;
+        h0, v0: (Bt, D, N) initial state or None (zero).
         """
         x, delta, A, B, C = (_f64(a) for a in (x, delta, A, B, C))
         Ds = None if Dskip is None else _f64(Dskip)
         Bt, L, D, N = _shapes(x, A, B)
         if delta.shape != x.shape or C.shape != B.shape or (Ds is not None and Ds.shape != (D,)):
             raise ValueError("inconsistent shapes")
+        h0, v0 = (None if a is None else _f64(a) for a in (h0, v0))
+        for a in (h0, v0):
+            if a is not None and a.shape != (Bt, D, N):
+                raise ValueError("initial state shape %s" % (a.shape,))
         y = np.empty((Bt, L, D), np.float64)
         last_h = np.empty((Bt, D, N), np.float64)
         last_v = np.empty((Bt, D, N), np.float64)
         rc = self.lib.msm_oracle_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds),
-                                     float(beta), float(alpha), Bt, L, D, N, _ptr(y),
-                                     _ptr(last_h), _ptr(last_v), int(threads))
+                                     _ptr(h0), _ptr(v0), float(beta), float(alpha), Bt, L, D, N,
+                                     _ptr(y), _ptr(last_h), _ptr(last_v), int(threads))
         if rc != 0:
             raise RuntimeError("msm_oracle_fwd failed (%d)" % rc)
         return y, last_h, last_v
@@ -116,25 +122,33 @@ class Oracle:
             raise RuntimeError("msm_oracle_fwd_plain failed (%d)" % rc)
         return y, last_h
 
-    def bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, threads=0):
-        """Gradients of sum(dy * y) in fp64.
+    def bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, threads=0, h0=None, v0=None,
+            dlast_h=None, dlast_v=None):
+        """Gradients of sum(dy * y) (+ <dlast_h, last_h> + <dlast_v, last_v>) in fp64, for the
+        scan started at (h0, v0) (None: zero).
 
-        Returns a dict with dx, ddelta (Bt, L, D), dA (D, N), dB, dC (Bt, L, N) and dDskip
-        (D,) (None when Dskip is None).
+        Returns a dict with dx, ddelta (Bt, L, D), dA (D, N), dB, dC (Bt, L, N), dDskip (D,)
+        (None when Dskip is None) and dh0, dv0 (Bt, D, N).
         """
         x, delta, A, B, C, dy = (_f64(a) for a in (x, delta, A, B, C, dy))
         Ds = None if Dskip is None else _f64(Dskip)
         Bt, L, D, N = _shapes(x, A, B)
         if dy.shape != x.shape:
             raise ValueError("dy shape")
+        st = [None if a is None else _f64(a) for a in (h0, v0, dlast_h, dlast_v)]
+        for a in st:
+            if a is not None and a.shape != (Bt, D, N):
+                raise ValueError("state shape %s" % (a.shape,))
         out = dict(dx=np.empty((Bt, L, D)), ddelta=np.empty((Bt, L, D)), dA=np.empty((D, N)),
                    dB=np.empty((Bt, L, N)), dC=np.empty((Bt, L, N)),
-                   dDskip=None if Ds is None else np.empty((D,)))
+                   dDskip=None if Ds is None else np.empty((D,)),
+                   dh0=np.empty((Bt, D, N)), dv0=np.empty((Bt, D, N)))
         rc = self.lib.msm_oracle_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds),
-                                     _ptr(dy), float(beta), float(alpha), Bt, L, D, N,
+                                     _ptr(dy), _ptr(st[0]), _ptr(st[1]), _ptr(st[2]), _ptr(st[3]),
+                                     float(beta), float(alpha), Bt, L, D, N,
                                      _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
                                      _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dDskip"]),
-                                     int(threads))
+                                     _ptr(out["dh0"]), _ptr(out["dv0"]), int(threads))
         if rc != 0:
             raise RuntimeError("msm_oracle_bwd failed (%d)" % rc)
         return out

@@ -11,7 +11,9 @@
  *     v_t = beta * v_{t-1} + alpha * (delta_t * B_t * x_t)
  *     h_t = exp(delta_t * A) * h_{t-1} + v_t
  *     y_t = C_t . h_t                 (sum over the N states)
- *   with v and h starting at zero (the README states this for v; h is read the same way).
+ *   with v and h starting at zero (the README states this for v; h is read the same way), or
+ *   at a given initial state (h0, v0) -- the state a previous segment of the same sequence
+ *   ended in (the README's `last_state` outputs, fed back to continue the scan).
  *   Layout of the arrays follows the selection semantics of "Mamba: Choosing What to Remember
  *   Based on the Input" (section "From input features to update coefficients"): B_t and C_t
  *   hold N values per position shared across channels, delta one value per channel, A fixed
@@ -20,7 +22,8 @@
  *     A, dA                       : (D, N)
  *     B, C, dB, dC                : (Bt, L, N)
  *     Dskip, dDskip               : (D,)          (the per-channel skip weight of the Mamba block)
- *     last_h, last_v              : (Bt, D, N)
+ *     last_h, last_v, h0, v0      : (Bt, D, N)
+ *     dlast_h, dlast_v, dh0, dv0  : (Bt, D, N)
  *   The optional skip adds Dskip[d] * x to y ("Where the state computation sits in a Mamba
  *   block": a learned per-channel weight times the current input).  alpha does not scale it.
  *
@@ -36,6 +39,10 @@
  *     dx       += Dskip * dy,  dDskip = sum_{b,t} dy * x      (only when Dskip is given)
  *   The page writes the velocity adjoint as a pure beta-decay; the velocity also enters h_t
  *   directly, so its adjoint carries gh_t as well (checked by finite differences in tests).
+ *   With terminal adjoints (the loss also holds <dlast_h, h_{L-1}> + <dlast_v, v_{L-1}>) they
+ *   enter at the last step: gh_{L-1} gets dlast_h and gv_{L-1} gets dlast_v.  The adjoints of
+ *   the initial state follow from h_0 = a_0 h0 + v_0 and v_0 = beta v0 + w_0:
+ *     dh0 = a_0 * gh_0,   dv0 = beta * gv_0.
  *
  * Threads: the forward is split over (b, d) channel pairs, which are independent.  The
  * backward is split over batch rows b; dA and dDskip are first summed per row and the rows are
@@ -65,11 +72,12 @@ int msm_oracle_max_threads(void) {
 #endif
 }
 
-/* Momentum recurrence, forward.  last_h / last_v may be NULL; Dskip may be NULL. */
+/* Momentum recurrence, forward.  last_h / last_v, h0 / v0 and Dskip may be NULL (a NULL
+ * initial state is zero). */
 int msm_oracle_fwd(const double* x, const double* delta, const double* A, const double* B,
-                   const double* C, const double* Dskip, double beta, double alpha, int64_t Bt,
-                   int64_t L, int64_t D, int64_t N, double* y, double* last_h, double* last_v,
-                   int nthreads) {
+                   const double* C, const double* Dskip, const double* h0, const double* v0,
+                   double beta, double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                   double* y, double* last_h, double* last_v, int nthreads) {
   if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
   set_threads(nthreads);
   int64_t nchan = Bt * D;
@@ -78,7 +86,8 @@ int msm_oracle_fwd(const double* x, const double* delta, const double* A, const 
     int64_t b = bd / D, d = bd % D;
     for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] = 0.0;
     for (int64_t n = 0; n < N; ++n) {
-      double v = 0.0, h = 0.0;
+      double v = v0 ? v0[(b * D + d) * N + n] : 0.0;
+      double h = h0 ? h0[(b * D + d) * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
         double dt = delta[(b * L + t) * D + d];
         double xt = x[(b * L + t) * D + d];
@@ -127,13 +136,16 @@ int msm_oracle_fwd_plain(const double* x, const double* delta, const double* A, 
   return 0;
 }
 
-/* Backward of l = sum(dy * y) for the momentum recurrence.  All outputs are overwritten.
- * dDskip must be non-NULL when Dskip is non-NULL and is ignored otherwise. */
+/* Backward of l = sum(dy * y) (+ <dlast_h, h_{L-1}> + <dlast_v, v_{L-1}>) for the momentum
+ * recurrence started at (h0, v0).  All outputs are overwritten.  dDskip must be non-NULL when
+ * Dskip is non-NULL and is ignored otherwise.  h0, v0, dlast_h, dlast_v may be NULL (zero);
+ * dh0, dv0 may be NULL (not written). */
 int msm_oracle_bwd(const double* x, const double* delta, const double* A, const double* B,
-                   const double* C, const double* Dskip, const double* dy, double beta,
+                   const double* C, const double* Dskip, const double* dy, const double* h0,
+                   const double* v0, const double* dlast_h, const double* dlast_v, double beta,
                    double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
                    double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
-                   int nthreads) {
+                   double* dh0, double* dv0, int nthreads) {
   if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
   if (Dskip && !dDskip) return 1;
   set_threads(nthreads);
@@ -158,9 +170,11 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
     for (int64_t d = 0; d < D; ++d) {
       for (int64_t n = 0; n < N; ++n) {
         double An = A[d * N + n];
-        /* forward, keeping every h_t: hs[t+1] = h_t, hs[0] = h_{-1} = 0 */
-        double v = 0.0, h = 0.0;
-        hs[0] = 0.0;
+        /* forward, keeping every h_t: hs[t+1] = h_t, hs[0] = h_{-1} (the initial state) */
+        const int64_t s_i = (b * D + d) * N + n;
+        double v = v0 ? v0[s_i] : 0.0;
+        double h = h0 ? h0[s_i] : 0.0;
+        hs[0] = h;
         for (int64_t t = 0; t < L; ++t) {
           double dt = delta[(b * L + t) * D + d];
           double xt = x[(b * L + t) * D + d];
@@ -169,8 +183,8 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
           h = a * h + v;
           hs[t + 1] = h;
         }
-        /* reverse sweep */
-        double gh_next = 0.0, gv_next = 0.0, a_next = 0.0;
+        /* reverse sweep; the terminal adjoint of h enters as a_next * gh_next at t = L-1 */
+        double gh_next = dlast_h ? dlast_h[s_i] : 0.0, gv_next = 0.0, a_next = 1.0;
         for (int64_t t = L - 1; t >= 0; --t) {
           int64_t i = (b * L + t) * D + d;
           int64_t j = (b * L + t) * N + n;
@@ -178,6 +192,7 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
           double a = exp(dt * An);
           double gh = C[j] * dyt + a_next * gh_next;
           double gv = gh + beta * gv_next;
+          if (t == L - 1 && dlast_v) gv += dlast_v[s_i];
           double hprev = hs[t]; /* h_{t-1} */
           dx[i] += alpha * dt * B[j] * gv;
           ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gh;
@@ -188,6 +203,9 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
           gv_next = gv;
           a_next = a;
         }
+        /* adjoints of the initial state (with L = 0 they are the terminal adjoints) */
+        if (dh0) dh0[s_i] = L > 0 ? a_next * gh_next : (dlast_h ? dlast_h[s_i] : 0.0);
+        if (dv0) dv0[s_i] = L > 0 ? beta * gv_next : (dlast_v ? dlast_v[s_i] : 0.0);
       }
       if (Dskip) {
         for (int64_t t = 0; t < L; ++t) {

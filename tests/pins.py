@@ -381,7 +381,130 @@ def pin_bwd_beta0_alpha0(orc):
     close(g["dx"], Ds * dy, rtol=1e-15, atol=0, what="alpha=0 dx")
 
 
+# ---------------------------------------------------------------------------------------------
+# Initial state and continuation (the README's last_state outputs fed back into the scan)
+# ---------------------------------------------------------------------------------------------
+
+def _rand_state(rng, Bt, D, N):
+    return rng.standard_normal((Bt, D, N)), rng.standard_normal((Bt, D, N))
+
+
+def pin_initial_state_filter(orc):
+    """Constant coefficients from a non-zero start: v and h are first-order IIR filters whose
+    initial conditions are the initial state (scipy.signal.lfilter with zi)."""
+    rng = np.random.default_rng(23)
+    L, N = 40, 3
+    A = np.array([-0.4, -1.1, 0.0])
+    dlt = 0.25
+    xs = rng.standard_normal(L)
+    Bv, Cv = rng.standard_normal(N), rng.standard_normal(N)
+    h0, v0 = rng.standard_normal((1, 1, N)), rng.standard_normal((1, 1, N))
+    for beta, alpha in [(0.0, 1.0), (0.85, 0.7)]:
+        want_y = np.zeros(L)
+        want_h, want_v = np.zeros(N), np.zeros(N)
+        for n in range(N):
+            a = math.exp(dlt * A[n])
+            w = alpha * dlt * Bv[n] * xs
+            v, _ = scipy.signal.lfilter([1.0], [1.0, -beta], w, zi=[beta * v0[0, 0, n]])
+            h, _ = scipy.signal.lfilter([1.0], [1.0, -a], v, zi=[a * h0[0, 0, n]])
+            want_y += Cv[n] * h
+            want_h[n], want_v[n] = h[-1], v[-1]
+        y, lh, lv = orc.fwd(xs.reshape(1, L, 1), np.full((1, L, 1), dlt), A.reshape(1, N),
+                            np.tile(Bv, (1, L, 1)), np.tile(Cv, (1, L, 1)), beta, alpha,
+                            h0=h0, v0=v0)
+        close(y[0, :, 0], want_y, rtol=1e-11, atol=1e-12, what="initial-state filter beta=%g" % beta)
+        close(lh[0, 0], want_h, rtol=1e-11, atol=1e-12, what="initial-state last h")
+        close(lv[0, 0], want_v, rtol=1e-11, atol=1e-12, what="initial-state last v")
+
+
+def pin_continuation(orc):
+    """Scanning L1 steps, then continuing from the state reached, equals scanning L1 + L2 steps
+    at once (bitwise: the same operations in the same order)."""
+    rng = np.random.default_rng(29)
+    Bt, L, D, N, L1 = 2, 23, 3, 4, 9
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    h0, v0 = _rand_state(rng, Bt, D, N)
+    beta, alpha = 0.8, 0.9
+    y, lh, lv = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds, h0=h0, v0=v0)
+    s1 = (slice(None), slice(0, L1))
+    s2 = (slice(None), slice(L1, L))
+    y1, lh1, lv1 = orc.fwd(x[s1], delta[s1], A, B[s1], C[s1], beta, alpha, Dskip=Ds, h0=h0, v0=v0)
+    y2, lh2, lv2 = orc.fwd(x[s2], delta[s2], A, B[s2], C[s2], beta, alpha, Dskip=Ds, h0=lh1,
+                           v0=lv1)
+    close(np.concatenate([y1, y2], axis=1), y, rtol=0, atol=0, what="continued y")
+    close(lh2, lh, rtol=0, atol=0, what="continued last h")
+    close(lv2, lv, rtol=0, atol=0, what="continued last v")
+
+
+def _state_loss(orc, p, dy, dlh, dlv, beta, alpha):
+    y, lh, lv = orc.fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], beta, alpha,
+                        Dskip=p["Dskip"], h0=p["h0"], v0=p["v0"])
+    return float(np.sum(dy * y) + np.sum(dlh * lh) + np.sum(dlv * lv))
+
+
+def pin_state_finite_differences(orc):
+    """Central differences of sum(dy y) + <dlast_h, last_h> + <dlast_v, last_v> for a scan
+    started at a non-zero state: the initial-state adjoints and every input gradient."""
+    rng = np.random.default_rng(31)
+    Bt, L, D, N = 2, 6, 2, 3
+    beta, alpha = 0.7, 0.8
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    h0, v0 = _rand_state(rng, Bt, D, N)
+    dy = rng.standard_normal((Bt, L, D))
+    dlh, dlv = _rand_state(rng, Bt, D, N)
+    p = dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Ds, h0=h0, v0=v0)
+    g = orc.bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds, h0=h0, v0=v0, dlast_h=dlh,
+                dlast_v=dlv)
+    eps = 1e-6
+    for pname, gname in [("h0", "dh0"), ("v0", "dv0"), ("x", "dx"), ("delta", "ddelta"),
+                         ("A", "dA"), ("B", "dB"), ("C", "dC"), ("Dskip", "dDskip")]:
+        arr = p[pname]
+        for i in np.ndindex(arr.shape):
+            orig = arr[i]
+            arr[i] = orig + eps
+            lp = _state_loss(orc, p, dy, dlh, dlv, beta, alpha)
+            arr[i] = orig - eps
+            lm = _state_loss(orc, p, dy, dlh, dlv, beta, alpha)
+            arr[i] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname][i]
+            if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                raise AssertionError("finite difference mismatch for %s%s: fd %.9g analytic %.9g"
+                                     % (gname, i, fd, an))
+    # no sequence: the initial-state adjoints are the terminal adjoints
+    g0 = orc.bwd(x[:, :0], delta[:, :0], A, B[:, :0], C[:, :0], dy[:, :0], beta, alpha, h0=h0,
+                 v0=v0, dlast_h=dlh, dlast_v=dlv)
+    close(g0["dh0"], dlh, rtol=0, atol=0, what="L=0 dh0")
+    close(g0["dv0"], dlv, rtol=0, atol=0, what="L=0 dv0")
+
+
+def pin_bwd_continuation(orc):
+    """The backward of a scan split in two: the second part's initial-state adjoints are the
+    first part's terminal adjoints, and the pieces add up to the backward of the whole."""
+    rng = np.random.default_rng(37)
+    Bt, L, D, N, L1 = 2, 17, 3, 2, 7
+    beta, alpha = 0.9, 0.6
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    h0, v0 = _rand_state(rng, Bt, D, N)
+    dy = rng.standard_normal((Bt, L, D))
+    g = orc.bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds, h0=h0, v0=v0)
+    s1 = (slice(None), slice(0, L1))
+    s2 = (slice(None), slice(L1, L))
+    _, lh1, lv1 = orc.fwd(x[s1], delta[s1], A, B[s1], C[s1], beta, alpha, h0=h0, v0=v0)
+    g2 = orc.bwd(x[s2], delta[s2], A, B[s2], C[s2], dy[s2], beta, alpha, Dskip=Ds, h0=lh1, v0=lv1)
+    g1 = orc.bwd(x[s1], delta[s1], A, B[s1], C[s1], dy[s1], beta, alpha, Dskip=Ds, h0=h0, v0=v0,
+                 dlast_h=g2["dh0"], dlast_v=g2["dv0"])
+    for k in ("dx", "ddelta", "dB", "dC"):
+        close(np.concatenate([g1[k], g2[k]], axis=1), g[k], rtol=1e-10, atol=1e-12,
+              what="split %s" % k)
+    for k in ("dA", "dDskip"):
+        close(g1[k] + g2[k], g[k], rtol=1e-10, atol=1e-12, what="split %s" % k)
+    close(g1["dh0"], g["dh0"], rtol=1e-10, atol=1e-12, what="split dh0")
+    close(g1["dv0"], g["dv0"], rtol=1e-10, atol=1e-12, what="split dv0")
+
+
 ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
             pin_beta0_equivalence, pin_structure, pin_finite_differences,
-            pin_scaling_identities, pin_bwd_beta0_alpha0]
+            pin_scaling_identities, pin_bwd_beta0_alpha0, pin_initial_state_filter,
+            pin_continuation, pin_state_finite_differences, pin_bwd_continuation]

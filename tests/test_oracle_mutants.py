@@ -41,6 +41,13 @@ MUTANTS = [
     ("bwd_dB_uses_gh", "dB[j] += alpha * dt * xt * gv;", "dB[j] += alpha * dt * xt * gh;", 0),
     ("bwd_dx_drops_alpha", "dx[i] += alpha * dt * B[j] * gv;", "dx[i] += dt * B[j] * gv;", 0),
     ("bwd_dDskip_uses_y", "dD_rows[b * D + d] += dy[i] * x[i];", "dD_rows[b * D + d] += dy[i];", 0),
+    # initial state and terminal adjoints
+    ("fwd_ignores_v0", "double v = v0 ? v0[(b * D + d) * N + n] : 0.0;", "double v = 0.0;", 0),
+    ("bwd_ignores_h0", "hs[0] = h;", "hs[0] = 0.0;", 0),
+    ("bwd_terminal_v_scaled", "gv += dlast_v[s_i];", "gv += beta * dlast_v[s_i];", 0),
+    ("bwd_drops_terminal_h", "gv_next = 0.0, a_next = 1.0;", "gv_next = 0.0, a_next = 0.0;", 0),
+    ("bwd_dh0_drops_a", "dh0[s_i] = L > 0 ? a_next * gh_next", "dh0[s_i] = L > 0 ? gh_next", 0),
+    ("bwd_dv0_drops_beta", "dv0[s_i] = L > 0 ? beta * gv_next", "dv0[s_i] = L > 0 ? gv_next", 0),
 ]
 
 
