@@ -106,6 +106,19 @@ msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float*
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const msm_plan* plan);
 
+/* Forward scan started at a given state: h0, v0 are (Bt, D, N) fp32, NULL meaning zero.  This
+ * continues a sequence from the last_h / last_v a previous call returned for its first part
+ * (the README's last_state outputs; chunked prefill and streaming).  The result equals one call
+ * over the whole sequence up to rounding.  h0 and v0 must not overlap any output (continue
+ * with a second pair of state buffers rather than in place).  plan may be NULL (automatic).
+ * Everything else as msm_scan_fwd_with_plan, which is this call with h0 = v0 = NULL. */
+msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const float* h0,
+                              const float* v0, void* y, float* last_h, float* last_v, int64_t Bt,
+                              int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                              msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan);
+
 /* Backward scan: gradients of sum(dy * y).  dx, ddelta, dB, dC, dA are overwritten (not
  * accumulated).  dDskip is required exactly when Dskip is non-NULL.  The forward is recomputed
  * inside; no saved activations are needed.  Same requirements as msm_scan_fwd. */
@@ -122,6 +135,24 @@ msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float*
                                   int64_t N, float beta, float alpha, msm_dtype io,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const msm_plan* plan);
+
+/* Backward of a scan started at (h0, v0) (NULL: zero), for the loss
+ *   sum(dy * y) + <dlast_h, last_h> + <dlast_v, last_v>
+ * (dlast_h, dlast_v: (Bt, D, N) fp32 adjoints of the final state, NULL meaning zero).  Besides
+ * the gradients of msm_scan_bwd it writes the adjoints of the initial state, dh0 = a_0 gh_0 and
+ * dv0 = beta gv_0 ((Bt, D, N) fp32), when dh0 / dv0 are non-NULL.  A sequence split in two is
+ * differentiated by running the second part first and passing its dh0 / dv0 as the first
+ * part's dlast_h / dlast_v (Momentum Mamba README, "Gradient Flow", read with the terminal
+ * terms of a split sequence).  msm_scan_bwd_with_plan is this call with every state pointer
+ * NULL. */
+msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const void* dy, const float* h0,
+                              const float* v0, const float* dlast_h, const float* dlast_v,
+                              void* dx, void* ddelta, float* dA, void* dB, void* dC,
+                              float* dDskip, float* dh0, float* dv0, int64_t Bt, int64_t L,
+                              int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan);
 
 #ifdef __cplusplus
 }

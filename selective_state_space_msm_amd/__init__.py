@@ -29,7 +29,8 @@ _STATUS = {0: "MSM_OK", 1: "MSM_ERR_INVALID_ARG", 2: "MSM_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = [
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
-    "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan",
+    "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan", "msm_scan_fwd_state",
+    "msm_scan_bwd_state",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +92,12 @@ def load_library():
     lib.msm_scan_bwd.restype = ctypes.c_int
     lib.msm_scan_bwd_with_plan.argtypes = bwd + [ctypes.POINTER(_Plan)]
     lib.msm_scan_bwd_with_plan.restype = ctypes.c_int
+    lib.msm_scan_fwd_state.argtypes = ([P] * 11 + [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P,
+                                                   ctypes.POINTER(_Plan)])
+    lib.msm_scan_fwd_state.restype = ctypes.c_int
+    lib.msm_scan_bwd_state.argtypes = ([P] * 19 + [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P,
+                                                   ctypes.POINTER(_Plan)])
+    lib.msm_scan_bwd_state.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -183,10 +190,13 @@ def _plan_arg(plan):
 
 
 def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=None,
-                 last_v=None, return_last_state=False, workspace=None, stream=None, plan=None):
+                 last_v=None, return_last_state=False, workspace=None, stream=None, plan=None,
+                 h0=None, v0=None):
     """Forward scan.  x, delta: (Bt, L, D); A: (D, N) fp32; B, C: (Bt, L, N); Dskip: (D,) fp32.
 
     x, delta, B, C share one dtype (float32 or bfloat16), which is also the dtype of y.
+    h0, v0: optional (Bt, D, N) fp32 initial state (msm_scan_fwd_state), e.g. the last state of
+    a previous call over the first part of the sequence.
     Returns y, or (y, last_h, last_v) when return_last_state is true.
     """
     import torch
@@ -210,18 +220,23 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
             last_h = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
         if last_v is None:
             last_v = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
-    for t, nm in ((last_h, "last_h"), (last_v, "last_v")):
+    for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
         if t is not None:
             _check(t, nm, (Bt, D, N), torch.float32, dev)
     nbytes = int(lib.msm_scan_fwd_workspace_bytes(Bt, L, D, N, io))
     ws, wsb = _workspace(nbytes, workspace, dev)
-    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(y), _ptr(last_h),
-            _ptr(last_v), Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb,
-            _stream_handle(stream, dev))
-    if plan is None:
-        st = lib.msm_scan_fwd(*args)
+    tail = (Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
+    if h0 is not None or v0 is not None:
+        st = lib.msm_scan_fwd_state(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
+                                    _ptr(h0), _ptr(v0), _ptr(y), _ptr(last_h), _ptr(last_v),
+                                    *tail, _plan_arg(plan))
     else:
-        st = lib.msm_scan_fwd_with_plan(*args, _plan_arg(plan))
+        args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(y),
+                _ptr(last_h), _ptr(last_v)) + tail
+        if plan is None:
+            st = lib.msm_scan_fwd(*args)
+        else:
+            st = lib.msm_scan_fwd_with_plan(*args, _plan_arg(plan))
     if st != 0:
         raise MsmError(st, "msm_scan_fwd")
     if return_last_state:
@@ -230,9 +245,15 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
 
 
 def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, workspace=None,
-                 stream=None, plan=None):
+                 stream=None, plan=None, h0=None, v0=None, dlast_h=None, dlast_v=None,
+                 state_grads=False):
     """Gradients of sum(dy * y).  Returns a dict: dx, ddelta (Bt, L, D) and dB, dC (Bt, L, N)
-    in the I/O dtype; dA (D, N) and dDskip (D,) (None without Dskip) in float32."""
+    in the I/O dtype; dA (D, N) and dDskip (D,) (None without Dskip) in float32.
+
+    With an initial state h0, v0 and/or adjoints dlast_h, dlast_v of the final state (all
+    (Bt, D, N) fp32; msm_scan_bwd_state), the loss also holds <dlast_h, last_h> +
+    <dlast_v, last_v>; with state_grads the dict also holds dh0, dv0 (fp32 (Bt, D, N)).
+    """
     import torch
     lib = load_library()
     dev = x.device
@@ -255,15 +276,27 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
         o.setdefault("dDskip", torch.empty((D,), dtype=torch.float32, device=dev))
     else:
         o["dDskip"] = None
+    states = (h0, v0, dlast_h, dlast_v)
+    for t, nm in zip(states, ("h0", "v0", "dlast_h", "dlast_v")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N), torch.float32, dev)
+    if state_grads:
+        o.setdefault("dh0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
+        o.setdefault("dv0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
     nbytes = int(lib.msm_scan_bwd_workspace_bytes(Bt, L, D, N, io))
     ws, wsb = _workspace(nbytes, workspace, dev)
-    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy), _ptr(o["dx"]),
-            _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]),
-            Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
-    if plan is None:
-        st = lib.msm_scan_bwd(*args)
+    tail = (Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
+    grads = (_ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+             _ptr(o["dDskip"]))
+    ins = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy))
+    if state_grads or any(t is not None for t in states):
+        st = lib.msm_scan_bwd_state(*ins, *(_ptr(t) for t in states), *grads,
+                                    _ptr(o.get("dh0")), _ptr(o.get("dv0")), *tail,
+                                    _plan_arg(plan))
+    elif plan is None:
+        st = lib.msm_scan_bwd(*ins, *grads, *tail)
     else:
-        st = lib.msm_scan_bwd_with_plan(*args, _plan_arg(plan))
+        st = lib.msm_scan_bwd_with_plan(*ins, *grads, *tail, _plan_arg(plan))
     if st != 0:
         raise MsmError(st, "msm_scan_bwd")
     return o

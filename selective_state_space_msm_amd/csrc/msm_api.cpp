@@ -223,12 +223,12 @@ msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dt
   return MSM_OK;
 }
 
-msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
-                                  const void* B, const void* C, const float* Dskip, void* y,
-                                  float* last_h, float* last_v, int64_t Bt, int64_t L, int64_t D,
-                                  int64_t N, float beta, float alpha, msm_dtype io,
-                                  void* workspace, size_t workspace_bytes, void* stream,
-                                  const msm_plan* plan) {
+msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const float* h0,
+                              const float* v0, void* y, float* last_h, float* last_v, int64_t Bt,
+                              int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                              msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
@@ -250,12 +250,14 @@ msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float*
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
   const FwdLayout lay = fwd_layout(Bt, L, D, N);
   if (workspace_bytes < lay.total || (lay.total > 0 && !workspace)) return MSM_ERR_WORKSPACE;
-  const Range ins[] = {rng(x, nxd * es), rng(delta, nxd * es), rng(A, (size_t)(D * N) * 4),
-                       rng(B, nbc * es), rng(C, nbc * es), rng(Dskip, Dskip ? (size_t)D * 4 : 0)};
-  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? (size_t)(Bt * D * N) * 4 : 0),
-                        rng(last_v, last_v ? (size_t)(Bt * D * N) * 4 : 0),
-                        rng(workspace, lay.total)};
-  if (any_overlap(outs, 4, ins, 6)) return MSM_ERR_INVALID_ARG;
+  const size_t nst = (size_t)(Bt * D * N) * 4;
+  const Range ins[] = {rng(x, nxd * es),        rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 4), rng(B, nbc * es),
+                       rng(C, nbc * es),        rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(h0, h0 ? nst : 0),   rng(v0, v0 ? nst : 0)};
+  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? nst : 0),
+                        rng(last_v, last_v ? nst : 0), rng(workspace, lay.total)};
+  if (any_overlap(outs, 4, ins, 8)) return MSM_ERR_INVALID_ARG;
 
   // chunk length: a multiple of the tile, so only the final chunk can end mid-tile.  The
   // kernels address a chunk with 32-bit byte offsets: keep every chunk of every (Bt,L,D)
@@ -273,6 +275,8 @@ msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float*
   a.B = B;
   a.C = C;
   a.Dskip = Dskip;
+  a.h0 = h0;
+  a.v0 = v0;
   a.y = y;
   a.last_h = last_h;
   a.last_v = last_v;
@@ -297,6 +301,16 @@ msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float*
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
 }
 
+msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, void* y,
+                                  float* last_h, float* last_v, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan) {
+  return msm_scan_fwd_state(x, delta, A, B, C, Dskip, nullptr, nullptr, y, last_h, last_v, Bt, L,
+                            D, N, beta, alpha, io, workspace, workspace_bytes, stream, plan);
+}
+
 msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
                         const void* C, const float* Dskip, void* y, float* last_h,
                         float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
@@ -306,13 +320,14 @@ msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const 
                                 alpha, io, workspace, workspace_bytes, stream, nullptr);
 }
 
-msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float* A,
-                                  const void* B, const void* C, const float* Dskip,
-                                  const void* dy, void* dx, void* ddelta, float* dA, void* dB,
-                                  void* dC, float* dDskip, int64_t Bt, int64_t L, int64_t D,
-                                  int64_t N, float beta, float alpha, msm_dtype io,
-                                  void* workspace, size_t workspace_bytes, void* stream,
-                                  const msm_plan* plan) {
+msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const void* dy, const float* h0,
+                              const float* v0, const float* dlast_h, const float* dlast_v,
+                              void* dx, void* ddelta, float* dA, void* dB, void* dC,
+                              float* dDskip, float* dh0, float* dv0, int64_t Bt, int64_t L,
+                              int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC)
@@ -333,14 +348,24 @@ msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float*
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
   const BwdLayout lay = bwd_layout(Bt, L, D, N);
   if (workspace_bytes < lay.total || !workspace) return MSM_ERR_WORKSPACE;
-  const Range ins[] = {rng(x, nxd * es), rng(delta, nxd * es), rng(A, (size_t)(D * N) * 4),
-                       rng(B, nbc * es), rng(C, nbc * es), rng(Dskip, Dskip ? (size_t)D * 4 : 0),
-                       rng(dy, nxd * es)};
+  const size_t nst = (size_t)(Bt * D * N) * 4;
+  const Range ins[] = {rng(x, nxd * es),
+                       rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 4),
+                       rng(B, nbc * es),
+                       rng(C, nbc * es),
+                       rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(dy, nxd * es),
+                       rng(h0, h0 ? nst : 0),
+                       rng(v0, v0 ? nst : 0),
+                       rng(dlast_h, dlast_h ? nst : 0),
+                       rng(dlast_v, dlast_v ? nst : 0)};
   const Range outs[] = {rng(dx, nxd * es),           rng(ddelta, nxd * es),
                         rng(dA, (size_t)(D * N) * 4), rng(dB, nbc * es),
                         rng(dC, nbc * es),           rng(dDskip, dDskip ? (size_t)D * 4 : 0),
+                        rng(dh0, dh0 ? nst : 0),     rng(dv0, dv0 ? nst : 0),
                         rng(workspace, lay.total)};
-  if (any_overlap(outs, 7, ins, 7)) return MSM_ERR_INVALID_ARG;
+  if (any_overlap(outs, 9, ins, 11)) return MSM_ERR_INVALID_ARG;
 
   msm::BwdArgs a{};
   a.x = x;
@@ -350,6 +375,12 @@ msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float*
   a.C = C;
   a.Dskip = Dskip;
   a.dy = dy;
+  a.h0 = h0;
+  a.v0 = v0;
+  a.dlast_h = dlast_h;
+  a.dlast_v = dlast_v;
+  a.dh0 = dh0;
+  a.dv0 = dv0;
   a.dx = dx;
   a.ddelta = ddelta;
   a.dA = dA;
@@ -373,6 +404,18 @@ msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float*
   hipError_t e = msm::launch_bwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f,
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip,
+                                  const void* dy, void* dx, void* ddelta, float* dA, void* dB,
+                                  void* dC, float* dDskip, int64_t Bt, int64_t L, int64_t D,
+                                  int64_t N, float beta, float alpha, msm_dtype io,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const msm_plan* plan) {
+  return msm_scan_bwd_state(x, delta, A, B, C, Dskip, dy, nullptr, nullptr, nullptr, nullptr, dx,
+                            ddelta, dA, dB, dC, dDskip, nullptr, nullptr, Bt, L, D, N, beta,
+                            alpha, io, workspace, workspace_bytes, stream, plan);
 }
 
 msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,

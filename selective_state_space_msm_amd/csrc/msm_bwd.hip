@@ -28,6 +28,8 @@
 //     then DPP), then across channel blocks in a small finalize kernel.
 // This kernel serves 4 and 16 padded states; 64 padded states use the full-wavefront
 // backward in msm_bwd_wide.hip.
+#include <type_traits>
+
 #include "msm_device.hpp"
 #include "msm_internal.h"
 
@@ -131,8 +133,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     Af[j] = an;
-    v[j] = 0.f;
-    h[j] = 0.f;
+    // the forward starts at the given initial state
+    const int64_t si = (b * D + dl) * N + n;
+    v[j] = (p.v0 && dvalid && n < N) ? p.v0[si] : 0.f;
+    h[j] = (p.h0 && dvalid && n < N) ? p.h0[si] : 0.f;
   }
 
   // ---- staging addresses (per-tile buffer resources, constant per-thread offsets) ----
@@ -391,9 +395,24 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   // inputs into registers), recompute and sweep `tile` (if it exists) from LDS, finish the
   // dx / ddelta of tile + 1, stage tile - 1 into the other LDS buffer.  Loads, stores and the
   // barrier are unconditional, so every step has the same memory pattern.
-  auto step2 = [&](int64_t tile, const float(&cv)[K], const float(&chh)[K], float(&nv_)[K],
-                   float(&nh_)[K]) {
+  // rows of the last tile: the terminal adjoints enter at its row nlast - 1 (the rows after
+  // it are past the end of the sequence and keep the adjoint state at zero)
+  const int nlast = (int)(L - (NT - 1) * TB);
+  // `first` (std::true_type for the step of tile NT-1 only) compiles the terminal-adjoint
+  // injection into that step alone
+  auto step2 = [&](auto first, int64_t tile, const float(&cv)[K], const float(&chh)[K],
+                   float(&nv_)[K], float(&nh_)[K]) {
+    constexpr bool FIRST = decltype(first)::value;
     const bool live = tile >= 0;
+    // adjoints of the final state, loaded in the first step only
+    double dlh[K], dlv[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)gs * K + j;
+      const int64_t si = (b * D + dl) * N + n;
+      dlh[j] = (FIRST && p.dlast_h && dvalid && n < N) ? (double)p.dlast_h[si] : 0.0;
+      dlv[j] = (FIRST && p.dlast_v && dvalid && n < N) ? (double)p.dlast_v[si] : 0.0;
+    }
     const int buf = (int)((NT - 1 - tile) & 1);
     const int pb = (int)(tile & 1);
     const int64_t tp = tile > 0 ? tile - 1 : 0;  // prefetch (tile 0 again at the end)
@@ -438,8 +457,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         float p1 = 0.f, p2 = 0.f;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
+          if (FIRST && tt == nlast - 1) ghn[j] = dlh[j];
           const double gh = fma(cs64[buf][tt][gs][j], gy64, ghn[j]);
-          const double gv = BETA0 ? gh : fma(beta64, gvp[j], gh);
+          double gv = BETA0 ? gh : fma(beta64, gvp[j], gh);
+          if (FIRST && tt == nlast - 1) gv += dlv[j];
           ghn[j] = (double)av[tt][j] * gh;
           if (!BETA0) gvp[j] = gv;
           const float gvf = (float)gv;
@@ -467,6 +488,17 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
       for (int j = 0; j < K; ++j) dA64[j] += (double)dAt[j];
       if (HAS_DSKIP) dD64 += (double)dDt;
     }
+    // after step 0 the adjoint carries are the adjoints of the initial state:
+    // dh0 = a_0 gh_0, dv0 = beta gv_0 (stores under this branch happen once per workgroup)
+    if (tile == 0 && dvalid) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t n = (int64_t)gs * K + j;
+        const int64_t si = (b * D + d) * N + n;
+        if (n < N && p.dh0) p.dh0[si] = (float)ghn[j];
+        if (n < N && p.dv0) p.dv0[si] = BETA0 ? 0.f : (float)(beta64 * gvp[j]);
+      }
+    }
     bc_store(buf ^ 1, true);
     x_store(buf ^ 1, true);
     __syncthreads();
@@ -479,11 +511,12 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   bc_store(0, true);
   x_store(0, true);
   __syncthreads();
-  // tiles NT-1 .. 0, then tile -1 (finishes tile 0), in pairs so the checkpoint registers
-  // alternate instead of being copied; a possible extra step (tile -2) does nothing but load
-  for (int64_t t = NT - 1; t >= -1; t -= 2) {
-    step2(t, ckv0, ckh0, ckv1, ckh1);
-    step2(t - 1, ckv1, ckh1, ckv0, ckh0);
+  // tile NT-1, then tiles NT-2 .. 0 and tile -1 (finishes tile 0) in pairs so the checkpoint
+  // registers alternate instead of being copied; a possible extra step (tile -2) only loads
+  step2(std::true_type{}, NT - 1, ckv0, ckh0, ckv1, ckh1);
+  for (int64_t t = NT - 2; t >= -1; t -= 2) {
+    step2(std::false_type{}, t, ckv1, ckh1, ckv0, ckh0);
+    step2(std::false_type{}, t - 1, ckv0, ckh0, ckv1, ckh1);
   }
 
   if (dvalid) {

@@ -86,8 +86,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     A64[j] = an;
-    v[j] = 0.f;
-    h[j] = 0.f;
+    const int64_t si = (b * D + dl) * N + n;
+    v[j] = (p.v0 && n < N) ? p.v0[si] : 0.f;
+    h[j] = (p.h0 && n < N) ? p.h0[si] : 0.f;
   }
 
   auto stage = [&](int64_t ts, int64_t nv) {
@@ -159,10 +160,13 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   // The adjoint state and the sums that feed ddelta are kept in fp64: ddelta is a difference
   // of two large terms (x * sum B gv and sum A a h gh), and fp32 adjoints lose too many bits.
   double ghn[K], gvn[K], dAacc[K];  // ghn = a_{t+1} gh_{t+1}, gvn = beta gv_{t+1}
+  // the adjoints of the final state enter as the carries into the last step
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    ghn[j] = 0.0;
-    gvn[j] = 0.0;
+    const int64_t n = (int64_t)g * K + j;
+    const int64_t si = (b * D + dl) * N + n;
+    ghn[j] = (p.dlast_h && n < N) ? (double)p.dlast_h[si] : 0.0;
+    gvn[j] = (p.dlast_v && n < N) ? (double)p.dlast_v[si] : 0.0;
     dAacc[j] = 0.0;
   }
   float dDacc = 0.f;
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
             for (int j = 0; j < K; ++j) {
               const double a64 = av[tt][j];
               const double gh = fma(bc[K + j], gy64, ghn[j]);
-              const double gv = BETA0 ? gh : gh + gvn[j];
+              const double gv = gh + gvn[j];
               s1 = fma(bc[j], gv, s1);
               const double gg = a64 * (double)hs[tt][j] * gh;
               s2 = fma(A64[j], gg, s2);
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
               vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
               vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
               ghn[j] = a64 * gh;
-              if (!BETA0) gvn[j] = beta64 * gv;
+              gvn[j] = BETA0 ? 0.0 : beta64 * gv;
             }
             spart[0][g][tr][lane] = s1;
             spart[1][g][tr][lane] = s2;
@@ -298,6 +302,16 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
     }
   }
 
+  // adjoints of the initial state: after step 0 the carries are a_0 gh_0 and beta gv_0
+  if (dvalid) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t n = (int64_t)g * K + j;
+      const int64_t si = (b * D + d) * N + n;
+      if (n < N && p.dh0) p.dh0[si] = (float)ghn[j];
+      if (n < N && p.dv0) p.dv0[si] = (float)gvn[j];
+    }
+  }
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {

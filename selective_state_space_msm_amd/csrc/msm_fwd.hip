@@ -72,15 +72,18 @@ void fwd_kernel(const FwdArgs p) {
   for (int j = 0; j < K; ++j) {
     const int64_t n = (int64_t)g * K + j;
     A2[j] = n < N ? p.A[dl * N + n] * kLog2e : 0.f;
-    v[j] = 0.f;
-    h[j] = 0.f;
+    // the scan starts at the given state; chunk summaries are maps from a zero start
+    const int64_t si = (b * D + dl) * N + n;
+    v[j] = (!SUMMARY && p.v0 && n < N) ? p.v0[si] : 0.f;
+    h[j] = (!SUMMARY && p.h0 && n < N) ? p.h0[si] : 0.f;
     q[j] = 0.f;
   }
   float sd = 0.f, bpow = 1.f;
   const float dsk = (HAS_DSKIP && g == 0) ? p.Dskip[dl] : 0.f;
 
   if (!SUMMARY && k > 0) {
-    // Exact start state of this chunk: apply the maps of chunks 0..k-1 in order.
+    // Exact start state of this chunk: apply the maps of chunks 0..k-1 in order to the
+    // initial state.
     for (int kk = 0; kk < k; ++kk) {
       const int64_t base = b * p.G + kk;
       const float sdv = p.s_sd[base * D + dl];

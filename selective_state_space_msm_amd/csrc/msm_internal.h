@@ -21,6 +21,8 @@ struct FwdArgs {
   const void* B;
   const void* C;
   const float* Dskip;
+  const float* h0;   // (Bt, D, N) initial state or null (zero)
+  const float* v0;
   void* y;
   float* last_h;
   float* last_v;
@@ -45,6 +47,12 @@ struct BwdArgs {
   const void* C;
   const float* Dskip;
   const void* dy;
+  const float* h0;       // (Bt, D, N) initial state or null (zero)
+  const float* v0;
+  const float* dlast_h;  // (Bt, D, N) adjoints of the final state or null (zero)
+  const float* dlast_v;
+  float* dh0;            // (Bt, D, N) adjoints of the initial state or null (not written)
+  float* dv0;
   void* dx;
   void* ddelta;
   float* dA;

@@ -140,6 +140,44 @@ def test_bwd_argument_validation_never_launches(lib):
     assert call(plan=msm._Plan(2, 2)) == UNSUPPORTED  # the backward is never chunked
 
 
+def test_state_entry_points_validation_never_launches(lib):
+    P = ctypes.c_void_p
+
+    def fwd(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, h0=None,
+                 v0=None, y=0x100000, lh=None, lv=None, Bt=1, L=8, D=4, N=4)
+        a.update(kw)
+        return lib.msm_scan_fwd_state(
+            P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["h0"]),
+            P(a["v0"]), P(a["y"]), P(a["lh"]), P(a["lv"]), a["Bt"], a["L"], a["D"], a["N"],
+            ctypes.c_float(0.5), ctypes.c_float(1.0), 0, None, 0, None, None)
+
+    def bwd(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, dy=0x6000,
+                 h0=None, v0=None, dlh=None, dlv=None, dx=0x100000, ddelta=0x200000,
+                 dA=0x300000, dB=0x400000, dC=0x500000, dDskip=None, dh0=None, dv0=None, Bt=1,
+                 L=8, D=4, N=4)
+        a.update(kw)
+        return lib.msm_scan_bwd_state(
+            P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["dy"]),
+            P(a["h0"]), P(a["v0"]), P(a["dlh"]), P(a["dlv"]), P(a["dx"]), P(a["ddelta"]),
+            P(a["dA"]), P(a["dB"]), P(a["dC"]), P(a["dDskip"]), P(a["dh0"]), P(a["dv0"]),
+            a["Bt"], a["L"], a["D"], a["N"], ctypes.c_float(0.5), ctypes.c_float(1.0), 0,
+            P(0x900000), 1 << 30, None, None)
+
+    # a state of 1*4*4 floats = 64 bytes
+    assert fwd(h0=0x100000 + 8) == INVALID        # y written over h0
+    assert fwd(lh=0x7000, h0=0x7000 + 32) == INVALID  # last_h written over h0 (in place)
+    assert fwd(lv=0x7000, v0=0x7000) == INVALID
+    assert fwd(lh=0x7000, lv=0x7000 + 32) == INVALID  # the two last states overlapping
+    assert fwd(L=0, h0=0x7000) == INVALID
+    assert bwd(dh0=0x100000) == INVALID           # dh0 over dx
+    assert bwd(dh0=0x8000, dlh=0x8000) == INVALID  # dh0 over its own terminal adjoint
+    assert bwd(dv0=0x8000, h0=0x8000 + 60) == INVALID
+    assert bwd(dh0=0x8000, dv0=0x8000 + 16) == INVALID
+    assert bwd(dx=None) == INVALID
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msm, "_lib", None)
     monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))

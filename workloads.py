@@ -125,3 +125,12 @@ def make_inputs(w: Workload, *, a_kind: str = "s4d", with_dy: bool | None = None
             dy = round_to_bf16(dy)
     return dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Dskip, dy=dy,
                 beta=float(np.float32(w.beta)), alpha=float(np.float32(w.alpha)), io=w.io)
+
+
+def make_state(w: Workload, seed: int, scale: float = 1.0):
+    """A seeded (Bt, D, N) float32 pair ~ N(0, scale^2): an initial state (h0, v0), or the
+    adjoints (dlast_h, dlast_v) of a final state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = (scale * rng.standard_normal((w.Bt, w.D, w.N))).astype(np.float32)
+    b = (scale * rng.standard_normal((w.Bt, w.D, w.N))).astype(np.float32)
+    return a, b
