@@ -75,6 +75,12 @@ class Oracle:
         lib.msm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64,
                                        I64, P, P, P, P, P, P, P, P, Int]
         lib.msm_oracle_bwd.restype = Int
+        lib.msm_oracle_fused_fwd.argtypes = [P, P, P, P, P, P, P, P, Int, P, P, Dbl, Dbl, I64, I64,
+                                             I64, I64, P, P, P, P, Int]
+        lib.msm_oracle_fused_fwd.restype = Int
+        lib.msm_oracle_fused_bwd.argtypes = [P, P, P, P, P, P, P, P, Int, P, P, P, P, P, Dbl, Dbl,
+                                             I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, Int]
+        lib.msm_oracle_fused_bwd.restype = Int
         lib.msm_oracle_max_threads.argtypes = []
         lib.msm_oracle_max_threads.restype = Int
         self.lib = lib
@@ -153,6 +159,56 @@ class Oracle:
             raise RuntimeError("msm_oracle_bwd failed (%d)" % rc)
         return out
 
+    def fused_fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, z=None, delta_bias=None,
+                  delta_softplus=False, h0=None, v0=None, threads=0):
+        """The fused op forward: delta_eff = softplus(delta + delta_bias) (or delta + delta_bias),
+        the momentum scan on delta_eff, then y = y_raw * silu(z).
+
+        Returns (y, y_raw, last_h, last_v) as float64; y_raw is the output before the gate.
+        """
+        x, delta, A, B, C = (_f64(a) for a in (x, delta, A, B, C))
+        Bt, L, D, N = _shapes(x, A, B)
+        Ds, zz, db, h0, v0 = (None if a is None else _f64(a) for a in (Dskip, z, delta_bias, h0, v0))
+        if zz is not None and zz.shape != x.shape:
+            raise ValueError("z shape %s" % (zz.shape,))
+        if db is not None and db.shape != (D,):
+            raise ValueError("delta_bias shape %s" % (db.shape,))
+        y, y_raw = np.empty((Bt, L, D)), np.empty((Bt, L, D))
+        last_h, last_v = np.empty((Bt, D, N)), np.empty((Bt, D, N))
+        rc = self.lib.msm_oracle_fused_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(Ds), _ptr(zz), _ptr(db), int(bool(delta_softplus)),
+                                           _ptr(h0), _ptr(v0), float(beta), float(alpha), Bt, L,
+                                           D, N, _ptr(y), _ptr(y_raw), _ptr(last_h), _ptr(last_v),
+                                           int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_fused_fwd failed (%d)" % rc)
+        return y, y_raw, last_h, last_v
+
+    def fused_bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, z=None, delta_bias=None,
+                  delta_softplus=False, h0=None, v0=None, dlast_h=None, dlast_v=None, threads=0):
+        """Gradients of the fused op.  Returns the dict of ``bwd`` (ddelta is the gradient of
+        the raw delta) plus dz (None without z) and ddelta_bias (None without delta_bias)."""
+        x, delta, A, B, C, dy = (_f64(a) for a in (x, delta, A, B, C, dy))
+        Bt, L, D, N = _shapes(x, A, B)
+        Ds, zz, db = (None if a is None else _f64(a) for a in (Dskip, z, delta_bias))
+        st = [None if a is None else _f64(a) for a in (h0, v0, dlast_h, dlast_v)]
+        out = dict(dx=np.empty((Bt, L, D)), ddelta=np.empty((Bt, L, D)), dA=np.empty((D, N)),
+                   dB=np.empty((Bt, L, N)), dC=np.empty((Bt, L, N)),
+                   dDskip=None if Ds is None else np.empty((D,)),
+                   dz=None if zz is None else np.empty((Bt, L, D)),
+                   ddelta_bias=None if db is None else np.empty((D,)),
+                   dh0=np.empty((Bt, D, N)), dv0=np.empty((Bt, D, N)))
+        rc = self.lib.msm_oracle_fused_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds), _ptr(zz), _ptr(db),
+            int(bool(delta_softplus)), _ptr(dy), _ptr(st[0]), _ptr(st[1]), _ptr(st[2]),
+            _ptr(st[3]), float(beta), float(alpha), Bt, L, D, N, _ptr(out["dx"]),
+            _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+            _ptr(out["dDskip"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+            _ptr(out["dv0"]), int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_fused_bwd failed (%d)" % rc)
+        return out
+
 
 _default = None
 
@@ -177,6 +233,14 @@ def fwd_plain(*args, **kw):
 
 def bwd(*args, **kw):
     return default().bwd(*args, **kw)
+
+
+def fused_fwd(*args, **kw):
+    return default().fused_fwd(*args, **kw)
+
+
+def fused_bwd(*args, **kw):
+    return default().fused_bwd(*args, **kw)
 
 
 def max_threads() -> int:

@@ -44,6 +44,20 @@
  *   the initial state follow from h_0 = a_0 h0 + v_0 and v_0 = beta v0 + w_0:
  *     dh0 = a_0 * gh_0,   dv0 = beta * gv_0.
  *
+ * The fused op (the selective-scan function of the Momentum Mamba README, "Low-Level
+ * Functions", with its z, delta_bias and delta_softplus arguments; the block layout of "Where the
+ * state computation sits in a Mamba block") wraps the same recurrence in two elementwise steps,
+ * read as follows:
+ *   delta_eff = softplus(delta + delta_bias[d])  with softplus(u) = log(1 + e^u), when
+ *               delta_softplus is set; delta + delta_bias[d] otherwise (a NULL bias is zero);
+ *   the scan above runs on delta_eff, giving y_raw (skip term included);
+ *   y = y_raw * silu(z)  with silu(z) = z / (1 + e^{-z}), when a gate z (Bt, L, D) is given.
+ * Its backward is the chain rule around the scan's backward:
+ *   dy_eff = dy * silu(z),  dz = dy * y_raw * silu'(z),  silu'(z) = s (1 + z (1 - s)),
+ *   s = 1 / (1 + e^{-z});   ddelta = ddelta_eff * s(delta + delta_bias) with softplus (the
+ *   derivative of softplus is the logistic function), ddelta_eff without;
+ *   ddelta_bias[d] = sum over b and t of ddelta.
+ *
  * Threads: the forward is split over (b, d) channel pairs, which are independent.  The
  * backward is split over batch rows b; dA and dDskip are first summed per row and the rows are
  * then added in order, so results do not depend on the thread count.
@@ -233,4 +247,109 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
   free(dA_rows);
   free(dD_rows);
   return 0;
+}
+
+/* ---- the fused op: delta bias and softplus before the scan, the SiLU gate after it ---- */
+
+static double softplus(double u) {
+  /* log(1 + e^u), written so that neither branch overflows */
+  return u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));
+}
+
+static double logistic(double u) {
+  return u >= 0.0 ? 1.0 / (1.0 + exp(-u)) : exp(u) / (1.0 + exp(u));
+}
+
+static double silu(double z) { return z * logistic(z); }
+
+static double silu_grad(double z) {
+  double s = logistic(z);
+  return s * (1.0 + z * (1.0 - s));
+}
+
+/* delta_eff as the fused op feeds it to the scan (see the header). */
+static void effective_delta(const double* delta, const double* delta_bias, int delta_softplus,
+                            int64_t Bt, int64_t L, int64_t D, double* out) {
+  for (int64_t i = 0; i < Bt * L * D; ++i) {
+    double u = delta[i] + (delta_bias ? delta_bias[i % D] : 0.0);
+    out[i] = delta_softplus ? softplus(u) : u;
+  }
+}
+
+/* Fused forward.  z, delta_bias, Dskip, h0, v0, y_raw (the output before the gate), last_h and
+ * last_v may be NULL. */
+int msm_oracle_fused_fwd(const double* x, const double* delta, const double* A, const double* B,
+                         const double* C, const double* Dskip, const double* z,
+                         const double* delta_bias, int delta_softplus, const double* h0,
+                         const double* v0, double beta, double alpha, int64_t Bt, int64_t L,
+                         int64_t D, int64_t N, double* y, double* y_raw, double* last_h,
+                         double* last_v, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  const size_t nxd = (size_t)(Bt * L * D);
+  double* de = (double*)malloc(sizeof(double) * nxd + 1);
+  double* yr = (double*)malloc(sizeof(double) * nxd + 1);
+  if (!de || !yr) { free(de); free(yr); return 2; }
+  effective_delta(delta, delta_bias, delta_softplus, Bt, L, D, de);
+  int rc = msm_oracle_fwd(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, last_h,
+                          last_v, nthreads);
+  if (rc == 0) {
+    for (size_t i = 0; i < nxd; ++i) {
+      if (y_raw) y_raw[i] = yr[i];
+      y[i] = z ? yr[i] * silu(z[i]) : yr[i];
+    }
+  }
+  free(de);
+  free(yr);
+  return rc;
+}
+
+/* Fused backward: gradients of sum(dy * y) (+ the terminal-adjoint terms) with respect to the
+ * fused op's inputs.  ddelta is the gradient of the raw delta (before bias and softplus).  dz
+ * is required when z is given, ddelta_bias when delta_bias is given. */
+int msm_oracle_fused_bwd(const double* x, const double* delta, const double* A, const double* B,
+                         const double* C, const double* Dskip, const double* z,
+                         const double* delta_bias, int delta_softplus, const double* dy,
+                         const double* h0, const double* v0, const double* dlast_h,
+                         const double* dlast_v, double beta, double alpha, int64_t Bt, int64_t L,
+                         int64_t D, int64_t N, double* dx, double* ddelta, double* dA,
+                         double* dB, double* dC, double* dDskip, double* dz,
+                         double* ddelta_bias, double* dh0, double* dv0, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  if ((z && !dz) || (delta_bias && !ddelta_bias)) return 1;
+  const size_t nxd = (size_t)(Bt * L * D);
+  double* de = (double*)malloc(sizeof(double) * nxd + 1);
+  double* ge = (double*)malloc(sizeof(double) * nxd + 1);
+  double* yr = (double*)malloc(sizeof(double) * nxd + 1);
+  if (!de || !ge || !yr) { free(de); free(ge); free(yr); return 2; }
+  effective_delta(delta, delta_bias, delta_softplus, Bt, L, D, de);
+  int rc = 0;
+  if (z) {
+    /* the gate's backward needs the output before the gate */
+    rc = msm_oracle_fwd(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, NULL, NULL,
+                        nthreads);
+    for (size_t i = 0; rc == 0 && i < nxd; ++i) {
+      ge[i] = dy[i] * silu(z[i]);
+      dz[i] = dy[i] * yr[i] * silu_grad(z[i]);
+    }
+  } else {
+    memcpy(ge, dy, sizeof(double) * nxd);
+  }
+  if (rc == 0)
+    rc = msm_oracle_bwd(x, de, A, B, C, Dskip, ge, h0, v0, dlast_h, dlast_v, beta, alpha, Bt, L,
+                        D, N, dx, ddelta, dA, dB, dC, dDskip, dh0, dv0, nthreads);
+  if (rc == 0) {
+    if (delta_softplus)
+      for (size_t i = 0; i < nxd; ++i)
+        ddelta[i] *= logistic(delta[i] + (delta_bias ? delta_bias[i % D] : 0.0));
+    if (delta_bias) {
+      for (int64_t d = 0; d < D; ++d) ddelta_bias[d] = 0.0;
+      for (int64_t b = 0; b < Bt; ++b)
+        for (int64_t t = 0; t < L; ++t)
+          for (int64_t d = 0; d < D; ++d) ddelta_bias[d] += ddelta[(b * L + t) * D + d];
+    }
+  }
+  free(de);
+  free(ge);
+  free(yr);
+  return rc;
 }

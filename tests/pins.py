@@ -16,6 +16,7 @@ import os
 
 import numpy as np
 import scipy.signal
+import scipy.special
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -503,8 +504,108 @@ def pin_bwd_continuation(orc):
     close(g1["dv0"], g["dv0"], rtol=1e-10, atol=1e-12, what="split dv0")
 
 
+
+# ---------------------------------------------------------------------------------------------
+# The fused op: delta bias + softplus before the scan, the SiLU gate after it (the README's
+# selective-scan function arguments; the gate branch of the Mamba block on the Mamba page)
+# ---------------------------------------------------------------------------------------------
+
+def pin_fused_delta_transform(orc):
+    """softplus(delta + bias) feeds the scan: a raw delta chosen as log(e^c - 1) - bias (numpy's
+    expm1 / log) must give the plain scan run on c; without softplus, delta = c - bias must.
+    The targets include large values (the overflow-free branch of softplus) and ln 2 = softplus(0)."""
+    rng = np.random.default_rng(41)
+    Bt, L, D, N = 2, 9, 4, 3
+    x, dstar, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    dstar[0, 0, 0] = 30.0                       # softplus far in its linear regime
+    dstar[1, 2, 1] = math.log(2.0)              # softplus(0)
+    bias = rng.standard_normal(D)
+    beta, alpha = 0.8, 0.9
+    want, wlh, wlv = orc.fwd(x, dstar, A, B, C, beta, alpha, Dskip=Ds)
+    raw = np.log(np.expm1(dstar)) - bias
+    raw[1, 2, 1] = -bias[1]                     # exactly zero after the bias
+    y, y_raw, lh, lv = orc.fused_fwd(x, raw, A, B, C, beta, alpha, Dskip=Ds, delta_bias=bias,
+                                     delta_softplus=True)
+    close(y, want, rtol=1e-9, atol=1e-12, what="softplus(delta + bias)")
+    close(y_raw, want, rtol=1e-9, atol=1e-12, what="ungated output")
+    close(lh, wlh, rtol=1e-9, atol=1e-12, what="softplus last h")
+    y, _, lh, _ = orc.fused_fwd(x, dstar - bias, A, B, C, beta, alpha, Dskip=Ds,
+                                delta_bias=bias, delta_softplus=False)
+    close(y, want, rtol=1e-12, atol=1e-12, what="delta + bias")
+    y, _, _, _ = orc.fused_fwd(x, dstar, A, B, C, beta, alpha, Dskip=Ds)
+    close(y, want, rtol=0, atol=0, what="no extras")
+
+
+def pin_fused_gate(orc):
+    """y = y_raw * z * logistic(z) (scipy.special.expit), the skip term included in y_raw;
+    z = 0 closes the gate."""
+    rng = np.random.default_rng(43)
+    Bt, L, D, N = 2, 8, 3, 2
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    z = 3.0 * rng.standard_normal((Bt, L, D))
+    z[0, 1, :] = 0.0
+    z[1, 3, 0] = 40.0
+    z[1, 4, 1] = -40.0
+    beta, alpha = 0.9, 0.5
+    want_raw, _, _ = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds)
+    y, y_raw, _, _ = orc.fused_fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds, z=z)
+    close(y_raw, want_raw, rtol=0, atol=0, what="gate: output before the gate")
+    close(y, want_raw * z * scipy.special.expit(z), rtol=1e-13, atol=1e-300, what="gated output")
+    assert np.all(y[0, 1, :] == 0.0), "z = 0 must close the gate"
+
+
+def _fused_loss(orc, p, dy, dlh, dlv, beta, alpha, softplus):
+    y, _, lh, lv = orc.fused_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], beta, alpha,
+                                 Dskip=p["Dskip"], z=p["z"], delta_bias=p["bias"],
+                                 delta_softplus=softplus, h0=p["h0"], v0=p["v0"])
+    return float(np.sum(dy * y) + np.sum(dlh * lh) + np.sum(dlv * lv))
+
+
+def pin_fused_finite_differences(orc):
+    """Central differences of the fused op's loss for every input: raw delta, its bias, the gate
+    z, the scan's inputs and the initial state; with and without softplus."""
+    rng = np.random.default_rng(47)
+    Bt, L, D, N = 2, 5, 3, 2
+    beta, alpha = 0.75, 0.8
+    for softplus, with_z in [(True, True), (False, True), (True, False)]:
+        x, _, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+        raw = rng.normal(-2.0, 1.0, size=(Bt, L, D)) if softplus else \
+            np.exp(rng.uniform(np.log(1e-2), np.log(0.5), size=(Bt, L, D)))
+        bias = 0.3 * rng.standard_normal(D)
+        z = 2.0 * rng.standard_normal((Bt, L, D)) if with_z else None
+        h0, v0 = _rand_state(rng, Bt, D, N)
+        dy = rng.standard_normal((Bt, L, D))
+        dlh, dlv = _rand_state(rng, Bt, D, N)
+        p = dict(x=x, delta=raw, A=A, B=B, C=C, Dskip=Ds, z=z, bias=bias, h0=h0, v0=v0)
+        g = orc.fused_bwd(x, raw, A, B, C, dy, beta, alpha, Dskip=Ds, z=z, delta_bias=bias,
+                          delta_softplus=softplus, h0=h0, v0=v0, dlast_h=dlh, dlast_v=dlv)
+        eps = 1e-6
+        names = [("x", "dx"), ("delta", "ddelta"), ("bias", "ddelta_bias"), ("A", "dA"),
+                 ("B", "dB"), ("C", "dC"), ("Dskip", "dDskip"), ("h0", "dh0"), ("v0", "dv0")]
+        if with_z:
+            names.append(("z", "dz"))
+        else:
+            assert g["dz"] is None
+        for pname, gname in names:
+            arr = p[pname]
+            for i in np.ndindex(arr.shape):
+                orig = arr[i]
+                arr[i] = orig + eps
+                lp = _fused_loss(orc, p, dy, dlh, dlv, beta, alpha, softplus)
+                arr[i] = orig - eps
+                lm = _fused_loss(orc, p, dy, dlh, dlv, beta, alpha, softplus)
+                arr[i] = orig
+                fd = (lp - lm) / (2 * eps)
+                an = g[gname][i]
+                if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                    raise AssertionError("fused finite difference mismatch for %s%s "
+                                         "(softplus=%s): fd %.9g analytic %.9g"
+                                         % (gname, i, softplus, fd, an))
+
+
 ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
             pin_beta0_equivalence, pin_structure, pin_finite_differences,
             pin_scaling_identities, pin_bwd_beta0_alpha0, pin_initial_state_filter,
-            pin_continuation, pin_state_finite_differences, pin_bwd_continuation]
+            pin_continuation, pin_state_finite_differences, pin_bwd_continuation,
+            pin_fused_delta_transform, pin_fused_gate, pin_fused_finite_differences]

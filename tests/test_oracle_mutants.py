@@ -48,6 +48,22 @@ MUTANTS = [
     ("bwd_drops_terminal_h", "gv_next = 0.0, a_next = 1.0;", "gv_next = 0.0, a_next = 0.0;", 0),
     ("bwd_dh0_drops_a", "dh0[s_i] = L > 0 ? a_next * gh_next", "dh0[s_i] = L > 0 ? gh_next", 0),
     ("bwd_dv0_drops_beta", "dv0[s_i] = L > 0 ? beta * gv_next", "dv0[s_i] = L > 0 ? gv_next", 0),
+    # the fused op's extras
+    ("fused_softplus_without_bias", "out[i] = delta_softplus ? softplus(u) : u;",
+     "out[i] = delta_softplus ? softplus(delta[i]) + (u - delta[i]) : u;", 0),
+    ("softplus_drops_linear_part", "return u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));",
+     "return u > 0.0 ? log1p(exp(-u)) : log1p(exp(u));", 0),
+    ("fused_gate_is_logistic", "y[i] = z ? yr[i] * silu(z[i]) : yr[i];",
+     "y[i] = z ? yr[i] * logistic(z[i]) : yr[i];", 0),
+    ("fused_dy_not_gated", "ge[i] = dy[i] * silu(z[i]);", "ge[i] = dy[i];", 0),
+    ("fused_dz_logistic_grad", "dz[i] = dy[i] * yr[i] * silu_grad(z[i]);",
+     "dz[i] = dy[i] * yr[i] * logistic(z[i]);", 0),
+    ("silu_grad_sign", "return s * (1.0 + z * (1.0 - s));", "return s * (1.0 + z * s);", 0),
+    ("fused_ddelta_chain_drops_bias",
+     "ddelta[i] *= logistic(delta[i] + (delta_bias ? delta_bias[i % D] : 0.0));",
+     "ddelta[i] *= logistic(delta[i]);", 0),
+    ("fused_dbias_first_row", "for (int64_t b = 0; b < Bt; ++b)\n        for (int64_t t = 0; t < L; ++t)",
+     "for (int64_t b = 0; b < 1; ++b)\n        for (int64_t t = 0; t < L; ++t)", 0),
 ]
 
 
