@@ -154,6 +154,45 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
                               void* workspace, size_t workspace_bytes, void* stream,
                               const msm_plan* plan);
 
+/* The full selective-scan operation: the function of the Momentum Mamba README ("Low-Level
+ * Functions": u, delta, A, B, C, D, z, delta_bias, delta_softplus, beta, alpha, with last
+ * states) plus the initial state of msm_scan_fwd_state.  Read as in the Mamba block of
+ * "Where the state computation sits in a Mamba block":
+ *     delta_eff[b,t,d] = softplus(delta[b,t,d] + delta_bias[d])   when delta_softplus == 1
+ *                      = delta[b,t,d] + delta_bias[d]             when delta_softplus == 0
+ *     (softplus(u) = log(1 + e^u); a NULL delta_bias is zero),
+ *     the scan of msm_scan_fwd_state runs on delta_eff, giving y_raw (skip term included),
+ *     y = y_raw * silu(z)  with silu(z) = z / (1 + e^-z), when z (Bt, L, D, io dtype) is given.
+ * delta_bias is (D,) fp32.  delta_softplus must be 0 or 1.  With z, delta_bias NULL and
+ * delta_softplus 0 this is msm_scan_fwd_state.  The bias, softplus and gate are applied inside
+ * the scan kernels (no extra pass over memory).  Everything else as msm_scan_fwd_state; z and
+ * delta_bias are inputs and must not overlap an output. */
+msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, const void* z,
+                                  const float* delta_bias, int32_t delta_softplus,
+                                  const float* h0, const float* v0, void* y, float* last_h,
+                                  float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                  float beta, float alpha, msm_dtype io, void* workspace,
+                                  size_t workspace_bytes, void* stream, const msm_plan* plan);
+
+/* Backward of msm_selective_scan_fwd for the loss of msm_scan_bwd_state.  ddelta is the
+ * gradient of the raw delta (through the bias and softplus); dz (Bt, L, D, io dtype) is
+ * required exactly when z is given and ddelta_bias ((D,) fp32, summed over batch and time)
+ * exactly when delta_bias is given.  The output before the gate, which dz needs, is recomputed
+ * inside: nothing from the forward is saved.  With z, delta_bias NULL and delta_softplus 0
+ * this is msm_scan_bwd_state.  The fused variant (any of z, delta_bias, delta_softplus) is
+ * built for N <= 16; for larger N it returns MSM_ERR_UNSUPPORTED. */
+msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, const void* z,
+                                  const float* delta_bias, int32_t delta_softplus, const void* dy,
+                                  const float* h0, const float* v0, const float* dlast_h,
+                                  const float* dlast_v, void* dx, void* ddelta, float* dA,
+                                  void* dB, void* dC, float* dDskip, void* dz,
+                                  float* ddelta_bias, float* dh0, float* dv0, int64_t Bt,
+                                  int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                                  msm_dtype io, void* workspace, size_t workspace_bytes,
+                                  void* stream, const msm_plan* plan);
+
 #ifdef __cplusplus
 }
 #endif

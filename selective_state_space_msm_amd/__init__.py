@@ -9,6 +9,11 @@ fallback implementation.
     y = msm_scan_fwd(x, delta, A, B, C, beta=0.9, alpha=1.0)             # (Bt, L, D)
     y, last_h, last_v = msm_scan_fwd(..., return_last_state=True)
     grads = msm_scan_bwd(x, delta, A, B, C, dy, beta=0.9, alpha=1.0)     # dict of tensors
+    # the full operation: delta bias + softplus, SiLU output gate, initial state
+    y = msm_selective_scan_fwd(x, delta, A, B, C, 0.9, 1.0, Dskip, z=z, delta_bias=bias,
+                               delta_softplus=True)
+    grads = msm_selective_scan_bwd(x, delta, A, B, C, dy, 0.9, 1.0, Dskip, z=z, delta_bias=bias,
+                                   delta_softplus=True)        # also dz, ddelta_bias
 """
 from __future__ import annotations
 
@@ -19,7 +24,7 @@ __all__ = [
     "MsmError", "MsmLibraryMissing", "MSM_F32", "MSM_BF16", "library_path", "load_library",
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
-    "msm_scan_bwd", "EXPORTED_SYMBOLS",
+    "msm_scan_bwd", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "EXPORTED_SYMBOLS",
 ]
 
 MSM_F32 = 0
@@ -30,7 +35,7 @@ EXPORTED_SYMBOLS = [
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
     "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan", "msm_scan_fwd_state",
-    "msm_scan_bwd_state",
+    "msm_scan_bwd_state", "msm_selective_scan_fwd", "msm_selective_scan_bwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +103,11 @@ def load_library():
     lib.msm_scan_bwd_state.argtypes = ([P] * 19 + [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P,
                                                    ctypes.POINTER(_Plan)])
     lib.msm_scan_bwd_state.restype = ctypes.c_int
+    tail = [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P, ctypes.POINTER(_Plan)]
+    lib.msm_selective_scan_fwd.argtypes = [P] * 8 + [I32] + [P] * 5 + tail
+    lib.msm_selective_scan_fwd.restype = ctypes.c_int
+    lib.msm_selective_scan_bwd.argtypes = [P] * 8 + [I32] + [P] * 15 + tail
+    lib.msm_selective_scan_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -299,4 +309,111 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
         st = lib.msm_scan_bwd_with_plan(*ins, *grads, *tail, _plan_arg(plan))
     if st != 0:
         raise MsmError(st, "msm_scan_bwd")
+    return o
+
+
+def _check_extras(x, z, delta_bias, dev):
+    import torch
+    Bt, L, D = x.shape
+    if z is not None:
+        _check(z, "z", (Bt, L, D), x.dtype, dev)
+    if delta_bias is not None:
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+
+
+def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None,
+                           delta_bias=None, delta_softplus=False, h0=None, v0=None, y=None,
+                           last_h=None, last_v=None, return_last_state=False, workspace=None,
+                           stream=None, plan=None):
+    """The full forward (msm_selective_scan_fwd): the scan on softplus(delta + delta_bias) (or
+    delta + delta_bias), output times silu(z).  z: (Bt, L, D) in the I/O dtype; delta_bias:
+    (D,) fp32; other arguments as msm_scan_fwd.  Returns y, or (y, last_h, last_v)."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for t, nm, shp in ((x, "x", (Bt, L, D)), (delta, "delta", (Bt, L, D)), (B, "B", (Bt, L, N)),
+                       (C, "C", (Bt, L, N))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    _check_extras(x, z, delta_bias, dev)
+    if y is None:
+        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+    _check(y, "y", (Bt, L, D), x.dtype, dev)
+    if return_last_state:
+        if last_h is None:
+            last_h = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+        if last_v is None:
+            last_v = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+    for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N), torch.float32, dev)
+    nbytes = int(lib.msm_scan_fwd_workspace_bytes(Bt, L, D, N, io))
+    ws, wsb = _workspace(nbytes, workspace, dev)
+    st = lib.msm_selective_scan_fwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(h0), _ptr(v0), _ptr(y), _ptr(last_h), _ptr(last_v), Bt,
+        L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
+        _plan_arg(plan))
+    if st != 0:
+        raise MsmError(st, "msm_selective_scan_fwd")
+    if return_last_state:
+        return y, last_h, last_v
+    return y
+
+
+def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=None,
+                           delta_bias=None, delta_softplus=False, h0=None, v0=None, dlast_h=None,
+                           dlast_v=None, state_grads=False, out=None, workspace=None,
+                           stream=None, plan=None):
+    """Gradients of the full operation (msm_selective_scan_bwd).  Returns the dict of
+    msm_scan_bwd, where ddelta is the gradient of the raw delta, plus dz (I/O dtype, None
+    without z), ddelta_bias (fp32 (D,), None without delta_bias) and, with state_grads, dh0 and
+    dv0."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for t, nm, shp in ((x, "x", (Bt, L, D)), (delta, "delta", (Bt, L, D)), (B, "B", (Bt, L, N)),
+                       (C, "C", (Bt, L, N)), (dy, "dy", (Bt, L, D))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    _check_extras(x, z, delta_bias, dev)
+    states = (h0, v0, dlast_h, dlast_v)
+    for t, nm in zip(states, ("h0", "v0", "dlast_h", "dlast_v")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N), torch.float32, dev)
+    o = dict(out or {})
+    for k, shp, dt in (("dx", (Bt, L, D), x.dtype), ("ddelta", (Bt, L, D), x.dtype),
+                       ("dA", (D, N), torch.float32), ("dB", (Bt, L, N), x.dtype),
+                       ("dC", (Bt, L, N), x.dtype)):
+        o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+    for k, given, shp, dt in (("dDskip", Dskip, (D,), torch.float32), ("dz", z, (Bt, L, D), x.dtype),
+                              ("ddelta_bias", delta_bias, (D,), torch.float32)):
+        if given is not None:
+            o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+        else:
+            o[k] = None
+    if state_grads:
+        o.setdefault("dh0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
+        o.setdefault("dv0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
+    nbytes = int(lib.msm_scan_bwd_workspace_bytes(Bt, L, D, N, io))
+    ws, wsb = _workspace(nbytes, workspace, dev)
+    st = lib.msm_selective_scan_bwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(dy), *(_ptr(t) for t in states), _ptr(o["dx"]),
+        _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]),
+        _ptr(o["dz"]), _ptr(o["ddelta_bias"]), _ptr(o.get("dh0")), _ptr(o.get("dv0")), Bt, L, D,
+        N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
+        _plan_arg(plan))
+    if st != 0:
+        raise MsmError(st, "msm_selective_scan_bwd")
     return o

@@ -14,7 +14,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsm.so")
-SOURCES = ["msm_api.cpp", "msm_fwd.hip", "msm_bwd.hip", "msm_bwd_wide.hip"]
+# (source, extra flags): the recurrence kernels are built once per (bf16 I/O, fused variant)
+# pair, all in parallel
+_PARTS = [("-DMSM_IO_BF16=%d" % io, "-DMSM_EXT=%d" % ext) for io in (0, 1) for ext in (0, 1)]
+SOURCES = ([("msm_api.cpp", ()), ("msm_launch.hip", ()), ("msm_bwd_wide.hip", ())]
+           + [("msm_fwd.hip", f) for f in _PARTS] + [("msm_bwd.hip", f) for f in _PARTS])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -24,9 +28,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Xclang", "-t
           "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> tuple[subprocess.Popen, str]:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, flags) -> tuple[subprocess.Popen, str]:
+    tag = "".join(f.split("=")[-1] for f in flags)
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (("." + tag) if tag else "") + ".o")
+    cmd = [HIPCC, *COMMON, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True), obj
 
 
@@ -34,14 +39,14 @@ def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libmsm.so.  Always recompiles."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     t0 = time.time()
-    procs = [_compile(s) for s in SOURCES]
+    procs = [_compile(src, flags) for src, flags in SOURCES]
     objs, failed = [], []
-    for (proc, obj), src in zip(procs, SOURCES):
+    for (proc, obj), (src, flags) in zip(procs, SOURCES):
         out, _ = proc.communicate()
         # the host pass does not know the packed-fp32 target feature; that warning is harmless
         lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l]
         if proc.returncode != 0:
-            failed.append((src, "\n".join(lines)))
+            failed.append((src + " " + " ".join(flags), "\n".join(lines)))
         elif verbose and lines:
             print("\n".join(lines))
         objs.append(obj)

@@ -139,7 +139,7 @@ msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
 }
 
 struct BwdLayout {
-  size_t off_ckpt, off_dbc, off_dA, off_dD, total;
+  size_t off_ckpt, off_dbc, off_dA, off_dD, off_dbias, total;
 };
 
 BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
@@ -152,7 +152,8 @@ BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   l.off_dbc = align_up(sizeof(float) * (size_t)(Bt * NT * 2 * N * D));
   l.off_dA = l.off_dbc + align_up(sizeof(float) * (size_t)(Bt * ncb * L * 2 * NP));
   l.off_dD = l.off_dA + align_up(sizeof(float) * (size_t)(Bt * N * D));
-  l.total = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.off_dbias = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.total = l.off_dbias + align_up(sizeof(float) * (size_t)(Bt * D));
   return l;
 }
 
@@ -223,15 +224,18 @@ msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dt
   return MSM_OK;
 }
 
-msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, const void* B,
-                              const void* C, const float* Dskip, const float* h0,
-                              const float* v0, void* y, float* last_h, float* last_v, int64_t Bt,
-                              int64_t L, int64_t D, int64_t N, float beta, float alpha,
-                              msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
-                              const msm_plan* plan) {
+msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, const void* z,
+                                  const float* delta_bias, int32_t delta_softplus,
+                                  const float* h0, const float* v0, void* y, float* last_h,
+                                  float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                  float beta, float alpha, msm_dtype io, void* workspace,
+                                  size_t workspace_bytes, void* stream, const msm_plan* plan) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
+  if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
+  const bool ext = z != nullptr || delta_bias != nullptr || delta_softplus != 0;
 
   msm_plan pl = auto_fwd_plan(Bt, L, D, N);
   const int NP = padded_states(N);
@@ -254,10 +258,11 @@ msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, 
   const Range ins[] = {rng(x, nxd * es),        rng(delta, nxd * es),
                        rng(A, (size_t)(D * N) * 4), rng(B, nbc * es),
                        rng(C, nbc * es),        rng(Dskip, Dskip ? (size_t)D * 4 : 0),
-                       rng(h0, h0 ? nst : 0),   rng(v0, v0 ? nst : 0)};
+                       rng(h0, h0 ? nst : 0),   rng(v0, v0 ? nst : 0),
+                       rng(z, z ? nxd * es : 0), rng(delta_bias, delta_bias ? (size_t)D * 4 : 0)};
   const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? nst : 0),
                         rng(last_v, last_v ? nst : 0), rng(workspace, lay.total)};
-  if (any_overlap(outs, 4, ins, 8)) return MSM_ERR_INVALID_ARG;
+  if (any_overlap(outs, 4, ins, 10)) return MSM_ERR_INVALID_ARG;
 
   // chunk length: a multiple of the tile, so only the final chunk can end mid-tile.  The
   // kernels address a chunk with 32-bit byte offsets: keep every chunk of every (Bt,L,D)
@@ -280,6 +285,9 @@ msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, 
   a.y = y;
   a.last_h = last_h;
   a.last_v = last_v;
+  a.z = z;
+  a.delta_bias = delta_bias;
+  a.delta_softplus = delta_softplus;
   char* ws = static_cast<char*>(workspace);
   a.s_bv = G > 1 ? reinterpret_cast<float*>(ws + lay.off_bv) : nullptr;
   a.s_bh = G > 1 ? reinterpret_cast<float*>(ws + lay.off_bh) : nullptr;
@@ -296,9 +304,20 @@ msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, 
   a.alpha = alpha;
   a.beta_pow_tc = (float)pow((double)beta, (double)Tc);
 
-  hipError_t e = msm::launch_fwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f,
+  hipError_t e = msm::launch_fwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f, ext,
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const float* h0,
+                              const float* v0, void* y, float* last_h, float* last_v, int64_t Bt,
+                              int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                              msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan) {
+  return msm_selective_scan_fwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, h0, v0, y, last_h,
+                                last_v, Bt, L, D, N, beta, alpha, io, workspace, workspace_bytes,
+                                stream, plan);
 }
 
 msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
@@ -320,19 +339,25 @@ msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const 
                                 alpha, io, workspace, workspace_bytes, stream, nullptr);
 }
 
-msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, const void* B,
-                              const void* C, const float* Dskip, const void* dy, const float* h0,
-                              const float* v0, const float* dlast_h, const float* dlast_v,
-                              void* dx, void* ddelta, float* dA, void* dB, void* dC,
-                              float* dDskip, float* dh0, float* dv0, int64_t Bt, int64_t L,
-                              int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
-                              void* workspace, size_t workspace_bytes, void* stream,
-                              const msm_plan* plan) {
+msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, const void* z,
+                                  const float* delta_bias, int32_t delta_softplus, const void* dy,
+                                  const float* h0, const float* v0, const float* dlast_h,
+                                  const float* dlast_v, void* dx, void* ddelta, float* dA,
+                                  void* dB, void* dC, float* dDskip, void* dz,
+                                  float* ddelta_bias, float* dh0, float* dv0, int64_t Bt,
+                                  int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                                  msm_dtype io, void* workspace, size_t workspace_bytes,
+                                  void* stream, const msm_plan* plan) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC)
     return MSM_ERR_INVALID_ARG;
   if ((Dskip != nullptr) != (dDskip != nullptr)) return MSM_ERR_INVALID_ARG;
+  if ((z != nullptr) != (dz != nullptr)) return MSM_ERR_INVALID_ARG;
+  if ((delta_bias != nullptr) != (ddelta_bias != nullptr)) return MSM_ERR_INVALID_ARG;
+  if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
+  const bool ext = z != nullptr || delta_bias != nullptr || delta_softplus != 0;
 
   msm_plan pl = auto_bwd_plan(Bt, L, D, N);
   const int NP = padded_states(N);
@@ -343,6 +368,8 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
     }
     if (plan->chunks != 0 && plan->chunks != 1) return MSM_ERR_UNSUPPORTED;
   }
+  // the fused variant of the 64-state backward is not built
+  if (ext && NP == 64) return MSM_ERR_UNSUPPORTED;
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
@@ -359,13 +386,17 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
                        rng(h0, h0 ? nst : 0),
                        rng(v0, v0 ? nst : 0),
                        rng(dlast_h, dlast_h ? nst : 0),
-                       rng(dlast_v, dlast_v ? nst : 0)};
+                       rng(dlast_v, dlast_v ? nst : 0),
+                       rng(z, z ? nxd * es : 0),
+                       rng(delta_bias, delta_bias ? (size_t)D * 4 : 0)};
   const Range outs[] = {rng(dx, nxd * es),           rng(ddelta, nxd * es),
                         rng(dA, (size_t)(D * N) * 4), rng(dB, nbc * es),
                         rng(dC, nbc * es),           rng(dDskip, dDskip ? (size_t)D * 4 : 0),
                         rng(dh0, dh0 ? nst : 0),     rng(dv0, dv0 ? nst : 0),
+                        rng(dz, dz ? nxd * es : 0),
+                        rng(ddelta_bias, ddelta_bias ? (size_t)D * 4 : 0),
                         rng(workspace, lay.total)};
-  if (any_overlap(outs, 9, ins, 11)) return MSM_ERR_INVALID_ARG;
+  if (any_overlap(outs, 11, ins, 13)) return MSM_ERR_INVALID_ARG;
 
   msm::BwdArgs a{};
   a.x = x;
@@ -387,11 +418,17 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
   a.dB = dB;
   a.dC = dC;
   a.dDskip = dDskip;
+  a.z = z;
+  a.delta_bias = delta_bias;
+  a.delta_softplus = delta_softplus;
+  a.dz = dz;
+  a.ddelta_bias = ddelta_bias;
   char* ws = static_cast<char*>(workspace);
   a.ckpt = reinterpret_cast<float*>(ws + lay.off_ckpt);
   a.dbc_part = reinterpret_cast<float*>(ws + lay.off_dbc);
   a.dA_part = reinterpret_cast<float*>(ws + lay.off_dA);
   a.dD_part = reinterpret_cast<float*>(ws + lay.off_dD);
+  a.dbias_part = reinterpret_cast<float*>(ws + lay.off_dbias);
   a.Bt = Bt;
   a.L = L;
   a.D = D;
@@ -401,9 +438,23 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
   a.NP = NP;
   a.beta = beta;
   a.alpha = alpha;
-  hipError_t e = msm::launch_bwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f,
+  hipError_t e = msm::launch_bwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f, ext,
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, const void* B,
+                              const void* C, const float* Dskip, const void* dy, const float* h0,
+                              const float* v0, const float* dlast_h, const float* dlast_v,
+                              void* dx, void* ddelta, float* dA, void* dB, void* dC,
+                              float* dDskip, float* dh0, float* dv0, int64_t Bt, int64_t L,
+                              int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const msm_plan* plan) {
+  return msm_selective_scan_bwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, dy, h0, v0,
+                                dlast_h, dlast_v, dx, ddelta, dA, dB, dC, dDskip, nullptr,
+                                nullptr, dh0, dv0, Bt, L, D, N, beta, alpha, io, workspace,
+                                workspace_bytes, stream, plan);
 }
 
 msm_status msm_scan_bwd_with_plan(const void* x, const void* delta, const float* A,

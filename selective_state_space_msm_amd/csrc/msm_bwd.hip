@@ -26,6 +26,13 @@
 //     across the S wavefronts through LDS;
 //   over d for dB / dC: across the 32 lanes of a half with a reduce-scatter (v_permlane16_swap
 //     then DPP), then across channel blocks in a small finalize kernel.
+// The fused variant (EXT) differentiates the selective-scan function's extras of the Momentum
+// Mamba README ("Low-Level Functions": z, delta_bias, delta_softplus) inside the same sweep:
+// delta_eff is re-formed where delta is staged; dy is gated (dy silu(z)) there too, and
+// dy silu'(z) and softplus' = logistic(delta + bias) are kept beside it in LDS; the output
+// before the gate, needed for dz, is re-formed from the recomputed states (C . h + Dskip x,
+// reduced across the state groups like dx); dz and the raw-delta gradient are finished with
+// dx / ddelta, and the bias gradient is summed per channel.
 // This kernel serves 4 and 16 padded states; 64 padded states use the full-wavefront
 // backward in msm_bwd_wide.hip.
 #include <type_traits>
@@ -90,7 +97,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return make_rsrc(static_cast<const char*>(base) + off, total - off);
 }
 
-template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP>
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, bool EXT>
 __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
@@ -110,6 +117,11 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   __shared__ float bs[2][TB][GS][K];        // alpha B
   __shared__ double cs64[2][TB][GS][K];     // C, widened for the adjoint recurrence
   __shared__ float spart[2][S][TB][kWave];  // per wavefront: dx (lanes < 32) | ddelta partials
+  // fused variant: (dy silu'(z), logistic(delta + bias)) per staged element, the per-wavefront
+  // partials of the output before the gate, and the bias-gradient partials
+  __shared__ float2 xe[EXT ? 2 : 1][EXT ? TB : 1][CB];
+  __shared__ float ypt[EXT ? 2 : 1][EXT ? S : 1][EXT ? TB : 1][CB];
+  __shared__ double bred[EXT ? S : 1][CB];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -138,6 +150,15 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     v[j] = (p.v0 && dvalid && n < N) ? p.v0[si] : 0.f;
     h[j] = (p.h0 && dvalid && n < N) ? p.h0[si] : 0.f;
   }
+  // fused extras: every x / delta element a thread stages belongs to its lane's channel
+  const float dbias = (EXT && p.delta_bias) ? p.delta_bias[dl] : 0.f;
+  const bool softplus = EXT && p.delta_softplus != 0;
+  const bool has_z = EXT && p.z != nullptr;
+  auto delta_eff = [&](float dv) {
+    if (!EXT) return dv;
+    const float u = dv + dbias;
+    return softplus ? softplus_f(u) : u;
+  };
 
   // ---- staging addresses (per-tile buffer resources, constant per-thread offsets) ----
   const int64_t row_bytes = D * T::es, bc_row_bytes = N * T::es;
@@ -147,6 +168,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const char* dy0 = static_cast<const char*>(p.dy) + b * tot_d;
   const char* B0 = static_cast<const char*>(p.B) + b * tot_n;
   const char* C0 = static_cast<const char*>(p.C) + b * tot_n;
+  const char* z0 = has_z ? static_cast<const char*>(p.z) + b * tot_d : x0;
 
   // x, delta, dy of channels past D are staged as zeros (their offset is past every extent),
   // so those lanes carry zero gradients without further masking
@@ -160,7 +182,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     const int dch = cb * CB + ic % CB;
     x_voff[r] = dch < D ? (uint32_t)((ic / CB) * row_bytes + dch * T::es) : 0x80000000u;
   }
-  raw xr[NX], dr[NX], gr[NX];
+  raw xr[NX], dr[NX], gr[NX], zr[EXT ? NX : 1];
   auto x_load = [&](int64_t ts, bool with_dy) {
     const auto rx = rows_rsrc(x0, ts, row_bytes, tot_d);
     const auto rd = rows_rsrc(dl0, ts, row_bytes, tot_d);
@@ -174,14 +196,32 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
       for (int r = 0; r < NX; ++r) gr[r] = T::bload(rg, x_voff[r], 0u);
     }
+    if (EXT) {
+      // without a gate the loads read zeros through an empty resource
+      const auto rz = has_z ? rows_rsrc(z0, ts, row_bytes, tot_d) : make_rsrc(x0, 0);
+#pragma unroll
+      for (int r = 0; r < NX; ++r) zr[r] = T::bload(rz, x_voff[r], 0u);
+    }
   };
   auto x_store = [&](int buf, bool with_dy) {
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       const int i = tid + r * NTHR;
       if (NX * NTHR == XE || i < XE) {
-        const float xv = T::widen(xr[r]), dv = T::widen(dr[r]);
-        xs[buf][i / CB][i % CB] = make_float4(xv, dv, with_dy ? T::widen(gr[r]) : 0.f, dv * xv);
+        const float xv = T::widen(xr[r]), draw = T::widen(dr[r]);
+        const float dv = delta_eff(draw);
+        float gy = with_dy ? T::widen(gr[r]) : 0.f;
+        if (EXT) {
+          const float dsp = softplus ? logistic_f(draw + dbias).s : 1.f;
+          float gz = 0.f;
+          if (has_z) {
+            const float zv = T::widen(zr[r]);
+            gz = gy * silu_grad_f(zv);
+            gy *= silu_f(zv);
+          }
+          xe[EXT ? buf : 0][EXT ? i / CB : 0][i % CB] = make_float2(gz, dsp);
+        }
+        xs[buf][i / CB][i % CB] = make_float4(xv, dv, gy, dv * xv);
       }
     }
   };
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
       for (int r = 0; r < NX; ++r) {
         const int i = tid + r * NTHR;
         if (NX * NTHR == XE || i < XE) {
-          const float xv = T::widen(st.x[r]), dv = T::widen(st.d[r]);
+          const float xv = T::widen(st.x[r]), dv = delta_eff(T::widen(st.d[r]));
           xs[buf][i / CB][i % CB] = make_float4(xv, dv, 0.f, dv * xv);
         }
       }
@@ -336,6 +376,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     dA64[j] = 0.0;
   }
   double dD64 = 0.0;
+  double dbias64 = 0.0;  // fused variant: this lane's rows of the bias gradient (lanes >= 32)
   const float dsk = (HAS_DSKIP && gs == 0) ? p.Dskip[dl] : 0.f;
   const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
   char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
@@ -350,11 +391,16 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   // compiler loop over the distinct descriptors.)
   const uint32_t vo_dx = (dvalid && lane < CB) ? lane_off : 0x80000000u;
   const uint32_t vo_dd = (dvalid && lane >= CB) ? lane_off : 0x80000000u;
-  auto finalize = [&](int64_t tile, int pb, bool valid) {
+  // fused variant: dz of the row comes from lanes 0-31 as well
+  char* dz0 = (EXT && p.dz) ? static_cast<char*>(p.dz) + b * tot_d : dx0;
+  const uint32_t vo_dz = (dvalid && lane < CB) ? lane_off : 0x80000000u;
+  // xb: the LDS staging buffer that still holds the tile's inputs
+  auto finalize = [&](int64_t tile, int pb, bool valid, int xb) {
     const int64_t ts = tile * TB;
     // an invalid tile gets empty resources: every store below is then dropped
     const auto rdx = valid ? rows_rsrc(dx0, ts, row_bytes, tot_d) : make_rsrc(dx0, 0);
     const auto rdd = valid ? rows_rsrc(ddl0, ts, row_bytes, tot_d) : make_rsrc(ddl0, 0);
+    const auto rdz = (valid && has_z) ? rows_rsrc(dz0, ts, row_bytes, tot_d) : make_rsrc(dz0, 0);
 #pragma unroll
     for (int tr0 = 0; tr0 < TB; tr0 += S) {
       const int tt = tr0 + g;
@@ -365,7 +411,20 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         // rows past the end of the sequence are past the extent: dropped
         const uint32_t ro = (uint32_t)(tt * row_bytes);
         T::bstore(rdx, vo_dx + ro, 0u, (float)q);
-        T::bstore(rdd, vo_dd + ro, 0u, (float)q);
+        if (EXT) {
+          // lanes 32-63: the gradient of the raw delta (through softplus); lanes 0-31: dz from
+          // the output before the gate, summed over the S wavefronts in a fixed order
+          const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
+          const double qd = q * (double)e.y;
+          if (valid) dbias64 += qd;
+          T::bstore(rdd, vo_dd + ro, 0u, (float)qd);
+          float yr = ypt[EXT ? pb : 0][0][EXT ? tt : 0][ch];
+#pragma unroll
+          for (int w = 1; w < S; ++w) yr += ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
+          T::bstore(rdz, vo_dz + ro, 0u, e.x * yr);
+        } else {
+          T::bstore(rdd, vo_dd + ro, 0u, (float)q);
+        }
       }
     }
   };
@@ -420,7 +479,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     bc_load(tp * TB, true);
     x_load(tp * TB, true);
     // tile + 1's partials were completed before the last barrier
-    finalize(tile + 1, pb ^ 1, tile + 1 < NT && tile + 1 >= 0);
+    finalize(tile + 1, pb ^ 1, tile + 1 < NT && tile + 1 >= 0, buf ^ 1);
 
     // The sweep runs in every step (a step past tile 0 sweeps stale LDS data): its stores are
     // dropped through an empty resource and its sums are not kept.  No memory operation
@@ -454,9 +513,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         const float4 r = xs[buf][tt][ch];
         const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
         const double gy64 = gy;
-        float p1 = 0.f, p2 = 0.f;
+        float p1 = 0.f, p2 = 0.f, yq = 0.f;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
+          if (EXT) yq = fmaf((float)cs64[buf][tt][gs][j], hs[tt + 1][j], yq);
           if (FIRST && tt == nlast - 1) ghn[j] = dlh[j];
           const double gh = fma(cs64[buf][tt][gs][j], gy64, ghn[j]);
           double gv = BETA0 ? gh : fma(beta64, gvp[j], gh);
@@ -478,6 +538,13 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         }
         const float qd = fmaf(xv, p1, p2);
         spart[pb][g][tt][lane] = swap_add32(qx, qd);
+        if (EXT) {
+          // the output before the gate: this lane's states (+ the skip term on group 0), then
+          // both halves of the wavefront
+          if (HAS_DSKIP) yq = fmaf(dsk, xv, yq);
+          const float ys = swap_add32(yq, yq);
+          if (lane < CB) ypt[EXT ? pb : 0][EXT ? g : 0][EXT ? tt : 0][lane] = ys;
+        }
       }
       reduce_scatter32(vals, lane);
       // rows past the end of the sequence are past the extent: dropped
@@ -527,85 +594,58 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     }
     if (HAS_DSKIP && gs == 0) p.dD_part[b * D + d] = (float)dD64;
   }
-}
-
-// Sums the per-block partials in a fixed order and writes dB, dC (I/O dtype), dA, dDskip.
-template <typename IO>
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdArgs p) {
-  using T = io<IO>;
-  const int64_t n_bc = p.Bt * p.L * 2 * p.N;
-  const int64_t n_a = p.D * p.N;
-  const int64_t n_d = p.Dskip ? p.D : 0;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n_bc) {
-    const int64_t n = i % p.N;
-    const int64_t which = (i / p.N) % 2;
-    const int64_t bt = i / (2 * p.N);  // b * L + t
-    const int64_t b = bt / p.L, t = bt % p.L;
-    float s = 0.f;
-    for (int cb = 0; cb < p.ncb; ++cb)
-      s += p.dbc_part[((b * p.ncb + cb) * p.L + t) * 2 * p.NP + which * p.NP + n];
-    if (which == 0)
-      T::store(p.dB, bt * p.N + n, s * p.alpha);
-    else
-      T::store(p.dC, bt * p.N + n, s);
-  } else if (i < n_bc + n_a) {
-    const int64_t k = i - n_bc;  // d * N + n
-    const int64_t dd = k / p.N, n = k % p.N;
-    float s = 0.f;
-    for (int64_t b = 0; b < p.Bt; ++b) s += p.dA_part[(b * p.N + n) * p.D + dd];
-    p.dA[k] = s;
-  } else if (i < n_bc + n_a + n_d) {
-    const int64_t dd = i - n_bc - n_a;
-    float s = 0.f;
-    for (int64_t b = 0; b < p.Bt; ++b) s += p.dD_part[b * p.D + dd];
-    p.dDskip[dd] = s;
+  if (EXT && p.delta_bias) {
+    // the bias gradient of the channel: lanes 32-63 of every wavefront hold their rows' sum
+    if (lane >= CB) bred[EXT ? g : 0][ch] = dbias64;
+    __syncthreads();
+    if (g == 0 && lane < CB && dvalid) {
+      double t = bred[0][ch];
+#pragma unroll
+      for (int w = 1; w < S; ++w) t += bred[EXT ? w : 0][ch];
+      p.dbias_part[b * D + d] = (float)t;
+    }
   }
 }
 
-template <typename IO, int K, int S, bool BETA0>
+template <typename IO, int K, int S, bool BETA0, bool EXT>
 hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(S * kWave);
   if (a.Dskip)
-    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false, EXT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-template <typename IO, bool BETA0>
+template <typename IO, bool BETA0, bool EXT>
 hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
   switch (a.NP * 100 + K) {
     // S = NP / (2K) wavefronts per workgroup
-    case 401: return launch_ks<IO, 1, 2, BETA0>(a, s);
-    case 402: return launch_ks<IO, 2, 1, BETA0>(a, s);
-    case 1601: return launch_ks<IO, 1, 8, BETA0>(a, s);
-    case 1602: return launch_ks<IO, 2, 4, BETA0>(a, s);
-    case 1604: return launch_ks<IO, 4, 2, BETA0>(a, s);
+    case 401: return launch_ks<IO, 1, 2, BETA0, EXT>(a, s);
+    case 402: return launch_ks<IO, 2, 1, BETA0, EXT>(a, s);
+    case 1601: return launch_ks<IO, 1, 8, BETA0, EXT>(a, s);
+    case 1602: return launch_ks<IO, 2, 4, BETA0, EXT>(a, s);
+    case 1604: return launch_ks<IO, 4, 2, BETA0, EXT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename IO>
-hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
-  const int64_t total = a.Bt * a.L * 2 * a.N + a.D * a.N + (a.Dskip ? a.D : 0);
-  hipLaunchKernelGGL((bwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256),
-                     0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s) {
-  hipError_t e;
-  if (a.NP == 64)
-    e = launch_bwd_wide(a, io_bf16, beta0, s);
-  else if (io_bf16)
-    e = beta0 ? launch_io<bf16_storage, true>(a, K, s) : launch_io<bf16_storage, false>(a, K, s);
-  else
-    e = beta0 ? launch_io<float, true>(a, K, s) : launch_io<float, false>(a, K, s);
-  if (e != hipSuccess) return e;
-  return io_bf16 ? launch_finalize<bf16_storage>(a, s) : launch_finalize<float>(a, s);
+// This file is compiled once per (I/O dtype, variant) pair; MSM_IO_BF16 and MSM_EXT select
+// which launcher a build of it defines.
+#if !defined(MSM_IO_BF16) || !defined(MSM_EXT)
+#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1"
+#endif
+#if MSM_IO_BF16
+using PartIO = bf16_storage;
+#else
+using PartIO = float;
+#endif
+
+hipError_t MSM_BWD_PART(MSM_IO_BF16, MSM_EXT)(const BwdArgs& a, int K, bool beta0, hipStream_t s) {
+  return beta0 ? launch_io<PartIO, true, MSM_EXT != 0>(a, K, s)
+               : launch_io<PartIO, false, MSM_EXT != 0>(a, K, s);
 }
 
 }  // namespace msm

@@ -11,6 +11,42 @@ constexpr float kLog2e = 1.4426950408889634f;  // A is rescaled once so that a =
 // 2^x on the transcendental unit (v_exp_f32, half rate on gfx950).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log2(x) and 1/x on the transcendental unit (v_log_f32, v_rcp_f32; about 1 ulp each).
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e^-|u|).  log1p(e) is formed as
+// log(w) * e / (w - 1) with w = 1 + e (Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", Theorem 4): the quotient cancels the rounding of 1 + e,
+// so tiny e keep their relative accuracy; nothing overflows for any u.
+__device__ __forceinline__ float softplus_f(float u) {
+  const float e = exp2_fast(-fabsf(u) * kLog2e);
+  const float w = 1.f + e;
+  const float l1p = w == 1.f ? e : log2_fast(w) * kLn2 * (e * rcp_fast(w - 1.f));
+  return fmaxf(u, 0.f) + l1p;
+}
+
+// logistic(z) = 1 / (1 + e^-z) and 1 - logistic(z), both from e = e^-|z| <= 1 (no overflow,
+// no cancellation in the complement).
+struct Logistic {
+  float s, sc;
+};
+__device__ __forceinline__ Logistic logistic_f(float z) {
+  const float e = exp2_fast(-fabsf(z) * kLog2e);
+  const float r = rcp_fast(1.f + e);
+  const float er = e * r;
+  return z >= 0.f ? Logistic{r, er} : Logistic{er, r};
+}
+
+// SiLU gate z * logistic(z) and its derivative logistic(z) (1 + z (1 - logistic(z))).
+__device__ __forceinline__ float silu_f(float z) { return z * logistic_f(z).s; }
+__device__ __forceinline__ float silu_grad_f(float z) {
+  const Logistic l = logistic_f(z);
+  return l.s * fmaf(z, l.sc, 1.f);
+}
+
 struct bf16_storage {
   uint16_t bits;
 };

@@ -21,6 +21,12 @@
 //     its affine map from a zero start (bv, bh, q and the sum of delta), and the main pass
 //     composes the maps of the preceding chunks in its prologue to get its exact start state.
 //
+// The fused variant (EXT) adds the selective-scan function's extras of the Momentum Mamba
+// README ("Low-Level Functions": z, delta_bias, delta_softplus) at no extra pass over memory:
+// delta_eff = softplus(delta + bias[d]) (or delta + bias[d]) is formed where delta is staged,
+// once per workgroup, and the output is multiplied by silu(z) where it is stored; z is loaded
+// with x and delta and stays in registers until its tile's y is stored.
+//
 // The y reduction never needs MFMA: the scan is a per-element recurrence bound by VALU issue
 // (one v_exp_f32 plus five fp32 multiply/FMA per state update), not a dense contraction.
 #include "msm_device.hpp"
@@ -31,7 +37,7 @@ namespace {
 
 // Occupancy hint: the launch plans put one or two wavefronts on a SIMD, so the scheduler may
 // spend registers on hiding LDS and transcendental latency instead of on more wavefronts.
-template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP>
+template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, bool EXT>
 __global__ __launch_bounds__(S* kWave) __attribute__((amdgpu_waves_per_eu(1, K >= 8 ? 1 : 2)))
 void fwd_kernel(const FwdArgs p) {
   using T = io<IO>;
@@ -40,7 +46,6 @@ void fwd_kernel(const FwdArgs p) {
   constexpr int BCW = 2 * K;                    // floats per (tile row, wave): B then C
   constexpr int BC_PER_TILE = TT * S * BCW;
   constexpr int NTHR = S * kWave;
-  constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
   constexpr bool YPART = !SUMMARY && S > 1;
   // y partials are double-buffered (one barrier per tile) except with 16 wavefronts, where
   // two buffers would not fit in LDS next to the staged tiles; those take a second barrier
@@ -80,6 +85,11 @@ void fwd_kernel(const FwdArgs p) {
   }
   float sd = 0.f, bpow = 1.f;
   const float dsk = (HAS_DSKIP && g == 0) ? p.Dskip[dl] : 0.f;
+  // fused extras: every x / delta element a thread stages belongs to its lane's channel
+  constexpr bool ZG = EXT && !SUMMARY;  // the gate is loaded (the summaries produce no y)
+  const float dbias = (EXT && p.delta_bias) ? p.delta_bias[dl] : 0.f;
+  const bool softplus = EXT && p.delta_softplus != 0;
+  const bool has_z = ZG && p.z != nullptr;
 
   if (!SUMMARY && k > 0) {
     // Exact start state of this chunk: apply the maps of chunks 0..k-1 in order to the
@@ -123,6 +133,9 @@ void fwd_kernel(const FwdArgs p) {
   char* y0 = static_cast<char*>(p.y) + (b * L + t0) * D * T::es;
   const char* B0 = static_cast<const char*>(p.B) + (b * L + t0) * N * T::es;
   const char* C0 = static_cast<const char*>(p.C) + (b * L + t0) * N * T::es;
+  // without a gate its loads go through an empty resource (they read zeros, touch no memory)
+  const char* z0 = has_z ? static_cast<const char*>(p.z) + (b * L + t0) * D * T::es : x0;
+  const uint32_t ext_z = has_z ? ext_d : 0u;
   // resource for the rows starting at chunk row r (r may lie past the chunk end)
   // (extents in signed 64-bit so that they stay scalar: an unsigned saturating subtract is
   // lowered to a vector instruction, which turns every load into a waterfall loop)
@@ -130,6 +143,11 @@ void fwd_kernel(const FwdArgs p) {
     const uint32_t off = r * row_bytes;
     const int64_t e = (int64_t)ext_d - (int64_t)off;
     return make_rsrc_u32(base + off, e > 0 ? (uint32_t)e : 0u);
+  };
+  auto rs_z = [&](uint32_t r) {
+    const uint32_t off = r * row_bytes;
+    const int64_t e = (int64_t)ext_z - (int64_t)off;
+    return make_rsrc_u32(z0 + off, e > 0 ? (uint32_t)e : 0u);
   };
   auto rs_n = [&](const char* base, uint32_t r) {
     const uint32_t off = r * bc_row_bytes;
@@ -155,8 +173,10 @@ void fwd_kernel(const FwdArgs p) {
   // Loads run two tiles ahead of the arithmetic through a ring of three such sets.
   constexpr int XE = TT * kWave;
   constexpr int NX = (XE + NTHR - 1) / NTHR;
+  // z[r] is the gate of row r * S + g, channel `lane` of the tile: the same (row, channel) this
+  // thread stores y for, so the gate never goes through LDS
   struct Set {
-    raw b[NPE], c[NPE], x[NX], d[NX];
+    raw b[NPE], c[NPE], x[NX], d[NX], z[ZG ? NX : 1];
   };
   auto stage_load = [&](Set& st, int64_t ts) {
     const auto rb = rs_n(B0, (uint32_t)(ts - t0));
@@ -199,6 +219,11 @@ void fwd_kernel(const FwdArgs p) {
       st.x[r] = T::bload(rx, x_voff[r], 0u);
       st.d[r] = T::bload(rd, x_voff[r], 0u);
     }
+    if (ZG) {
+      const auto rz = rs_z((uint32_t)(ts - t0));
+#pragma unroll
+      for (int r = 0; r < NX; ++r) st.z[r] = T::bload(rz, x_voff[r], 0u);
+    }
   };
   auto store_xd = [&](const Set& st, int buf) {
 #pragma unroll
@@ -206,7 +231,13 @@ void fwd_kernel(const FwdArgs p) {
       const int i = tid + r * NTHR;
       if (NX * NTHR == XE || i < XE) {
         const float xv = T::widen(st.x[r]), dv = T::widen(st.d[r]);
-        xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
+        if (EXT) {
+          const float u = dv + dbias;
+          const float de = softplus ? softplus_f(u) : u;
+          xdl[buf][i / kWave][i % kWave] = make_float2(de, de * xv);
+        } else {
+          xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
+        }
         if (HAS_DSKIP) xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? i / kWave : 0][i % kWave] = xv;
       }
     }
@@ -247,11 +278,12 @@ void fwd_kernel(const FwdArgs p) {
   // every extent, and rows past the chunk end lie past the tile resource's extent, so the
   // buffer unit drops both.
   const uint32_t lane_off_y = dvalid ? lane_off : 0x80000000u;
-  // ry: resource of the tile being computed (only used when S == 1)
-  auto emit = [&](int buf, int tt, __amdgpu_buffer_rsrc_t ry, float ysum) {
+  auto gate = [&](float y, raw zr) { return (ZG && has_z) ? y * silu_f(T::widen(zr)) : y; };
+  // ry: resource of the tile being computed; cur: its inputs (only used when S == 1)
+  auto emit = [&](int buf, int tt, __amdgpu_buffer_rsrc_t ry, float ysum, const Set& cur) {
     if (SUMMARY) return;
     if (S == 1) {
-      T::bstore(ry, (uint32_t)tt * row_bytes + lane_off_y, 0u, ysum);
+      T::bstore(ry, (uint32_t)tt * row_bytes + lane_off_y, 0u, gate(ysum, cur.z[ZG ? tt : 0]));
     } else {
       ypart[YPART && YB == 2 ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
     }
@@ -262,7 +294,7 @@ void fwd_kernel(const FwdArgs p) {
   // wavefront per SIMD has nothing else to issue meanwhile).
   constexpr int RB = (32 / K) < TT ? (32 / K) : TT;
   constexpr int NB = TT / RB;
-  auto compute_tile = [&](int buf, int64_t ts) {
+  auto compute_tile = [&](int buf, int64_t ts, const Set& cur) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     float bcv[2][RB][BCW];
     float2 dcv[2][RB];
@@ -285,13 +317,13 @@ void fwd_kernel(const FwdArgs p) {
         const int tt = jb * RB + i;
         const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
         const float ysum = step(xv, dcv[jb & 1][i].x, dcv[jb & 1][i].y, bcv[jb & 1][i]);
-        emit(buf, tt, ry, ysum);
+        emit(buf, tt, ry, ysum, cur);
       }
     }
   };
   // The ragged last tile of a chunk (nv < TT rows), once per chunk after the main loop: rows
   // past nv must leave the state alone, so each row is guarded (a uniform branch).
-  auto compute_tail = [&](int buf, int64_t ts, int nv) {
+  auto compute_tail = [&](int buf, int64_t ts, int nv, const Set& cur) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -299,13 +331,13 @@ void fwd_kernel(const FwdArgs p) {
         const float2 dc = xdl[buf][tt][lane];
         const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
         const float ysum = step(xv, dc.x, dc.y, &bcs[buf][tt][g][0]);
-        emit(buf, tt, ry, ysum);
+        emit(buf, tt, ry, ysum, cur);
       }
     }
   };
   // y of the tile whose partials are in ypart[buf]: each wavefront takes rows g, g + S, ...,
   // adds the S partials in a fixed order and stores, a fixed number of stores per wavefront.
-  auto finalize = [&](int buf, int64_t ts) {
+  auto finalize = [&](int buf, int64_t ts, const Set& cur) {
     if (!YPART) return;
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
 #pragma unroll
@@ -314,7 +346,7 @@ void fwd_kernel(const FwdArgs p) {
       float s = 0.f;
 #pragma unroll
       for (int gg = 0; gg < S; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][lane];
-      T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, s);
+      T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, gate(s, cur.z[ZG ? r : 0]));
     }
   };
 
@@ -329,27 +361,28 @@ void fwd_kernel(const FwdArgs p) {
   __syncthreads();
 
   // One step: issue the loads of tile k + 2, compute tile k (if it exists) from LDS, stage
-  // tile k + 1 into the other LDS buffer, one barrier, store tile k's y.  No memory operation
+  // tile k + 1 into the other LDS buffer, one barrier, store tile k's y.  `cur` still holds
+  // tile k's inputs (its gate, in the fused variant).  No memory operation
   // depends on a branch (the compute issues none when there are y partials): past the chunk
   // end the loads read zeros, the staged buffer goes unused and the y stores are dropped.
-  auto stepk = [&](int64_t k, Set& ld, const Set& st) {
+  auto stepk = [&](int64_t k, Set& ld, const Set& st, const Set& cur) {
     const int64_t ts = t0 + k * TT;
     const int buf = (int)(k & 1);
     load_set(ld, ts + 2 * TT);
     if (k < nfull)
-      compute_tile(buf, ts);
+      compute_tile(buf, ts, cur);
     else if (k == nfull && nrem > 0)
-      compute_tail(buf, ts, nrem);
+      compute_tail(buf, ts, nrem, cur);
     store_set(st, buf ^ 1);
     __syncthreads();
-    finalize(buf, ts);
+    finalize(buf, ts, cur);
     if (YPART && YB == 1) __syncthreads();  // partials read before the next tile rewrites them
   };
   // groups of three steps so the three register sets rotate without copies; one loop exit
   for (int64_t k = 0; k < ntile; k += 3) {
-    stepk(k, sc, sb);
-    stepk(k + 1, sa, sc);
-    stepk(k + 2, sb, sa);
+    stepk(k, sc, sb, sa);
+    stepk(k + 1, sa, sc, sb);
+    stepk(k + 2, sb, sa, sc);
   }
 
   if (SUMMARY) {
@@ -381,50 +414,59 @@ void fwd_kernel(const FwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S, bool BETA0>
+template <typename IO, int K, int S, bool BETA0, bool EXT>
 hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
   const dim3 block(S * kWave);
   if (a.G > 1) {
     const dim3 grid((unsigned)(a.ncb * a.Bt * (a.G - 1)));
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false, EXT>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(a.ncb * a.Bt * a.G));
   if (a.Dskip)
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true, EXT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false, EXT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-template <typename IO, bool BETA0>
+template <typename IO, bool BETA0, bool EXT>
 hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
   // padded state count NP = K * S is 4, 16 or 64
   const int NP = a.N <= 4 ? 4 : (a.N <= 16 ? 16 : 64);
   switch (NP * 100 + K) {
-    case 401: return launch_ks<IO, 1, 4, BETA0>(a, s);
-    case 402: return launch_ks<IO, 2, 2, BETA0>(a, s);
-    case 404: return launch_ks<IO, 4, 1, BETA0>(a, s);
-    case 1601: return launch_ks<IO, 1, 16, BETA0>(a, s);
-    case 1602: return launch_ks<IO, 2, 8, BETA0>(a, s);
-    case 1604: return launch_ks<IO, 4, 4, BETA0>(a, s);
-    case 1608: return launch_ks<IO, 8, 2, BETA0>(a, s);
-    case 1616: return launch_ks<IO, 16, 1, BETA0>(a, s);
-    case 6404: return launch_ks<IO, 4, 16, BETA0>(a, s);
-    case 6408: return launch_ks<IO, 8, 8, BETA0>(a, s);
-    case 6416: return launch_ks<IO, 16, 4, BETA0>(a, s);
+    case 401: return launch_ks<IO, 1, 4, BETA0, EXT>(a, s);
+    case 402: return launch_ks<IO, 2, 2, BETA0, EXT>(a, s);
+    case 404: return launch_ks<IO, 4, 1, BETA0, EXT>(a, s);
+    case 1601: return launch_ks<IO, 1, 16, BETA0, EXT>(a, s);
+    case 1602: return launch_ks<IO, 2, 8, BETA0, EXT>(a, s);
+    case 1604: return launch_ks<IO, 4, 4, BETA0, EXT>(a, s);
+    case 1608: return launch_ks<IO, 8, 2, BETA0, EXT>(a, s);
+    case 1616: return launch_ks<IO, 16, 1, BETA0, EXT>(a, s);
+    case 6404: return launch_ks<IO, 4, 16, BETA0, EXT>(a, s);
+    case 6408: return launch_ks<IO, 8, 8, BETA0, EXT>(a, s);
+    case 6416: return launch_ks<IO, 16, 4, BETA0, EXT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s) {
-  if (io_bf16) {
-    return beta0 ? launch_io<bf16_storage, true>(a, K, s) : launch_io<bf16_storage, false>(a, K, s);
-  }
-  return beta0 ? launch_io<float, true>(a, K, s) : launch_io<float, false>(a, K, s);
+// This file is compiled once per (I/O dtype, variant) pair; MSM_IO_BF16 and MSM_EXT select
+// which launcher a build of it defines.
+#if !defined(MSM_IO_BF16) || !defined(MSM_EXT)
+#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1"
+#endif
+#if MSM_IO_BF16
+using PartIO = bf16_storage;
+#else
+using PartIO = float;
+#endif
+
+hipError_t MSM_FWD_PART(MSM_IO_BF16, MSM_EXT)(const FwdArgs& a, int K, bool beta0, hipStream_t s) {
+  return beta0 ? launch_io<PartIO, true, MSM_EXT != 0>(a, K, s)
+               : launch_io<PartIO, false, MSM_EXT != 0>(a, K, s);
 }
 
 }  // namespace msm

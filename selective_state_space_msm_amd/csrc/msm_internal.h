@@ -26,6 +26,11 @@ struct FwdArgs {
   void* y;
   float* last_h;
   float* last_v;
+  // fused extras (used by the EXT kernels only): delta_eff = softplus(delta + delta_bias[d])
+  // (or delta + delta_bias[d]), y = y_raw * silu(z); null pointers mean no bias / no gate
+  const void* z;
+  const float* delta_bias;
+  int32_t delta_softplus;
   // chunk summaries, [Bt][G][N][D] (sd: [Bt][G][D]); unused when G == 1
   float* s_bv;
   float* s_bh;
@@ -53,6 +58,13 @@ struct BwdArgs {
   const float* dlast_v;
   float* dh0;            // (Bt, D, N) adjoints of the initial state or null (not written)
   float* dv0;
+  // fused extras (EXT kernels only): gate z and its gradient dz (Bt, L, D, I/O dtype), the
+  // delta bias (D,) and its gradient; ddelta is then the gradient of the raw delta
+  const void* z;
+  const float* delta_bias;
+  int32_t delta_softplus;
+  void* dz;
+  float* ddelta_bias;
   void* dx;
   void* ddelta;
   float* dA;
@@ -65,6 +77,7 @@ struct BwdArgs {
                      // of dB/alpha and dC
   float* dA_part;    // [Bt][N][D]
   float* dD_part;    // [Bt][D]
+  float* dbias_part; // [Bt][D] per batch row partial sums of the delta-bias gradient
   int64_t Bt, L, D, N;
   int64_t NT;        // tiles = ceil(L / kBwdTile)
   int32_t ncb;       // channel blocks: kBwdChans channels, or 64 when NP == 64
@@ -72,9 +85,24 @@ struct BwdArgs {
   float beta, alpha;
 };
 
-// Both return hipSuccess or the first launch error.
-hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, hipStream_t s);
+// Both return hipSuccess or the first launch error; `ext` selects the fused variant.
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);
+
+// The recurrence kernels are compiled once per (I/O dtype, variant) pair, each build of
+// msm_fwd.hip / msm_bwd.hip defining one of these (suffix: bf16 I/O, fused variant).
+#define MSM_PART_NAME_(prefix, io, ext) prefix##io##_##ext
+#define MSM_PART_NAME(prefix, io, ext) MSM_PART_NAME_(prefix, io, ext)
+#define MSM_FWD_PART(io, ext) MSM_PART_NAME(launch_fwd_part_, io, ext)
+#define MSM_BWD_PART(io, ext) MSM_PART_NAME(launch_bwd_part_, io, ext)
+hipError_t launch_fwd_part_0_0(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_fwd_part_0_1(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_fwd_part_1_0(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_fwd_part_1_1(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_0_0(const BwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_0_1(const BwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_1_0(const BwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_1_1(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 // The 64-state backward (channel blocks of 64, K = 4); launch_bwd calls it for NP == 64.
 hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, hipStream_t s);
 

@@ -1,0 +1,82 @@
+// Launchers: the forward and backward recurrence kernels (one build of msm_fwd.hip /
+// msm_bwd.hip per I/O dtype and variant; the full-wave backward for 64 padded states), and
+// the kernel that finishes the backward by summing its per-block partials.
+#include "msm_device.hpp"
+#include "msm_internal.h"
+
+namespace msm {
+namespace {
+
+// Sums the per-block partials in a fixed order and writes dB, dC (I/O dtype), dA, dDskip and
+// the delta-bias gradient.
+template <typename IO>
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdArgs p) {
+  using T = io<IO>;
+  const int64_t n_bc = p.Bt * p.L * 2 * p.N;
+  const int64_t n_a = p.D * p.N;
+  const int64_t n_d = p.Dskip ? p.D : 0;
+  const int64_t n_g = p.ddelta_bias ? p.D : 0;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_bc) {
+    const int64_t n = i % p.N;
+    const int64_t which = (i / p.N) % 2;
+    const int64_t bt = i / (2 * p.N);  // b * L + t
+    const int64_t b = bt / p.L, t = bt % p.L;
+    float s = 0.f;
+    for (int cb = 0; cb < p.ncb; ++cb)
+      s += p.dbc_part[((b * p.ncb + cb) * p.L + t) * 2 * p.NP + which * p.NP + n];
+    if (which == 0)
+      T::store(p.dB, bt * p.N + n, s * p.alpha);
+    else
+      T::store(p.dC, bt * p.N + n, s);
+  } else if (i < n_bc + n_a) {
+    const int64_t k = i - n_bc;  // d * N + n
+    const int64_t dd = k / p.N, n = k % p.N;
+    float s = 0.f;
+    for (int64_t b = 0; b < p.Bt; ++b) s += p.dA_part[(b * p.N + n) * p.D + dd];
+    p.dA[k] = s;
+  } else if (i < n_bc + n_a + n_d) {
+    const int64_t dd = i - n_bc - n_a;
+    float s = 0.f;
+    for (int64_t b = 0; b < p.Bt; ++b) s += p.dD_part[b * p.D + dd];
+    p.dDskip[dd] = s;
+  } else if (i < n_bc + n_a + n_d + n_g) {
+    const int64_t dd = i - n_bc - n_a - n_d;
+    float s = 0.f;
+    for (int64_t b = 0; b < p.Bt; ++b) s += p.dbias_part[b * p.D + dd];
+    p.ddelta_bias[dd] = s;
+  }
+}
+
+template <typename IO>
+hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
+  const int64_t total =
+      a.Bt * a.L * 2 * a.N + a.D * a.N + (a.Dskip ? a.D : 0) + (a.ddelta_bias ? a.D : 0);
+  hipLaunchKernelGGL((bwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s) {
+  hipError_t e;
+  if (a.NP == 64) {
+    if (ext) return hipErrorInvalidValue;
+    e = launch_bwd_wide(a, io_bf16, beta0, s);
+  } else if (io_bf16) {
+    e = ext ? launch_bwd_part_1_1(a, K, beta0, s) : launch_bwd_part_1_0(a, K, beta0, s);
+  } else {
+    e = ext ? launch_bwd_part_0_1(a, K, beta0, s) : launch_bwd_part_0_0(a, K, beta0, s);
+  }
+  if (e != hipSuccess) return e;
+  return io_bf16 ? launch_finalize<bf16_storage>(a, s) : launch_finalize<float>(a, s);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s) {
+  if (io_bf16)
+    return ext ? launch_fwd_part_1_1(a, K, beta0, s) : launch_fwd_part_1_0(a, K, beta0, s);
+  return ext ? launch_fwd_part_0_1(a, K, beta0, s) : launch_fwd_part_0_0(a, K, beta0, s);
+}
+
+}  // namespace msm

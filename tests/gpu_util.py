@@ -95,16 +95,17 @@ def sub_problem(inp, dsel=None, bsel=None):
     independent in the forward, so the oracle on the slice gives those outputs exactly."""
     out = dict(inp)
     if bsel is not None:
-        for k in ("x", "delta", "B", "C", "dy"):
+        for k in ("x", "delta", "B", "C", "dy", "z"):
             if out.get(k) is not None:
                 out[k] = out[k][bsel]
     if dsel is not None:
-        for k in ("x", "delta", "dy"):
+        for k in ("x", "delta", "dy", "z"):
             if out.get(k) is not None:
                 out[k] = out[k][:, :, dsel]
         out["A"] = out["A"][dsel]
-        if out.get("Dskip") is not None:
-            out["Dskip"] = out["Dskip"][dsel]
+        for k in ("Dskip", "delta_bias"):
+            if out.get(k) is not None:
+                out[k] = out[k][dsel]
     return out
 
 

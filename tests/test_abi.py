@@ -178,6 +178,45 @@ def test_state_entry_points_validation_never_launches(lib):
     assert bwd(dx=None) == INVALID
 
 
+def test_fused_entry_points_validation_never_launches(lib):
+    P = ctypes.c_void_p
+
+    def fwd(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
+                 bias=None, sp=0, h0=None, v0=None, y=0x100000, lh=None, lv=None, N=4)
+        a.update(kw)
+        return lib.msm_selective_scan_fwd(
+            P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["z"]),
+            P(a["bias"]), a["sp"], P(a["h0"]), P(a["v0"]), P(a["y"]), P(a["lh"]), P(a["lv"]), 1,
+            8, 4, a["N"], ctypes.c_float(0.5), ctypes.c_float(1.0), 0, None, 0, None, None)
+
+    def bwd(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
+                 bias=None, sp=0, dy=0x6000, dx=0x100000, ddelta=0x200000, dA=0x300000,
+                 dB=0x400000, dC=0x500000, dDskip=None, dz=None, dbias=None, N=4)
+        a.update(kw)
+        return lib.msm_selective_scan_bwd(
+            P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["z"]),
+            P(a["bias"]), a["sp"], P(a["dy"]), None, None, None, None, P(a["dx"]),
+            P(a["ddelta"]), P(a["dA"]), P(a["dB"]), P(a["dC"]), P(a["dDskip"]), P(a["dz"]),
+            P(a["dbias"]), None, None, 1, 8, 4, a["N"], ctypes.c_float(0.5),
+            ctypes.c_float(1.0), 0, P(0x900000), 1 << 30, None, None)
+
+    # x, y: 1*8*4 floats = 128 bytes; bias: 16 bytes
+    assert fwd(sp=2) == INVALID                   # softplus flag is 0 or 1
+    assert fwd(z=0x100000 + 64) == INVALID        # the gate overlapping y
+    assert fwd(bias=0x100000) == INVALID          # the bias overlapping y
+    assert bwd(z=0x7000) == INVALID               # z without dz
+    assert bwd(dz=0x700000) == INVALID            # dz without z
+    assert bwd(bias=0x7000) == INVALID            # bias without its gradient
+    assert bwd(dbias=0x700000) == INVALID
+    assert bwd(z=0x7000, dz=0x7000 + 8) == INVALID  # dz over z
+    assert bwd(bias=0x7000, dbias=0x100000 + 4) == INVALID  # bias gradient over dx
+    assert bwd(sp=-1) == INVALID
+    # the fused backward is built for N <= 16
+    assert bwd(N=33, sp=1) == UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msm, "_lib", None)
     monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))

@@ -134,3 +134,30 @@ def make_state(w: Workload, seed: int, scale: float = 1.0):
     a = (scale * rng.standard_normal((w.Bt, w.D, w.N))).astype(np.float32)
     b = (scale * rng.standard_normal((w.Bt, w.D, w.N))).astype(np.float32)
     return a, b
+
+
+def make_fused_extras(w: Workload, seed: int, softplus: bool = True) -> dict:
+    """Inputs of the fused op for workload ``w``: a raw delta that replaces ``delta``, the
+    per-channel delta bias and the gate z (float32 numpy; raw delta and z bf16-representable
+    when w.io == "bf16").
+
+    With softplus the bias is the inverse softplus of a log-uniform step in [1e-3, 1e-1] (the
+    usual initialisation of a Mamba layer's step bias) and the raw delta is N(0, 0.5^2)
+    projection noise around it, so softplus(delta + bias) covers the same range as the
+    workload's own delta.  Without softplus the raw delta is the workload's delta distribution
+    and the bias a small positive shift U(0, 0.02), keeping delta + bias positive.
+    z ~ N(0, 1), the gate branch's activations.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Bt, L, D = w.Bt, w.L, w.D
+    if softplus:
+        dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=D))
+        bias = np.log(np.expm1(dt)).astype(np.float32)
+        raw = (0.5 * rng.standard_normal((Bt, L, D))).astype(np.float32)
+    else:
+        bias = rng.uniform(0.0, 0.02, size=D).astype(np.float32)
+        raw = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(Bt, L, D))).astype(np.float32)
+    z = rng.standard_normal((Bt, L, D)).astype(np.float32)
+    if w.io == "bf16":
+        raw, z = round_to_bf16(raw), round_to_bf16(z)
+    return dict(delta_raw=raw, delta_bias=bias, z=z, softplus=softplus)
