@@ -209,6 +209,23 @@ class Oracle:
             raise RuntimeError("msm_oracle_fused_bwd failed (%d)" % rc)
         return out
 
+    def step(self, x, delta, A, B, C, h, v, beta, alpha, Dskip=None, z=None, delta_bias=None,
+             delta_softplus=False):
+        """One decode step (the README's ``step``: one token, the ssm and velocity states
+        carried in and out).  x, delta, z: (Bt, D); B, C: (Bt, N); h, v: (Bt, D, N).  It is the
+        fused forward over a sequence of length one started at (h, v).
+        Returns (y (Bt, D), h_new, v_new) as float64."""
+        x, delta, B, C = (_f64(a) for a in (x, delta, B, C))
+        Bt, D = x.shape
+        N = B.shape[1]
+        y, _, hn, vn = self.fused_fwd(x.reshape(Bt, 1, D), delta.reshape(Bt, 1, D), A,
+                                      B.reshape(Bt, 1, N), C.reshape(Bt, 1, N), beta, alpha,
+                                      Dskip=Dskip,
+                                      z=None if z is None else _f64(z).reshape(Bt, 1, D),
+                                      delta_bias=delta_bias, delta_softplus=delta_softplus,
+                                      h0=h, v0=v)
+        return y.reshape(Bt, D), hn, vn
+
 
 _default = None
 
@@ -241,6 +258,10 @@ def fused_fwd(*args, **kw):
 
 def fused_bwd(*args, **kw):
     return default().fused_bwd(*args, **kw)
+
+
+def step(*args, **kw):
+    return default().step(*args, **kw)
 
 
 def max_threads() -> int:

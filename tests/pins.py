@@ -603,9 +603,39 @@ def pin_fused_finite_differences(orc):
                                          % (gname, i, softplus, fd, an))
 
 
+
+def pin_step_sequence(orc):
+    """L decode steps, each fed the state the previous one returned, reproduce the fused forward
+    over the whole sequence (y row by row and the final state), bit for bit: the step is one
+    iteration of the same recurrence."""
+    rng = np.random.default_rng(53)
+    Bt, L, D, N = 2, 7, 3, 4
+    beta, alpha = 0.85, 0.7
+    x, _, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    raw = rng.normal(-2.0, 1.0, size=(Bt, L, D))
+    bias = 0.3 * rng.standard_normal(D)
+    z = rng.standard_normal((Bt, L, D))
+    h, v = _rand_state(rng, Bt, D, N)
+    want, _, wh, wv = orc.fused_fwd(x, raw, A, B, C, beta, alpha, Dskip=Ds, z=z, delta_bias=bias,
+                                    delta_softplus=True, h0=h, v0=v)
+    for t in range(L):
+        y, h, v = orc.step(x[:, t], raw[:, t], A, B[:, t], C[:, t], h, v, beta, alpha, Dskip=Ds,
+                           z=z[:, t], delta_bias=bias, delta_softplus=True)
+        close(y, want[:, t], rtol=0, atol=0, what="step %d y" % t)
+    close(h, wh, rtol=0, atol=0, what="stepped h")
+    close(v, wv, rtol=0, atol=0, what="stepped v")
+    # one step of a single state from zero with beta = 0, alpha = 1: h = delta B x
+    y, h1, v1 = orc.step(np.array([[2.0]]), np.array([[0.5]]), np.array([[-1.0]]),
+                         np.array([[3.0]]), np.array([[1.5]]), np.zeros((1, 1, 1)),
+                         np.zeros((1, 1, 1)), 0.0, 1.0)
+    close(h1[0, 0, 0], 3.0, what="single write")
+    close(y[0, 0], 4.5, what="single readout")
+
+
 ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
             pin_beta0_equivalence, pin_structure, pin_finite_differences,
             pin_scaling_identities, pin_bwd_beta0_alpha0, pin_initial_state_filter,
             pin_continuation, pin_state_finite_differences, pin_bwd_continuation,
-            pin_fused_delta_transform, pin_fused_gate, pin_fused_finite_differences]
+            pin_fused_delta_transform, pin_fused_gate, pin_fused_finite_differences,
+            pin_step_sequence]
