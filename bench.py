@@ -3,7 +3,8 @@
 One step = one msm_scan_fwd call over the Mamba-1.4B layer shape (Bt=4, L=4096, D=4096, N=16,
 bf16 I/O with fp32 state, beta=0.9, alpha=1) with inputs already resident in HBM.  The line
 also reports the backward on its own workload (Bt=4, L=2048, D=2048, N=16, fp32) timed the
-same way, the ALU roofline of the forward's single kernel, the algorithmic HBM rate, and the
+same way, one decode step (msm_scan_step, Bt=1024 sequences of the same layer shape) with its
+HBM roofline, the ALU roofline of the forward's single kernel, the algorithmic HBM rate, and the
 fp64 oracle timed on the host cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload m1p4b] [--no-cpu-baseline]
@@ -52,6 +53,14 @@ def alg_bytes_bwd(w: workloads.Workload) -> int:
     if w.dskip:
         b += 8 * w.D
     return b
+
+
+def alg_bytes_step(w: workloads.Workload) -> int:
+    """One decode step: the fp32 h and v states read and written, x / delta / z read and y
+    written per channel, B and C per batch row, A, Dskip and the delta bias once."""
+    s = 2 if w.io == "bf16" else 4
+    return (16 * w.Bt * w.D * w.N + 4 * w.Bt * w.D * s + 2 * w.Bt * w.N * s + 4 * w.D * w.N
+            + 8 * w.D)
 
 
 def source_hash() -> str:
@@ -144,6 +153,24 @@ def bench_bwd(w, steps, warmup, stream):
     return ms, per, plan
 
 
+def bench_step(w, steps, warmup, stream):
+    import torch
+    import selective_state_space_msm_amd as msm
+    si = workloads.make_step_inputs(w)
+    dt = torch.float32 if w.io == "f32" else torch.bfloat16
+    g = {k: torch.from_numpy(si[k]).to("cuda").to(dt) for k in ("x", "delta", "z", "B", "C")}
+    for k in ("A", "Dskip", "delta_bias", "h", "v"):
+        g[k] = torch.from_numpy(si[k]).to("cuda")
+    y = torch.empty_like(g["x"])
+
+    def step():
+        msm.msm_scan_step(g["x"], g["delta"], g["A"], g["B"], g["C"], g["h"], g["v"], w.beta,
+                          w.alpha, g["Dskip"], z=g["z"], delta_bias=g["delta_bias"],
+                          delta_softplus=True, y=y, stream=stream)
+
+    return timed(step, stream, steps, warmup)
+
+
 def cpu_baseline(w, target_s=12.0):
     """The fp64 oracle, as it stands, on a bounded slice of the workload: every batch row and
     every step of a block of channels sized for roughly target_s seconds on the host cores."""
@@ -211,6 +238,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="m1p4b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--bwd-workload", default="bwd", choices=sorted(workloads.WORKLOADS) + ["none"])
+    ap.add_argument("--step-workload", default="decode",
+                    choices=[k for k, v in workloads.WORKLOADS.items() if v.direction == "step"]
+                    + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -274,6 +304,18 @@ def main(argv=None):
                       "ms_per_call": bms, "state_updates_per_s": wb.updates / (bms / 1e3),
                       "algorithmic_GBs": bbytes / (bms / 1e3) / 1e9,
                       "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": bplan}
+    if args.step_workload != "none":
+        ws_ = workloads.WORKLOADS[args.step_workload]
+        sms, sper = bench_step(ws_, max(5, args.steps), max(2, args.warmup // 2), stream)
+        sbytes = alg_bytes_step(ws_)
+        rec["decode"] = {"workload": "%s: one decode step with bias, softplus and gate, Bt=%d D=%d "
+                                     "N=%d io=%s" % (ws_.name, ws_.Bt, ws_.D, ws_.N, ws_.io),
+                         "ms_per_call": sms, "state_updates_per_s": ws_.Bt * ws_.D * ws_.N / (sms / 1e3),
+                         "roofline": {"bound": "hbm", "achieved": sbytes / (sms / 1e3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                      "traffic": measured_traffic("step_%s" % ws_.name),
+                                      "algorithmic_bytes": sbytes}}
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

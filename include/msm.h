@@ -193,6 +193,25 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
                                   msm_dtype io, void* workspace, size_t workspace_bytes,
                                   void* stream, const msm_plan* plan);
 
+/* Single-token decode step (the README's Mamba `step`: hidden_states of one position plus the
+ * ssm_state and velocity_state caches, "Low-Level Functions" / `allocate_inference_cache`),
+ * for the scan part of the block.  x, delta, z, y: (Bt, D) io dtype -- the token's input, raw
+ * step size, gate and output; B, C: (Bt, N) io; A (D, N), Dskip (D,), delta_bias (D,) fp32;
+ * h, v: (Bt, D, N) fp32 ssm and velocity states, read and overwritten IN PLACE with the states
+ * after this token.  Computes, per (b, d, n), with delta_eff as in msm_selective_scan_fwd:
+ *     v <- beta v + alpha delta_eff B x,  h <- exp(delta_eff A) h + v,
+ *     y  = (sum_n C h + Dskip x) * silu(z)        (gate only when z is non-NULL)
+ * which is msm_selective_scan_fwd over a sequence of length one started at (h, v), up to fp32
+ * rounding.  Zero-initialised h, v start a new sequence; the last_h / last_v of a prefill call
+ * continue one.  z, Dskip and delta_bias may be NULL; delta_softplus is 0 or 1.  h and v must
+ * not overlap each other, an input or y.  Needs no workspace.  Same requirements on Bt, D, N,
+ * beta, alpha and io as msm_scan_fwd. */
+msm_status msm_scan_step(const void* x, const void* delta, const float* A, const void* B,
+                         const void* C, const float* Dskip, const void* z,
+                         const float* delta_bias, int32_t delta_softplus, float* h, float* v,
+                         void* y, int64_t Bt, int64_t D, int64_t N, float beta, float alpha,
+                         msm_dtype io, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ __all__ = [
     "MsmError", "MsmLibraryMissing", "MSM_F32", "MSM_BF16", "library_path", "load_library",
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
-    "msm_scan_bwd", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "EXPORTED_SYMBOLS",
+    "msm_scan_bwd", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
+    "EXPORTED_SYMBOLS",
 ]
 
 MSM_F32 = 0
@@ -35,7 +36,7 @@ EXPORTED_SYMBOLS = [
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
     "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan", "msm_scan_fwd_state",
-    "msm_scan_bwd_state", "msm_selective_scan_fwd", "msm_selective_scan_bwd",
+    "msm_scan_bwd_state", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +109,9 @@ def load_library():
     lib.msm_selective_scan_fwd.restype = ctypes.c_int
     lib.msm_selective_scan_bwd.argtypes = [P] * 8 + [I32] + [P] * 15 + tail
     lib.msm_selective_scan_bwd.restype = ctypes.c_int
+    lib.msm_scan_step.argtypes = ([P] * 8 + [I32] + [P] * 3 + [I64, I64, I64, F, F, ctypes.c_int,
+                                                               P])
+    lib.msm_scan_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -417,3 +421,36 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
     if st != 0:
         raise MsmError(st, "msm_selective_scan_bwd")
     return o
+
+
+def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, delta_bias=None,
+                  delta_softplus=False, y=None, stream=None):
+    """One decode step (msm_scan_step): x, delta, z (Bt, D) and B, C (Bt, N) in the I/O dtype;
+    h, v (Bt, D, N) fp32 states, updated in place.  Returns y (Bt, D)."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for t, nm, shp in ((x, "x", (Bt, D)), (delta, "delta", (Bt, D)), (B, "B", (Bt, N)),
+                       (C, "C", (Bt, N))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    for t, nm in ((h, "h"), (v, "v")):
+        _check(t, nm, (Bt, D, N), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    if z is not None:
+        _check(z, "z", (Bt, D), x.dtype, dev)
+    if delta_bias is not None:
+        _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bt, D), dtype=x.dtype, device=dev)
+    _check(y, "y", (Bt, D), x.dtype, dev)
+    st = lib.msm_scan_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h), _ptr(v), _ptr(y),
+                           Bt, D, N, float(beta), float(alpha), io, _stream_handle(stream, dev))
+    if st != 0:
+        raise MsmError(st, "msm_scan_step")
+    return y

@@ -17,7 +17,8 @@ LIB = os.path.join(PKG, "libmsm.so")
 # (source, extra flags): the recurrence kernels are built once per (bf16 I/O, fused variant)
 # pair, all in parallel
 _PARTS = [("-DMSM_IO_BF16=%d" % io, "-DMSM_EXT=%d" % ext) for io in (0, 1) for ext in (0, 1)]
-SOURCES = ([("msm_api.cpp", ()), ("msm_launch.hip", ()), ("msm_bwd_wide.hip", ())]
+SOURCES = ([("msm_api.cpp", ()), ("msm_launch.hip", ()), ("msm_bwd_wide.hip", ()),
+            ("msm_step.hip", ())]
            + [("msm_fwd.hip", f) for f in _PARTS] + [("msm_bwd.hip", f) for f in _PARTS])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

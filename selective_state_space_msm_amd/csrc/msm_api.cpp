@@ -479,4 +479,49 @@ msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const 
                                 nullptr);
 }
 
+msm_status msm_scan_step(const void* x, const void* delta, const float* A, const void* B,
+                         const void* C, const float* Dskip, const void* z,
+                         const float* delta_bias, int32_t delta_softplus, float* h, float* v,
+                         void* y, int64_t Bt, int64_t D, int64_t N, float beta, float alpha,
+                         msm_dtype io, void* stream) {
+  msm_status st = check_common(Bt, 1, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!x || !delta || !A || !B || !C || !h || !v || !y) return MSM_ERR_INVALID_ARG;
+  if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
+  const size_t es = io == MSM_BF16 ? 2 : 4;
+  const size_t nxd = (size_t)(Bt * D), nbc = (size_t)(Bt * N), nst = (size_t)(Bt * D * N) * 4;
+  const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 4), rng(B, nbc * es),
+                       rng(C, nbc * es),          rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(z, z ? nxd * es : 0),  rng(delta_bias, delta_bias ? (size_t)D * 4 : 0)};
+  // h and v are read and written in place: they may not overlap an input, y or each other
+  const Range outs[] = {rng(y, nxd * es), rng(h, nst), rng(v, nst)};
+  if (any_overlap(outs, 3, ins, 8)) return MSM_ERR_INVALID_ARG;
+
+  int G = 1;
+  while (4 * G < N) G *= 2;
+  msm::StepArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.z = z;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.delta_bias = delta_bias;
+  a.delta_softplus = delta_softplus;
+  a.h = h;
+  a.v = v;
+  a.y = y;
+  a.Bt = Bt;
+  a.D = D;
+  a.N = N;
+  a.G = G;
+  a.beta = beta;
+  a.alpha = alpha;
+  const bool vec = N % 4 == 0 && (((uintptr_t)h | (uintptr_t)v | (uintptr_t)A) & 15) == 0;
+  hipError_t e = msm::launch_step(a, io == MSM_BF16, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -44,7 +44,6 @@ void fwd_kernel(const FwdArgs p) {
   using raw = typename T::raw;
   constexpr int TT = kTile;
   constexpr int BCW = 2 * K;                    // floats per (tile row, wave): B then C
-  constexpr int BC_PER_TILE = TT * S * BCW;
   constexpr int NTHR = S * kWave;
   constexpr bool YPART = !SUMMARY && S > 1;
   // y partials are double-buffered (one barrier per tile) except with 16 wavefronts, where

@@ -85,6 +85,28 @@ struct BwdArgs {
   float beta, alpha;
 };
 
+struct StepArgs {
+  const void* x;          // (Bt, D) I/O dtype: the token's input, raw delta and gate
+  const void* delta;
+  const void* z;          // or null (no gate)
+  const float* A;         // (D, N)
+  const void* B;          // (Bt, N) I/O dtype
+  const void* C;
+  const float* Dskip;     // (D,) or null
+  const float* delta_bias;  // (D,) or null
+  int32_t delta_softplus;
+  float* h;               // (Bt, D, N) fp32 states, updated in place
+  float* v;
+  void* y;                // (Bt, D) I/O dtype
+  int64_t Bt, D, N;
+  int32_t G;              // lanes per channel: ceil(N / 4) rounded up to a power of two
+  float beta, alpha;
+};
+
+// One decode step; vec selects 16-byte state access (N % 4 == 0 and 16-byte aligned states
+// and A).  Returns hipSuccess or the launch error.
+hipError_t launch_step(const StepArgs& a, int io_bf16, bool vec, hipStream_t s);
+
 // Both return hipSuccess or the first launch error; `ext` selects the fused variant.
 hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);

@@ -1,0 +1,130 @@
+// Single-token decode step of the momentum selective scan (gfx950).
+//
+// The `step` of the Momentum Mamba README (one token in, the ssm and velocity states carried in
+// and out), for the scan part of the block: with the fused op's extras,
+//   delta_eff = softplus(delta + bias[d]) (or delta + bias[d]),
+//   v' = beta v + alpha delta_eff B x,  h' = exp(delta_eff A) h + v',
+//   y  = (C . h' + Dskip x) * silu(z)   (the gate when z is given),
+// with h and v, (Bt, D, N) fp32, updated in place.
+//
+// The step reads and writes every state once and does a handful of flops per state: it is
+// bound by HBM bandwidth (16 bytes of state traffic per (b, d, n)).  The layout follows that:
+// a channel's N states are contiguous, G = ceil(N / 4) rounded up to a power of two lanes
+// share a channel and each lane moves four consecutive states with 16-byte loads and stores,
+// so a wavefront streams one contiguous block of both state arrays.  The readout sum over the
+// channel's lanes is a butterfly of lane swaps inside the group.  B, C (per batch row), A (per
+// channel) and x / delta / z (per channel) are shared between lanes and come from cache.
+#include "msm_device.hpp"
+#include "msm_internal.h"
+
+namespace msm {
+namespace {
+
+template <typename IO, bool VEC>
+__global__ __launch_bounds__(256) void step_kernel(const StepArgs p) {
+  using T = io<IO>;
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int G = p.G;
+  const int64_t npair = p.Bt * p.D;
+  const int64_t pr_raw = gtid / G;
+  const bool valid = pr_raw < npair;
+  // lanes past the last channel compute on the last one and store nothing (the butterfly
+  // below needs every lane of a group)
+  const int64_t pr = valid ? pr_raw : npair - 1;
+  const int q = (int)(gtid - pr_raw * G);
+  const int64_t N = p.N, D = p.D;
+  const int64_t b = pr / D, d = pr - b * D;
+  const int n0 = 4 * q;
+
+  const float xv = T::widen(T::load(p.x, pr));
+  const float draw = T::widen(T::load(p.delta, pr));
+  const float u = draw + (p.delta_bias ? p.delta_bias[d] : 0.f);
+  const float de = p.delta_softplus ? softplus_f(u) : u;
+  const float c = p.alpha * de * xv;
+
+  float hs[4], vs[4], As[4], Bs[4], Cs[4];
+  float* hp = p.h + pr * N + n0;
+  float* vp = p.v + pr * N + n0;
+  if (VEC) {
+    // N is a multiple of 4 here, so a lane's four states are all real or all padding
+    if (n0 < N) {
+      const float4 h4 = *reinterpret_cast<const float4*>(hp);
+      const float4 v4 = *reinterpret_cast<const float4*>(vp);
+      const float4 a4 = *reinterpret_cast<const float4*>(p.A + d * N + n0);
+      hs[0] = h4.x; hs[1] = h4.y; hs[2] = h4.z; hs[3] = h4.w;
+      vs[0] = v4.x; vs[1] = v4.y; vs[2] = v4.z; vs[3] = v4.w;
+      As[0] = a4.x; As[1] = a4.y; As[2] = a4.z; As[3] = a4.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Bs[j] = T::widen(T::load(p.B, b * N + n0 + j));
+        Cs[j] = T::widen(T::load(p.C, b * N + n0 + j));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hs[j] = vs[j] = As[j] = Bs[j] = Cs[j] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool on = n0 + j < N;
+      hs[j] = on ? hp[j] : 0.f;
+      vs[j] = on ? vp[j] : 0.f;
+      As[j] = on ? p.A[d * N + n0 + j] : 0.f;
+      Bs[j] = on ? T::widen(T::load(p.B, b * N + n0 + j)) : 0.f;
+      Cs[j] = on ? T::widen(T::load(p.C, b * N + n0 + j)) : 0.f;
+    }
+  }
+
+  float ys = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = exp2_fast(de * (As[j] * kLog2e));
+    vs[j] = fmaf(p.beta, vs[j], c * Bs[j]);
+    hs[j] = fmaf(a, hs[j], vs[j]);
+    ys = fmaf(Cs[j], hs[j], ys);  // padding states have C = 0
+  }
+
+  if (valid) {
+    if (VEC) {
+      if (n0 < N) {
+        *reinterpret_cast<float4*>(hp) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+        *reinterpret_cast<float4*>(vp) = make_float4(vs[0], vs[1], vs[2], vs[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (n0 + j < N) {
+          hp[j] = hs[j];
+          vp[j] = vs[j];
+        }
+      }
+    }
+  }
+
+  // readout: sum over the G lanes of the channel (groups are aligned inside the wavefront)
+  for (int m = G >> 1; m > 0; m >>= 1) ys += __shfl_xor(ys, m, 64);
+  if (valid && q == 0) {
+    float yv = p.Dskip ? fmaf(p.Dskip[d], xv, ys) : ys;
+    if (p.z) yv *= silu_f(T::widen(T::load(p.z, pr)));
+    T::store(p.y, pr, yv);
+  }
+}
+
+template <typename IO>
+hipError_t launch_io(const StepArgs& a, bool vec, hipStream_t s) {
+  const int64_t threads = a.Bt * a.D * a.G;
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (vec)
+    hipLaunchKernelGGL((step_kernel<IO, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel<IO, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs& a, int io_bf16, bool vec, hipStream_t s) {
+  return io_bf16 ? launch_io<bf16_storage>(a, vec, s) : launch_io<float>(a, vec, s);
+}
+
+}  // namespace msm

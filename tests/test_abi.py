@@ -217,6 +217,30 @@ def test_fused_entry_points_validation_never_launches(lib):
     assert bwd(N=33, sp=1) == UNSUPPORTED
 
 
+def test_step_validation_never_launches(lib):
+    P = ctypes.c_void_p
+
+    def step(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
+                 bias=None, sp=0, h=0x100000, v=0x200000, y=0x300000, Bt=2, D=4, N=4)
+        a.update(kw)
+        return lib.msm_scan_step(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
+                                 P(a["Dskip"]), P(a["z"]), P(a["bias"]), a["sp"], P(a["h"]),
+                                 P(a["v"]), P(a["y"]), a["Bt"], a["D"], a["N"],
+                                 ctypes.c_float(0.5), ctypes.c_float(1.0), 0, None)
+
+    # states: 2*4*4 floats = 128 bytes
+    assert step(h=None) == INVALID
+    assert step(y=None) == INVALID
+    assert step(Bt=0) == INVALID
+    assert step(N=65) == UNSUPPORTED
+    assert step(sp=3) == INVALID
+    assert step(v=0x100000 + 64) == INVALID        # h and v overlapping
+    assert step(h=0x1000) == INVALID               # a state over an input
+    assert step(y=0x200000 + 8) == INVALID         # y over a state
+    assert step(z=0x100000) == INVALID             # the gate over a state
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msm, "_lib", None)
     monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))

@@ -16,6 +16,11 @@ Distributions (one recipe per named workload):
              (forward; long enough that the sequence is split into chunks).
 * ``bwd``    Bt=4, L=2048,  D=2048, N=16, fp32 I/O, beta=0.9, alpha=1, plus dy ~ N(0,1)
              (backward).
+* ``decode`` Bt=1024, L=1,  D=4096, N=16, bf16 I/O, beta=0.9, alpha=1, Dskip ~ N(0,1): one
+             token of the Mamba-1.4B layer shape for a serving batch of 1024 sequences, with
+             (Bt, D, N) fp32 ssm / velocity states ~ N(0,1) (``make_state``) and the fused op's
+             extras (``make_fused_extras``).  Large enough that the states (2 x 268 MB) do not
+             stay in the last-level cache between steps.
 
 Draws are made in float64 with ``numpy.random.Generator(PCG64(seed))``, cast to float32, and for
 bf16 workloads rounded once to bfloat16 (round-to-nearest-even) on the host.  Arrays are always
@@ -42,7 +47,7 @@ class Workload:
     beta: float
     alpha: float
     dskip: bool
-    direction: str     # "fwd" or "bwd"
+    direction: str     # "fwd", "bwd" or "step" (one decode token)
     delta_dist: str    # "loguniform" or "softplus"
     seed: int
 
@@ -60,6 +65,8 @@ WORKLOADS = {
     "m1p4b": Workload("m1p4b", 4, 4096, 4096, 16, "bf16", 0.9, 1.0, False, "fwd", "softplus", 1003),
     "long": Workload("long", 1, 65536, 2048, 16, "bf16", 0.95, 0.5, True, "fwd", "softplus", 1004),
     "bwd": Workload("bwd", 4, 2048, 2048, 16, "f32", 0.9, 1.0, False, "bwd", "softplus", 1005),
+    "decode": Workload("decode", 1024, 1, 4096, 16, "bf16", 0.9, 1.0, True, "step", "softplus",
+                       1006),
 }
 
 
@@ -161,3 +168,17 @@ def make_fused_extras(w: Workload, seed: int, softplus: bool = True) -> dict:
     if w.io == "bf16":
         raw, z = round_to_bf16(raw), round_to_bf16(z)
     return dict(delta_raw=raw, delta_bias=bias, z=z, softplus=softplus)
+
+
+def make_step_inputs(w: Workload, seed: int | None = None, softplus: bool = True) -> dict:
+    """Inputs of one decode step for workload ``w`` (L is ignored): x, raw delta, z (Bt, D);
+    B, C (Bt, N); A, Dskip, delta_bias; states h, v (Bt, D, N) ~ N(0, 1).  Recipes as in
+    ``make_inputs``, ``make_fused_extras`` and ``make_state``."""
+    s0 = w.seed if seed is None else seed
+    w1 = w.replace(L=1)
+    inp = make_inputs(w1, a_kind="s4d", seed=s0, with_dy=False)
+    ex = make_fused_extras(w1, s0 + 11, softplus=softplus)
+    h, v = make_state(w1, s0 + 13)
+    return dict(x=inp["x"][:, 0], delta=ex["delta_raw"][:, 0], z=ex["z"][:, 0], B=inp["B"][:, 0],
+                C=inp["C"][:, 0], A=inp["A"], Dskip=inp["Dskip"], delta_bias=ex["delta_bias"],
+                softplus=softplus, h=h, v=v, beta=inp["beta"], alpha=inp["alpha"], io=w.io)
