@@ -180,8 +180,7 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
  * required exactly when z is given and ddelta_bias ((D,) fp32, summed over batch and time)
  * exactly when delta_bias is given.  The output before the gate, which dz needs, is recomputed
  * inside: nothing from the forward is saved.  With z, delta_bias NULL and delta_softplus 0
- * this is msm_scan_bwd_state.  The fused variant (any of z, delta_bias, delta_softplus) is
- * built for N <= 16; for larger N it returns MSM_ERR_UNSUPPORTED. */
+ * this is msm_scan_bwd_state. */
 msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,
                                   const float* delta_bias, int32_t delta_softplus, const void* dy,

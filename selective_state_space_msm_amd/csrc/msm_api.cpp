@@ -368,8 +368,6 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
     }
     if (plan->chunks != 0 && plan->chunks != 1) return MSM_ERR_UNSUPPORTED;
   }
-  // the fused variant of the 64-state backward is not built
-  if (ext && NP == 64) return MSM_ERR_UNSUPPORTED;
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);

@@ -5,6 +5,10 @@
 // states and a workgroup of 16 wavefronts covers the 64 states.  The sums over channels for
 // dB / dC use a butterfly reduce-scatter over the 64 lanes; dx / ddelta sum the 16 wavefront
 // partials through LDS in a fixed order.  Partials go through the shared finalize kernel.
+// The fused variant (EXT: delta bias + softplus, SiLU gate) re-forms delta_eff and the gated dy
+// from the raw inputs wherever they are read, adds the wavefront partials of the pre-gate
+// output C . h for dz, and sums the bias gradient per channel; it works in rounds of 4 rows
+// so that the extra partials fit in LDS.
 #include "msm_device.hpp"
 #include "msm_internal.h"
 
@@ -44,7 +48,7 @@ __device__ __forceinline__ void reduce_scatter64(float (&v)[M], int lane) {
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP>
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, bool EXT>
 __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   constexpr int NTHR = S * kWave;
   constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
   // rows whose per-wavefront partials sit in LDS at once (fp64, so fewer rows for big S)
-  constexpr int SR = S >= 16 ? 8 : TB;
+  constexpr int SR = EXT ? 4 : (S >= 16 ? 8 : TB);
   constexpr int NSR = TB / SR;
   // steps per lane-reduce block of dB/dC values (at most 64 values per block)
   constexpr int RB = (64 / (2 * K)) < SR ? (64 / (2 * K)) : SR;
@@ -65,6 +69,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   __shared__ float bcs[TB][S][BCW];       // fp32 B (alpha-scaled) | C, for the recompute
   __shared__ double bcs64[TB][S][BCW];    // the same values widened, for the adjoint sweep
   __shared__ double spart[2][S][SR][kWave];
+  __shared__ float ypart[EXT ? S : 1][EXT ? SR : 1][kWave];  // fused: partials of C . h
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -90,6 +95,17 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
     v[j] = (p.v0 && n < N) ? p.v0[si] : 0.f;
     h[j] = (p.h0 && n < N) ? p.h0[si] : 0.f;
   }
+  // fused extras of this lane's channel
+  const float dbias = (EXT && p.delta_bias) ? p.delta_bias[dl] : 0.f;
+  const bool softplus = EXT && p.delta_softplus != 0;
+  const bool has_z = EXT && p.z != nullptr;
+  auto delta_eff = [&](float dv) {
+    if (!EXT) return dv;
+    const float u = dv + dbias;
+    return softplus ? softplus_f(u) : u;
+  };
+  // dy as the scan sees it: gated by silu(z)
+  auto gated = [&](float gy, raw zr) { return has_z ? gy * silu_f(T::widen(zr)) : gy; };
 
   auto stage = [&](int64_t ts, int64_t nv) {
 #pragma unroll
@@ -142,7 +158,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       if (tt < nv) {
-        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
+        const float xv = T::widen(xr[tt]), dv = delta_eff(T::widen(dr[tt]));
         const float c = dv * xv;
         const float* bc = &bcs[tt][g][0];
 #pragma unroll
@@ -170,13 +186,14 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
     dAacc[j] = 0.0;
   }
   float dDacc = 0.f;
+  double dbias64 = 0.0;  // fused: this lane's rows of the channel's bias gradient
   const float dsk = HAS_DSKIP ? p.Dskip[dl] : 0.f;
   float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * p.NP;
 
   for (int64_t tile = NT - 1; tile >= 0; --tile) {
     const int64_t ts = tile * TB;
     const int nv = (int)((L - ts < TB) ? L - ts : TB);
-    raw xr[TB], dr[TB], gr[TB];
+    raw xr[TB], dr[TB], gr[TB], zr[EXT ? TB : 1];
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       const int64_t t = ts + (tt < nv ? tt : nv - 1);
@@ -184,6 +201,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
       xr[tt] = T::load(p.x, idx);
       dr[tt] = T::load(p.delta, idx);
       gr[tt] = T::load(p.dy, idx);
+      if (EXT) zr[EXT ? tt : 0] = has_z ? T::load(p.z, idx) : raw{};
     }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       if (tt < nv) {
-        const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]);
+        const float xv = T::widen(xr[tt]), dv = delta_eff(T::widen(dr[tt]));
         const float c = dv * xv;
         const float* bc = &bcs[tt][g][0];
 #pragma unroll
@@ -234,8 +252,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
           const int tr = rb * RB + tb;  // row within the round
           const int tt = sr * SR + tr;  // row within the tile
           if (tt < nv) {
-            const float xv = T::widen(xr[tt]), dv = T::widen(dr[tt]), gy = T::widen(gr[tt]);
+            const float xv = T::widen(xr[tt]), dv = delta_eff(T::widen(dr[tt]));
+            const float gy = EXT ? gated(T::widen(gr[tt]), zr[EXT ? tt : 0]) : T::widen(gr[tt]);
             const float c = dv * xv;
+            float yq = 0.f;
             const double gy64 = gy, dv64 = dv;
             const double* bc = &bcs64[tt][g][0];
             double s1 = 0.0, s2 = 0.0;
@@ -250,11 +270,13 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
               dAacc[j] = fma(dv64, gg, dAacc[j]);
               vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
               vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
+              if (EXT) yq = fmaf(bcs[tt][g][K + j], hs[tt + 1][j], yq);
               ghn[j] = a64 * gh;
               gvn[j] = BETA0 ? 0.0 : beta64 * gv;
             }
             spart[0][g][tr][lane] = s1;
             spart[1][g][tr][lane] = s2;
+            if (EXT) ypart[EXT ? g : 0][EXT ? tr : 0][lane] = yq;
             if (HAS_DSKIP) dDacc = fmaf(gy, xv, dDacc);
           } else {
 #pragma unroll
@@ -291,11 +313,35 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
         }
         if (dvalid) {
           const int64_t idx = (b * L + ts + tt) * D + d;
-          const double xv = T::widen(T::load(p.x, idx)), dv = T::widen(T::load(p.delta, idx));
-          double dxv = dv * s1;
-          if (HAS_DSKIP) dxv = fma((double)dsk, (double)T::widen(T::load(p.dy, idx)), dxv);
-          T::store(p.dx, idx, (float)dxv);
-          T::store(p.ddelta, idx, (float)fma(xv, s1, s2));
+          if (!EXT) {
+            const double xv = T::widen(T::load(p.x, idx)), dv = T::widen(T::load(p.delta, idx));
+            double dxv = dv * s1;
+            if (HAS_DSKIP) dxv = fma((double)dsk, (double)T::widen(T::load(p.dy, idx)), dxv);
+            T::store(p.dx, idx, (float)dxv);
+            T::store(p.ddelta, idx, (float)fma(xv, s1, s2));
+          } else {
+            const float xf = T::widen(T::load(p.x, idx)), draw = T::widen(T::load(p.delta, idx));
+            const float gyr = T::widen(T::load(p.dy, idx));
+            const float zv = has_z ? T::widen(T::load(p.z, idx)) : 0.f;
+            const float gy = has_z ? gyr * silu_f(zv) : gyr;
+            const double xv = xf, dv = delta_eff(draw);
+            double dxv = dv * s1;
+            if (HAS_DSKIP) dxv = fma((double)dsk, (double)gy, dxv);
+            T::store(p.dx, idx, (float)dxv);
+            // through softplus: d softplus(u) / du = logistic(u)
+            const double dsp = softplus ? (double)logistic_f(draw + dbias).s : 1.0;
+            const double qd = fma(xv, s1, s2) * dsp;
+            T::store(p.ddelta, idx, (float)qd);
+            dbias64 += qd;
+            if (has_z) {
+              // dz from the pre-gate output: the wavefront partials plus the skip term
+              float yr = ypart[0][EXT ? tr : 0][lane];
+#pragma unroll
+              for (int gg = 1; gg < S; ++gg) yr += ypart[EXT ? gg : 0][EXT ? tr : 0][lane];
+              if (HAS_DSKIP) yr = fmaf(dsk, xf, yr);
+              T::store(p.dz, idx, gyr * silu_grad_f(zv) * yr);
+            }
+          }
         }
       }
       if (NSR > 1) __syncthreads();  // spart is reused by the next round of this tile
@@ -320,24 +366,43 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
     }
     if (HAS_DSKIP && g == 0) p.dD_part[b * D + d] = dDacc;
   }
+  if (EXT && p.delta_bias) {
+    // the bias gradient of the channel: each wavefront holds the sum over its rows
+    __syncthreads();
+    spart[0][g][0][lane] = dbias64;
+    __syncthreads();
+    if (g == 0 && dvalid) {
+      double t = spart[0][0][0][lane];
+#pragma unroll
+      for (int gg = 1; gg < S; ++gg) t += spart[0][gg][0][lane];
+      p.dbias_part[b * D + d] = (float)t;
+    }
+  }
 }
 
-template <typename IO, bool BETA0>
+template <typename IO, bool BETA0, bool EXT>
 hipError_t launch_wide(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(16 * kWave);
   if (a.Dskip)
-    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, true, EXT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_wide_kernel<IO, 4, 16, BETA0, false, EXT>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <typename IO, bool BETA0>
+hipError_t launch_wide_ext(const BwdArgs& a, bool ext, hipStream_t s) {
+  return ext ? launch_wide<IO, BETA0, true>(a, s) : launch_wide<IO, BETA0, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, hipStream_t s) {
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, bool ext, hipStream_t s) {
   if (a.NP != 64) return hipErrorInvalidValue;
-  if (io_bf16) return beta0 ? launch_wide<bf16_storage, true>(a, s) : launch_wide<bf16_storage, false>(a, s);
-  return beta0 ? launch_wide<float, true>(a, s) : launch_wide<float, false>(a, s);
+  if (io_bf16)
+    return beta0 ? launch_wide_ext<bf16_storage, true>(a, ext, s)
+                 : launch_wide_ext<bf16_storage, false>(a, ext, s);
+  return beta0 ? launch_wide_ext<float, true>(a, ext, s) : launch_wide_ext<float, false>(a, ext, s);
 }
 
 }  // namespace msm

@@ -126,6 +126,6 @@ hipError_t launch_bwd_part_0_1(const BwdArgs& a, int K, bool beta0, hipStream_t 
 hipError_t launch_bwd_part_1_0(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd_part_1_1(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 // The 64-state backward (channel blocks of 64, K = 4); launch_bwd calls it for NP == 64.
-hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, hipStream_t s);
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, bool ext, hipStream_t s);
 
 }  // namespace msm

@@ -62,8 +62,7 @@ hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
 hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s) {
   hipError_t e;
   if (a.NP == 64) {
-    if (ext) return hipErrorInvalidValue;
-    e = launch_bwd_wide(a, io_bf16, beta0, s);
+    e = launch_bwd_wide(a, io_bf16, beta0, ext, s);
   } else if (io_bf16) {
     e = ext ? launch_bwd_part_1_1(a, K, beta0, s) : launch_bwd_part_1_0(a, K, beta0, s);
   } else {

@@ -213,8 +213,7 @@ def test_fused_entry_points_validation_never_launches(lib):
     assert bwd(z=0x7000, dz=0x7000 + 8) == INVALID  # dz over z
     assert bwd(bias=0x7000, dbias=0x100000 + 4) == INVALID  # bias gradient over dx
     assert bwd(sp=-1) == INVALID
-    # the fused backward is built for N <= 16
-    assert bwd(N=33, sp=1) == UNSUPPORTED
+    assert bwd(N=65, sp=1) == UNSUPPORTED
 
 
 def test_step_validation_never_launches(lib):

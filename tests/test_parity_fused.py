@@ -137,16 +137,13 @@ def test_state_counts(N):
     check(inp, tag="N=%d" % N)
 
 
-def test_many_states_forward():
-    # 33 states: the 64-state forward kernels; the fused backward for them is not built
-    import selective_state_space_msm_amd as msm
-    w = SMALL.replace(L=40, D=50, N=33, dskip=True)
-    inp = fused_inputs(w, 441)
-    g = to_device(inp)
-    compare(gpu_fwd(inp, g), oracle_fwd(inp), FWD_OUT, w.io, "fwd N=33")
-    with pytest.raises(msm.MsmError) as e:
-        gpu_bwd(inp, g)
-    assert e.value.status == 2
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [33, 64])
+def test_many_states(io, N):
+    # 64 padded states: the 64-state forward kernels and the full-wavefront backward
+    w = SMALL.replace(L=40, D=70, N=N, io=io, dskip=True)
+    check(fused_inputs(w, 441 + N), tag="N=%d" % N, state=True)
+    check(fused_inputs(w.replace(dskip=False, beta=0.0), 442 + N, softplus=False), tag="N=%d" % N)
 
 
 def test_plain_equivalence():
