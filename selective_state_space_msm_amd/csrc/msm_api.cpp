@@ -68,8 +68,11 @@ bool allowed_k(int NP, int K) {
 // Launch plan.  Measured on MI355X: the scan is VALU-bound, and two wavefronts per SIMD hide
 // each other's LDS, memory and scalar instructions, so the preferred plan keeps S = NP/K
 // wavefronts of few states each per 64-channel block when the channels alone give at least
-// one wavefront per SIMD.  Otherwise the sequence is cut into chunks of wavefronts with more
-// states each, until there are about two wavefronts per SIMD.
+// one wavefront per SIMD.  Otherwise the sequence is cut into chunks until there are a few
+// wavefronts per SIMD: shorter chunks shorten the sequential path of every wavefront, and the
+// extra summary work is small.  Measured on MI355X (Bt=1): L=65536 D=2048 N=16, 2 states per
+// wavefront: 16 chunks 1.34 ms, 8 chunks 1.49 ms (4 states, 16 chunks: 1.47 ms); L=16384
+// D=1024 N=16: 32 chunks best; N=4 and N=64 are best at about two wavefronts per SIMD.
 msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int NP = padded_states(N);
   const int64_t chan_blocks = Bt * ceil_div(D, kWave);
@@ -79,9 +82,10 @@ msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
     pl.states_per_wave = kpref;
     return pl;
   }
-  const int kchunk = NP == 4 ? 2 : (NP == 16 ? 4 : 8);
+  const int kchunk = NP == 4 ? 2 : (NP == 16 ? 2 : 8);
   const int64_t waves = chan_blocks * (NP / kchunk);
-  int64_t G = ceil_div(2 * kTargetWaves, waves);
+  const int per_simd = NP == 16 ? 4 : 2;
+  int64_t G = ceil_div(per_simd * kTargetWaves, waves);
   const int64_t gmax = fwd_max_chunks(Bt, L, D);
   if (G > gmax) G = gmax;
   if (G < 1) G = 1;
