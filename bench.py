@@ -115,19 +115,32 @@ def to_dev(inp):
     return d
 
 
-def bench_fwd(w, steps, warmup, stream):
+def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False):
+    """Time msm_scan_fwd on workload w (fused: msm_selective_scan_fwd with a delta bias,
+    softplus and the gate, on the raw-delta recipe of the fused op)."""
     import torch
     import selective_state_space_msm_amd as msm
-    inp = workloads.make_inputs(w)
+    inp = workloads.make_inputs(w, a_kind=a_kind, with_dy=False)
     g = to_dev(inp)
+    if fused:
+        ex = workloads.make_fused_extras(w, w.seed + 7)
+        dt = g["x"].dtype
+        g["delta"] = torch.from_numpy(ex["delta_raw"]).to("cuda").to(dt)
+        g["z"] = torch.from_numpy(ex["z"]).to("cuda").to(dt)
+        g["delta_bias"] = torch.from_numpy(ex["delta_bias"]).to("cuda")
     y = torch.empty_like(g["x"])
     nbytes = msm.msm_scan_fwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     plan = msm.msm_scan_fwd_plan(w.Bt, w.L, w.D, w.N, w.io, w.beta)
 
     def step():
-        msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta, w.alpha, g["Dskip"],
-                         y=y, workspace=ws, stream=stream)
+        if fused:
+            msm.msm_selective_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta,
+                                       w.alpha, g["Dskip"], z=g["z"], delta_bias=g["delta_bias"],
+                                       delta_softplus=True, y=y, workspace=ws, stream=stream)
+        else:
+            msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta, w.alpha,
+                             g["Dskip"], y=y, workspace=ws, stream=stream)
 
     ms, per = timed(step, stream, steps, warmup)
     return ms, per, plan
@@ -136,7 +149,7 @@ def bench_fwd(w, steps, warmup, stream):
 def bench_bwd(w, steps, warmup, stream):
     import torch
     import selective_state_space_msm_amd as msm
-    inp = workloads.make_inputs(w)
+    inp = workloads.make_inputs(w, with_dy=True)
     g = to_dev(inp)
     nbytes = msm.msm_scan_bwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
@@ -169,6 +182,34 @@ def bench_step(w, steps, warmup, stream):
                           delta_softplus=True, y=y, stream=stream)
 
     return timed(step, stream, steps, warmup)
+
+
+def bench_configs(steps, warmup, stream):
+    """Every other configuration the measurement plan lists, one line each: the forward at
+    each forward shape (both beta where listed), the forward with an unstructured A, the fused
+    forward, and the README benchmark shape forward and backward."""
+    W = workloads.WORKLOADS
+    runs = [("m130m", "fwd", {}, "s4d", False), ("m130m", "fwd", {"beta": 0.0}, "s4d", False),
+            ("m130m", "fwd", {}, "random", False), ("m1p4b", "fwd", {}, "random", False),
+            ("m1p4b", "fwd", {}, "s4d", True), ("long", "fwd", {}, "s4d", False),
+            ("pages", "fwd", {}, "s4d", False), ("pages", "fwd", {"beta": 0.0}, "s4d", False),
+            ("pages", "bwd", {}, "s4d", False), ("pages", "bwd", {"beta": 0.0}, "s4d", False)]
+    out = []
+    for name, direction, kw, a_kind, fused in runs:
+        w = W[name].replace(**kw)
+        if direction == "fwd":
+            ms, per, plan = bench_fwd(w, steps, warmup, stream, a_kind=a_kind, fused=fused)
+            nb = alg_bytes_fwd(w)
+        else:
+            ms, per, plan = bench_bwd(w, steps, warmup, stream)
+            nb = alg_bytes_bwd(w)
+        out.append({"workload": name, "direction": direction, "beta": w.beta, "A": a_kind,
+                    "fused_extras": fused, "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io,
+                    "ms": ms, "ms_min": min(per), "state_updates_per_s": w.updates / (ms / 1e3),
+                    "algorithmic_GBs": nb / (ms / 1e3) / 1e9, "plan": plan})
+        import torch
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -242,6 +283,8 @@ def main(argv=None):
                     choices=[k for k, v in workloads.WORKLOADS.items() if v.direction == "step"]
                     + ["none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (m130m, long, README shape, ...)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "NAME",
@@ -316,6 +359,16 @@ def main(argv=None):
                                       "frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS,
                                       "traffic": measured_traffic("step_%s" % ws_.name),
                                       "algorithmic_bytes": sbytes}}
+    # practical streaming rate of the box: a 1 GiB device-to-device copy (read + write),
+    # a second denominator next to the 8 TB/s peak
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    cms, _ = timed(lambda: dst.copy_(src), stream, 10, 3)
+    rec["hbm"]["copy_probe_GBs"] = 2 * src.numel() / (cms / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        rec["configs"] = bench_configs(max(5, args.steps // 2), max(3, args.warmup // 2), stream)
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

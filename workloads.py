@@ -16,6 +16,9 @@ Distributions (one recipe per named workload):
              (forward; long enough that the sequence is split into chunks).
 * ``bwd``    Bt=4, L=2048,  D=2048, N=16, fp32 I/O, beta=0.9, alpha=1, plus dy ~ N(0,1)
              (backward).
+* ``pages``  Bt=2, L=512, D=256, N=16, fp32 I/O, beta in {0, 0.9}, alpha=1: the shape of the
+             benchmark table in the Momentum Mamba README (batch 2, dim 256, seqlen 512,
+             dstate 16; its precision is not stated), distributions as ``m130m``.  Context only.
 * ``decode`` Bt=1024, L=1,  D=4096, N=16, bf16 I/O, beta=0.9, alpha=1, Dskip ~ N(0,1): one
              token of the Mamba-1.4B layer shape for a serving batch of 1024 sequences, with
              (Bt, D, N) fp32 ssm / velocity states ~ N(0,1) (``make_state``) and the fused op's
@@ -65,6 +68,7 @@ WORKLOADS = {
     "m1p4b": Workload("m1p4b", 4, 4096, 4096, 16, "bf16", 0.9, 1.0, False, "fwd", "softplus", 1003),
     "long": Workload("long", 1, 65536, 2048, 16, "bf16", 0.95, 0.5, True, "fwd", "softplus", 1004),
     "bwd": Workload("bwd", 4, 2048, 2048, 16, "f32", 0.9, 1.0, False, "bwd", "softplus", 1005),
+    "pages": Workload("pages", 2, 512, 256, 16, "f32", 0.9, 1.0, False, "fwd", "softplus", 1007),
     "decode": Workload("decode", 1024, 1, 4096, 16, "bf16", 0.9, 1.0, True, "step", "softplus",
                        1006),
 }
