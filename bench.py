@@ -244,7 +244,7 @@ def pmc_summary(fetch_csv, write_csv, kernel_substr, name, command):
     import csv
 
     def per_kernel(path, counter):
-        vals, copy = [], []
+        vals, copies = [], []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
@@ -252,8 +252,11 @@ def pmc_summary(fetch_csv, write_csv, kernel_substr, name, command):
             if kernel_substr in r["Kernel_Name"]:
                 vals.append(v)
             elif "copyBuffer" in r["Kernel_Name"]:
-                copy.append(v)
-        return vals, copy
+                copies.append((int(r["Grid_Size"]), v))
+        # the calibration copies are the largest copy dispatches of the run (small host-to-device
+        # staging copies use the same kernel)
+        big = max(g for g, _ in copies)
+        return vals, [v for g, v in copies if g == big]
 
     fk, fcopy = per_kernel(fetch_csv, "FETCH_SIZE")
     wk, wcopy = per_kernel(write_csv, "WRITE_SIZE")
@@ -346,7 +349,8 @@ def main(argv=None):
                                   % (wb.name, wb.Bt, wb.L, wb.D, wb.N, wb.io, wb.beta),
                       "ms_per_call": bms, "state_updates_per_s": wb.updates / (bms / 1e3),
                       "algorithmic_GBs": bbytes / (bms / 1e3) / 1e9,
-                      "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": bplan}
+                      "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": bplan,
+                      "traffic": measured_traffic("bwd_%s" % wb.name)}
     if args.step_workload != "none":
         ws_ = workloads.WORKLOADS[args.step_workload]
         sms, sper = bench_step(ws_, max(5, args.steps), max(2, args.warmup // 2), stream)
@@ -359,14 +363,16 @@ def main(argv=None):
                                       "frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS,
                                       "traffic": measured_traffic("step_%s" % ws_.name),
                                       "algorithmic_bytes": sbytes}}
-    # practical streaming rate of the box: a 1 GiB device-to-device copy (read + write),
-    # a second denominator next to the 8 TB/s peak
-    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    cms, _ = timed(lambda: dst.copy_(src), stream, 10, 3)
-    rec["hbm"]["copy_probe_GBs"] = 2 * src.numel() / (cms / 1e3) / 1e9
-    del src, dst
-    torch.cuda.empty_cache()
+    if not args.calib_copy:
+        # practical streaming rate of the box: a 1 GiB device-to-device copy (read + write),
+        # a second denominator next to the 8 TB/s peak (left out of counter runs, whose only
+        # copy must be the calibration copy)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        cms, _ = timed(lambda: dst.copy_(src), stream, 10, 3)
+        rec["hbm"]["copy_probe_GBs"] = 2 * src.numel() / (cms / 1e3) / 1e9
+        del src, dst
+        torch.cuda.empty_cache()
     if not args.no_configs:
         rec["configs"] = bench_configs(max(5, args.steps // 2), max(3, args.warmup // 2), stream)
     if args.calib_copy:
