@@ -75,11 +75,12 @@ class Oracle:
         lib.msm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Dbl, Dbl, I64, I64, I64,
                                        I64, P, P, P, P, P, P, P, P, Int]
         lib.msm_oracle_bwd.restype = Int
-        lib.msm_oracle_fused_fwd.argtypes = [P, P, P, P, P, P, P, P, Int, P, P, Dbl, Dbl, I64, I64,
-                                             I64, I64, P, P, P, P, Int]
+        lib.msm_oracle_fused_fwd.argtypes = [P, P, P, P, P, P, P, P, Int, Int, P, P, Dbl, Dbl, I64,
+                                             I64, I64, I64, P, P, P, P, Int]
         lib.msm_oracle_fused_fwd.restype = Int
-        lib.msm_oracle_fused_bwd.argtypes = [P, P, P, P, P, P, P, P, Int, P, P, P, P, P, Dbl, Dbl,
-                                             I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, Int]
+        lib.msm_oracle_fused_bwd.argtypes = [P, P, P, P, P, P, P, P, Int, Int, P, P, P, P, P, Dbl,
+                                             Dbl, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P,
+                                             Int]
         lib.msm_oracle_fused_bwd.restype = Int
         lib.msm_oracle_max_threads.argtypes = []
         lib.msm_oracle_max_threads.restype = Int
@@ -160,9 +161,10 @@ class Oracle:
         return out
 
     def fused_fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, z=None, delta_bias=None,
-                  delta_softplus=False, h0=None, v0=None, threads=0):
+                  delta_softplus=False, h0=None, v0=None, threads=0, zoh=False):
         """The fused op forward: delta_eff = softplus(delta + delta_bias) (or delta + delta_bias),
-        the momentum scan on delta_eff, then y = y_raw * silu(z).
+        the momentum scan on delta_eff (zoh: zero-order-hold write coefficient), then
+        y = y_raw * silu(z).
 
         Returns (y, y_raw, last_h, last_v) as float64; y_raw is the output before the gate.
         """
@@ -177,7 +179,7 @@ class Oracle:
         last_h, last_v = np.empty((Bt, D, N)), np.empty((Bt, D, N))
         rc = self.lib.msm_oracle_fused_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                            _ptr(Ds), _ptr(zz), _ptr(db), int(bool(delta_softplus)),
-                                           _ptr(h0), _ptr(v0), float(beta), float(alpha), Bt, L,
+                                           int(bool(zoh)), _ptr(h0), _ptr(v0), float(beta), float(alpha), Bt, L,
                                            D, N, _ptr(y), _ptr(y_raw), _ptr(last_h), _ptr(last_v),
                                            int(threads))
         if rc != 0:
@@ -185,7 +187,8 @@ class Oracle:
         return y, y_raw, last_h, last_v
 
     def fused_bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, z=None, delta_bias=None,
-                  delta_softplus=False, h0=None, v0=None, dlast_h=None, dlast_v=None, threads=0):
+                  delta_softplus=False, h0=None, v0=None, dlast_h=None, dlast_v=None, threads=0,
+                  zoh=False):
         """Gradients of the fused op.  Returns the dict of ``bwd`` (ddelta is the gradient of
         the raw delta) plus dz (None without z) and ddelta_bias (None without delta_bias)."""
         x, delta, A, B, C, dy = (_f64(a) for a in (x, delta, A, B, C, dy))
@@ -200,7 +203,7 @@ class Oracle:
                    dh0=np.empty((Bt, D, N)), dv0=np.empty((Bt, D, N)))
         rc = self.lib.msm_oracle_fused_bwd(
             _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds), _ptr(zz), _ptr(db),
-            int(bool(delta_softplus)), _ptr(dy), _ptr(st[0]), _ptr(st[1]), _ptr(st[2]),
+            int(bool(delta_softplus)), int(bool(zoh)), _ptr(dy), _ptr(st[0]), _ptr(st[1]), _ptr(st[2]),
             _ptr(st[3]), float(beta), float(alpha), Bt, L, D, N, _ptr(out["dx"]),
             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
             _ptr(out["dDskip"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
@@ -210,7 +213,7 @@ class Oracle:
         return out
 
     def step(self, x, delta, A, B, C, h, v, beta, alpha, Dskip=None, z=None, delta_bias=None,
-             delta_softplus=False):
+             delta_softplus=False, zoh=False):
         """One decode step (the README's ``step``: one token, the ssm and velocity states
         carried in and out).  x, delta, z: (Bt, D); B, C: (Bt, N); h, v: (Bt, D, N).  It is the
         fused forward over a sequence of length one started at (h, v).
@@ -223,7 +226,7 @@ class Oracle:
                                       Dskip=Dskip,
                                       z=None if z is None else _f64(z).reshape(Bt, 1, D),
                                       delta_bias=delta_bias, delta_softplus=delta_softplus,
-                                      h0=h, v0=v)
+                                      h0=h, v0=v, zoh=zoh)
         return y.reshape(Bt, D), hn, vn
 
 

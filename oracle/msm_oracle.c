@@ -58,6 +58,15 @@
  *   derivative of softplus is the logistic function), ddelta_eff without;
  *   ddelta_bias[d] = sum over b and t of ddelta.
  *
+ * Zero-order hold (the fused op's `zoh` switch): the write coefficient delta of the first-order
+ * form becomes g = (exp(delta A) - 1) / A, the exact discretisation Bbar = (Abar - 1) A^{-1} B of
+ * the glossary page and of the complextorch page ("The diagonal SSM"), with g = delta at A = 0:
+ *     v_t = beta v_{t-1} + alpha g_t B_t x_t.
+ * Its derivatives: dg/ddelta = exp(delta A) = a and dg/dA = (delta a - g) / A, which is
+ * delta^2 (1/2 + u/3 + u^2/8 + u^3/30 + ...) with u = delta A (used for |u| < 1e-3).  The
+ * backward then reads dx += alpha g B gv, ddelta += alpha B x gv a + A a h gh,
+ * dA += delta a h gh + alpha B x gv dg/dA, dB += alpha g x gv.
+ *
  * Threads: the forward is split over (b, d) channel pairs, which are independent.  The
  * backward is split over batch rows b; dA and dDskip are first summed per row and the rows are
  * then added in order, so results do not depend on the thread count.
@@ -86,12 +95,49 @@ int msm_oracle_max_threads(void) {
 #endif
 }
 
+/* Write coefficient of the update: delta (first-order) or (exp(delta A) - 1) / A (zero-order
+ * hold, delta at A = 0), and its derivatives with respect to delta and A. */
+static double write_coef(double dt, double An, int zoh) {
+  if (!zoh) return dt;
+  return An == 0.0 ? dt : expm1(dt * An) / An;
+}
+
+static double write_coef_ddelta(double dt, double An, int zoh) {
+  return zoh ? exp(dt * An) : 1.0;
+}
+
+static double write_coef_dA(double dt, double An, int zoh) {
+  if (!zoh) return 0.0;
+  double u = dt * An;
+  if (fabs(u) < 1e-3) return dt * dt * (0.5 + u / 3.0 + u * u / 8.0 + u * u * u / 30.0);
+  return (dt * exp(u) - expm1(u) / An) / An;
+}
+
+static int fwd_core(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* Dskip, const double* h0, const double* v0,
+                    double beta, double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                    double* y, double* last_h, double* last_v, int zoh, int nthreads);
+static int bwd_core(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* Dskip, const double* dy, const double* h0,
+                    const double* v0, const double* dlast_h, const double* dlast_v, double beta,
+                    double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
+                    double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
+                    double* dh0, double* dv0, int zoh, int nthreads);
+
 /* Momentum recurrence, forward.  last_h / last_v, h0 / v0 and Dskip may be NULL (a NULL
  * initial state is zero). */
 int msm_oracle_fwd(const double* x, const double* delta, const double* A, const double* B,
                    const double* C, const double* Dskip, const double* h0, const double* v0,
                    double beta, double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N,
                    double* y, double* last_h, double* last_v, int nthreads) {
+  return fwd_core(x, delta, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, y, last_h, last_v,
+                  0, nthreads);
+}
+
+static int fwd_core(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* Dskip, const double* h0, const double* v0,
+                    double beta, double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                    double* y, double* last_h, double* last_v, int zoh, int nthreads) {
   if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
   set_threads(nthreads);
   int64_t nchan = Bt * D;
@@ -106,7 +152,8 @@ int msm_oracle_fwd(const double* x, const double* delta, const double* A, const 
         double dt = delta[(b * L + t) * D + d];
         double xt = x[(b * L + t) * D + d];
         double a = exp(dt * A[d * N + n]);
-        double w = alpha * (dt * B[(b * L + t) * N + n] * xt);
+        double g = write_coef(dt, A[d * N + n], zoh);
+        double w = alpha * (g * B[(b * L + t) * N + n] * xt);
         v = beta * v + w;
         h = a * h + v;
         y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * h;
@@ -160,6 +207,16 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
                    double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
                    double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
                    double* dh0, double* dv0, int nthreads) {
+  return bwd_core(x, delta, A, B, C, Dskip, dy, h0, v0, dlast_h, dlast_v, beta, alpha, Bt, L, D,
+                  N, dx, ddelta, dA, dB, dC, dDskip, dh0, dv0, 0, nthreads);
+}
+
+static int bwd_core(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* Dskip, const double* dy, const double* h0,
+                    const double* v0, const double* dlast_h, const double* dlast_v, double beta,
+                    double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
+                    double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
+                    double* dh0, double* dv0, int zoh, int nthreads) {
   if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
   if (Dskip && !dDskip) return 1;
   set_threads(nthreads);
@@ -193,7 +250,8 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
           double dt = delta[(b * L + t) * D + d];
           double xt = x[(b * L + t) * D + d];
           double a = exp(dt * An);
-          v = beta * v + alpha * (dt * B[(b * L + t) * N + n] * xt);
+          double g = write_coef(dt, An, zoh);
+          v = beta * v + alpha * (g * B[(b * L + t) * N + n] * xt);
           h = a * h + v;
           hs[t + 1] = h;
         }
@@ -208,10 +266,12 @@ int msm_oracle_bwd(const double* x, const double* delta, const double* A, const 
           double gv = gh + beta * gv_next;
           if (t == L - 1 && dlast_v) gv += dlast_v[s_i];
           double hprev = hs[t]; /* h_{t-1} */
-          dx[i] += alpha * dt * B[j] * gv;
-          ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gh;
-          dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh;
-          dB[j] += alpha * dt * xt * gv;
+          double g = write_coef(dt, An, zoh);
+          double gd = write_coef_ddelta(dt, An, zoh), gA = write_coef_dA(dt, An, zoh);
+          dx[i] += alpha * g * B[j] * gv;
+          ddelta[i] += alpha * B[j] * xt * gv * gd + An * a * hprev * gh;
+          dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh + alpha * B[j] * xt * gv * gA;
+          dB[j] += alpha * g * xt * gv;
           dC[j] += dyt * hs[t + 1];
           gh_next = gh;
           gv_next = gv;
@@ -280,7 +340,7 @@ static void effective_delta(const double* delta, const double* delta_bias, int d
  * last_v may be NULL. */
 int msm_oracle_fused_fwd(const double* x, const double* delta, const double* A, const double* B,
                          const double* C, const double* Dskip, const double* z,
-                         const double* delta_bias, int delta_softplus, const double* h0,
+                         const double* delta_bias, int delta_softplus, int zoh, const double* h0,
                          const double* v0, double beta, double alpha, int64_t Bt, int64_t L,
                          int64_t D, int64_t N, double* y, double* y_raw, double* last_h,
                          double* last_v, int nthreads) {
@@ -290,8 +350,8 @@ int msm_oracle_fused_fwd(const double* x, const double* delta, const double* A, 
   double* yr = (double*)malloc(sizeof(double) * nxd + 1);
   if (!de || !yr) { free(de); free(yr); return 2; }
   effective_delta(delta, delta_bias, delta_softplus, Bt, L, D, de);
-  int rc = msm_oracle_fwd(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, last_h,
-                          last_v, nthreads);
+  int rc = fwd_core(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, last_h, last_v,
+                    zoh, nthreads);
   if (rc == 0) {
     for (size_t i = 0; i < nxd; ++i) {
       if (y_raw) y_raw[i] = yr[i];
@@ -308,7 +368,7 @@ int msm_oracle_fused_fwd(const double* x, const double* delta, const double* A, 
  * is required when z is given, ddelta_bias when delta_bias is given. */
 int msm_oracle_fused_bwd(const double* x, const double* delta, const double* A, const double* B,
                          const double* C, const double* Dskip, const double* z,
-                         const double* delta_bias, int delta_softplus, const double* dy,
+                         const double* delta_bias, int delta_softplus, int zoh, const double* dy,
                          const double* h0, const double* v0, const double* dlast_h,
                          const double* dlast_v, double beta, double alpha, int64_t Bt, int64_t L,
                          int64_t D, int64_t N, double* dx, double* ddelta, double* dA,
@@ -325,8 +385,8 @@ int msm_oracle_fused_bwd(const double* x, const double* delta, const double* A, 
   int rc = 0;
   if (z) {
     /* the gate's backward needs the output before the gate */
-    rc = msm_oracle_fwd(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, NULL, NULL,
-                        nthreads);
+    rc = fwd_core(x, de, A, B, C, Dskip, h0, v0, beta, alpha, Bt, L, D, N, yr, NULL, NULL, zoh,
+                  nthreads);
     for (size_t i = 0; rc == 0 && i < nxd; ++i) {
       ge[i] = dy[i] * silu(z[i]);
       dz[i] = dy[i] * yr[i] * silu_grad(z[i]);
@@ -335,8 +395,8 @@ int msm_oracle_fused_bwd(const double* x, const double* delta, const double* A, 
     memcpy(ge, dy, sizeof(double) * nxd);
   }
   if (rc == 0)
-    rc = msm_oracle_bwd(x, de, A, B, C, Dskip, ge, h0, v0, dlast_h, dlast_v, beta, alpha, Bt, L,
-                        D, N, dx, ddelta, dA, dB, dC, dDskip, dh0, dv0, nthreads);
+    rc = bwd_core(x, de, A, B, C, Dskip, ge, h0, v0, dlast_h, dlast_v, beta, alpha, Bt, L, D, N,
+                  dx, ddelta, dA, dB, dC, dDskip, dh0, dv0, zoh, nthreads);
   if (rc == 0) {
     if (delta_softplus)
       for (size_t i = 0; i < nxd; ++i)

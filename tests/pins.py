@@ -16,6 +16,7 @@ import os
 
 import numpy as np
 import scipy.signal
+import scipy.integrate
 import scipy.special
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -632,10 +633,109 @@ def pin_step_sequence(orc):
     close(y[0, 0], 4.5, what="single readout")
 
 
+
+# ---------------------------------------------------------------------------------------------
+# Zero-order hold: Bbar = (Abar - 1) A^{-1} B (glossary page; complextorch, "The diagonal SSM")
+# ---------------------------------------------------------------------------------------------
+
+def pin_zoh_ode(orc):
+    """beta = 0, alpha = 1 with the zero-order hold samples the continuous system
+    h' = A h + B_t x_t exactly when the input is held over each step: a high-accuracy ODE
+    integration (scipy.integrate.solve_ivp, DOP853) over the same piecewise-constant input."""
+    rng = np.random.default_rng(59)
+    L, N = 7, 3
+    A = np.array([-0.7, -2.5, 0.3])
+    dts = np.exp(rng.uniform(np.log(0.05), np.log(0.8), size=L))
+    xs = rng.standard_normal(L)
+    Bm, Cm = rng.standard_normal((L, N)), rng.standard_normal((L, N))
+    h0 = rng.standard_normal(N)
+    h = h0.copy()
+    want = np.zeros(L)
+    for t in range(L):
+        sol = scipy.integrate.solve_ivp(lambda _s, hh, t=t: A * hh + Bm[t] * xs[t], (0.0, dts[t]), h,
+                                        method="DOP853", rtol=1e-13, atol=1e-14)
+        h = sol.y[:, -1]
+        want[t] = Cm[t] @ h
+    y, _, lh, _ = orc.fused_fwd(xs.reshape(1, L, 1), dts.reshape(1, L, 1), A.reshape(1, N),
+                                Bm.reshape(1, L, N), Cm.reshape(1, L, N), 0.0, 1.0, zoh=True,
+                                h0=h0.reshape(1, 1, N), v0=np.zeros((1, 1, N)))
+    close(y[0, :, 0], want, rtol=1e-9, atol=1e-11, what="zero-order hold vs ODE")
+    close(lh[0, 0], h, rtol=1e-9, atol=1e-11, what="zero-order hold final state")
+
+
+def pin_zoh_retention_gate_table(orc):
+    """The glossary's retention-gate table with the zero-order hold itself (A = -1, B = 1, a
+    state of 1 carried in, x = 3): delta = ln 2 gives 2, delta = ln 4 gives 2.5."""
+    g = golden("retention_gate_table.json")
+    for case in g["cases"]:
+        dt = num(case["delta"])
+        _, _, lh, _ = orc.fused_fwd(np.full((1, 1, 1), float(g["held_input"])),
+                                    np.full((1, 1, 1), dt), np.full((1, 1), float(g["A"])),
+                                    np.ones((1, 1, 1)), np.ones((1, 1, 1)), 0.0, 1.0, zoh=True,
+                                    h0=np.full((1, 1, 1), float(g["prev_state"])),
+                                    v0=np.zeros((1, 1, 1)))
+        close(lh[0, 0, 0], case["state"], rtol=1e-12, atol=1e-12,
+              what="zero-order hold table row %s" % case["delta"])
+
+
+def pin_zoh_limit(orc):
+    """A = 0 makes the zero-order hold coefficient delta exactly (the first-order form); a tiny
+    A differs from it only at second order."""
+    rng = np.random.default_rng(61)
+    Bt, L, D, N = 2, 9, 3, 2
+    x, delta, _, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    A0 = np.zeros((D, N))
+    y0, _, _, _ = orc.fused_fwd(x, delta, A0, B, C, 0.8, 0.9, Dskip=Ds, zoh=True)
+    y1, _, _ = orc.fwd(x, delta, A0, B, C, 0.8, 0.9, Dskip=Ds)
+    close(y0, y1, rtol=0, atol=0, what="zero-order hold at A = 0")
+    At = np.full((D, N), -1e-9)
+    y2, _, _, _ = orc.fused_fwd(x, delta, At, B, C, 0.8, 0.9, Dskip=Ds, zoh=True)
+    close(y2, y1, rtol=1e-7, atol=1e-9, what="zero-order hold at tiny A")
+
+
+def pin_zoh_finite_differences(orc):
+    """Central differences of the zero-order-hold loss for every input, including steps where
+    delta A is small enough for the series form of dg/dA."""
+    rng = np.random.default_rng(67)
+    Bt, L, D, N = 2, 5, 3, 2
+    beta, alpha = 0.7, 0.9
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    A[0, 0] = -3e-4                    # delta A below 1e-3: the series branch
+    h0, v0 = _rand_state(rng, Bt, D, N)
+    dy = rng.standard_normal((Bt, L, D))
+    dlh, dlv = _rand_state(rng, Bt, D, N)
+    p = dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Ds, z=None, bias=None, h0=h0, v0=v0)
+    g = orc.fused_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds, h0=h0, v0=v0, dlast_h=dlh,
+                      dlast_v=dlv, zoh=True)
+
+    def loss():
+        y, _, lh, lv = orc.fused_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], beta, alpha,
+                                     Dskip=p["Dskip"], h0=p["h0"], v0=p["v0"], zoh=True)
+        return float(np.sum(dy * y) + np.sum(dlh * lh) + np.sum(dlv * lv))
+
+    eps = 1e-6
+    for pname, gname in [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
+                         ("Dskip", "dDskip"), ("h0", "dh0"), ("v0", "dv0")]:
+        arr = p[pname]
+        for i in np.ndindex(arr.shape):
+            orig = arr[i]
+            arr[i] = orig + eps
+            lp = loss()
+            arr[i] = orig - eps
+            lm = loss()
+            arr[i] = orig
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname][i]
+            if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                raise AssertionError("zero-order hold finite difference mismatch for %s%s: "
+                                     "fd %.9g analytic %.9g" % (gname, i, fd, an))
+
+
 ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
             pin_beta0_equivalence, pin_structure, pin_finite_differences,
             pin_scaling_identities, pin_bwd_beta0_alpha0, pin_initial_state_filter,
             pin_continuation, pin_state_finite_differences, pin_bwd_continuation,
             pin_fused_delta_transform, pin_fused_gate, pin_fused_finite_differences,
-            pin_step_sequence]
+            pin_step_sequence, pin_zoh_ode, pin_zoh_retention_gate_table, pin_zoh_limit,
+            pin_zoh_finite_differences]

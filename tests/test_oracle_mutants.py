@@ -16,7 +16,7 @@ MUTANTS = [
     ("fwd_velocity_reads_h", "v = beta * v + w;", "v = beta * h + w;", 0),
     ("fwd_h_skips_velocity", "h = a * h + v;", "h = a * h + w;", 0),
     ("fwd_exp_sign", "double a = exp(dt * A[d * N + n]);", "double a = exp(-dt * A[d * N + n]);", 0),
-    ("fwd_write_drops_delta", "double w = alpha * (dt * B[(b * L + t) * N + n] * xt);",
+    ("fwd_write_drops_delta", "double w = alpha * (g * B[(b * L + t) * N + n] * xt);",
      "double w = alpha * (B[(b * L + t) * N + n] * xt);", 0),
     ("fwd_reads_velocity", "y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * h;",
      "y[(b * L + t) * D + d] += C[(b * L + t) * N + n] * v;", 0),
@@ -29,17 +29,17 @@ MUTANTS = [
      "h = exp(dt * A[d * N + n]) * h + B[(b * L + t) * N + n] * xt;", 0),
     ("bwd_velocity_adjoint_pure_decay", "double gv = gh + beta * gv_next;",
      "double gv = C[j] * dyt + beta * gv_next;", 0),
-    ("bwd_exp_path_uses_gv", "ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gh;",
-     "ddelta[i] += alpha * B[j] * xt * gv + An * a * hprev * gv;", 0),
+    ("bwd_exp_path_uses_gv", "ddelta[i] += alpha * B[j] * xt * gv * gd + An * a * hprev * gh;",
+     "ddelta[i] += alpha * B[j] * xt * gv * gd + An * a * hprev * gv;", 0),
     ("bwd_dC_off_by_one", "dC[j] += dyt * hs[t + 1];", "dC[j] += dyt * hs[t];", 0),
     ("bwd_hprev_off_by_one", "double hprev = hs[t];", "double hprev = hs[t + 1];", 0),
-    ("bwd_dA_drops_a", "dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh;",
-     "dA_rows[(b * D + d) * N + n] += dt * hprev * gh;", 0),
+    ("bwd_dA_drops_a", "dA_rows[(b * D + d) * N + n] += dt * a * hprev * gh",
+     "dA_rows[(b * D + d) * N + n] += dt * hprev * gh", 0),
     ("bwd_gh_uses_a_t", "double gh = C[j] * dyt + a_next * gh_next;",
      "double gh = C[j] * dyt + a * gh_next;", 0),
     ("bwd_skip_dx_uses_x", "dx[i] += Dskip[d] * dy[i];", "dx[i] += Dskip[d] * x[i];", 0),
-    ("bwd_dB_uses_gh", "dB[j] += alpha * dt * xt * gv;", "dB[j] += alpha * dt * xt * gh;", 0),
-    ("bwd_dx_drops_alpha", "dx[i] += alpha * dt * B[j] * gv;", "dx[i] += dt * B[j] * gv;", 0),
+    ("bwd_dB_uses_gh", "dB[j] += alpha * g * xt * gv;", "dB[j] += alpha * g * xt * gh;", 0),
+    ("bwd_dx_drops_alpha", "dx[i] += alpha * g * B[j] * gv;", "dx[i] += g * B[j] * gv;", 0),
     ("bwd_dDskip_uses_y", "dD_rows[b * D + d] += dy[i] * x[i];", "dD_rows[b * D + d] += dy[i];", 0),
     # initial state and terminal adjoints
     ("fwd_ignores_v0", "double v = v0 ? v0[(b * D + d) * N + n] : 0.0;", "double v = 0.0;", 0),
@@ -64,6 +64,13 @@ MUTANTS = [
      "ddelta[i] *= logistic(delta[i]);", 0),
     ("fused_dbias_first_row", "for (int64_t b = 0; b < Bt; ++b)\n        for (int64_t t = 0; t < L; ++t)",
      "for (int64_t b = 0; b < 1; ++b)\n        for (int64_t t = 0; t < L; ++t)", 0),
+    # zero-order hold
+    ("zoh_write_uses_a", "return An == 0.0 ? dt : expm1(dt * An) / An;",
+     "return An == 0.0 ? dt : exp(dt * An) / An;", 0),
+    ("zoh_ddelta_drops_a", "return zoh ? exp(dt * An) : 1.0;", "return 1.0;", 0),
+    ("zoh_dA_drops_g", "return (dt * exp(u) - expm1(u) / An) / An;", "return (dt * exp(u)) / An;", 0),
+    ("zoh_ignored_in_fused", "double g = write_coef(dt, A[d * N + n], zoh);",
+     "double g = write_coef(dt, A[d * N + n], 0);", 0),
 ]
 
 
