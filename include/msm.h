@@ -163,14 +163,19 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
  *     (softplus(u) = log(1 + e^u); a NULL delta_bias is zero),
  *     the scan of msm_scan_fwd_state runs on delta_eff, giving y_raw (skip term included),
  *     y = y_raw * silu(z)  with silu(z) = z / (1 + e^-z), when z (Bt, L, D, io dtype) is given.
- * delta_bias is (D,) fp32.  delta_softplus must be 0 or 1.  With z, delta_bias NULL and
- * delta_softplus 0 this is msm_scan_fwd_state.  The bias, softplus and gate are applied inside
+ * delta_bias is (D,) fp32.  delta_softplus must be 0 or 1.
+ * zero_order_hold (0 or 1) selects the write coefficient: 0 keeps the first-order delta of the
+ * README's "Discretization Note"; 1 uses the zero-order hold Bbar = (exp(delta_eff A) - 1) A^{-1} B
+ * of the glossary and complextorch pages ("The diagonal SSM"), i.e.
+ *     v_t = beta v_{t-1} + alpha ((exp(delta_eff A) - 1) / A) B_t x_t   (delta_eff at A = 0).
+ * With z, delta_bias NULL and delta_softplus = zero_order_hold = 0 this is msm_scan_fwd_state.  The bias, softplus and gate are applied inside
  * the scan kernels (no extra pass over memory).  Everything else as msm_scan_fwd_state; z and
  * delta_bias are inputs and must not overlap an output. */
 msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,
                                   const float* delta_bias, int32_t delta_softplus,
-                                  const float* h0, const float* v0, void* y, float* last_h,
+                                  int32_t zero_order_hold, const float* h0, const float* v0,
+                                  void* y, float* last_h,
                                   float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
                                   float beta, float alpha, msm_dtype io, void* workspace,
                                   size_t workspace_bytes, void* stream, const msm_plan* plan);
@@ -179,11 +184,12 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
  * gradient of the raw delta (through the bias and softplus); dz (Bt, L, D, io dtype) is
  * required exactly when z is given and ddelta_bias ((D,) fp32, summed over batch and time)
  * exactly when delta_bias is given.  The output before the gate, which dz needs, is recomputed
- * inside: nothing from the forward is saved.  With z, delta_bias NULL and delta_softplus 0
- * this is msm_scan_bwd_state. */
+ * inside: nothing from the forward is saved.  zero_order_hold as in msm_selective_scan_fwd.
+ * With z, delta_bias NULL and delta_softplus = zero_order_hold = 0 this is msm_scan_bwd_state. */
 msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,
-                                  const float* delta_bias, int32_t delta_softplus, const void* dy,
+                                  const float* delta_bias, int32_t delta_softplus,
+                                  int32_t zero_order_hold, const void* dy,
                                   const float* h0, const float* v0, const float* dlast_h,
                                   const float* dlast_v, void* dx, void* ddelta, float* dA,
                                   void* dB, void* dC, float* dDskip, void* dz,
@@ -202,14 +208,16 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
  *     y  = (sum_n C h + Dskip x) * silu(z)        (gate only when z is non-NULL)
  * which is msm_selective_scan_fwd over a sequence of length one started at (h, v), up to fp32
  * rounding.  Zero-initialised h, v start a new sequence; the last_h / last_v of a prefill call
- * continue one.  z, Dskip and delta_bias may be NULL; delta_softplus is 0 or 1.  h and v must
+ * continue one.  z, Dskip and delta_bias may be NULL; delta_softplus and zero_order_hold
+ * (as in msm_selective_scan_fwd) are 0 or 1.  h and v must
  * not overlap each other, an input or y.  Needs no workspace.  Same requirements on Bt, D, N,
  * beta, alpha and io as msm_scan_fwd. */
 msm_status msm_scan_step(const void* x, const void* delta, const float* A, const void* B,
                          const void* C, const float* Dskip, const void* z,
-                         const float* delta_bias, int32_t delta_softplus, float* h, float* v,
-                         void* y, int64_t Bt, int64_t D, int64_t N, float beta, float alpha,
-                         msm_dtype io, void* stream);
+                         const float* delta_bias, int32_t delta_softplus,
+                         int32_t zero_order_hold, float* h, float* v, void* y, int64_t Bt,
+                         int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                         void* stream);
 
 #ifdef __cplusplus
 }

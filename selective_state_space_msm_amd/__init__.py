@@ -105,12 +105,12 @@ def load_library():
                                                    ctypes.POINTER(_Plan)])
     lib.msm_scan_bwd_state.restype = ctypes.c_int
     tail = [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P, ctypes.POINTER(_Plan)]
-    lib.msm_selective_scan_fwd.argtypes = [P] * 8 + [I32] + [P] * 5 + tail
+    lib.msm_selective_scan_fwd.argtypes = [P] * 8 + [I32, I32] + [P] * 5 + tail
     lib.msm_selective_scan_fwd.restype = ctypes.c_int
-    lib.msm_selective_scan_bwd.argtypes = [P] * 8 + [I32] + [P] * 15 + tail
+    lib.msm_selective_scan_bwd.argtypes = [P] * 8 + [I32, I32] + [P] * 15 + tail
     lib.msm_selective_scan_bwd.restype = ctypes.c_int
-    lib.msm_scan_step.argtypes = ([P] * 8 + [I32] + [P] * 3 + [I64, I64, I64, F, F, ctypes.c_int,
-                                                               P])
+    lib.msm_scan_step.argtypes = ([P] * 8 + [I32, I32] + [P] * 3
+                                  + [I64, I64, I64, F, F, ctypes.c_int, P])
     lib.msm_scan_step.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -326,12 +326,13 @@ def _check_extras(x, z, delta_bias, dev):
 
 
 def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None,
-                           delta_bias=None, delta_softplus=False, h0=None, v0=None, y=None,
-                           last_h=None, last_v=None, return_last_state=False, workspace=None,
-                           stream=None, plan=None):
+                           delta_bias=None, delta_softplus=False, zero_order_hold=False, h0=None,
+                           v0=None, y=None, last_h=None, last_v=None, return_last_state=False,
+                           workspace=None, stream=None, plan=None):
     """The full forward (msm_selective_scan_fwd): the scan on softplus(delta + delta_bias) (or
-    delta + delta_bias), output times silu(z).  z: (Bt, L, D) in the I/O dtype; delta_bias:
-    (D,) fp32; other arguments as msm_scan_fwd.  Returns y, or (y, last_h, last_v)."""
+    delta + delta_bias), output times silu(z); zero_order_hold selects the exact discretisation
+    of the write.  z: (Bt, L, D) in the I/O dtype; delta_bias: (D,) fp32; other arguments as
+    msm_scan_fwd.  Returns y, or (y, last_h, last_v)."""
     import torch
     lib = load_library()
     dev = x.device
@@ -360,7 +361,8 @@ def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None
     ws, wsb = _workspace(nbytes, workspace, dev)
     st = lib.msm_selective_scan_fwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
-        int(bool(delta_softplus)), _ptr(h0), _ptr(v0), _ptr(y), _ptr(last_h), _ptr(last_v), Bt,
+        int(bool(delta_softplus)), int(bool(zero_order_hold)), _ptr(h0), _ptr(v0), _ptr(y),
+        _ptr(last_h), _ptr(last_v), Bt,
         L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
         _plan_arg(plan))
     if st != 0:
@@ -371,9 +373,9 @@ def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None
 
 
 def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=None,
-                           delta_bias=None, delta_softplus=False, h0=None, v0=None, dlast_h=None,
-                           dlast_v=None, state_grads=False, out=None, workspace=None,
-                           stream=None, plan=None):
+                           delta_bias=None, delta_softplus=False, zero_order_hold=False, h0=None,
+                           v0=None, dlast_h=None, dlast_v=None, state_grads=False, out=None,
+                           workspace=None, stream=None, plan=None):
     """Gradients of the full operation (msm_selective_scan_bwd).  Returns the dict of
     msm_scan_bwd, where ddelta is the gradient of the raw delta, plus dz (I/O dtype, None
     without z), ddelta_bias (fp32 (D,), None without delta_bias) and, with state_grads, dh0 and
@@ -413,7 +415,8 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
     ws, wsb = _workspace(nbytes, workspace, dev)
     st = lib.msm_selective_scan_bwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
-        int(bool(delta_softplus)), _ptr(dy), *(_ptr(t) for t in states), _ptr(o["dx"]),
+        int(bool(delta_softplus)), int(bool(zero_order_hold)), _ptr(dy),
+        *(_ptr(t) for t in states), _ptr(o["dx"]),
         _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]),
         _ptr(o["dz"]), _ptr(o["ddelta_bias"]), _ptr(o.get("dh0")), _ptr(o.get("dv0")), Bt, L, D,
         N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
@@ -424,7 +427,7 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
 
 
 def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, delta_bias=None,
-                  delta_softplus=False, y=None, stream=None):
+                  delta_softplus=False, zero_order_hold=False, y=None, stream=None):
     """One decode step (msm_scan_step): x, delta, z (Bt, D) and B, C (Bt, N) in the I/O dtype;
     h, v (Bt, D, N) fp32 states, updated in place.  Returns y (Bt, D)."""
     import torch
@@ -449,7 +452,8 @@ def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, d
         y = torch.empty((Bt, D), dtype=x.dtype, device=dev)
     _check(y, "y", (Bt, D), x.dtype, dev)
     st = lib.msm_scan_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
-                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h), _ptr(v), _ptr(y),
+                           _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zero_order_hold)),
+                           _ptr(h), _ptr(v), _ptr(y),
                            Bt, D, N, float(beta), float(alpha), io, _stream_handle(stream, dev))
     if st != 0:
         raise MsmError(st, "msm_scan_step")

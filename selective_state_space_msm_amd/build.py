@@ -14,9 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsm.so")
-# (source, extra flags): the recurrence kernels are built once per (bf16 I/O, fused variant)
-# pair, all in parallel
-_PARTS = [("-DMSM_IO_BF16=%d" % io, "-DMSM_EXT=%d" % ext) for io in (0, 1) for ext in (0, 1)]
+# (source, extra flags): the recurrence kernels are built once per (bf16 I/O, variant) pair --
+# variant 0 plain, 1 fused extras, 2 fused extras with the zero-order hold -- all in parallel
+_PARTS = [("-DMSM_IO_BF16=%d" % io, "-DMSM_EXT=%d" % ext) for io in (0, 1) for ext in (0, 1, 2)]
 SOURCES = ([("msm_api.cpp", ()), ("msm_launch.hip", ()), ("msm_bwd_wide.hip", ()),
             ("msm_step.hip", ())]
            + [("msm_fwd.hip", f) for f in _PARTS] + [("msm_bwd.hip", f) for f in _PARTS])

@@ -231,7 +231,8 @@ msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dt
 msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,
                                   const float* delta_bias, int32_t delta_softplus,
-                                  const float* h0, const float* v0, void* y, float* last_h,
+                                  int32_t zero_order_hold, const float* h0, const float* v0,
+                                  void* y, float* last_h,
                                   float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
                                   float beta, float alpha, msm_dtype io, void* workspace,
                                   size_t workspace_bytes, void* stream, const msm_plan* plan) {
@@ -239,7 +240,8 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
   if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
-  const bool ext = z != nullptr || delta_bias != nullptr || delta_softplus != 0;
+  if (zero_order_hold != 0 && zero_order_hold != 1) return MSM_ERR_INVALID_ARG;
+  const int ext = zero_order_hold ? 2 : (z || delta_bias || delta_softplus ? 1 : 0);
 
   msm_plan pl = auto_fwd_plan(Bt, L, D, N);
   const int NP = padded_states(N);
@@ -319,9 +321,9 @@ msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, 
                               int64_t L, int64_t D, int64_t N, float beta, float alpha,
                               msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
                               const msm_plan* plan) {
-  return msm_selective_scan_fwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, h0, v0, y, last_h,
-                                last_v, Bt, L, D, N, beta, alpha, io, workspace, workspace_bytes,
-                                stream, plan);
+  return msm_selective_scan_fwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, 0, h0, v0, y,
+                                last_h, last_v, Bt, L, D, N, beta, alpha, io, workspace,
+                                workspace_bytes, stream, plan);
 }
 
 msm_status msm_scan_fwd_with_plan(const void* x, const void* delta, const float* A,
@@ -345,7 +347,8 @@ msm_status msm_scan_fwd(const void* x, const void* delta, const float* A, const 
 
 msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,
-                                  const float* delta_bias, int32_t delta_softplus, const void* dy,
+                                  const float* delta_bias, int32_t delta_softplus,
+                                  int32_t zero_order_hold, const void* dy,
                                   const float* h0, const float* v0, const float* dlast_h,
                                   const float* dlast_v, void* dx, void* ddelta, float* dA,
                                   void* dB, void* dC, float* dDskip, void* dz,
@@ -361,7 +364,8 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   if ((z != nullptr) != (dz != nullptr)) return MSM_ERR_INVALID_ARG;
   if ((delta_bias != nullptr) != (ddelta_bias != nullptr)) return MSM_ERR_INVALID_ARG;
   if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
-  const bool ext = z != nullptr || delta_bias != nullptr || delta_softplus != 0;
+  if (zero_order_hold != 0 && zero_order_hold != 1) return MSM_ERR_INVALID_ARG;
+  const int ext = zero_order_hold ? 2 : (z || delta_bias || delta_softplus ? 1 : 0);
 
   msm_plan pl = auto_bwd_plan(Bt, L, D, N);
   const int NP = padded_states(N);
@@ -453,7 +457,7 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
                               int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
                               void* workspace, size_t workspace_bytes, void* stream,
                               const msm_plan* plan) {
-  return msm_selective_scan_bwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, dy, h0, v0,
+  return msm_selective_scan_bwd(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, 0, dy, h0, v0,
                                 dlast_h, dlast_v, dx, ddelta, dA, dB, dC, dDskip, nullptr,
                                 nullptr, dh0, dv0, Bt, L, D, N, beta, alpha, io, workspace,
                                 workspace_bytes, stream, plan);
@@ -483,13 +487,15 @@ msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const 
 
 msm_status msm_scan_step(const void* x, const void* delta, const float* A, const void* B,
                          const void* C, const float* Dskip, const void* z,
-                         const float* delta_bias, int32_t delta_softplus, float* h, float* v,
-                         void* y, int64_t Bt, int64_t D, int64_t N, float beta, float alpha,
-                         msm_dtype io, void* stream) {
+                         const float* delta_bias, int32_t delta_softplus,
+                         int32_t zero_order_hold, float* h, float* v, void* y, int64_t Bt,
+                         int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                         void* stream) {
   msm_status st = check_common(Bt, 1, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !h || !v || !y) return MSM_ERR_INVALID_ARG;
   if (delta_softplus != 0 && delta_softplus != 1) return MSM_ERR_INVALID_ARG;
+  if (zero_order_hold != 0 && zero_order_hold != 1) return MSM_ERR_INVALID_ARG;
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * D), nbc = (size_t)(Bt * N), nst = (size_t)(Bt * D * N) * 4;
   const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),
@@ -512,6 +518,7 @@ msm_status msm_scan_step(const void* x, const void* delta, const float* A, const
   a.Dskip = Dskip;
   a.delta_bias = delta_bias;
   a.delta_softplus = delta_softplus;
+  a.zoh = zero_order_hold;
   a.h = h;
   a.v = v;
   a.y = y;

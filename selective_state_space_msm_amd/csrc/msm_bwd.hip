@@ -32,7 +32,9 @@
 // dy silu'(z) and softplus' = logistic(delta + bias) are kept beside it in LDS; the output
 // before the gate, needed for dz, is re-formed from the recomputed states (C . h + Dskip x,
 // reduced across the state groups like dx); dz and the raw-delta gradient are finished with
-// dx / ddelta, and the bias gradient is summed per channel.
+// dx / ddelta, and the bias gradient is summed per channel.  Its zero-order-hold form (EXT = 2)
+// also carries the write coefficient g = delta phi(delta A) and its derivatives (dg/ddelta =
+// e^(delta A), dg/dA = delta^2 psi(delta A)) through dx, ddelta, dA and dB.
 // This kernel serves 4 and 16 padded states; 64 padded states use the full-wavefront
 // backward in msm_bwd_wide.hip.
 #include <type_traits>
@@ -97,7 +99,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return make_rsrc(static_cast<const char*>(base) + off, total - off);
 }
 
-template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, bool EXT>
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, int EXT>
 __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   constexpr int RB = M / (2 * K);        // rows per reduce-scatter
   constexpr int NRB = TB / RB;
   static_assert(P == 2, "the lane pairing below assumes two 32-lane halves");
+  constexpr bool ZOH = EXT == 2;  // zero-order-hold write coefficient g = delta phi(delta A)
   static_assert(RB >= 1 && TB % RB == 0, "tile must split into reduce blocks");
 
   __shared__ float4 xs[2][TB][CB];          // x, delta, dy, delta * x
@@ -279,8 +282,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   auto fstep = [&](float dv, float c, const float* bb, float* a_out, float* h_out) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const float a = exp2_fast(dv * A2[j]);
-      const float w = c * bb[j];
+      const float arg = dv * A2[j];
+      const float a = exp2_fast(arg);
+      float w = c * bb[j];
+      if (ZOH) w *= zoh_phi(arg * kLn2, a);
       v[j] = BETA0 ? w : fmaf(beta, v[j], w);
       h[j] = fmaf(a, h[j], v[j]);
       if (a_out) a_out[j] = a;
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         const float4 r = xs[buf][tt][ch];
         const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
         const double gy64 = gy;
-        float p1 = 0.f, p2 = 0.f, yq = 0.f;
+        float p1 = 0.f, p2 = 0.f, yq = 0.f, p1d = 0.f;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
           if (EXT) yq = fmaf((float)cs64[buf][tt][gs][j], hs[tt + 1][j], yq);
@@ -525,10 +530,23 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           if (!BETA0) gvp[j] = gv;
           const float gvf = (float)gv;
           const float gg = (float)ghn[j] * hs[tt][j];  // a_t h_{t-1} gh_t
-          p1 = j == 0 ? bs[buf][tt][gs][j] * gvf : fmaf(bs[buf][tt][gs][j], gvf, p1);
           p2 = j == 0 ? Af[j] * gg : fmaf(Af[j], gg, p2);
           dAt[j] = fmaf(dv, gg, dAt[j]);
-          vals[(tb * 2 + 0) * K + j] = c * gvf;             // dB / alpha
+          if (!ZOH) {
+            p1 = j == 0 ? bs[buf][tt][gs][j] * gvf : fmaf(bs[buf][tt][gs][j], gvf, p1);
+            vals[(tb * 2 + 0) * K + j] = c * gvf;             // dB / alpha
+          } else {
+            // g = delta phi: dx and dB take phi, ddelta's write part dg/ddelta = a, and dA
+            // gains alpha B x gv delta^2 psi
+            const float a = av[tt][j];
+            const float u = dv * A2[j] * kLn2;
+            const float ph = zoh_phi(u, a);
+            const float bg = bs[buf][tt][gs][j] * gvf;  // alpha B gv
+            p1 = j == 0 ? bg * ph : fmaf(bg, ph, p1);
+            p1d = j == 0 ? bg * a : fmaf(bg, a, p1d);
+            dAt[j] = fmaf(bg * (xv * dv * dv), zoh_psi(u, a, ph), dAt[j]);
+            vals[(tb * 2 + 0) * K + j] = c * ph * gvf;        // dB / alpha
+          }
           vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
         }
         float qx = dv * p1;
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           qx = fmaf(dsk, gy, qx);
           dDt = fmaf(gy, xv, dDt);
         }
-        const float qd = fmaf(xv, p1, p2);
+        const float qd = fmaf(xv, ZOH ? p1d : p1, p2);
         spart[pb][g][tt][lane] = swap_add32(qx, qd);
         if (EXT) {
           // the output before the gate: this lane's states (+ the skip term on group 0), then
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S, bool BETA0, bool EXT>
+template <typename IO, int K, int S, bool BETA0, int EXT>
 hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(S * kWave);
   if (a.Dskip)
@@ -617,7 +635,7 @@ hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename IO, bool BETA0, bool EXT>
+template <typename IO, bool BETA0, int EXT>
 hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
   switch (a.NP * 100 + K) {
     // S = NP / (2K) wavefronts per workgroup
@@ -635,7 +653,7 @@ hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
 // This file is compiled once per (I/O dtype, variant) pair; MSM_IO_BF16 and MSM_EXT select
 // which launcher a build of it defines.
 #if !defined(MSM_IO_BF16) || !defined(MSM_EXT)
-#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1"
+#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1|2"
 #endif
 #if MSM_IO_BF16
 using PartIO = bf16_storage;
@@ -644,8 +662,8 @@ using PartIO = float;
 #endif
 
 hipError_t MSM_BWD_PART(MSM_IO_BF16, MSM_EXT)(const BwdArgs& a, int K, bool beta0, hipStream_t s) {
-  return beta0 ? launch_io<PartIO, true, MSM_EXT != 0>(a, K, s)
-               : launch_io<PartIO, false, MSM_EXT != 0>(a, K, s);
+  return beta0 ? launch_io<PartIO, true, MSM_EXT>(a, K, s)
+               : launch_io<PartIO, false, MSM_EXT>(a, K, s);
 }
 
 }  // namespace msm

@@ -8,7 +8,8 @@
 // The fused variant (EXT: delta bias + softplus, SiLU gate) re-forms delta_eff and the gated dy
 // from the raw inputs wherever they are read, adds the wavefront partials of the pre-gate
 // output C . h for dz, and sums the bias gradient per channel; it works in rounds of 4 rows
-// so that the extra partials fit in LDS.
+// so that the extra partials fit in LDS.  Its zero-order-hold form (EXT = 2) also carries the
+// write coefficient g = delta phi(delta A) and its derivatives through dx, ddelta, dA and dB.
 #include "msm_device.hpp"
 #include "msm_internal.h"
 
@@ -48,7 +49,7 @@ __device__ __forceinline__ void reduce_scatter64(float (&v)[M], int lane) {
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, bool EXT>
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, int EXT>
 __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   constexpr int NPER = (BC_PER_TILE + NTHR - 1) / NTHR;
   // rows whose per-wavefront partials sit in LDS at once (fp64, so fewer rows for big S)
   constexpr int SR = EXT ? 4 : (S >= 16 ? 8 : TB);
+  constexpr bool ZOH = EXT == 2;  // zero-order-hold write coefficient g = delta phi(delta A)
   constexpr int NSR = TB / SR;
   // steps per lane-reduce block of dB/dC values (at most 64 values per block)
   constexpr int RB = (64 / (2 * K)) < SR ? (64 / (2 * K)) : SR;
@@ -163,8 +165,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
         const float* bc = &bcs[tt][g][0];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          const float a = exp2_fast(dv * A2[j]);
-          const float w = c * bc[j];
+          const float arg = dv * A2[j];
+          const float a = exp2_fast(arg);
+          float w = c * bc[j];
+          if (ZOH) w *= zoh_phi(arg * kLn2, a);
           v[j] = BETA0 ? w : fmaf(beta, v[j], w);
           h[j] = fmaf(a, h[j], v[j]);
         }
@@ -225,8 +229,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
         const float* bc = &bcs[tt][g][0];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          const float a = exp2_fast(dv * A2[j]);
-          const float w = c * bc[j];
+          const float arg = dv * A2[j];
+          const float a = exp2_fast(arg);
+          float w = c * bc[j];
+          if (ZOH) w *= zoh_phi(arg * kLn2, a);
           v[j] = BETA0 ? w : fmaf(beta, v[j], w);
           h[j] = fmaf(a, h[j], v[j]);
           av[tt][j] = a;
@@ -258,24 +264,37 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
             float yq = 0.f;
             const double gy64 = gy, dv64 = dv;
             const double* bc = &bcs64[tt][g][0];
-            double s1 = 0.0, s2 = 0.0;
+            double s1 = 0.0, s2 = 0.0, s1d = 0.0;
 #pragma unroll
             for (int j = 0; j < K; ++j) {
               const double a64 = av[tt][j];
               const double gh = fma(bc[K + j], gy64, ghn[j]);
               const double gv = gh + gvn[j];
-              s1 = fma(bc[j], gv, s1);
               const double gg = a64 * (double)hs[tt][j] * gh;
               s2 = fma(A64[j], gg, s2);
               dAacc[j] = fma(dv64, gg, dAacc[j]);
-              vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
+              if (!ZOH) {
+                s1 = fma(bc[j], gv, s1);
+                vals[(tb * 2 + 0) * K + j] = c * (float)gv;       // dB / alpha
+              } else {
+                // g = delta phi: dx and dB take phi, ddelta's write part dg/ddelta = a, and dA
+                // gains alpha B x gv delta^2 psi
+                const float u = dv * A2[j] * kLn2;
+                const float ph = zoh_phi(u, av[tt][j]);
+                const double bgv = bc[j] * gv;  // alpha B gv
+                s1 = fma(bgv, (double)ph, s1);
+                s1d = fma(bgv, a64, s1d);
+                dAacc[j] = fma(bgv, (double)(xv * dv * dv * zoh_psi(u, av[tt][j], ph)), dAacc[j]);
+                vals[(tb * 2 + 0) * K + j] = c * ph * (float)gv;  // dB / alpha
+              }
               vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
               if (EXT) yq = fmaf(bcs[tt][g][K + j], hs[tt + 1][j], yq);
               ghn[j] = a64 * gh;
               gvn[j] = BETA0 ? 0.0 : beta64 * gv;
             }
             spart[0][g][tr][lane] = s1;
-            spart[1][g][tr][lane] = s2;
+            // the zero-order hold's ddelta write part is not x times the dx sum: add it here
+            spart[1][g][tr][lane] = ZOH ? fma((double)xv, s1d, s2) : s2;
             if (EXT) ypart[EXT ? g : 0][EXT ? tr : 0][lane] = yq;
             if (HAS_DSKIP) dDacc = fmaf(gy, xv, dDacc);
           } else {
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
             T::store(p.dx, idx, (float)dxv);
             // through softplus: d softplus(u) / du = logistic(u)
             const double dsp = softplus ? (double)logistic_f(draw + dbias).s : 1.0;
-            const double qd = fma(xv, s1, s2) * dsp;
+            const double qd = (ZOH ? s2 : fma(xv, s1, s2)) * dsp;
             T::store(p.ddelta, idx, (float)qd);
             dbias64 += qd;
             if (has_z) {
@@ -380,7 +399,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_wide_kernel(const BwdArgs p) {
   }
 }
 
-template <typename IO, bool BETA0, bool EXT>
+template <typename IO, bool BETA0, int EXT>
 hipError_t launch_wide(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(16 * kWave);
   if (a.Dskip)
@@ -391,13 +410,18 @@ hipError_t launch_wide(const BwdArgs& a, hipStream_t s) {
 }
 
 template <typename IO, bool BETA0>
-hipError_t launch_wide_ext(const BwdArgs& a, bool ext, hipStream_t s) {
-  return ext ? launch_wide<IO, BETA0, true>(a, s) : launch_wide<IO, BETA0, false>(a, s);
+hipError_t launch_wide_ext(const BwdArgs& a, int ext, hipStream_t s) {
+  switch (ext) {
+    case 0: return launch_wide<IO, BETA0, 0>(a, s);
+    case 1: return launch_wide<IO, BETA0, 1>(a, s);
+    case 2: return launch_wide<IO, BETA0, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, bool ext, hipStream_t s) {
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, int ext, hipStream_t s) {
   if (a.NP != 64) return hipErrorInvalidValue;
   if (io_bf16)
     return beta0 ? launch_wide_ext<bf16_storage, true>(a, ext, s)

@@ -47,6 +47,32 @@ __device__ __forceinline__ float silu_grad_f(float z) {
   return l.s * fmaf(z, l.sc, 1.f);
 }
 
+// Zero-order hold.  The write coefficient is g = (e^u - 1) / A = delta phi(u) with u = delta A,
+// phi(u) = (e^u - 1) / u, and dg/dA = delta^2 psi(u) with psi(u) = (u e^u - e^u + 1) / u^2.
+// Near u = 0 both quotients cancel, so they come from their Taylor series there
+// (phi = sum u^k / (k+1)!, psi = sum (k+1) u^k / (k+2)!, truncated below 2e-9 relative for
+// |u| < 1/4); elsewhere from a = e^u, which keeps its relative accuracy in a - 1 and a - phi.
+__device__ __forceinline__ float zoh_phi(float u, float a) {
+  float p = fmaf(u, 1.f / 5040.f, 1.f / 720.f);
+  p = fmaf(p, u, 1.f / 120.f);
+  p = fmaf(p, u, 1.f / 24.f);
+  p = fmaf(p, u, 1.f / 6.f);
+  p = fmaf(p, u, 0.5f);
+  p = fmaf(p, u, 1.f);
+  const float q = (a - 1.f) * rcp_fast(u);
+  return fabsf(u) < 0.25f ? p : q;
+}
+__device__ __forceinline__ float zoh_psi(float u, float a, float phi) {
+  float p = fmaf(u, 1.f / 5760.f, 1.f / 840.f);
+  p = fmaf(p, u, 1.f / 144.f);
+  p = fmaf(p, u, 1.f / 30.f);
+  p = fmaf(p, u, 1.f / 8.f);
+  p = fmaf(p, u, 1.f / 3.f);
+  p = fmaf(p, u, 0.5f);
+  const float q = (a - phi) * rcp_fast(u);
+  return fabsf(u) < 0.25f ? p : q;
+}
+
 struct bf16_storage {
   uint16_t bits;
 };

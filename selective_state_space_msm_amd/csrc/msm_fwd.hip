@@ -26,6 +26,9 @@
 // delta_eff = softplus(delta + bias[d]) (or delta + bias[d]) is formed where delta is staged,
 // once per workgroup, and the output is multiplied by silu(z) where it is stored; z is loaded
 // with x and delta and stays in registers until its tile's y is stored.
+// The zero-order-hold variant (EXT = 2) also replaces the write coefficient delta by
+// (e^(delta A) - 1) / A = delta phi(delta A) (the exact discretisation of the glossary and
+// complextorch pages), at a few more instructions per state update.
 //
 // The y reduction never needs MFMA: the scan is a per-element recurrence bound by VALU issue
 // (one v_exp_f32 plus five fp32 multiply/FMA per state update), not a dense contraction.
@@ -37,7 +40,7 @@ namespace {
 
 // Occupancy hint: the launch plans put one or two wavefronts on a SIMD, so the scheduler may
 // spend registers on hiding LDS and transcendental latency instead of on more wavefronts.
-template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, bool EXT>
+template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, int EXT>
 __global__ __launch_bounds__(S* kWave) __attribute__((amdgpu_waves_per_eu(1, K >= 8 ? 1 : 2)))
 void fwd_kernel(const FwdArgs p) {
   using T = io<IO>;
@@ -86,6 +89,7 @@ void fwd_kernel(const FwdArgs p) {
   const float dsk = (HAS_DSKIP && g == 0) ? p.Dskip[dl] : 0.f;
   // fused extras: every x / delta element a thread stages belongs to its lane's channel
   constexpr bool ZG = EXT && !SUMMARY;  // the gate is loaded (the summaries produce no y)
+  constexpr bool ZOH = EXT == 2;        // zero-order-hold write coefficient
   const float dbias = (EXT && p.delta_bias) ? p.delta_bias[dl] : 0.f;
   const bool softplus = EXT && p.delta_softplus != 0;
   const bool has_z = ZG && p.z != nullptr;
@@ -256,8 +260,10 @@ void fwd_kernel(const FwdArgs p) {
     if (SUMMARY) bpow *= beta;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const float a = exp2_fast(dv * A2[j]);
-      const float w = c * bc[j];
+      const float arg = dv * A2[j];
+      const float a = exp2_fast(arg);
+      float w = c * bc[j];
+      if (ZOH) w *= zoh_phi(arg * kLn2, a);  // g = delta phi(delta A) instead of delta
       if (BETA0)
         v[j] = w;
       else
@@ -413,7 +419,7 @@ void fwd_kernel(const FwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S, bool BETA0, bool EXT>
+template <typename IO, int K, int S, bool BETA0, int EXT>
 hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
   const dim3 block(S * kWave);
   if (a.G > 1) {
@@ -430,7 +436,7 @@ hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename IO, bool BETA0, bool EXT>
+template <typename IO, bool BETA0, int EXT>
 hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
   // padded state count NP = K * S is 4, 16 or 64
   const int NP = a.N <= 4 ? 4 : (a.N <= 16 ? 16 : 64);
@@ -455,7 +461,7 @@ hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
 // This file is compiled once per (I/O dtype, variant) pair; MSM_IO_BF16 and MSM_EXT select
 // which launcher a build of it defines.
 #if !defined(MSM_IO_BF16) || !defined(MSM_EXT)
-#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1"
+#error "compile with -DMSM_IO_BF16=0|1 -DMSM_EXT=0|1|2"
 #endif
 #if MSM_IO_BF16
 using PartIO = bf16_storage;
@@ -464,8 +470,8 @@ using PartIO = float;
 #endif
 
 hipError_t MSM_FWD_PART(MSM_IO_BF16, MSM_EXT)(const FwdArgs& a, int K, bool beta0, hipStream_t s) {
-  return beta0 ? launch_io<PartIO, true, MSM_EXT != 0>(a, K, s)
-               : launch_io<PartIO, false, MSM_EXT != 0>(a, K, s);
+  return beta0 ? launch_io<PartIO, true, MSM_EXT>(a, K, s)
+               : launch_io<PartIO, false, MSM_EXT>(a, K, s);
 }
 
 }  // namespace msm

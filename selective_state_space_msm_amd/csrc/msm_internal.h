@@ -95,6 +95,7 @@ struct StepArgs {
   const float* Dskip;     // (D,) or null
   const float* delta_bias;  // (D,) or null
   int32_t delta_softplus;
+  int32_t zoh;            // zero-order-hold write coefficient
   float* h;               // (Bt, D, N) fp32 states, updated in place
   float* v;
   void* y;                // (Bt, D) I/O dtype
@@ -107,12 +108,13 @@ struct StepArgs {
 // and A).  Returns hipSuccess or the launch error.
 hipError_t launch_step(const StepArgs& a, int io_bf16, bool vec, hipStream_t s);
 
-// Both return hipSuccess or the first launch error; `ext` selects the fused variant.
-hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s);
+// Both return hipSuccess or the first launch error.  `ext` selects the variant: 0 plain,
+// 1 fused (bias, softplus, gate), 2 fused with the zero-order-hold write coefficient.
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s);
 
 // The recurrence kernels are compiled once per (I/O dtype, variant) pair, each build of
-// msm_fwd.hip / msm_bwd.hip defining one of these (suffix: bf16 I/O, fused variant).
+// msm_fwd.hip / msm_bwd.hip defining one of these (suffix: bf16 I/O, variant 0 / 1 / 2).
 #define MSM_PART_NAME_(prefix, io, ext) prefix##io##_##ext
 #define MSM_PART_NAME(prefix, io, ext) MSM_PART_NAME_(prefix, io, ext)
 #define MSM_FWD_PART(io, ext) MSM_PART_NAME(launch_fwd_part_, io, ext)
@@ -121,11 +123,15 @@ hipError_t launch_fwd_part_0_0(const FwdArgs& a, int K, bool beta0, hipStream_t 
 hipError_t launch_fwd_part_0_1(const FwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_fwd_part_1_0(const FwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_fwd_part_1_1(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_fwd_part_0_2(const FwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_fwd_part_1_2(const FwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd_part_0_0(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd_part_0_1(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd_part_1_0(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 hipError_t launch_bwd_part_1_1(const BwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_0_2(const BwdArgs& a, int K, bool beta0, hipStream_t s);
+hipError_t launch_bwd_part_1_2(const BwdArgs& a, int K, bool beta0, hipStream_t s);
 // The 64-state backward (channel blocks of 64, K = 4); launch_bwd calls it for NP == 64.
-hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, bool ext, hipStream_t s);
+hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, int ext, hipStream_t s);
 
 }  // namespace msm

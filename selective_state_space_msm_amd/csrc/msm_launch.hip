@@ -59,23 +59,31 @@ hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s) {
+hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s) {
   hipError_t e;
   if (a.NP == 64) {
     e = launch_bwd_wide(a, io_bf16, beta0, ext, s);
   } else if (io_bf16) {
-    e = ext ? launch_bwd_part_1_1(a, K, beta0, s) : launch_bwd_part_1_0(a, K, beta0, s);
+    e = ext == 2 ? launch_bwd_part_1_2(a, K, beta0, s)
+        : ext == 1 ? launch_bwd_part_1_1(a, K, beta0, s)
+                   : launch_bwd_part_1_0(a, K, beta0, s);
   } else {
-    e = ext ? launch_bwd_part_0_1(a, K, beta0, s) : launch_bwd_part_0_0(a, K, beta0, s);
+    e = ext == 2 ? launch_bwd_part_0_2(a, K, beta0, s)
+        : ext == 1 ? launch_bwd_part_0_1(a, K, beta0, s)
+                   : launch_bwd_part_0_0(a, K, beta0, s);
   }
   if (e != hipSuccess) return e;
   return io_bf16 ? launch_finalize<bf16_storage>(a, s) : launch_finalize<float>(a, s);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, bool ext, hipStream_t s) {
+hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s) {
   if (io_bf16)
-    return ext ? launch_fwd_part_1_1(a, K, beta0, s) : launch_fwd_part_1_0(a, K, beta0, s);
-  return ext ? launch_fwd_part_0_1(a, K, beta0, s) : launch_fwd_part_0_0(a, K, beta0, s);
+    return ext == 2   ? launch_fwd_part_1_2(a, K, beta0, s)
+           : ext == 1 ? launch_fwd_part_1_1(a, K, beta0, s)
+                      : launch_fwd_part_1_0(a, K, beta0, s);
+  return ext == 2   ? launch_fwd_part_0_2(a, K, beta0, s)
+         : ext == 1 ? launch_fwd_part_0_1(a, K, beta0, s)
+                    : launch_fwd_part_0_0(a, K, beta0, s);
 }
 
 }  // namespace msm

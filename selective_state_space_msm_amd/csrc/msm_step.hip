@@ -3,7 +3,8 @@
 // The `step` of the Momentum Mamba README (one token in, the ssm and velocity states carried in
 // and out), for the scan part of the block: with the fused op's extras,
 //   delta_eff = softplus(delta + bias[d]) (or delta + bias[d]),
-//   v' = beta v + alpha delta_eff B x,  h' = exp(delta_eff A) h + v',
+//   v' = beta v + alpha g B x,  h' = exp(delta_eff A) h + v',
+//   (g = delta_eff, or (exp(delta_eff A) - 1) / A with the zero-order hold),
 //   y  = (C . h' + Dskip x) * silu(z)   (the gate when z is given),
 // with h and v, (Bt, D, N) fp32, updated in place.
 //
@@ -83,8 +84,11 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs p) {
   float ys = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float a = exp2_fast(de * (As[j] * kLog2e));
-    vs[j] = fmaf(p.beta, vs[j], c * Bs[j]);
+    const float arg = de * (As[j] * kLog2e);
+    const float a = exp2_fast(arg);
+    float w = c * Bs[j];
+    if (p.zoh) w *= zoh_phi(arg * kLn2, a);  // zero-order hold: g = delta phi(delta A)
+    vs[j] = fmaf(p.beta, vs[j], w);
     hs[j] = fmaf(a, hs[j], vs[j]);
     ys = fmaf(Cs[j], hs[j], ys);  // padding states have C = 0
   }

@@ -183,21 +183,22 @@ def test_fused_entry_points_validation_never_launches(lib):
 
     def fwd(**kw):
         a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
-                 bias=None, sp=0, h0=None, v0=None, y=0x100000, lh=None, lv=None, N=4)
+                 bias=None, sp=0, zoh=0, h0=None, v0=None, y=0x100000, lh=None, lv=None, N=4)
         a.update(kw)
         return lib.msm_selective_scan_fwd(
             P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["z"]),
-            P(a["bias"]), a["sp"], P(a["h0"]), P(a["v0"]), P(a["y"]), P(a["lh"]), P(a["lv"]), 1,
+            P(a["bias"]), a["sp"], a["zoh"], P(a["h0"]), P(a["v0"]), P(a["y"]), P(a["lh"]),
+            P(a["lv"]), 1,
             8, 4, a["N"], ctypes.c_float(0.5), ctypes.c_float(1.0), 0, None, 0, None, None)
 
     def bwd(**kw):
         a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
-                 bias=None, sp=0, dy=0x6000, dx=0x100000, ddelta=0x200000, dA=0x300000,
+                 bias=None, sp=0, zoh=0, dy=0x6000, dx=0x100000, ddelta=0x200000, dA=0x300000,
                  dB=0x400000, dC=0x500000, dDskip=None, dz=None, dbias=None, N=4)
         a.update(kw)
         return lib.msm_selective_scan_bwd(
             P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["z"]),
-            P(a["bias"]), a["sp"], P(a["dy"]), None, None, None, None, P(a["dx"]),
+            P(a["bias"]), a["sp"], a["zoh"], P(a["dy"]), None, None, None, None, P(a["dx"]),
             P(a["ddelta"]), P(a["dA"]), P(a["dB"]), P(a["dC"]), P(a["dDskip"]), P(a["dz"]),
             P(a["dbias"]), None, None, 1, 8, 4, a["N"], ctypes.c_float(0.5),
             ctypes.c_float(1.0), 0, P(0x900000), 1 << 30, None, None)
@@ -213,6 +214,8 @@ def test_fused_entry_points_validation_never_launches(lib):
     assert bwd(z=0x7000, dz=0x7000 + 8) == INVALID  # dz over z
     assert bwd(bias=0x7000, dbias=0x100000 + 4) == INVALID  # bias gradient over dx
     assert bwd(sp=-1) == INVALID
+    assert fwd(zoh=2) == INVALID
+    assert bwd(zoh=-1) == INVALID
     assert bwd(N=65, sp=1) == UNSUPPORTED
 
 
@@ -221,10 +224,10 @@ def test_step_validation_never_launches(lib):
 
     def step(**kw):
         a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, z=None,
-                 bias=None, sp=0, h=0x100000, v=0x200000, y=0x300000, Bt=2, D=4, N=4)
+                 bias=None, sp=0, zoh=0, h=0x100000, v=0x200000, y=0x300000, Bt=2, D=4, N=4)
         a.update(kw)
         return lib.msm_scan_step(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
-                                 P(a["Dskip"]), P(a["z"]), P(a["bias"]), a["sp"], P(a["h"]),
+                                 P(a["Dskip"]), P(a["z"]), P(a["bias"]), a["sp"], a["zoh"], P(a["h"]),
                                  P(a["v"]), P(a["y"]), a["Bt"], a["D"], a["N"],
                                  ctypes.c_float(0.5), ctypes.c_float(1.0), 0, None)
 
@@ -234,6 +237,7 @@ def test_step_validation_never_launches(lib):
     assert step(Bt=0) == INVALID
     assert step(N=65) == UNSUPPORTED
     assert step(sp=3) == INVALID
+    assert step(zoh=5) == INVALID
     assert step(v=0x100000 + 64) == INVALID        # h and v overlapping
     assert step(h=0x1000) == INVALID               # a state over an input
     assert step(y=0x200000 + 8) == INVALID         # y over a state

@@ -18,13 +18,14 @@ F32_OUT = ("last_h", "last_v", "dA", "dDskip", "ddelta_bias", "dh0", "dv0")
 
 
 def fused_inputs(w, seed, softplus=True, use_z=True, use_bias=True, a_kind="random",
-                 with_dy=True):
+                 with_dy=True, zoh=False):
     inp = workloads.make_inputs(w, a_kind=a_kind, seed=seed, with_dy=with_dy)
     ex = workloads.make_fused_extras(w, seed + 7, softplus=softplus)
     inp["delta"] = ex["delta_raw"]
     inp["z"] = ex["z"] if use_z else None
     inp["delta_bias"] = ex["delta_bias"] if use_bias else None
     inp["softplus"] = softplus
+    inp["zoh"] = zoh
     return inp
 
 
@@ -41,6 +42,7 @@ def gpu_fwd(inp, g, plan=None, h0=None, v0=None):
     y, lh, lv = msm.msm_selective_scan_fwd(
         g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"], inp["alpha"], g["Dskip"],
         z=g["z"], delta_bias=g["delta_bias"], delta_softplus=inp["softplus"],
+        zero_order_hold=inp.get("zoh", False),
         h0=None if h0 is None else dev(h0), v0=None if v0 is None else dev(v0),
         return_last_state=True, plan=plan)
     torch.cuda.synchronize()
@@ -54,7 +56,8 @@ def gpu_bwd(inp, g, plan=None, h0=None, v0=None, dlh=None, dlv=None):
     o = msm.msm_selective_scan_bwd(
         g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], inp["beta"], inp["alpha"],
         g["Dskip"], z=g["z"], delta_bias=g["delta_bias"], delta_softplus=inp["softplus"],
-        h0=t(h0), v0=t(v0), dlast_h=t(dlh), dlast_v=t(dlv), state_grads=True, plan=plan)
+        zero_order_hold=inp.get("zoh", False), h0=t(h0), v0=t(v0), dlast_h=t(dlh),
+        dlast_v=t(dlv), state_grads=True, plan=plan)
     torch.cuda.synchronize()
     return o
 
@@ -63,7 +66,8 @@ def oracle_fwd(inp, h0=None, v0=None):
     y, _, lh, lv = oracle.fused_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
                                     inp["beta"], inp["alpha"], Dskip=inp["Dskip"], z=inp["z"],
                                     delta_bias=inp["delta_bias"],
-                                    delta_softplus=inp["softplus"], h0=h0, v0=v0)
+                                    delta_softplus=inp["softplus"], h0=h0, v0=v0,
+                                    zoh=inp.get("zoh", False))
     return dict(y=y, last_h=lh, last_v=lv)
 
 
@@ -71,7 +75,7 @@ def oracle_bwd(inp, h0=None, v0=None, dlh=None, dlv=None):
     return oracle.fused_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["dy"],
                             inp["beta"], inp["alpha"], Dskip=inp["Dskip"], z=inp["z"],
                             delta_bias=inp["delta_bias"], delta_softplus=inp["softplus"],
-                            h0=h0, v0=v0, dlast_h=dlh, dlast_v=dlv)
+                            h0=h0, v0=v0, dlast_h=dlh, dlast_v=dlv, zoh=inp.get("zoh", False))
 
 
 def compare(got, want, names, io, tag):
@@ -91,9 +95,9 @@ def check(inp, fplan=None, bplan=None, state=False, tag=""):
         rng = np.random.default_rng(5)
         h0, v0, dlh, dlv = (rng.standard_normal((w[0], w[2], inp["A"].shape[1])).astype(np.float32)
                             for _ in range(4))
-    log("fused %s shape=%s io=%s softplus=%s z=%s bias=%s state=%s plans=%s/%s"
+    log("fused %s shape=%s io=%s softplus=%s z=%s bias=%s zoh=%s state=%s plans=%s/%s"
         % (tag, w, io, inp["softplus"], inp["z"] is not None, inp["delta_bias"] is not None,
-           state, fplan, bplan))
+           inp.get("zoh", False), state, fplan, bplan))
     g = to_device(inp)
     compare(gpu_fwd(inp, g, fplan, h0, v0), oracle_fwd(inp, h0, v0), FWD_OUT, io, "fwd " + tag)
     compare(gpu_bwd(inp, g, bplan, h0, v0, dlh, dlv), oracle_bwd(inp, h0, v0, dlh, dlv), BWD_OUT,
@@ -209,3 +213,52 @@ def test_full_size_backward():
         assert_close(got[k][:, :, dsel], od[k], w.io, "%s sampled" % k)
     for k in ("dA", "ddelta_bias", "dDskip"):
         assert_close(got[k][dsel], od[k], w.io, "%s sampled" % k)
+
+
+# ---- zero-order hold ----
+
+@pytest.mark.parametrize("softplus,use_z,use_bias", [(True, True, True), (False, False, False)])
+@pytest.mark.parametrize("beta", [0.9, 0.0])
+def test_zoh_tiny(softplus, use_z, use_bias, beta):
+    w = W["tiny"].replace(beta=beta, dskip=True)
+    inp = fused_inputs(w, 481, softplus, use_z, use_bias, zoh=True)
+    check(inp, {"states_per_wave": 2, "chunks": 2}, {"states_per_wave": 1}, tag="zoh tiny")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_zoh_small(io, K):
+    w = SMALL.replace(io=io, dskip=True, beta=0.85, alpha=0.6)
+    inp = fused_inputs(w, 491, zoh=True)
+    check(inp, {"states_per_wave": 4 if K == 4 else 2 * K, "chunks": K}, {"states_per_wave": K},
+          state=True, tag="zoh small K=%d" % K)
+
+
+@pytest.mark.parametrize("N", [5, 33])
+def test_zoh_state_counts(N):
+    w = SMALL.replace(L=40, D=70, N=N, dskip=True)
+    check(fused_inputs(w, 500 + N, softplus=False, use_z=False, use_bias=False, zoh=True),
+          tag="zoh N=%d" % N)
+
+
+def test_zoh_full_size():
+    """The headline forward shape and the backward shape with the zero-order hold and every
+    extra, on sampled outputs."""
+    w = W["m1p4b"].replace(dskip=True)
+    inp = fused_inputs(w, 511, a_kind="s4d", with_dy=False, zoh=True)
+    got = gpu_fwd(inp, to_device(inp))
+    dsel = sample_channels(w.D, 8, seed=w.seed)
+    want = oracle_fwd(sub_problem(inp, dsel=dsel))
+    assert_close(host(got["y"])[:, :, dsel], want["y"], w.io, "zoh y sampled")
+    wb = W["bwd"].replace(dskip=True)
+    inp = fused_inputs(wb, 521, a_kind="s4d", zoh=True)
+    got = {k: (None if v is None else host(v)) for k, v in gpu_bwd(inp, to_device(inp)).items()}
+    dsel = sample_channels(wb.D, 8, seed=wb.seed)
+    od = oracle_bwd(sub_problem(inp, dsel=dsel))
+    for k in ("dx", "ddelta", "dz"):
+        assert_close(got[k][:, :, dsel], od[k], wb.io, "zoh %s sampled" % k)
+    for k in ("dA", "ddelta_bias", "dDskip"):
+        assert_close(got[k][dsel], od[k], wb.io, "zoh %s sampled" % k)
+    o0 = oracle_bwd(sub_problem(inp, bsel=slice(0, 1)))
+    for k in ("dB", "dC"):
+        assert_close(got[k][0:1], o0[k], wb.io, "zoh %s row 0" % k)

@@ -22,31 +22,31 @@ def to_dev(si):
     return g
 
 
-def gpu_step(si, g, use_z=True, use_bias=True):
+def gpu_step(si, g, use_z=True, use_bias=True, zoh=False):
     import torch
     import selective_state_space_msm_amd as msm
     y = msm.msm_scan_step(g["x"], g["delta"], g["A"], g["B"], g["C"], g["h"], g["v"], si["beta"],
                           si["alpha"], g["Dskip"], z=g["z"] if use_z else None,
                           delta_bias=g["delta_bias"] if use_bias else None,
-                          delta_softplus=si["softplus"])
+                          delta_softplus=si["softplus"], zero_order_hold=zoh)
     torch.cuda.synchronize()
     return y
 
 
-def oracle_step(si, use_z=True, use_bias=True):
+def oracle_step(si, use_z=True, use_bias=True, zoh=False):
     return oracle.step(si["x"], si["delta"], si["A"], si["B"], si["C"], si["h"], si["v"],
                        si["beta"], si["alpha"], Dskip=si["Dskip"], z=si["z"] if use_z else None,
                        delta_bias=si["delta_bias"] if use_bias else None,
-                       delta_softplus=si["softplus"])
+                       delta_softplus=si["softplus"], zoh=zoh)
 
 
-def check_step(si, use_z=True, use_bias=True, tag=""):
+def check_step(si, use_z=True, use_bias=True, tag="", zoh=False):
     log("step %s Bt=%d D=%d N=%d io=%s softplus=%s z=%s bias=%s"
         % (tag, si["x"].shape[0], si["x"].shape[1], si["A"].shape[1], si["io"], si["softplus"],
            use_z, use_bias))
     g = to_dev(si)
-    y = gpu_step(si, g, use_z, use_bias)
-    oy, oh, ov = oracle_step(si, use_z, use_bias)
+    y = gpu_step(si, g, use_z, use_bias, zoh)
+    oy, oh, ov = oracle_step(si, use_z, use_bias, zoh)
     assert_close(host(y), oy, si["io"], "y " + tag)
     assert_close(host(g["h"]), oh, "f32", "h " + tag)
     assert_close(host(g["v"]), ov, "f32", "v " + tag)
@@ -151,3 +151,10 @@ def test_full_size_decode():
     oy2, oh2, ov2 = oracle_step(si2)
     assert_close(host(y2), oy2, w.io, "second y")
     assert_close(host(g["h"]), oh2, "f32", "second h")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [4, 16, 33])
+def test_zero_order_hold(io, N):
+    w = W["decode"].replace(Bt=3, D=70, N=N, io=io)
+    check_step(workloads.make_step_inputs(w, seed=560 + N), tag="zoh N=%d" % N, zoh=True)
