@@ -115,9 +115,10 @@ def to_dev(inp):
     return d
 
 
-def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False):
+def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False, zoh=False):
     """Time msm_scan_fwd on workload w (fused: msm_selective_scan_fwd with a delta bias,
-    softplus and the gate, on the raw-delta recipe of the fused op)."""
+    softplus and the gate, on the raw-delta recipe of the fused op; zoh: also the zero-order
+    hold)."""
     import torch
     import selective_state_space_msm_amd as msm
     inp = workloads.make_inputs(w, a_kind=a_kind, with_dy=False)
@@ -137,7 +138,8 @@ def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False):
         if fused:
             msm.msm_selective_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta,
                                        w.alpha, g["Dskip"], z=g["z"], delta_bias=g["delta_bias"],
-                                       delta_softplus=True, y=y, workspace=ws, stream=stream)
+                                       delta_softplus=True, zero_order_hold=zoh, y=y,
+                                       workspace=ws, stream=stream)
         else:
             msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta, w.alpha,
                              g["Dskip"], y=y, workspace=ws, stream=stream)
@@ -146,11 +148,19 @@ def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False):
     return ms, per, plan
 
 
-def bench_bwd(w, steps, warmup, stream):
+def bench_bwd(w, steps, warmup, stream, fused=False, zoh=False):
+    """Time msm_scan_bwd on workload w (fused: msm_selective_scan_bwd with the fused op's extras,
+    zoh: also the zero-order hold)."""
     import torch
     import selective_state_space_msm_amd as msm
     inp = workloads.make_inputs(w, with_dy=True)
     g = to_dev(inp)
+    if fused:
+        ex = workloads.make_fused_extras(w, w.seed + 7)
+        dt = g["x"].dtype
+        g["delta"] = torch.from_numpy(ex["delta_raw"]).to("cuda").to(dt)
+        g["z"] = torch.from_numpy(ex["z"]).to("cuda").to(dt)
+        g["delta_bias"] = torch.from_numpy(ex["delta_bias"]).to("cuda")
     nbytes = msm.msm_scan_bwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     out = {"dx": torch.empty_like(g["x"]), "ddelta": torch.empty_like(g["x"]),
@@ -158,9 +168,19 @@ def bench_bwd(w, steps, warmup, stream):
            "dC": torch.empty_like(g["C"])}
     plan = msm.msm_scan_bwd_plan(w.Bt, w.L, w.D, w.N, w.io, w.beta)
 
+    if fused:
+        out["dz"] = torch.empty_like(g["x"])
+        out["ddelta_bias"] = torch.empty_like(g["delta_bias"])
+
     def step():
-        msm.msm_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], w.beta, w.alpha,
-                         g["Dskip"], out=out, workspace=ws, stream=stream)
+        if fused:
+            msm.msm_selective_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"],
+                                       w.beta, w.alpha, g["Dskip"], z=g["z"],
+                                       delta_bias=g["delta_bias"], delta_softplus=True,
+                                       zero_order_hold=zoh, out=out, workspace=ws, stream=stream)
+        else:
+            msm.msm_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], w.beta,
+                             w.alpha, g["Dskip"], out=out, workspace=ws, stream=stream)
 
     ms, per = timed(step, stream, steps, warmup)
     return ms, per, plan
@@ -189,22 +209,30 @@ def bench_configs(steps, warmup, stream):
     each forward shape (both beta where listed), the forward with an unstructured A, the fused
     forward, and the README benchmark shape forward and backward."""
     W = workloads.WORKLOADS
-    runs = [("m130m", "fwd", {}, "s4d", False), ("m130m", "fwd", {"beta": 0.0}, "s4d", False),
-            ("m130m", "fwd", {}, "random", False), ("m1p4b", "fwd", {}, "random", False),
-            ("m1p4b", "fwd", {}, "s4d", True), ("long", "fwd", {}, "s4d", False),
-            ("pages", "fwd", {}, "s4d", False), ("pages", "fwd", {"beta": 0.0}, "s4d", False),
-            ("pages", "bwd", {}, "s4d", False), ("pages", "bwd", {"beta": 0.0}, "s4d", False)]
+    # (workload, direction, overrides, A, fused extras, zero-order hold)
+    runs = [("m130m", "fwd", {}, "s4d", False, False),
+            ("m130m", "fwd", {"beta": 0.0}, "s4d", False, False),
+            ("m130m", "fwd", {}, "random", False, False),
+            ("m1p4b", "fwd", {}, "random", False, False),
+            ("m1p4b", "fwd", {}, "s4d", True, False), ("m1p4b", "fwd", {}, "s4d", True, True),
+            ("long", "fwd", {}, "s4d", False, False),
+            ("bwd", "bwd", {}, "s4d", True, False), ("bwd", "bwd", {}, "s4d", True, True),
+            ("pages", "fwd", {}, "s4d", False, False),
+            ("pages", "fwd", {"beta": 0.0}, "s4d", False, False),
+            ("pages", "bwd", {}, "s4d", False, False),
+            ("pages", "bwd", {"beta": 0.0}, "s4d", False, False)]
     out = []
-    for name, direction, kw, a_kind, fused in runs:
+    for name, direction, kw, a_kind, fused, zoh in runs:
         w = W[name].replace(**kw)
         if direction == "fwd":
-            ms, per, plan = bench_fwd(w, steps, warmup, stream, a_kind=a_kind, fused=fused)
+            ms, per, plan = bench_fwd(w, steps, warmup, stream, a_kind=a_kind, fused=fused, zoh=zoh)
             nb = alg_bytes_fwd(w)
         else:
-            ms, per, plan = bench_bwd(w, steps, warmup, stream)
+            ms, per, plan = bench_bwd(w, steps, warmup, stream, fused=fused, zoh=zoh)
             nb = alg_bytes_bwd(w)
         out.append({"workload": name, "direction": direction, "beta": w.beta, "A": a_kind,
-                    "fused_extras": fused, "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io,
+                    "fused_extras": fused, "zero_order_hold": zoh, "Bt": w.Bt, "L": w.L,
+                    "D": w.D, "N": w.N, "io": w.io,
                     "ms": ms, "ms_min": min(per), "state_updates_per_s": w.updates / (ms / 1e3),
                     "algorithmic_GBs": nb / (ms / 1e3) / 1e9, "plan": plan})
         import torch

@@ -278,14 +278,23 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
                      ck_tile_bytes);
   };
 
-  // one forward step of the K states (recurrence only); c = delta * x
-  auto fstep = [&](float dv, float c, const float* bb, float* a_out, float* h_out) {
+  // one forward step of the K states (recurrence only); c = delta * x.  The zero-order hold
+  // also hands out phi and psi of the step for the reverse sweep (ph_out / ps_out).
+  auto fstep = [&](float dv, float c, const float* bb, float* a_out, float* h_out,
+                   float* ph_out = nullptr, float* ps_out = nullptr) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float arg = dv * A2[j];
       const float a = exp2_fast(arg);
       float w = c * bb[j];
-      if (ZOH) w *= zoh_phi(arg * kLn2, a);
+      if (ZOH) {
+        const float ph = zoh_phi(arg * kLn2, a);
+        w *= ph;
+        if (ph_out) {
+          ph_out[j] = ph;
+          ps_out[j] = zoh_psi(arg * kLn2, a, ph);
+        }
+      }
       v[j] = BETA0 ? w : fmaf(beta, v[j], w);
       h[j] = fmaf(a, h[j], v[j]);
       if (a_out) a_out[j] = a;
@@ -491,8 +500,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     // depends on a branch, so the compiler can count the loads still in flight exactly.
     const int64_t ts = tile * TB;
     const auto rdbc = live ? rows_rsrc(dbc, ts, dbc_row_bytes, dbc_tot) : make_rsrc(dbc, 0);
-    // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt}
+    // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt} (and for
+    // the zero-order hold phi and psi of each step)
     float hs[TB + 1][K], av[TB][K];
+    float phs[ZOH ? TB : 1][K], pss[ZOH ? TB : 1][K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       v[j] = cv[j];
@@ -502,7 +513,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       const float4 r = xs[buf][tt][ch];
-      fstep(r.y, r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1]);
+      fstep(r.y, r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1], ZOH ? phs[ZOH ? tt : 0] : nullptr,
+            ZOH ? pss[ZOH ? tt : 0] : nullptr);
     }
 
     float dAt[K];
@@ -539,12 +551,11 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
             // g = delta phi: dx and dB take phi, ddelta's write part dg/ddelta = a, and dA
             // gains alpha B x gv delta^2 psi
             const float a = av[tt][j];
-            const float u = dv * A2[j] * kLn2;
-            const float ph = zoh_phi(u, a);
+            const float ph = phs[ZOH ? tt : 0][j];
             const float bg = bs[buf][tt][gs][j] * gvf;  // alpha B gv
             p1 = j == 0 ? bg * ph : fmaf(bg, ph, p1);
             p1d = j == 0 ? bg * a : fmaf(bg, a, p1d);
-            dAt[j] = fmaf(bg * (xv * dv * dv), zoh_psi(u, a, ph), dAt[j]);
+            dAt[j] = fmaf(bg * (xv * dv * dv), pss[ZOH ? tt : 0][j], dAt[j]);
             vals[(tb * 2 + 0) * K + j] = c * ph * gvf;        // dB / alpha
           }
           vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
@@ -563,6 +574,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           const float ys = swap_add32(yq, yq);
           if (lane < CB) ypt[EXT ? pb : 0][EXT ? g : 0][EXT ? tt : 0][lane] = ys;
         }
+        // the zero-order hold's extra per-row values would otherwise be interleaved across rows
+        // by the scheduler and overflow the registers
+        if (ZOH) __builtin_amdgcn_sched_barrier(0);
       }
       reduce_scatter32(vals, lane);
       // rows past the end of the sequence are past the extent: dropped
