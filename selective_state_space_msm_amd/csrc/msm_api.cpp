@@ -309,6 +309,14 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   a.beta = beta;
   a.alpha = alpha;
   a.beta_pow_tc = (float)pow((double)beta, (double)Tc);
+  a.cus = 256;  // MI355X; replaced by the current device's count when the runtime reports it
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      a.cus = cus;
+  }
 
   hipError_t e = msm::launch_fwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f, ext,
                                  static_cast<hipStream_t>(stream));

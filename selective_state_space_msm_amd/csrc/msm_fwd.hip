@@ -40,7 +40,7 @@ namespace {
 
 // Occupancy hint: the launch plans put one or two wavefronts on a SIMD, so the scheduler may
 // spend registers on hiding LDS and transcendental latency instead of on more wavefronts.
-template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, int EXT>
+template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, int EXT, int YBP>
 __global__ __launch_bounds__(S* kWave) __attribute__((amdgpu_waves_per_eu(1, K >= 8 ? 1 : 2)))
 void fwd_kernel(const FwdArgs p) {
   using T = io<IO>;
@@ -49,9 +49,13 @@ void fwd_kernel(const FwdArgs p) {
   constexpr int BCW = 2 * K;                    // floats per (tile row, wave): B then C
   constexpr int NTHR = S * kWave;
   constexpr bool YPART = !SUMMARY && S > 1;
-  // y partials are double-buffered (one barrier per tile) except with 16 wavefronts, where
-  // two buffers would not fit in LDS next to the staged tiles; those take a second barrier
-  constexpr int YB = S >= 16 ? 1 : 2;
+  // y partials are double-buffered (one barrier per tile) when one workgroup per CU is all
+  // the grid provides (YBP = 2).  With more workgroups than CUs (YBP = 1), and always with 16
+  // wavefronts, they are single-buffered and take a second barrier: the smaller LDS lets two
+  // workgroups share a CU (measured at Bt=1, L=65536, D=2048, N=16 in 16 chunks: 1.13 ms
+  // single-buffered, 1.27 ms double-buffered; at Bt=4, L=4096, D=4096: 0.366 ms double,
+  // 0.388 ms single)
+  constexpr int YB = (S >= 16 || YBP == 1) ? 1 : 2;
 
   __shared__ float bcs[2][TT][S][BCW];
   __shared__ float ypart[YPART ? YB : 1][YPART ? S : 1][TT][kWave];
@@ -295,9 +299,11 @@ void fwd_kernel(const FwdArgs p) {
   };
   // Full tile.  The B/C broadcasts of the next batch of RB steps are read from LDS into
   // registers before the current batch is computed; the scheduling barrier keeps the compiler
-  // from sinking those reads next to their uses, where their latency would be exposed (one
-  // wavefront per SIMD has nothing else to issue meanwhile).
-  constexpr int RB = (32 / K) < TT ? (32 / K) : TT;
+  // from sinking those reads next to their uses, where their latency would be exposed.
+  // Batches of 4 steps (2 for 16 states per wavefront) keep the double buffer small (measured
+  // at Bt=4, L=4096, D=4096, N=16, 2 states per wavefront: 0.366 ms against 0.399 ms with the
+  // whole tile as one batch).
+  constexpr int RB = (32 / K) < 4 ? (32 / K) : 4;
   constexpr int NB = TT / RB;
   auto compute_tile = [&](int buf, int64_t ts, const Set& cur) {
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
@@ -419,20 +425,34 @@ void fwd_kernel(const FwdArgs p) {
   }
 }
 
+template <typename IO, int K, int S, bool BETA0, int EXT, int YBP>
+void launch_main(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.Dskip)
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true, EXT, YBP>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false, EXT, YBP>), grid, block, 0, s,
+                       a);
+}
+
 template <typename IO, int K, int S, bool BETA0, int EXT>
 hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
   const dim3 block(S * kWave);
   if (a.G > 1) {
     const dim3 grid((unsigned)(a.ncb * a.Bt * (a.G - 1)));
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false, EXT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false, EXT, 1>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(a.ncb * a.Bt * a.G));
-  if (a.Dskip)
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true, EXT>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false, EXT>), grid, block, 0, s, a);
+  // single-buffered y partials when the grid has more workgroups than the GPU has CUs
+  if constexpr (S >= 16) {
+    launch_main<IO, K, S, BETA0, EXT, 1>(a, grid, block, s);
+  } else {
+    if ((int64_t)grid.x > a.cus)
+      launch_main<IO, K, S, BETA0, EXT, 1>(a, grid, block, s);
+    else
+      launch_main<IO, K, S, BETA0, EXT, 2>(a, grid, block, s);
+  }
   return hipGetLastError();
 }
 

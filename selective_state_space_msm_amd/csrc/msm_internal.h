@@ -42,6 +42,7 @@ struct FwdArgs {
   int32_t ncb;       // channel blocks of 64
   float beta, alpha;
   float beta_pow_tc;  // beta^Tc, the velocity decay across one full chunk
+  int32_t cus;        // compute units of the device (picks the LDS layout of the y partials)
 };
 
 struct BwdArgs {
