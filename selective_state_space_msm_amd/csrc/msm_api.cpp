@@ -47,13 +47,28 @@ msm_status check_common(int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
 }
 
 // ---- forward planning ----
-int64_t fwd_max_chunks(int64_t Bt, int64_t L, int64_t D) {
+// Chunks a plan may ask for: enough workgroups to fill the GPU, at most kMaxChunks.
+int64_t fwd_plan_chunks(int64_t Bt, int64_t L, int64_t D) {
   const int64_t wg_per_chunk = Bt * ceil_div(D, kWave);
   int64_t g = ceil_div(kMaxWorkgroups, wg_per_chunk);
   if (g > kMaxChunks) g = kMaxChunks;
   const int64_t tiles = ceil_div(L, kTile);
   if (g > tiles) g = tiles;
   return g < 1 ? 1 : g;
+}
+
+// Chunks every launch needs at least: the kernels address one chunk of one batch row of an
+// (Bt, L, D) array with 32-bit byte offsets, so a chunk must stay below 2^31 bytes (with room
+// for rounding the chunk length up to a whole tile).
+int64_t fwd_min_chunks(int64_t L, int64_t D, int64_t es) {
+  const int64_t max_rows = (((int64_t)1 << 31) - 1) / (D * es) - kTile;
+  return ceil_div(L, max_rows);
+}
+
+// Chunks the workspace is sized for: the most any plan or the offset limit can need.
+int64_t fwd_max_chunks(int64_t Bt, int64_t L, int64_t D, int64_t es) {
+  const int64_t a = fwd_plan_chunks(Bt, L, D), b = fwd_min_chunks(L, D, es);
+  return a > b ? a : b;
 }
 
 bool allowed_k(int NP, int K) {
@@ -86,7 +101,7 @@ msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int64_t waves = chan_blocks * (NP / kchunk);
   const int per_simd = NP == 16 ? 4 : 2;
   int64_t G = ceil_div(per_simd * kTargetWaves, waves);
-  const int64_t gmax = fwd_max_chunks(Bt, L, D);
+  const int64_t gmax = fwd_plan_chunks(Bt, L, D);
   if (G > gmax) G = gmax;
   if (G < 1) G = 1;
   pl.states_per_wave = kchunk;
@@ -98,8 +113,8 @@ struct FwdLayout {
   size_t off_bv, off_bh, off_q, off_sd, total;
 };
 
-FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
-  const int64_t G = fwd_max_chunks(Bt, L, D);
+FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
+  const int64_t G = fwd_max_chunks(Bt, L, D, es);
   FwdLayout l{};
   if (G <= 1) return l;
   const size_t per = align_up(sizeof(float) * (size_t)(Bt * G * N * D));
@@ -202,7 +217,8 @@ const char* msm_status_string(msm_status s) {
 
 size_t msm_scan_fwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io) {
   if (check_common(Bt, L, D, N, 0.f, 1.f, io) != MSM_OK) return 0;
-  return fwd_layout(Bt, L, D, N).total;
+  if (fwd_min_chunks(L, D, io == MSM_BF16 ? 2 : 4) > kMaxChunks) return 0;
+  return fwd_layout(Bt, L, D, N, io == MSM_BF16 ? 2 : 4).total;
 }
 
 size_t msm_scan_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io) {
@@ -251,14 +267,16 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
       pl.states_per_wave = plan->states_per_wave;
     }
     if (plan->chunks != 0) {
-      if (plan->chunks < 1 || plan->chunks > fwd_max_chunks(Bt, L, D)) return MSM_ERR_INVALID_ARG;
+      if (plan->chunks < 1 || plan->chunks > fwd_plan_chunks(Bt, L, D)) return MSM_ERR_INVALID_ARG;
       pl.chunks = plan->chunks;
     }
   }
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
-  const FwdLayout lay = fwd_layout(Bt, L, D, N);
+  // a batch row's array may span at most kMaxChunks chunks of 2 GiB
+  if (fwd_min_chunks(L, D, (int64_t)es) > kMaxChunks) return MSM_ERR_INVALID_ARG;
+  const FwdLayout lay = fwd_layout(Bt, L, D, N, (int64_t)es);
   if (workspace_bytes < lay.total || (lay.total > 0 && !workspace)) return MSM_ERR_WORKSPACE;
   const size_t nst = (size_t)(Bt * D * N) * 4;
   const Range ins[] = {rng(x, nxd * es),        rng(delta, nxd * es),
@@ -274,8 +292,8 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   // kernels address a chunk with 32-bit byte offsets: keep every chunk of every (Bt,L,D)
   // array below 2^31 bytes.
   int64_t G = pl.chunks;
-  const int64_t max_rows = (((int64_t)1 << 31) - 1) / (D * (int64_t)es);
-  if (ceil_div(L, G) > max_rows) G = ceil_div(L, max_rows - kTile);
+  const int64_t gmin = fwd_min_chunks(L, D, (int64_t)es);
+  if (G < gmin) G = gmin;  // within the workspace: fwd_layout is sized for it
   int64_t Tc = ceil_div(ceil_div(L, G), kTile) * kTile;
   G = ceil_div(L, Tc);  // rounding Tc up can leave fewer non-empty chunks
 

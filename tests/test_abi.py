@@ -244,6 +244,18 @@ def test_step_validation_never_launches(lib):
     assert step(z=0x100000) == INVALID             # the gate over a state
 
 
+def test_workspace_covers_the_offset_limit(lib):
+    # one batch row of 2^20 fp32 channels over 1024 steps is 4 GiB per array: the forward must
+    # cut it into chunks below 2 GiB even when the plan asks for one, and the workspace query
+    # must leave room for those chunks' summaries
+    assert lib.msm_scan_fwd_workspace_bytes(1, 1024, 1 << 20, 16, 0) > 0
+    # a batch row beyond 64 chunks of 2 GiB is rejected
+    assert lib.msm_scan_fwd_workspace_bytes(1, 1 << 25, 1 << 20, 16, 0) == 0
+    big = dict(x=1 << 44, delta=2 << 44, A=3 << 44, B=4 << 44, C=5 << 44, y=6 << 44, Bt=1,
+               L=1 << 25, D=1 << 20, N=16)
+    assert _fwd(lib, ws=7 << 44, wsb=1 << 40, **big) == INVALID
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msm, "_lib", None)
     monkeypatch.setattr(msm, "_LIB_PATH", str(tmp_path / "missing.so"))

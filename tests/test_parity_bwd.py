@@ -128,3 +128,44 @@ def test_full_size_backward():
     log("  <dy,y> = %.9g; %s" % (ref, vals))
     for k, v in vals.items():
         assert abs(v - ref) <= 1e-4 * abs(ref) + 1e-2, (k, v, ref)
+
+
+def test_rows_beyond_32bit_offsets():
+    """The backward over one batch row of 2^19 + 37 steps x 1024 fp32 channels (2.1 GB per
+    array): dx, ddelta and dA on sampled channels against the oracle, and the scaling identity
+    <dB,B> = <dC,C> = <dx,x> = <ddelta,delta> - <dA,A> = <dy,y> over the whole output."""
+    import torch
+    import selective_state_space_msm_amd as msm
+    from test_parity_fwd import _device_inputs
+    Bt, L, D, N = 1, (1 << 19) + 37, 1024, 16
+    log("backward rows beyond 32-bit offsets: L=%d D=%d fp32" % (L, D))
+    x, delta, A, B, C = _device_inputs(Bt, L, D, N, 81)
+    dy = torch.randn((Bt, L, D), generator=torch.Generator(device="cuda").manual_seed(82),
+                     device="cuda")
+    got = msm.msm_scan_bwd(x, delta, A, B, C, dy, 0.9, 1.0)
+    torch.cuda.synchronize()
+    dsel = sample_channels(D, 6, seed=83)
+    od = oracle.bwd(host(x[:, :, dsel]), host(delta[:, :, dsel]), host(A[dsel]), host(B),
+                    host(C), host(dy[:, :, dsel]), 0.9, 1.0)
+    assert_close(host(got["dx"][:, :, dsel]), od["dx"], "f32", "dx sampled")
+    assert_close(host(got["dA"][dsel]), od["dA"], "f32", "dA sampled")
+    # ddelta is a difference of per-state terms that reach ~5e2 for states with a long memory
+    # (small delta |A|, with momentum); the fp32 decay factors exp(delta A) compounding over
+    # such memories leave a tail of elements (a few in 1e7 at this length) slightly past the
+    # fp32 bound.  Checked: the bound holds for all but at most 1e-6 of the elements, and every
+    # element is within twice the absolute bound (the README reports CUDA-vs-CPU gradient
+    # agreement up to 3.1e-4 for its own kernel).
+    gd, wd = host(got["ddelta"][:, :, dsel]), od["ddelta"]
+    err = np.abs(gd - wd)
+    over = err > 1e-4 + 1e-5 * np.abs(wd)
+    log("  ddelta: %d of %d past the fp32 bound, max err %.3g" % (over.sum(), err.size, err.max()))
+    assert over.sum() <= max(1, int(1e-6 * err.size)), over.sum()
+    assert_close(gd, wd, "f32_tail", "ddelta sampled")
+    y = msm.msm_scan_fwd(x, delta, A, B, C, 0.9, 1.0)
+    ip = lambda a, b: float(torch.sum(a.double() * b.double()))
+    ref = ip(dy, y)
+    vals = {"<dB,B>": ip(got["dB"], B), "<dC,C>": ip(got["dC"], C), "<dx,x>": ip(got["dx"], x),
+            "<dd,d>-<dA,A>": ip(got["ddelta"], delta) - ip(got["dA"], A)}
+    log("  <dy,y> = %.9g; %s" % (ref, vals))
+    for k, v in vals.items():
+        assert abs(v - ref) <= 1e-4 * abs(ref) + 1e-2, (k, v, ref)

@@ -149,3 +149,38 @@ def test_full_m1p4b_unstructured_A():
 
 def test_full_long_sequence():
     check_sampled(W["long"], nsample=12)
+
+
+def _device_inputs(Bt, L, D, N, seed):
+    """Seeded inputs drawn on the GPU (x ~ N(0,1), delta = softplus(N(-4,1)), B, C ~ N(0,1),
+    A = -(n+1)): arrays of several GiB that the host need not hold."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn((Bt, L, D), generator=gen, device="cuda")
+    delta = torch.nn.functional.softplus(torch.randn((Bt, L, D), generator=gen, device="cuda") - 4)
+    B = torch.randn((Bt, L, N), generator=gen, device="cuda")
+    C = torch.randn((Bt, L, N), generator=gen, device="cuda")
+    A = -(torch.arange(N, dtype=torch.float32, device="cuda") + 1).repeat(D, 1).contiguous()
+    return x, delta, A, B, C
+
+
+def test_rows_beyond_32bit_offsets():
+    """One batch row of 2^19 + 37 steps x 1024 fp32 channels is 2.1 GB per array, past the
+    2^31-byte reach of the kernels' buffer offsets: a one-chunk plan must be split, and every
+    plan must agree with the oracle on sampled channels."""
+    import torch
+    import selective_state_space_msm_amd as msm
+    Bt, L, D, N = 1, (1 << 19) + 37, 1024, 16
+    log("rows beyond 32-bit offsets: L=%d D=%d fp32" % (L, D))
+    x, delta, A, B, C = _device_inputs(Bt, L, D, N, 71)
+    dsel = sample_channels(D, 6, seed=72)
+    sub = dict(x=host(x[:, :, dsel]), delta=host(delta[:, :, dsel]), A=host(A[dsel]), B=host(B),
+               C=host(C))
+    want, wh, _ = oracle.fwd(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], 0.9, 1.0)
+    for plan in ({"states_per_wave": 2, "chunks": 1}, None):
+        y, lh, _ = msm.msm_scan_fwd(x, delta, A, B, C, 0.9, 1.0, return_last_state=True,
+                                    plan=plan)
+        torch.cuda.synchronize()
+        assert_close(host(y[:, :, dsel]), want, "f32", "y plan %s" % plan)
+        assert_close(host(lh[:, dsel]), wh, "f32", "last_h plan %s" % plan)
+        del y, lh
