@@ -84,13 +84,30 @@ def measured_traffic(name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+WARM_SECONDS = 0.2
+last_warmup = 0  # warm-up calls run by the latest timed()
+
+
 def timed(fn, stream, steps, warmup):
-    """Run fn warmup times, then time `steps` calls with HIP events on `stream`.  Returns the
-    mean duration per call in ms and the list of per-call durations."""
+    """Run fn at least `warmup` times and for at least WARM_SECONDS of sustained work (the GPU
+    raises its clocks only under sustained load: after an idle gap, a few milliseconds of
+    warm-up time the kernels at lower clocks), then time `steps` calls with HIP events on
+    `stream`.  Returns the mean duration per call in ms and the list of per-call durations;
+    the number of warm-up calls run is left in last_warmup."""
     import torch
+    n = 0
     for _ in range(warmup):
         fn()
+        n += 1
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARM_SECONDS:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    global last_warmup
+    last_warmup = n
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with torch.cuda.stream(stream):
         evs[0].record(stream)
@@ -338,6 +355,7 @@ def main(argv=None):
     if w.direction != "fwd":
         raise SystemExit("--workload must be a forward workload")
     ms, per, plan = bench_fwd(w, args.steps, args.warmup, stream)
+    fwd_warmup_run = last_warmup
     sec = ms / 1e3
     beta0 = w.beta == 0.0
     slots = w.updates * SLOTS_PER_UPDATE[beta0]
@@ -351,6 +369,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": fwd_warmup_run,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
