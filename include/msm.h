@@ -83,7 +83,9 @@ const char* msm_status_string(msm_status s);
 size_t msm_scan_fwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io);
 size_t msm_scan_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io);
 
-/* The plan msm_scan_fwd / msm_scan_bwd would use for this shape (written to *plan). */
+/* The plan msm_scan_fwd / msm_scan_bwd would use for this shape (written to *plan).  The fused
+ * backward (msm_selective_scan_bwd with any extra) takes two states per wavefront half at 5-16
+ * states instead. */
 msm_status msm_scan_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
                              float beta, msm_plan* plan);
 msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import assert_close, dev, host, inputs_to_device, log, sample_channels, sub_problem
+from gpu_util import (TOL, assert_close, dev, host, inputs_to_device, log, sample_channels,
+                      sub_problem)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,13 +79,31 @@ def oracle_bwd(inp, h0=None, v0=None, dlh=None, dlv=None):
                             h0=h0, v0=v0, dlast_h=dlh, dlast_v=dlv, zoh=inp.get("zoh", False))
 
 
+def assert_sum_close(got, want, absum, io, what):
+    """A sum over batch and time (the bias gradient) against the oracle, to the error bound of a
+    sum of rounded terms: atol + rtol * (sum of the terms' magnitudes), per channel.  ddelta's
+    terms carry a consistent-sign error from the fp32 decay factors, which adds up over the
+    rows, so the bound scales with the magnitudes summed rather than with the (cancelling)
+    result."""
+    rtol, atol = TOL[io]
+    err = np.abs(np.asarray(got, np.float64) - want)
+    lim = atol + rtol * absum
+    bad = err > lim
+    assert not bad.any(), "%s: %d of %d past the sum bound; worst err %.3g (bound %.3g)" % (
+        what, bad.sum(), bad.size, err.max(), lim[np.argmax(err - lim)])
+
+
 def compare(got, want, names, io, tag):
     for k in names:
         if want.get(k) is None:
             assert got.get(k) is None, k
             continue
         tol = "f32" if (k in F32_OUT and io == "f32") or k in ("last_h", "last_v") else io
-        assert_close(host(got[k]), want[k], tol, "%s %s" % (k, tag))
+        if k == "ddelta_bias":
+            assert_sum_close(host(got[k]), want[k], np.abs(want["ddelta"]).sum(axis=(0, 1)), tol,
+                             "%s %s" % (k, tag))
+        else:
+            assert_close(host(got[k]), want[k], tol, "%s %s" % (k, tag))
 
 
 def check(inp, fplan=None, bplan=None, state=False, tag=""):
@@ -173,8 +192,11 @@ def test_plain_equivalence():
     for k in ("dx", "ddelta", "dA", "dB", "dC", "dDskip"):
         assert torch.equal(b0[k], b1[k]), k
         assert_close(host(b2[k]), host(b0[k]), w.io, "zero bias " + k)
-    assert_close(host(b2["ddelta_bias"]), host(b0["ddelta"]).sum(axis=(0, 1)), w.io,
-                 "zero bias ddelta_bias")
+    want = oracle.fused_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["dy"],
+                            inp["beta"], inp["alpha"], Dskip=inp["Dskip"],
+                            delta_bias=np.zeros(w.D, np.float32))
+    assert_sum_close(host(b2["ddelta_bias"]), want["ddelta_bias"],
+                     np.abs(want["ddelta"]).sum(axis=(0, 1)), w.io, "zero bias ddelta_bias")
 
 
 def test_full_size_forward():
@@ -211,8 +233,10 @@ def test_full_size_backward():
     od = oracle_bwd(sub)
     for k in ("dx", "ddelta", "dz"):
         assert_close(got[k][:, :, dsel], od[k], w.io, "%s sampled" % k)
-    for k in ("dA", "ddelta_bias", "dDskip"):
+    for k in ("dA", "dDskip"):
         assert_close(got[k][dsel], od[k], w.io, "%s sampled" % k)
+    assert_sum_close(got["ddelta_bias"][dsel], od["ddelta_bias"],
+                     np.abs(od["ddelta"]).sum(axis=(0, 1)), w.io, "ddelta_bias sampled")
 
 
 # ---- zero-order hold ----
@@ -257,8 +281,10 @@ def test_zoh_full_size():
     od = oracle_bwd(sub_problem(inp, dsel=dsel))
     for k in ("dx", "ddelta", "dz"):
         assert_close(got[k][:, :, dsel], od[k], wb.io, "zoh %s sampled" % k)
-    for k in ("dA", "ddelta_bias", "dDskip"):
+    for k in ("dA", "dDskip"):
         assert_close(got[k][dsel], od[k], wb.io, "zoh %s sampled" % k)
+    assert_sum_close(got["ddelta_bias"][dsel], od["ddelta_bias"],
+                     np.abs(od["ddelta"]).sum(axis=(0, 1)), wb.io, "zoh ddelta_bias sampled")
     o0 = oracle_bwd(sub_problem(inp, bsel=slice(0, 1)))
     for k in ("dB", "dC"):
         assert_close(got[k][0:1], o0[k], wb.io, "zoh %s row 0" % k)
