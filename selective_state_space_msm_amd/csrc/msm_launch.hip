@@ -22,9 +22,20 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdArgs p) {
     const int64_t which = (i / p.N) % 2;
     const int64_t bt = i / (2 * p.N);  // b * L + t
     const int64_t b = bt / p.L, t = bt % p.L;
+    // the channel blocks' partials sit L * 2 * NP floats apart; eight loads are issued before
+    // they are added (in the same fixed order), which keeps several in flight per thread
+    const float* src = p.dbc_part + ((b * p.ncb) * p.L + t) * 2 * p.NP + which * p.NP + n;
+    const int64_t stride = p.L * 2 * p.NP;
     float s = 0.f;
-    for (int cb = 0; cb < p.ncb; ++cb)
-      s += p.dbc_part[((b * p.ncb + cb) * p.L + t) * 2 * p.NP + which * p.NP + n];
+    int cb = 0;
+    for (; cb + 8 <= p.ncb; cb += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(cb + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; cb < p.ncb; ++cb) s += src[cb * stride];
     if (which == 0)
       T::store(p.dB, bt * p.N + n, s * p.alpha);
     else
