@@ -82,6 +82,10 @@ class Oracle:
                                              Dbl, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P,
                                              Int]
         lib.msm_oracle_fused_bwd.restype = Int
+        lib.msm_oracle_complex_fwd.argtypes = lib.msm_oracle_fwd.argtypes
+        lib.msm_oracle_complex_fwd.restype = Int
+        lib.msm_oracle_complex_bwd.argtypes = lib.msm_oracle_bwd.argtypes
+        lib.msm_oracle_complex_bwd.restype = Int
         lib.msm_oracle_max_threads.argtypes = []
         lib.msm_oracle_max_threads.restype = Int
         self.lib = lib
@@ -229,6 +233,55 @@ class Oracle:
                                       h0=h, v0=v, zoh=zoh)
         return y.reshape(Bt, D), hn, vn
 
+    def complex_fwd(self, x, delta, A, B, C, beta, alpha, Dskip=None, h0=None, v0=None,
+                    threads=0):
+        """Complex-valued SSM forward in fp64: A (D, N), B, C (Bt, L, N), h0, v0 (Bt, D, N)
+        complex; x, delta (Bt, L, D) real.  y = Re(sum_n C h) (+ Dskip x).  Returns (y real,
+        last_h, last_v complex)."""
+        x, delta = _f64(x), _f64(delta)
+        cz = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a, np.complex128))
+        A, B, C, h0, v0 = (cz(a) for a in (A, B, C, h0, v0))
+        Bt, L, D = x.shape
+        N = A.shape[1]
+        if A.shape != (D, N) or B.shape != (Bt, L, N) or C.shape != B.shape:
+            raise ValueError("inconsistent shapes")
+        Ds = None if Dskip is None else _f64(Dskip)
+        y = np.empty((Bt, L, D))
+        lh, lv = np.empty((Bt, D, N), np.complex128), np.empty((Bt, D, N), np.complex128)
+        rc = self.lib.msm_oracle_complex_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                             _ptr(Ds), _ptr(h0), _ptr(v0), float(beta),
+                                             float(alpha), Bt, L, D, N, _ptr(y), _ptr(lh),
+                                             _ptr(lv), int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_complex_fwd failed (%d)" % rc)
+        return y, lh, lv
+
+    def complex_bwd(self, x, delta, A, B, C, dy, beta, alpha, Dskip=None, h0=None, v0=None,
+                    dlast_h=None, dlast_v=None, threads=0):
+        """Gradients of the complex-valued SSM (real loss; each complex gradient is
+        dl/d(re) + i dl/d(im)).  Returns dx, ddelta, dDskip real and dA, dB, dC, dh0, dv0
+        complex."""
+        x, delta, dy = _f64(x), _f64(delta), _f64(dy)
+        cz = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a, np.complex128))
+        A, B, C, h0, v0, dlh, dlv = (cz(a) for a in (A, B, C, h0, v0, dlast_h, dlast_v))
+        Bt, L, D = x.shape
+        N = A.shape[1]
+        Ds = None if Dskip is None else _f64(Dskip)
+        out = dict(dx=np.empty((Bt, L, D)), ddelta=np.empty((Bt, L, D)),
+                   dA=np.empty((D, N), np.complex128), dB=np.empty((Bt, L, N), np.complex128),
+                   dC=np.empty((Bt, L, N), np.complex128),
+                   dDskip=None if Ds is None else np.empty((D,)),
+                   dh0=np.empty((Bt, D, N), np.complex128), dv0=np.empty((Bt, D, N), np.complex128))
+        rc = self.lib.msm_oracle_complex_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Ds), _ptr(dy), _ptr(h0),
+            _ptr(v0), _ptr(dlh), _ptr(dlv), float(beta), float(alpha), Bt, L, D, N,
+            _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out["dDskip"]), _ptr(out["dh0"]), _ptr(out["dv0"]),
+            int(threads))
+        if rc != 0:
+            raise RuntimeError("msm_oracle_complex_bwd failed (%d)" % rc)
+        return out
+
 
 _default = None
 
@@ -265,6 +318,14 @@ def fused_bwd(*args, **kw):
 
 def step(*args, **kw):
     return default().step(*args, **kw)
+
+
+def complex_fwd(*args, **kw):
+    return default().complex_fwd(*args, **kw)
+
+
+def complex_bwd(*args, **kw):
+    return default().complex_bwd(*args, **kw)
 
 
 def max_threads() -> int:

@@ -67,10 +67,25 @@
  * backward then reads dx += alpha g B gv, ddelta += alpha B x gv a + A a h gh,
  * dA += delta a h gh + alpha B x gv dg/dA, dB += alpha g x gv.
  *
+ * Complex-valued SSM (Momentum Mamba README, "Complex Number Support": A, B and C complex; the
+ * complextorch page, "The diagonal SSM": a complex diagonal state).  Per (b, d, n), with complex
+ * a_t = exp(delta_t A), v_t = beta v_{t-1} + alpha delta_t B_t x_t, h_t = a_t h_{t-1} + v_t, and
+ * the real output y_t = Re(sum_n C_t h_t) (+ Dskip x_t) -- x, delta, y stay real; the pages do not
+ * say how a real output is taken from the complex readout, and the real part is the plainest
+ * reading.  Complex arrays are interleaved (re, im): A (D, N, 2), B, C (Bt, L, N, 2), states
+ * (Bt, D, N, 2).  Its backward, for the real loss sum(dy y) (+ <dlast_h, last_h> + <dlast_v,
+ * last_v> over real and imaginary parts), with every complex gradient written as
+ * G = dl/d(re) + i dl/d(im):
+ *   gh_t = dy_t conj(C_t) + conj(a_{t+1}) gh_{t+1},   gv_t = gh_t + beta gv_{t+1}
+ *   dx += alpha delta Re(conj(gv) B),   ddelta += alpha x Re(conj(gv) B) + Re(conj(gh) A a h_{t-1})
+ *   dA += conj(delta a h_{t-1}) gh,     dB += alpha delta x gv,     dC += dy conj(h_t)
+ *   dh0 = conj(a_0) gh_0,   dv0 = beta gv_0.
+ *
  * Threads: the forward is split over (b, d) channel pairs, which are independent.  The
  * backward is split over batch rows b; dA and dDskip are first summed per row and the rows are
  * then added in order, so results do not depend on the thread count.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -412,4 +427,151 @@ int msm_oracle_fused_bwd(const double* x, const double* delta, const double* A, 
   free(ge);
   free(yr);
   return rc;
+}
+
+/* ---- complex-valued SSM (see the header) ---- */
+
+static double complex cget(const double* p, int64_t i) { return p[2 * i] + I * p[2 * i + 1]; }
+
+static void cput(double* p, int64_t i, double complex z) {
+  p[2 * i] = creal(z);
+  p[2 * i + 1] = cimag(z);
+}
+
+int msm_oracle_complex_fwd(const double* x, const double* delta, const double* A,
+                           const double* B, const double* C, const double* Dskip,
+                           const double* h0, const double* v0, double beta, double alpha,
+                           int64_t Bt, int64_t L, int64_t D, int64_t N, double* y,
+                           double* last_h, double* last_v, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  set_threads(nthreads);
+  int64_t nchan = Bt * D;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t bd = 0; bd < nchan; ++bd) {
+    int64_t b = bd / D, d = bd % D;
+    for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const int64_t s_i = (b * D + d) * N + n;
+      double complex v = v0 ? cget(v0, s_i) : 0.0;
+      double complex h = h0 ? cget(h0, s_i) : 0.0;
+      double complex An = cget(A, d * N + n);
+      for (int64_t t = 0; t < L; ++t) {
+        double dt = delta[(b * L + t) * D + d];
+        double xt = x[(b * L + t) * D + d];
+        double complex a = cexp(dt * An);
+        double complex w = alpha * dt * xt * cget(B, (b * L + t) * N + n);
+        v = beta * v + w;
+        h = a * h + v;
+        y[(b * L + t) * D + d] += creal(cget(C, (b * L + t) * N + n) * h);
+      }
+      if (last_h) cput(last_h, s_i, h);
+      if (last_v) cput(last_v, s_i, v);
+    }
+    if (Dskip)
+      for (int64_t t = 0; t < L; ++t) y[(b * L + t) * D + d] += Dskip[d] * x[(b * L + t) * D + d];
+  }
+  return 0;
+}
+
+int msm_oracle_complex_bwd(const double* x, const double* delta, const double* A,
+                           const double* B, const double* C, const double* Dskip,
+                           const double* dy, const double* h0, const double* v0,
+                           const double* dlast_h, const double* dlast_v, double beta,
+                           double alpha, int64_t Bt, int64_t L, int64_t D, int64_t N, double* dx,
+                           double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
+                           double* dh0, double* dv0, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 0) return 1;
+  if (Dskip && !dDskip) return 1;
+  set_threads(nthreads);
+  memset(dx, 0, sizeof(double) * (size_t)(Bt * L * D));
+  memset(ddelta, 0, sizeof(double) * (size_t)(Bt * L * D));
+  memset(dB, 0, sizeof(double) * (size_t)(Bt * L * N * 2));
+  memset(dC, 0, sizeof(double) * (size_t)(Bt * L * N * 2));
+  double* dA_rows = (double*)calloc((size_t)(Bt * D * N * 2) + 1, sizeof(double));
+  double* dD_rows = (double*)calloc((size_t)(Bt * D) + 1, sizeof(double));
+  if (!dA_rows || !dD_rows) { free(dA_rows); free(dD_rows); return 2; }
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bt; ++b) {
+    double complex* hs = (double complex*)malloc(sizeof(double complex) * (size_t)(L + 1));
+    if (!hs) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t n = 0; n < N; ++n) {
+        const double complex An = cget(A, d * N + n);
+        const int64_t s_i = (b * D + d) * N + n;
+        double complex v = v0 ? cget(v0, s_i) : 0.0;
+        double complex h = h0 ? cget(h0, s_i) : 0.0;
+        hs[0] = h;
+        for (int64_t t = 0; t < L; ++t) {
+          double dt = delta[(b * L + t) * D + d];
+          double xt = x[(b * L + t) * D + d];
+          v = beta * v + alpha * dt * xt * cget(B, (b * L + t) * N + n);
+          h = cexp(dt * An) * h + v;
+          hs[t + 1] = h;
+        }
+        double complex gh_next = dlast_h ? cget(dlast_h, s_i) : 0.0, gv_next = 0.0;
+        double complex a_next = 1.0;
+        double complex dAn = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          int64_t i = (b * L + t) * D + d;
+          int64_t j = (b * L + t) * N + n;
+          double dt = delta[i], xt = x[i], dyt = dy[i];
+          double complex a = cexp(dt * An);
+          double complex Bj = cget(B, j), Cj = cget(C, j);
+          double complex gh = dyt * conj(Cj) + conj(a_next) * gh_next;
+          double complex gv = gh + beta * gv_next;
+          if (t == L - 1 && dlast_v) gv += cget(dlast_v, s_i);
+          double complex hprev = hs[t];
+          double wr = creal(conj(gv) * Bj); /* Re(conj(gv) B) */
+          dx[i] += alpha * dt * wr;
+          ddelta[i] += alpha * xt * wr + creal(conj(gh) * An * a * hprev);
+          dAn += conj(dt * a * hprev) * gh;
+          double complex gB = alpha * dt * xt * gv;
+          double complex gC = dyt * conj(hs[t + 1]);
+          /* j belongs to batch row b: one thread writes it, channels in order */
+          dB[2 * j] += creal(gB);
+          dB[2 * j + 1] += cimag(gB);
+          dC[2 * j] += creal(gC);
+          dC[2 * j + 1] += cimag(gC);
+          gh_next = gh;
+          gv_next = gv;
+          a_next = a;
+        }
+        dA_rows[2 * ((b * D + d) * N + n)] = creal(dAn);
+        dA_rows[2 * ((b * D + d) * N + n) + 1] = cimag(dAn);
+        if (dh0)
+          cput(dh0, s_i, L > 0 ? conj(a_next) * gh_next : (dlast_h ? cget(dlast_h, s_i) : 0.0));
+        if (dv0) cput(dv0, s_i, L > 0 ? beta * gv_next : (dlast_v ? cget(dlast_v, s_i) : 0.0));
+      }
+      if (Dskip) {
+        for (int64_t t = 0; t < L; ++t) {
+          int64_t i = (b * L + t) * D + d;
+          dx[i] += Dskip[d] * dy[i];
+          dD_rows[b * D + d] += dy[i] * x[i];
+        }
+      }
+    }
+    free(hs);
+  }
+  if (failed) { free(dA_rows); free(dD_rows); return 2; }
+  for (int64_t k = 0; k < D * N * 2; ++k) {
+    double s = 0.0;
+    for (int64_t b = 0; b < Bt; ++b) s += dA_rows[b * D * N * 2 + k];
+    dA[k] = s;
+  }
+  if (Dskip) {
+    for (int64_t d = 0; d < D; ++d) {
+      double s = 0.0;
+      for (int64_t b = 0; b < Bt; ++b) s += dD_rows[b * D + d];
+      dDskip[d] = s;
+    }
+  }
+  free(dA_rows);
+  free(dD_rows);
+  return 0;
 }

@@ -731,6 +731,125 @@ def pin_zoh_finite_differences(orc):
                                      "fd %.9g analytic %.9g" % (gname, i, fd, an))
 
 
+
+# ---------------------------------------------------------------------------------------------
+# Complex-valued SSM (README, "Complex Number Support"; complextorch, "The diagonal SSM")
+# ---------------------------------------------------------------------------------------------
+
+def _rand_complex_problem(rng, Bt, L, D, N):
+    x = rng.standard_normal((Bt, L, D))
+    delta = np.exp(rng.uniform(np.log(1e-2), np.log(0.5), size=(Bt, L, D)))
+    A = (-np.exp(rng.uniform(np.log(0.3), np.log(3.0), size=(D, N)))
+         + 1j * rng.uniform(-4.0, 4.0, size=(D, N)))
+    B = rng.standard_normal((Bt, L, N)) + 1j * rng.standard_normal((Bt, L, N))
+    C = rng.standard_normal((Bt, L, N)) + 1j * rng.standard_normal((Bt, L, N))
+    return x, delta, A, B, C
+
+
+def pin_complex_real_case(orc):
+    """With every imaginary part zero the complex scan is the real one: same y, states and
+    gradients, and zero imaginary gradients."""
+    rng = np.random.default_rng(71)
+    Bt, L, D, N = 2, 9, 3, 4
+    x, delta, A, B, C, Ds = _rand_problem(rng, Bt, L, D, N, True)
+    h0, v0 = _rand_state(rng, Bt, D, N)
+    dy = rng.standard_normal((Bt, L, D))
+    dlh, dlv = _rand_state(rng, Bt, D, N)
+    beta, alpha = 0.8, 0.7
+    y, lh, lv = orc.fwd(x, delta, A, B, C, beta, alpha, Dskip=Ds, h0=h0, v0=v0)
+    yc, lhc, lvc = orc.complex_fwd(x, delta, A + 0j, B + 0j, C + 0j, beta, alpha, Dskip=Ds,
+                                   h0=h0 + 0j, v0=v0 + 0j)
+    close(yc, y, rtol=1e-13, atol=1e-14, what="complex real-case y")
+    close(lhc.real, lh, rtol=1e-13, atol=1e-14, what="complex real-case h")
+    close(lvc.imag, 0.0 * lv, rtol=0, atol=0, what="complex real-case v imaginary part")
+    g = orc.bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds, h0=h0, v0=v0, dlast_h=dlh,
+                dlast_v=dlv)
+    gc = orc.complex_bwd(x, delta, A + 0j, B + 0j, C + 0j, dy, beta, alpha, Dskip=Ds,
+                         h0=h0 + 0j, v0=v0 + 0j, dlast_h=dlh + 0j, dlast_v=dlv + 0j)
+    for k in ("dx", "ddelta", "dDskip"):
+        close(gc[k], g[k], rtol=1e-12, atol=1e-13, what="complex real-case %s" % k)
+    for k in ("dA", "dB", "dC", "dh0", "dv0"):
+        close(gc[k].real, g[k], rtol=1e-12, atol=1e-13, what="complex real-case %s" % k)
+        close(gc[k].imag, 0.0 * g[k], rtol=0, atol=1e-15, what="complex real-case Im %s" % k)
+
+
+def pin_complex_convolution(orc):
+    """beta = 0 with constant coefficients: y is the real part of the convolution of x with the
+    complex kernel K_k = sum_n C_n a_n^k delta B_n (numpy's complex powers and np.convolve), the
+    convolution view of the complextorch page's diagonal SSM."""
+    rng = np.random.default_rng(73)
+    L, N = 30, 4
+    A = np.array([-0.5 + 3.1j, -0.9 - 1.2j, -0.2 + 0.4j, -1.5 + 0.0j])
+    dlt = 0.3
+    xs = rng.standard_normal(L)
+    Bv = rng.standard_normal(N) + 1j * rng.standard_normal(N)
+    Cv = rng.standard_normal(N) + 1j * rng.standard_normal(N)
+    a = np.exp(dlt * A)
+    K = np.array([np.sum(Cv * a ** k * dlt * Bv) for k in range(L)])
+    want = np.convolve(xs, K.real)[:L]
+    y, _, _ = orc.complex_fwd(xs.reshape(1, L, 1), np.full((1, L, 1), dlt), A.reshape(1, N),
+                              np.tile(Bv, (1, L, 1)), np.tile(Cv, (1, L, 1)), 0.0, 1.0)
+    close(y[0, :, 0], want, rtol=1e-11, atol=1e-12, what="complex convolution")
+
+
+def pin_complex_conjugate_pairs(orc):
+    """States in conjugate pairs (A, B, C and their conjugates) give twice the real part of one
+    of them: y(pair) = 2 y(single) - the convention S4D uses to keep half the states."""
+    rng = np.random.default_rng(79)
+    Bt, L, D, N = 1, 12, 2, 3
+    x, delta, A, B, C = _rand_complex_problem(rng, Bt, L, D, N)
+    y1, _, _ = orc.complex_fwd(x, delta, A, B, C, 0.6, 1.0)
+    y2, _, _ = orc.complex_fwd(x, delta, np.concatenate([A, A.conj()], 1),
+                               np.concatenate([B, B.conj()], 2), np.concatenate([C, C.conj()], 2),
+                               0.6, 1.0)
+    close(y2, 2 * y1, rtol=1e-12, atol=1e-13, what="conjugate pairs")
+
+
+def pin_complex_finite_differences(orc):
+    """Central differences of the complex scan's real loss for every input, real and imaginary
+    parts separately, with an initial state and terminal adjoints."""
+    rng = np.random.default_rng(83)
+    Bt, L, D, N = 2, 5, 2, 2
+    beta, alpha = 0.7, 0.9
+    x, delta, A, B, C = _rand_complex_problem(rng, Bt, L, D, N)
+    Ds = rng.standard_normal(D)
+    h0 = rng.standard_normal((Bt, D, N)) + 1j * rng.standard_normal((Bt, D, N))
+    v0 = rng.standard_normal((Bt, D, N)) + 1j * rng.standard_normal((Bt, D, N))
+    dy = rng.standard_normal((Bt, L, D))
+    dlh = rng.standard_normal((Bt, D, N)) + 1j * rng.standard_normal((Bt, D, N))
+    dlv = rng.standard_normal((Bt, D, N)) + 1j * rng.standard_normal((Bt, D, N))
+    p = dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Ds, h0=h0, v0=v0)
+    g = orc.complex_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=Ds, h0=h0, v0=v0, dlast_h=dlh,
+                        dlast_v=dlv)
+
+    def loss():
+        y, lh, lv = orc.complex_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], beta, alpha,
+                                    Dskip=p["Dskip"], h0=p["h0"], v0=p["v0"])
+        return float(np.sum(dy * y) + np.sum(dlh.real * lh.real + dlh.imag * lh.imag)
+                     + np.sum(dlv.real * lv.real + dlv.imag * lv.imag))
+
+    eps = 1e-6
+    for pname, gname in [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
+                         ("Dskip", "dDskip"), ("h0", "dh0"), ("v0", "dv0")]:
+        arr = p[pname]
+        parts = [1.0, 1j] if np.iscomplexobj(arr) else [1.0]
+        for i in np.ndindex(arr.shape):
+            for u in parts:
+                orig = arr[i]
+                arr[i] = orig + eps * u
+                lp = loss()
+                arr[i] = orig - eps * u
+                lm = loss()
+                arr[i] = orig
+                fd = (lp - lm) / (2 * eps)
+                an = g[gname][i]
+                an = an.real if u == 1.0 else an.imag
+                if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                    raise AssertionError("complex finite difference mismatch for %s%s %s: fd %.9g "
+                                         "analytic %.9g" % (gname, i, "re" if u == 1.0 else "im",
+                                                            fd, an))
+
+
 ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_retention_gate_table, pin_closed_form, pin_matrix_form, pin_convolution,
             pin_beta0_equivalence, pin_structure, pin_finite_differences,
@@ -738,4 +857,5 @@ ALL_PINS = [pin_retention_fig2, pin_write_ratio_fig3, pin_two_updates_fig5,
             pin_continuation, pin_state_finite_differences, pin_bwd_continuation,
             pin_fused_delta_transform, pin_fused_gate, pin_fused_finite_differences,
             pin_step_sequence, pin_zoh_ode, pin_zoh_retention_gate_table, pin_zoh_limit,
-            pin_zoh_finite_differences]
+            pin_zoh_finite_differences, pin_complex_real_case, pin_complex_convolution,
+            pin_complex_conjugate_pairs, pin_complex_finite_differences]

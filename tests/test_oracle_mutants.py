@@ -71,6 +71,16 @@ MUTANTS = [
     ("zoh_dA_drops_g", "return (dt * exp(u) - expm1(u) / An) / An;", "return (dt * exp(u)) / An;", 0),
     ("zoh_ignored_in_fused", "double g = write_coef(dt, A[d * N + n], zoh);",
      "double g = write_coef(dt, A[d * N + n], 0);", 0),
+    # complex-valued SSM
+    ("complex_adjoint_without_conj", "double complex gh = dyt * conj(Cj) + conj(a_next) * gh_next;",
+     "double complex gh = dyt * conj(Cj) + a_next * gh_next;", 0),
+    ("complex_readout_conj", "double complex gh = dyt * conj(Cj) + conj(a_next) * gh_next;",
+     "double complex gh = dyt * Cj + conj(a_next) * gh_next;", 0),
+    ("complex_dA_without_conj", "dAn += conj(dt * a * hprev) * gh;", "dAn += dt * a * hprev * gh;", 0),
+    ("complex_dC_without_conj", "double complex gC = dyt * conj(hs[t + 1]);",
+     "double complex gC = dyt * hs[t + 1];", 0),
+    ("complex_output_imag", "y[(b * L + t) * D + d] += creal(cget(C, (b * L + t) * N + n) * h);",
+     "y[(b * L + t) * D + d] += cimag(cget(C, (b * L + t) * N + n) * h);", 0),
 ]
 
 
