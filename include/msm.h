@@ -221,6 +221,49 @@ msm_status msm_scan_step(const void* x, const void* delta, const float* A, const
                          int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
                          void* stream);
 
+/* Complex-valued scan (Momentum Mamba README, "Complex Number Support": the same recurrence
+ * with A, B and C complex; complextorch, "The diagonal SSM", for the complex diagonal state).
+ * x, delta, y, dy, dx, ddelta are real (Bt, L, D) io arrays as above; for every (b, d, n):
+ *     a_t = exp(delta[b,t,d] * A[d,n])                 (complex exponential)
+ *     v_t = beta * v_{t-1} + alpha * delta[b,t,d] * x[b,t,d] * B[b,t,n]
+ *     h_t = a_t * h_{t-1} + v_t
+ *     y[b,t,d] = Re(sum_n C[b,t,n] * h_t)  (+ Dskip[d] * x[b,t,d])
+ * Complex arrays are interleaved (re, im) pairs, i.e. an extra trailing dimension of 2:
+ *   A, dA: (D, N, 2) fp32; B, C, dB, dC: (Bt, L, N, 2) in the io dtype (for MSM_F32 the memory
+ *   of a complex64 array); h0, v0, last_h, last_v, dlast_h, dlast_v, dh0, dv0: (Bt, D, N, 2) fp32.
+ * The real part of C h is the readout (a conjugate-pair convention, C h + conj(C h), would be
+ * twice this).  h0, v0 (NULL = zero) start the scan; last_h, last_v (may be NULL) receive the
+ * final state.  Requirements as msm_scan_fwd, and 17 * N * D * 8 < 2^31 (the kernels address
+ * 17 rows of the state history with 32-bit offsets).
+ * Needs no workspace. */
+msm_status msm_scan_complex_fwd(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, const float* h0,
+                                const float* v0, void* y, float* last_h, float* last_v,
+                                int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                                float alpha, msm_dtype io, void* stream);
+
+/* Workspace of msm_scan_complex_bwd: the state history Bt * (L + 1) * N * D * 8 bytes plus the
+ * per-block partial sums.  Returns 0 for invalid sizes. */
+size_t msm_scan_complex_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                            msm_dtype io);
+
+/* Backward of msm_scan_complex_fwd for the real loss
+ *     sum(dy * y) + <dlast_h, last_h> + <dlast_v, last_v>,   <u, w> = Re sum conj(u) w
+ * (dlast_h, dlast_v NULL = zero).  The gradient of a complex input is written as
+ * dL/dRe + i dL/dIm (the convention of PyTorch's complex autograd for a real loss): dA (summed
+ * over batch and time), dB, dC (summed over channels), and dh0, dv0 when non-NULL.  dx, ddelta
+ * are real; dDskip is required exactly when Dskip is given.  A forward pass that records every
+ * state into the workspace runs first; nothing from an earlier forward call is needed.
+ * Everything else as msm_scan_complex_fwd. */
+msm_status msm_scan_complex_bwd(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, const float* h0,
+                                const float* v0, const void* dy, const float* dlast_h,
+                                const float* dlast_v, void* dx, void* ddelta, float* dA,
+                                void* dB, void* dC, float* dDskip, float* dh0, float* dv0,
+                                int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                                float alpha, msm_dtype io, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ __all__ = [
     "msm_version", "msm_status_string", "msm_scan_fwd_workspace_bytes",
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
     "msm_scan_bwd", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
+    "msm_scan_complex_fwd", "msm_scan_complex_bwd", "msm_scan_complex_bwd_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = [
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
     "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan", "msm_scan_fwd_state",
     "msm_scan_bwd_state", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
+    "msm_scan_complex_fwd", "msm_scan_complex_bwd_workspace_bytes", "msm_scan_complex_bwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -112,6 +114,13 @@ def load_library():
     lib.msm_scan_step.argtypes = ([P] * 8 + [I32, I32] + [P] * 3
                                   + [I64, I64, I64, F, F, ctypes.c_int, P])
     lib.msm_scan_step.restype = ctypes.c_int
+    lib.msm_scan_complex_fwd.argtypes = [P] * 11 + [I64, I64, I64, I64, F, F, ctypes.c_int, P]
+    lib.msm_scan_complex_fwd.restype = ctypes.c_int
+    lib.msm_scan_complex_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, ctypes.c_int]
+    lib.msm_scan_complex_bwd_workspace_bytes.restype = SZ
+    lib.msm_scan_complex_bwd.argtypes = [P] * 19 + [I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ,
+                                                    P]
+    lib.msm_scan_complex_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -458,3 +467,93 @@ def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, d
     if st != 0:
         raise MsmError(st, "msm_scan_step")
     return y
+
+
+# ----------------------------------------------------------------------------------------------
+# complex-valued scan: complex arrays are passed as real tensors with a trailing dimension of 2
+# (torch.view_as_real of a complex64 tensor for float32 I/O)
+# ----------------------------------------------------------------------------------------------
+
+def msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, io) -> int:
+    return int(load_library().msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, _io_code(io)))
+
+
+def _complex_inputs(x, delta, A, B, C, Dskip):
+    import torch
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    for t, nm, shp in ((x, "x", (Bt, L, D)), (delta, "delta", (Bt, L, D)),
+                       (B, "B", (Bt, L, N, 2)), (C, "C", (Bt, L, N, 2))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N, 2), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    return dev, Bt, L, D, N, _io_code(x.dtype)
+
+
+def msm_scan_complex_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, h0=None, v0=None, y=None,
+                         last_h=None, last_v=None, return_last_state=False, stream=None):
+    """Complex forward (msm_scan_complex_fwd).  x, delta: (Bt, L, D); A: (D, N, 2) fp32;
+    B, C: (Bt, L, N, 2) in the dtype of x; h0, v0: optional (Bt, D, N, 2) fp32.  Returns y
+    (Bt, L, D), or (y, last_h, last_v)."""
+    import torch
+    lib = load_library()
+    dev, Bt, L, D, N, io = _complex_inputs(x, delta, A, B, C, Dskip)
+    if y is None:
+        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+    _check(y, "y", (Bt, L, D), x.dtype, dev)
+    if return_last_state:
+        if last_h is None:
+            last_h = torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev)
+        if last_v is None:
+            last_v = torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev)
+    for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N, 2), torch.float32, dev)
+    st = lib.msm_scan_complex_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
+                                  _ptr(h0), _ptr(v0), _ptr(y), _ptr(last_h), _ptr(last_v), Bt, L,
+                                  D, N, float(beta), float(alpha), io, _stream_handle(stream, dev))
+    if st != 0:
+        raise MsmError(st, "msm_scan_complex_fwd")
+    if return_last_state:
+        return y, last_h, last_v
+    return y
+
+
+def msm_scan_complex_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, h0=None, v0=None,
+                         dlast_h=None, dlast_v=None, state_grads=False, out=None, workspace=None,
+                         stream=None):
+    """Gradients of the complex scan's real loss (msm_scan_complex_bwd).  Returns a dict: dx,
+    ddelta (Bt, L, D) and dB, dC (Bt, L, N, 2) in the I/O dtype, dA (D, N, 2) and dDskip (D,)
+    (None without Dskip) in float32, and with state_grads dh0, dv0 (Bt, D, N, 2) fp32.  Complex
+    gradients hold dL/dRe and dL/dIm in their last dimension."""
+    import torch
+    lib = load_library()
+    dev, Bt, L, D, N, io = _complex_inputs(x, delta, A, B, C, Dskip)
+    _check(dy, "dy", (Bt, L, D), x.dtype, dev)
+    for t, nm in ((h0, "h0"), (v0, "v0"), (dlast_h, "dlast_h"), (dlast_v, "dlast_v")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N, 2), torch.float32, dev)
+    o = dict(out or {})
+    for k, shp, dt in (("dx", (Bt, L, D), x.dtype), ("ddelta", (Bt, L, D), x.dtype),
+                       ("dA", (D, N, 2), torch.float32), ("dB", (Bt, L, N, 2), x.dtype),
+                       ("dC", (Bt, L, N, 2), x.dtype)):
+        o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+    if Dskip is not None:
+        o.setdefault("dDskip", torch.empty((D,), dtype=torch.float32, device=dev))
+    else:
+        o["dDskip"] = None
+    if state_grads:
+        o.setdefault("dh0", torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev))
+        o.setdefault("dv0", torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev))
+    nbytes = int(lib.msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, io))
+    ws, wsb = _workspace(nbytes, workspace, dev)
+    st = lib.msm_scan_complex_bwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(h0), _ptr(v0), _ptr(dy),
+        _ptr(dlast_h), _ptr(dlast_v), _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]),
+        _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]), _ptr(o.get("dh0")), _ptr(o.get("dv0")),
+        Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
+    if st != 0:
+        raise MsmError(st, "msm_scan_complex_bwd")
+    return o

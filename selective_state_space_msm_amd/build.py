@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmsm.so")
 # variant 0 plain, 1 fused extras, 2 fused extras with the zero-order hold -- all in parallel
 _PARTS = [("-DMSM_IO_BF16=%d" % io, "-DMSM_EXT=%d" % ext) for io in (0, 1) for ext in (0, 1, 2)]
 SOURCES = ([("msm_api.cpp", ()), ("msm_launch.hip", ()), ("msm_bwd_wide.hip", ()),
-            ("msm_step.hip", ())]
+            ("msm_step.hip", ()), ("msm_cfwd.hip", ()), ("msm_cbwd.hip", ())]
            + [("msm_fwd.hip", f) for f in _PARTS] + [("msm_bwd.hip", f) for f in _PARTS])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -202,6 +202,41 @@ bool any_overlap(const Range* outs, int nout, const Range* ins, int nin) {
   return false;
 }
 
+
+// ---- complex scan ----
+// The complex kernels address a tile of the state history ((kTile + 1) rows of N * D complex
+// fp32 values) with 32-bit byte offsets.
+bool complex_shape_ok(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  if (!shape_ok(Bt, L, D, N)) return false;
+  if ((int64_t)(kTile + 1) * N * D * 8 > ((int64_t)1 << 31) - 1) return false;
+  if (ceil_div(D, msm::kBwdChans) * Bt > ((int64_t)1 << 31) - 1) return false;
+  return true;
+}
+
+struct CBwdLayout {
+  size_t off_hist, off_dbc, off_dA, off_dD, total;
+};
+
+CBwdLayout cbwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
+  const int64_t ncb = ceil_div(D, msm::kBwdChans);
+  const int NP = msm::complex_padded_states(N);
+  CBwdLayout l{};
+  l.off_hist = 0;
+  l.off_dbc = align_up(sizeof(float) * 2 * (size_t)(Bt * (L + 1) * N * D));
+  l.off_dA = l.off_dbc + align_up(sizeof(float) * 4 * (size_t)(Bt * ncb * L * NP));
+  l.off_dD = l.off_dA + align_up(sizeof(float) * 2 * (size_t)(Bt * D * N));
+  l.total = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  return l;
+}
+
+msm_status check_complex(int64_t Bt, int64_t L, int64_t D, int64_t N, float beta, float alpha,
+                         msm_dtype io) {
+  msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!complex_shape_ok(Bt, L, D, N)) return MSM_ERR_INVALID_ARG;
+  return MSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -560,6 +595,142 @@ msm_status msm_scan_step(const void* x, const void* delta, const float* A, const
   a.alpha = alpha;
   const bool vec = N % 4 == 0 && (((uintptr_t)h | (uintptr_t)v | (uintptr_t)A) & 15) == 0;
   hipError_t e = msm::launch_step(a, io == MSM_BF16, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+
+size_t msm_scan_complex_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                            msm_dtype io) {
+  if (check_complex(Bt, L, D, N, 0.f, 1.f, io) != MSM_OK) return 0;
+  return cbwd_layout(Bt, L, D, N).total;
+}
+
+msm_status msm_scan_complex_fwd(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, const float* h0,
+                                const float* v0, void* y, float* last_h, float* last_v,
+                                int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                                float alpha, msm_dtype io, void* stream) {
+  msm_status st = check_complex(Bt, L, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
+  const size_t es = io == MSM_BF16 ? 2 : 4;
+  const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
+  const size_t nst = (size_t)(Bt * D * N) * 8;
+  const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 8), rng(B, nbc * 2 * es),
+                       rng(C, nbc * 2 * es),      rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(h0, h0 ? nst : 0),     rng(v0, v0 ? nst : 0)};
+  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? nst : 0),
+                        rng(last_v, last_v ? nst : 0)};
+  if (any_overlap(outs, 3, ins, 8)) return MSM_ERR_INVALID_ARG;
+  msm::CFwdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.h0 = h0;
+  a.v0 = v0;
+  a.y = y;
+  a.last_h = last_h;
+  a.last_v = last_v;
+  a.hist = nullptr;
+  a.Bt = Bt;
+  a.L = L;
+  a.D = D;
+  a.N = N;
+  a.ncb = (int32_t)ceil_div(D, msm::kBwdChans);
+  a.beta = beta;
+  a.alpha = alpha;
+  hipError_t e = msm::launch_cfwd(a, io == MSM_BF16, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+msm_status msm_scan_complex_bwd(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, const float* h0,
+                                const float* v0, const void* dy, const float* dlast_h,
+                                const float* dlast_v, void* dx, void* ddelta, float* dA,
+                                void* dB, void* dC, float* dDskip, float* dh0, float* dv0,
+                                int64_t Bt, int64_t L, int64_t D, int64_t N, float beta,
+                                float alpha, msm_dtype io, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  msm_status st = check_complex(Bt, L, D, N, beta, alpha, io);
+  if (st != MSM_OK) return st;
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC)
+    return MSM_ERR_INVALID_ARG;
+  if ((Dskip == nullptr) != (dDskip == nullptr)) return MSM_ERR_INVALID_ARG;
+  const CBwdLayout lay = cbwd_layout(Bt, L, D, N);
+  if (workspace_bytes < lay.total || !workspace) return MSM_ERR_WORKSPACE;
+  const size_t es = io == MSM_BF16 ? 2 : 4;
+  const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
+  const size_t nst = (size_t)(Bt * D * N) * 8;
+  const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 8), rng(B, nbc * 2 * es),
+                       rng(C, nbc * 2 * es),      rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(h0, h0 ? nst : 0),     rng(v0, v0 ? nst : 0),
+                       rng(dy, nxd * es),         rng(dlast_h, dlast_h ? nst : 0),
+                       rng(dlast_v, dlast_v ? nst : 0)};
+  const Range outs[] = {rng(dx, nxd * es),       rng(ddelta, nxd * es),
+                        rng(dA, (size_t)(D * N) * 8), rng(dB, nbc * 2 * es),
+                        rng(dC, nbc * 2 * es),   rng(dDskip, dDskip ? (size_t)D * 4 : 0),
+                        rng(dh0, dh0 ? nst : 0), rng(dv0, dv0 ? nst : 0),
+                        rng(workspace, lay.total)};
+  if (any_overlap(outs, 9, ins, 11)) return MSM_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  float* hist = reinterpret_cast<float*>(ws + lay.off_hist);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  msm::CFwdArgs f{};
+  f.x = x;
+  f.delta = delta;
+  f.A = A;
+  f.B = B;
+  f.C = C;
+  f.h0 = h0;
+  f.v0 = v0;
+  f.hist = hist;
+  f.Bt = Bt;
+  f.L = L;
+  f.D = D;
+  f.N = N;
+  f.ncb = (int32_t)ceil_div(D, msm::kBwdChans);
+  f.beta = beta;
+  f.alpha = alpha;
+  hipError_t e = msm::launch_cfwd(f, io == MSM_BF16, true, s);
+  if (e != hipSuccess) return MSM_ERR_LAUNCH;
+
+  msm::CBwdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dskip = Dskip;
+  a.dy = dy;
+  a.dlast_h = dlast_h;
+  a.dlast_v = dlast_v;
+  a.dh0 = dh0;
+  a.dv0 = dv0;
+  a.dx = dx;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dDskip = dDskip;
+  a.hist = hist;
+  a.dbc_part = reinterpret_cast<float*>(ws + lay.off_dbc);
+  a.dA_part = reinterpret_cast<float*>(ws + lay.off_dA);
+  a.dD_part = reinterpret_cast<float*>(ws + lay.off_dD);
+  a.Bt = Bt;
+  a.L = L;
+  a.D = D;
+  a.N = N;
+  a.ncb = f.ncb;
+  a.NP = msm::complex_padded_states(N);
+  a.beta = beta;
+  a.alpha = alpha;
+  e = msm::launch_cbwd(a, io == MSM_BF16, s);
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
 }
 

@@ -1,0 +1,195 @@
+// Complex-valued elements for the complex scan kernels (gfx950): interleaved (re, im) pairs.
+#pragma once
+
+#include "msm_device.hpp"
+
+namespace msm {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr double kTwoPiD = 6.283185307179586;
+
+// Im A in revolutions, split into a float pair (hi + lo) so that the phase delta * Im A / 2 pi
+// keeps its accuracy when it spans several turns.
+struct RevPair {
+  float hi, lo;
+};
+__device__ __forceinline__ RevPair to_revolutions(float im_a) {
+  const double r = (double)im_a / kTwoPiD;
+  const float hi = (float)r;
+  return RevPair{hi, (float)(r - (double)hi)};
+}
+
+// e^(i delta Im A) = (c, s), to about one unit in the last place.  The phase in revolutions is
+// formed as p + lo with p = fl(delta hi) and lo carrying the rounding error of that product
+// (exact, from an FMA) plus delta lo.  The quarter-turn count k = rint(4 p) is split off
+// exactly (u = p - k/4 needs no rounding, |u| <= 1/8 turn), cos and sin of 2 pi u come from
+// their Taylor series (truncated below 2e-9 for |2 pi u| <= pi/4), and k mod 4 rotates the
+// pair by quarter turns (bit 1 of k and of k + 1 give the signs, two's complement keeps that
+// right for negative k).  The hardware v_sin_f32 / v_cos_f32 are not used: their error (about
+// 1e-6 absolute, judging by the parity errors they caused) is carried into the delta gradient
+// with a factor |A|, beyond the fp32 tolerance.
+__device__ __forceinline__ void cis_delta(float delta, RevPair a, float& c, float& s) {
+  constexpr float S1 = (float)kTwoPiD;
+  constexpr float S3 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD / 6.0);
+  constexpr float S5 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 120.0);
+  constexpr float S7 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD /
+                               5040.0);
+  constexpr float S9 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
+                               kTwoPiD * kTwoPiD / 362880.0);
+  constexpr float C2 = (float)(-kTwoPiD * kTwoPiD / 2.0);
+  constexpr float C4 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 24.0);
+  constexpr float C6 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 720.0);
+  constexpr float C8 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
+                               kTwoPiD / 40320.0);
+  constexpr float C10 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
+                                kTwoPiD * kTwoPiD * kTwoPiD / 3628800.0);
+  const float p = delta * a.hi;
+  const float lo = fmaf(delta, a.lo, fmaf(delta, a.hi, -p));
+  const float k = __builtin_rintf(4.f * p);
+  const float u = fmaf(k, -0.25f, p) + lo;
+  const float z = u * u;
+  float ps = fmaf(z, S9, S7);
+  ps = fmaf(z, ps, S5);
+  ps = fmaf(z, ps, S3);
+  ps = fmaf(z, ps, S1);
+  const float sn = u * ps;
+  float pc = fmaf(z, C10, C8);
+  pc = fmaf(z, pc, C6);
+  pc = fmaf(z, pc, C4);
+  pc = fmaf(z, pc, C2);
+  const float cs = fmaf(z, pc, 1.f);
+  const int q = (int)k;
+  const bool odd = (q & 1) != 0;
+  const float cr = odd ? sn : cs, sr = odd ? cs : sn;
+  c = __uint_as_float(__float_as_uint(cr) ^ ((uint32_t)((q + 1) & 2) << 30));
+  s = __uint_as_float(__float_as_uint(sr) ^ ((uint32_t)(q & 2) << 30));
+}
+
+// (2 pi)^m / m! and 1 / m!, the Taylor coefficients of the fp64 rotation and exponential.
+constexpr double taylor_2pi(int m) {
+  double r = 1.0;
+  for (int i = 1; i <= m; ++i) r *= kTwoPiD / i;
+  return r;
+}
+constexpr double inv_fact(int m) {
+  double r = 1.0;
+  for (int i = 1; i <= m; ++i) r /= i;
+  return r;
+}
+
+// e^(2 pi i r) in fp64 for r in revolutions: the same exact quarter-turn split as cis_delta,
+// then the Taylor series of sin to the 15th and of cos to the 16th power of 2 pi u (truncated
+// below 5e-17 for |2 pi u| <= pi/4).
+struct CisD {
+  double c, s;
+};
+__device__ __forceinline__ CisD cis_rev_d(double r) {
+  const double k = __builtin_rint(4.0 * r);
+  const double u = __builtin_fma(k, -0.25, r);
+  const double z = u * u;
+  double ps = __builtin_fma(z, -taylor_2pi(15), taylor_2pi(13));
+  ps = __builtin_fma(z, ps, -taylor_2pi(11));
+  ps = __builtin_fma(z, ps, taylor_2pi(9));
+  ps = __builtin_fma(z, ps, -taylor_2pi(7));
+  ps = __builtin_fma(z, ps, taylor_2pi(5));
+  ps = __builtin_fma(z, ps, -taylor_2pi(3));
+  ps = __builtin_fma(z, ps, taylor_2pi(1));
+  const double sn = u * ps;
+  double pc = __builtin_fma(z, taylor_2pi(16), -taylor_2pi(14));
+  pc = __builtin_fma(z, pc, taylor_2pi(12));
+  pc = __builtin_fma(z, pc, -taylor_2pi(10));
+  pc = __builtin_fma(z, pc, taylor_2pi(8));
+  pc = __builtin_fma(z, pc, -taylor_2pi(6));
+  pc = __builtin_fma(z, pc, taylor_2pi(4));
+  pc = __builtin_fma(z, pc, -taylor_2pi(2));
+  const double cs = __builtin_fma(z, pc, 1.0);
+  const int q = (int)k;
+  const bool odd = (q & 1) != 0;
+  const double cr = odd ? sn : cs, sr = odd ? cs : sn;
+  return CisD{((q + 1) & 2) ? -cr : cr, (q & 2) ? -sr : sr};
+}
+
+// e^x in fp64 for the decay factor (x = delta Re A <= 0 in use): x = k ln 2 + g with
+// k = rint(x log2 e), |g| <= ln(2) / 2 + tiny, e^g from its Taylor series to g^13 (truncated
+// below 5e-18), scaled by 2^k.  The reduction's rounding (k times the error of ln 2 in fp64) is
+// below 1e-13 relative for |x| < 1000; results under the fp64 range flush to zero through
+// ldexp.
+__device__ __forceinline__ double exp_d(double x) {
+  constexpr double kLog2eD = 1.4426950408889634, kLn2D = 0.6931471805599453;
+  const double k = __builtin_rint(x * kLog2eD);
+  const double g = __builtin_fma(-k, kLn2D, x);
+  double p = __builtin_fma(g, inv_fact(13), inv_fact(12));
+  p = __builtin_fma(p, g, inv_fact(11));
+  p = __builtin_fma(p, g, inv_fact(10));
+  p = __builtin_fma(p, g, inv_fact(9));
+  p = __builtin_fma(p, g, inv_fact(8));
+  p = __builtin_fma(p, g, inv_fact(7));
+  p = __builtin_fma(p, g, inv_fact(6));
+  p = __builtin_fma(p, g, inv_fact(5));
+  p = __builtin_fma(p, g, inv_fact(4));
+  p = __builtin_fma(p, g, inv_fact(3));
+  p = __builtin_fma(p, g, 0.5);
+  p = __builtin_fma(p, g, 1.0);
+  p = __builtin_fma(p, g, 1.0);
+  const double kc = k < -2000.0 ? -2000.0 : k;  // keeps the int conversion in range
+  return ldexp(p, (int)kc);
+}
+
+// Adds an fp64 value across the two 32-lane halves (both halves get the same sum).
+__device__ __forceinline__ double half_sum_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double a = __longlong_as_double((long long)(((uint64_t)rh[0] << 32) | rl[0]));
+  const double b = __longlong_as_double((long long)(((uint64_t)rh[1] << 32) | rl[1]));
+  return a + b;
+}
+
+// One complex element of an I/O array (B, C and their gradients) as it sits in a register
+// between its load and its first use.
+template <typename IO>
+struct cio;
+
+template <>
+struct cio<float> {
+  using raw = u32x2;
+  static constexpr int es = 8;  // bytes per complex element
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ float re(raw v) { return __uint_as_float(v.x); }
+  static __device__ __forceinline__ float im(raw v) { return __uint_as_float(v.y); }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float re, float im) {
+    float* q = static_cast<float*>(p) + 2 * i;
+    q[0] = re;
+    q[1] = im;
+  }
+};
+
+template <>
+struct cio<bf16_storage> {
+  using raw = uint32_t;  // re in the low half, im in the high half (little-endian pair)
+  static constexpr int es = 4;
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ float re(raw v) { return __uint_as_float(v << 16); }
+  static __device__ __forceinline__ float im(raw v) { return __uint_as_float(v & 0xffff0000u); }
+  // fp32 -> bf16 round to nearest even, each part
+  static __device__ __forceinline__ void store(void* p, int64_t i, float re, float im) {
+    __bf16* q = static_cast<__bf16*>(p) + 2 * i;
+    q[0] = static_cast<__bf16>(re);
+    q[1] = static_cast<__bf16>(im);
+  }
+};
+
+// Adds v across the two 32-lane halves of a wavefront (lanes l and l ^ 32 both get the sum).
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace msm

@@ -105,6 +105,61 @@ struct StepArgs {
   float beta, alpha;
 };
 
+// Complex-valued scan: A (D, N), B, C (Bt, L, N), the states and their adjoints are
+// interleaved (re, im) pairs; x, delta, y, dy, dx, ddelta are real.
+struct CFwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;       // (D, N) complex fp32
+  const void* B;        // (Bt, L, N) complex, I/O dtype
+  const void* C;
+  const float* Dskip;
+  const float* h0;      // (Bt, D, N) complex fp32 or null (zero)
+  const float* v0;
+  void* y;              // (Bt, L, D); unused by the recording pass
+  float* last_h;        // (Bt, D, N) complex fp32 or null
+  float* last_v;
+  float* hist;          // recording pass: (Bt, L + 1, N, D) complex fp32, row r = h_{r-1}
+  int64_t Bt, L, D, N;
+  int32_t ncb;          // channel blocks of kBwdChans
+  float beta, alpha;
+};
+
+struct CBwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;
+  const void* dy;
+  const float* dlast_h;  // (Bt, D, N) complex fp32 or null (zero)
+  const float* dlast_v;
+  float* dh0;            // (Bt, D, N) complex fp32 or null (not written)
+  float* dv0;
+  void* dx;
+  void* ddelta;
+  float* dA;             // (D, N) complex fp32
+  void* dB;              // (Bt, L, N) complex, I/O dtype
+  void* dC;
+  float* dDskip;
+  const float* hist;     // written by the recording forward pass
+  float* dbc_part;       // [Bt][ncb][L][NP][4]: per channel block (dB re, im, dC re, im)
+  float* dA_part;        // [Bt][D][N][2]
+  float* dD_part;        // [Bt][D]
+  int64_t Bt, L, D, N;
+  int32_t ncb;
+  int32_t NP;            // padded states
+  float beta, alpha;
+};
+
+// Complex forward (record = false: y and the last states; record = true: the state history
+// only, for the backward) and complex backward (its sweep and the partial-sum reduction).
+hipError_t launch_cfwd(const CFwdArgs& a, int io_bf16, bool record, hipStream_t s);
+hipError_t launch_cbwd(const CBwdArgs& a, int io_bf16, hipStream_t s);
+// padded complex states of a plan: 4, 16 or 64
+inline int complex_padded_states(int64_t N) { return N <= 4 ? 4 : (N <= 16 ? 16 : 64); }
+
 // One decode step; vec selects 16-byte state access (N % 4 == 0 and 16-byte aligned states
 // and A).  Returns hipSuccess or the launch error.
 hipError_t launch_step(const StepArgs& a, int io_bf16, bool vec, hipStream_t s);

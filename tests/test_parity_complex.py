@@ -1,0 +1,229 @@
+"""The complex-valued scan on the GPU (msm_scan_complex_fwd / msm_scan_complex_bwd through the C
+ABI) against the fp64 oracle: small shapes with ragged tiles, channel blocks and state groups
+for every plan (4, 16 and 64 padded states) and both I/O dtypes, then the full-size workload on
+sampled channels, its channel sums on one full batch row, and the degenerate cases."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import assert_close, dev, host, log, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+CW = W["complex"]
+SMALL = CW.replace(Bt=2, L=100, D=70)
+
+
+def cx(a):
+    """(..., 2) interleaved float array -> complex128 (None passes through)."""
+    if a is None:
+        return None
+    a = np.asarray(a, np.float64)
+    return a[..., 0] + 1j * a[..., 1]
+
+
+def ri(z):
+    """complex array -> (..., 2) float64."""
+    return np.stack([np.real(z), np.imag(z)], axis=-1)
+
+
+def to_dev(inp):
+    io = inp["io"]
+    g = dict(x=dev(inp["x"], io), delta=dev(inp["delta"], io), A=dev(inp["A"]),
+             B=dev(inp["B"], io), C=dev(inp["C"], io),
+             Dskip=None if inp["Dskip"] is None else dev(inp["Dskip"]))
+    if inp.get("dy") is not None:
+        g["dy"] = dev(inp["dy"], io)
+    return g
+
+
+def opt(a):
+    return None if a is None else dev(a)
+
+
+def run_fwd(inp, h0=None, v0=None):
+    import torch
+    import selective_state_space_msm_amd as msm
+    g = to_dev(inp)
+    y, lh, lv = msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"],
+                                         inp["alpha"], g["Dskip"], h0=opt(h0), v0=opt(v0),
+                                         return_last_state=True)
+    torch.cuda.synchronize()
+    return y, lh, lv
+
+
+def run_bwd(inp, h0=None, v0=None, dlh=None, dlv=None):
+    import torch
+    import selective_state_space_msm_amd as msm
+    g = to_dev(inp)
+    out = msm.msm_scan_complex_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"],
+                                   inp["beta"], inp["alpha"], g["Dskip"], h0=opt(h0), v0=opt(v0),
+                                   dlast_h=opt(dlh), dlast_v=opt(dlv), state_grads=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_fwd(inp, h0=None, v0=None):
+    return oracle.complex_fwd(inp["x"], inp["delta"], cx(inp["A"]), cx(inp["B"]), cx(inp["C"]),
+                              inp["beta"], inp["alpha"], Dskip=inp["Dskip"], h0=cx(h0), v0=cx(v0))
+
+
+def oracle_bwd(inp, h0=None, v0=None, dlh=None, dlv=None):
+    return oracle.complex_bwd(inp["x"], inp["delta"], cx(inp["A"]), cx(inp["B"]), cx(inp["C"]),
+                              inp["dy"], inp["beta"], inp["alpha"], Dskip=inp["Dskip"], h0=cx(h0),
+                              v0=cx(v0), dlast_h=cx(dlh), dlast_v=cx(dlv))
+
+
+def check_fwd(inp, h0=None, v0=None, tag=""):
+    io = inp["io"]
+    log("complex fwd %s shape=%s N=%d io=%s" % (tag, inp["x"].shape, inp["A"].shape[1], io))
+    y, lh, lv = run_fwd(inp, h0, v0)
+    oy, olh, olv = oracle_fwd(inp, h0, v0)
+    assert_close(host(y), oy, io, "y " + tag)
+    assert_close(host(lh), ri(olh), "f32" if io == "f32" else io, "last_h " + tag)
+    assert_close(host(lv), ri(olv), "f32" if io == "f32" else io, "last_v " + tag)
+
+
+def check_bwd(inp, h0=None, v0=None, dlh=None, dlv=None, tag=""):
+    io = inp["io"]
+    log("complex bwd %s shape=%s N=%d io=%s" % (tag, inp["x"].shape, inp["A"].shape[1], io))
+    got = run_bwd(inp, h0, v0, dlh, dlv)
+    want = oracle_bwd(inp, h0, v0, dlh, dlv)
+    for k in ("dx", "ddelta", "dDskip"):
+        if want[k] is not None:
+            assert_close(host(got[k]), want[k], io, "%s %s" % (k, tag))
+    for k in ("dA", "dB", "dC", "dh0", "dv0"):
+        assert_close(host(got[k]), ri(want[k]), io, "%s %s" % (k, tag))
+
+
+# ---- small shapes: every plan, ragged tiles / channel blocks / states, both dtypes ----
+
+@pytest.mark.parametrize("beta", [0.9, 0.0])
+@pytest.mark.parametrize("N", [4, 16])
+def test_fwd_tiny(beta, N):
+    w = W["tiny"].replace(beta=beta, N=N)
+    check_fwd(workloads.make_complex_inputs(w, seed=301), tag="tiny")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [3, 16, 40])
+@pytest.mark.parametrize("a_kind", ["s4d_lin", "random"])
+def test_fwd_small_ragged(io, N, a_kind):
+    w = SMALL.replace(io=io, N=N, dskip=True, beta=0.8, alpha=0.7)
+    inp = workloads.make_complex_inputs(w, a_kind=a_kind, seed=311)
+    h0, v0 = workloads.make_complex_state(w, 312)
+    check_fwd(inp, h0, v0, tag="small")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [3, 16, 40])
+@pytest.mark.parametrize("dskip", [True, False])
+def test_bwd_small_ragged(io, N, dskip):
+    w = SMALL.replace(io=io, N=N, dskip=dskip, beta=0.8, alpha=0.7, direction="bwd")
+    inp = workloads.make_complex_inputs(w, a_kind="random", seed=321)
+    h0, v0 = workloads.make_complex_state(w, 322)
+    dlh, dlv = workloads.make_complex_state(w, 323)
+    check_bwd(inp, h0, v0, dlh, dlv, tag="small")
+
+
+@pytest.mark.parametrize("beta", [0.9, 0.0])
+def test_bwd_tiny_no_state(beta):
+    w = W["tiny"].replace(beta=beta, N=4, direction="bwd")
+    check_bwd(workloads.make_complex_inputs(w, seed=331), tag="tiny")
+
+
+# ---- degenerate cases ----
+
+def test_single_step_and_channel():
+    w = CW.replace(Bt=1, L=1, D=1, N=1, dskip=True, direction="bwd")
+    inp = workloads.make_complex_inputs(w, a_kind="random", seed=341)
+    h0, v0 = workloads.make_complex_state(w, 342)
+    check_fwd(inp, h0, v0, tag="L=D=N=1")
+    check_bwd(inp, h0, v0, *workloads.make_complex_state(w, 343), tag="L=D=N=1")
+
+
+def test_real_inputs_match_real_scan():
+    """Zero imaginary parts: the complex kernels give the real scan's outputs (the real
+    kernels' results through the real entry point, to the parity tolerance of each)."""
+    w = SMALL.replace(N=16, dskip=True, direction="bwd")
+    inp = workloads.make_complex_inputs(w, a_kind="random", seed=351)
+    for k in ("A", "B", "C"):
+        inp[k] = inp[k].copy()
+        inp[k][..., 1] = 0.0
+    y, _, _ = run_fwd(inp)
+    oy, _, _ = oracle.fwd(inp["x"], inp["delta"], inp["A"][..., 0], inp["B"][..., 0],
+                          inp["C"][..., 0], inp["beta"], inp["alpha"], Dskip=inp["Dskip"])
+    assert_close(host(y), oy, "f32", "y (real inputs)")
+    got = run_bwd(inp)
+    want = oracle.bwd(inp["x"], inp["delta"], inp["A"][..., 0], inp["B"][..., 0], inp["C"][..., 0],
+                      inp["dy"], inp["beta"], inp["alpha"], Dskip=inp["Dskip"])
+    for k in ("dx", "ddelta", "dDskip"):
+        assert_close(host(got[k]), want[k], "f32", k + " (real inputs)")
+    for k in ("dA", "dB", "dC"):
+        assert_close(host(got[k])[..., 0], want[k], "f32", k + " (real inputs)")
+        assert_close(host(got[k])[..., 1], 0.0 * want[k], "f32", "Im " + k + " (real inputs)")
+
+
+def test_argument_errors():
+    import torch
+    import selective_state_space_msm_amd as msm
+    w = CW.replace(Bt=1, L=8, D=4, N=4, direction="bwd")
+    g = to_dev(workloads.make_complex_inputs(w, seed=361))
+    with pytest.raises(ValueError):  # A without its (re, im) dimension
+        msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"][..., 0].contiguous(), g["B"], g["C"],
+                                 0.9, 1.0)
+    with pytest.raises(msm.MsmError):  # beta out of range
+        msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], 1.5, 1.0)
+    with pytest.raises(msm.MsmError):  # N beyond 64
+        A = torch.zeros((4, 65, 2), dtype=torch.float32, device="cuda")
+        B = torch.zeros((1, 8, 65, 2), dtype=torch.float32, device="cuda")
+        msm.msm_scan_complex_fwd(g["x"], g["delta"], A, B, B, 0.9, 1.0)
+    with pytest.raises(msm.MsmError):  # workspace too small
+        msm.msm_scan_complex_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], 0.9, 1.0,
+                                 workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+# ---- the full-size workload (Bt=4, L=2048, D=2048, N=16) ----
+
+@pytest.fixture(scope="module")
+def full():
+    w = CW.replace(direction="bwd")
+    inp = workloads.make_complex_inputs(w)
+    return inp, to_dev(inp)
+
+
+def test_full_size_fwd_sampled_channels(full):
+    import torch
+    import selective_state_space_msm_amd as msm
+    inp, g = full
+    log("complex fwd full size %s" % (inp["x"].shape,))
+    y, lh, _ = msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"],
+                                        inp["alpha"], g["Dskip"], return_last_state=True)
+    torch.cuda.synchronize()
+    ds = sample_channels(inp["x"].shape[2], 24, 371)
+    sub = dict(inp, x=inp["x"][:, :, ds], delta=inp["delta"][:, :, ds], A=inp["A"][ds])
+    oy, olh, _ = oracle_fwd(sub)
+    assert_close(host(y)[:, :, ds], oy, "f32", "y (sampled channels)")
+    assert_close(host(lh)[:, ds], ri(olh), "f32", "last_h (sampled channels)")
+
+
+def test_full_size_bwd(full):
+    """Per-channel gradients (dx, ddelta, dA) on sampled channels of every batch row; the channel
+    sums dB, dC on batch row 0 with all its channels."""
+    inp, g = full
+    log("complex bwd full size %s" % (inp["x"].shape,))
+    got = run_bwd(inp)
+    ds = sample_channels(inp["x"].shape[2], 16, 381)
+    sub = dict(inp, x=inp["x"][:, :, ds], delta=inp["delta"][:, :, ds], dy=inp["dy"][:, :, ds],
+               A=inp["A"][ds])
+    want = oracle_bwd(sub)
+    for k in ("dx", "ddelta"):
+        assert_close(host(got[k])[:, :, ds], want[k], "f32", k + " (sampled channels)")
+    assert_close(host(got["dA"])[ds], ri(want["dA"]), "f32", "dA (sampled channels)")
+    row = dict(inp, x=inp["x"][:1], delta=inp["delta"][:1], dy=inp["dy"][:1], B=inp["B"][:1],
+               C=inp["C"][:1])
+    want0 = oracle_bwd(row)
+    for k in ("dB", "dC"):
+        assert_close(host(got[k])[:1], ri(want0[k]), "f32", k + " (batch row 0)")

@@ -25,6 +25,12 @@ Distributions (one recipe per named workload):
              extras (``make_fused_extras``).  Large enough that the states (2 x 268 MB) do not
              stay in the last-level cache between steps.
 
+* ``complex`` Bt=4, L=2048, D=2048, N=16 complex states, fp32 I/O, beta=0.9, alpha=1 (the
+             complex scan, forward and backward; ``make_complex_inputs``): A[d, n] = -1/2 + i pi n
+             (the S4D-Lin initialisation named on the complextorch page), B, C complex with
+             independent N(0, 1/2) real and imaginary parts (unit variance), x ~ N(0, 1),
+             delta = softplus(N(-4, 1)), dy ~ N(0, 1).
+
 Draws are made in float64 with ``numpy.random.Generator(PCG64(seed))``, cast to float32, and for
 bf16 workloads rounded once to bfloat16 (round-to-nearest-even) on the host.  Arrays are always
 returned as float32 numpy arrays whose values are exactly representable in the I/O dtype, so the
@@ -36,7 +42,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16", "bf16_bits"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_complex_inputs", "make_complex_state",
+           "round_to_bf16", "bf16_bits"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -71,6 +78,8 @@ WORKLOADS = {
     "pages": Workload("pages", 2, 512, 256, 16, "f32", 0.9, 1.0, False, "fwd", "softplus", 1007),
     "decode": Workload("decode", 1024, 1, 4096, 16, "bf16", 0.9, 1.0, True, "step", "softplus",
                        1006),
+    "complex": Workload("complex", 4, 2048, 2048, 16, "f32", 0.9, 1.0, False, "fwd", "softplus",
+                        1008),
 }
 
 
@@ -186,3 +195,54 @@ def make_step_inputs(w: Workload, seed: int | None = None, softplus: bool = True
     return dict(x=inp["x"][:, 0], delta=ex["delta_raw"][:, 0], z=ex["z"][:, 0], B=inp["B"][:, 0],
                 C=inp["C"][:, 0], A=inp["A"], Dskip=inp["Dskip"], delta_bias=ex["delta_bias"],
                 softplus=softplus, h=h, v=v, beta=inp["beta"], alpha=inp["alpha"], io=w.io)
+
+
+def make_complex_inputs(w: Workload, *, a_kind: str = "s4d_lin", with_dy: bool | None = None,
+                        seed: int | None = None) -> dict:
+    """Inputs of the complex scan for workload ``w``: x, delta, dy (Bt, L, D) and Dskip as in
+    ``make_inputs``; A (D, N, 2) float32 and B, C (Bt, L, N, 2) as interleaved (re, im) pairs.
+
+    a_kind: "s4d_lin" -> A[d, n] = -1/2 + i pi n
+            "random"  -> Re A = -exp(U(ln 0.3, ln 3)), Im A ~ U(-10, 10)  (no structure)
+    """
+    s = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(s))
+    Bt, L, D, N = w.Bt, w.L, w.D, w.N
+    x = rng.standard_normal((Bt, L, D)).astype(np.float32)
+    if w.delta_dist == "loguniform":
+        delta = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(Bt, L, D))).astype(np.float32)
+    else:
+        delta = _softplus(rng.normal(-4.0, 1.0, size=(Bt, L, D))).astype(np.float32)
+    B = (rng.standard_normal((Bt, L, N, 2)) * np.sqrt(0.5)).astype(np.float32)
+    C = (rng.standard_normal((Bt, L, N, 2)) * np.sqrt(0.5)).astype(np.float32)
+    A = np.empty((D, N, 2), np.float32)
+    if a_kind == "s4d_lin":
+        A[..., 0] = -0.5
+        A[..., 1] = (np.pi * np.arange(N)).astype(np.float32)
+    elif a_kind == "random":
+        A[..., 0] = -np.exp(rng.uniform(np.log(0.3), np.log(3.0), size=(D, N)))
+        A[..., 1] = rng.uniform(-10.0, 10.0, size=(D, N))
+    else:
+        raise ValueError(a_kind)
+    Dskip = rng.standard_normal(D).astype(np.float32) if w.dskip else None
+    need_dy = (w.direction == "bwd") if with_dy is None else with_dy
+    dy = None
+    if need_dy:
+        rng_dy = np.random.Generator(np.random.PCG64(s + 1000))
+        dy = rng_dy.standard_normal((Bt, L, D)).astype(np.float32)
+    if w.io == "bf16":
+        x, delta, B, C = (round_to_bf16(a) for a in (x, delta, B, C))
+        if dy is not None:
+            dy = round_to_bf16(dy)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, Dskip=Dskip, dy=dy,
+                beta=float(np.float32(w.beta)), alpha=float(np.float32(w.alpha)), io=w.io)
+
+
+def make_complex_state(w: Workload, seed: int, scale: float = 1.0):
+    """A seeded (Bt, D, N, 2) float32 pair of complex states (or adjoints), independent
+    N(0, scale^2 / 2) real and imaginary parts."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shp = (w.Bt, w.D, w.N, 2)
+    h = (rng.standard_normal(shp) * scale * np.sqrt(0.5)).astype(np.float32)
+    v = (rng.standard_normal(shp) * scale * np.sqrt(0.5)).astype(np.float32)
+    return h, v
