@@ -221,10 +221,51 @@ def bench_step(w, steps, warmup, stream):
     return timed(step, stream, steps, warmup)
 
 
+def bench_complex(w, steps, warmup, stream, direction):
+    """Time msm_scan_complex_fwd or msm_scan_complex_bwd on workload w (complex A, B, C)."""
+    import torch
+    import selective_state_space_msm_amd as msm
+    inp = workloads.make_complex_inputs(w, with_dy=direction == "bwd")
+    dt = torch.float32 if w.io == "f32" else torch.bfloat16
+    g = {k: torch.from_numpy(inp[k]).to("cuda").to(dt) for k in ("x", "delta", "B", "C")}
+    g["A"] = torch.from_numpy(inp["A"]).to("cuda")
+    if direction == "fwd":
+        y = torch.empty_like(g["x"])
+
+        def step():
+            msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], w.beta, w.alpha,
+                                     y=y, stream=stream)
+    else:
+        g["dy"] = torch.from_numpy(inp["dy"]).to("cuda").to(dt)
+        nbytes = msm.msm_scan_complex_bwd_workspace_bytes(w.Bt, w.L, w.D, w.N, w.io)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = {"dx": torch.empty_like(g["x"]), "ddelta": torch.empty_like(g["x"]),
+               "dA": torch.empty_like(g["A"]), "dB": torch.empty_like(g["B"]),
+               "dC": torch.empty_like(g["C"])}
+
+        def step():
+            msm.msm_scan_complex_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], g["dy"], w.beta,
+                                     w.alpha, out=out, workspace=ws, stream=stream)
+
+    return timed(step, stream, steps, warmup)
+
+
+def alg_bytes_complex(w: workloads.Workload, direction: str) -> int:
+    """Bytes a complex call must move at least: x, delta, y (fwd) or x, delta, dy, dx, ddelta
+    (bwd) per (b, t, d); B, C (fwd) or B, C, dB, dC (bwd) as (re, im) pairs per (b, t, n)."""
+    es = 4 if w.io == "f32" else 2
+    rows_d = w.Bt * w.L * w.D
+    rows_n = w.Bt * w.L * w.N * 2
+    if direction == "fwd":
+        return es * (3 * rows_d + 2 * rows_n) + 8 * w.D * w.N
+    return es * (5 * rows_d + 4 * rows_n) + 16 * w.D * w.N
+
+
 def bench_configs(steps, warmup, stream):
-    """Every other configuration the measurement plan lists, one line each: the forward at
-    each forward shape (both beta where listed), the forward with an unstructured A, the fused
-    forward, and the README benchmark shape forward and backward."""
+    """Every other configuration the measurement plan lists, one line each: the complex scan
+    forward and backward, the forward at each forward shape (both beta where listed), the
+    forward with an unstructured A, the fused forward, and the README benchmark shape forward
+    and backward."""
     W = workloads.WORKLOADS
     # (workload, direction, overrides, A, fused extras, zero-order hold)
     runs = [("m130m", "fwd", {}, "s4d", False, False),
@@ -239,6 +280,16 @@ def bench_configs(steps, warmup, stream):
             ("pages", "bwd", {}, "s4d", False, False),
             ("pages", "bwd", {"beta": 0.0}, "s4d", False, False)]
     out = []
+    # the complex-valued scan (A = -1/2 + i pi n, complex B and C), forward and backward
+    for direction in ("fwd", "bwd"):
+        w = W["complex"]
+        ms, per = bench_complex(w, steps, warmup, stream, direction)
+        out.append({"workload": "complex", "direction": direction, "beta": w.beta, "A": "s4d_lin",
+                    "complex": True, "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io,
+                    "ms": ms, "ms_min": min(per), "state_updates_per_s": w.updates / (ms / 1e3),
+                    "algorithmic_GBs": alg_bytes_complex(w, direction) / (ms / 1e3) / 1e9})
+        import torch
+        torch.cuda.empty_cache()
     for name, direction, kw, a_kind, fused, zoh in runs:
         w = W[name].replace(**kw)
         if direction == "fwd":
