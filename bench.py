@@ -261,7 +261,7 @@ def alg_bytes_complex(w: workloads.Workload, direction: str) -> int:
     return es * (5 * rows_d + 4 * rows_n) + 16 * w.D * w.N
 
 
-def bench_configs(steps, warmup, stream):
+def bench_configs(steps, warmup, stream, only=None):
     """Every other configuration the measurement plan lists, one line each: the complex scan
     forward and backward, the forward at each forward shape (both beta where listed), the
     forward with an unstructured A, the fused forward, and the README benchmark shape forward
@@ -281,7 +281,7 @@ def bench_configs(steps, warmup, stream):
             ("pages", "bwd", {"beta": 0.0}, "s4d", False, False)]
     out = []
     # the complex-valued scan (A = -1/2 + i pi n, complex B and C), forward and backward
-    for direction in ("fwd", "bwd"):
+    for direction in ("fwd", "bwd") if only is None or "complex" in only else ():
         w = W["complex"]
         ms, per = bench_complex(w, steps, warmup, stream, direction)
         out.append({"workload": "complex", "direction": direction, "beta": w.beta, "A": "s4d_lin",
@@ -291,6 +291,8 @@ def bench_configs(steps, warmup, stream):
         import torch
         torch.cuda.empty_cache()
     for name, direction, kw, a_kind, fused, zoh in runs:
+        if only is not None and name not in only:
+            continue
         w = W[name].replace(**kw)
         if direction == "fwd":
             ms, per, plan = bench_fwd(w, steps, warmup, stream, a_kind=a_kind, fused=fused, zoh=zoh)
@@ -384,6 +386,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations (m130m, long, README shape, ...)")
+    ap.add_argument("--configs-only", default=None,
+                    help="comma-separated workload names: run only their configuration lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "NAME",
@@ -472,7 +476,9 @@ def main(argv=None):
         del src, dst
         torch.cuda.empty_cache()
     if not args.no_configs:
-        rec["configs"] = bench_configs(max(5, args.steps // 2), max(3, args.warmup // 2), stream)
+        only = None if args.configs_only is None else set(args.configs_only.split(","))
+        rec["configs"] = bench_configs(max(5, args.steps // 2), max(3, args.warmup // 2), stream,
+                                       only)
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
