@@ -338,7 +338,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
   double dD64 = 0.0;
   double dbias64 = 0.0;  // fused variant: this lane's rows of the bias gradient (lanes >= 32)
-  const float dsk = (HAS_DSKIP && gs == 0) ? p.Dskip[dl] : 0.f;
+  // (the zero-order-hold variant always runs with the skip term compiled in, a zero weight
+  // when no Dskip is given; see launch_ks)
+  const float dsk = (HAS_DSKIP && gs == 0 && p.Dskip) ? p.Dskip[dl] : 0.f;
   const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
   char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
   char* ddl0 = static_cast<char*>(p.ddelta) + b * tot_d;
@@ -589,10 +591,17 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 template <typename IO, int K, int S, bool BETA0, int EXT>
 hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(S * kWave);
-  if (a.Dskip)
+  // The zero-order-hold variant takes the skip-term build even without Dskip (weight zero, its
+  // partials left unread): the compiler schedules that build with far fewer spills (measured
+  // at Bt=4, L=2048, D=2048, N=16, fp32: 1.16 ms against 2.24 ms without the skip term).
+  if constexpr (EXT == 2) {
     hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false, EXT>), grid, block, 0, s, a);
+  } else {
+    if (a.Dskip)
+      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false, EXT>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
