@@ -272,3 +272,64 @@ def test_bwd_plan_choice():
     assert msm.msm_scan_bwd_plan(1, 64, 64, 4, "f32", 0.9)["states_per_wave"] == 1
     # 64 padded states: the full-wavefront backward, 4 states per lane
     assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 4
+
+
+def test_complex_workspace_query(lib):
+    align = lambda v: (v + 255) // 256 * 256
+    Bt, L, D, N = 4, 2048, 2048, 16
+    ncb, NP = (D + 31) // 32, 16
+    want = (align(8 * Bt * (L + 1) * N * D) + align(16 * Bt * ncb * L * NP) + align(8 * Bt * D * N)
+            + align(4 * Bt * D))
+    assert msm.msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, "f32") == want
+    assert msm.msm_scan_complex_bwd_workspace_bytes(0, L, D, N, "f32") == 0
+    assert msm.msm_scan_complex_bwd_workspace_bytes(1, L, D, 65, "f32") == 0
+    # 17 history rows of N * D complex fp32 values must stay below 2^31 bytes
+    assert msm.msm_scan_complex_bwd_workspace_bytes(1, 16, 1 << 21, 64, "bf16") == 0
+    assert msm.msm_scan_complex_bwd_workspace_bytes(1, 16, 1 << 19, 16, "bf16") > 0
+
+
+def test_complex_validation_never_launches(lib):
+    P = ctypes.c_void_p
+    F = ctypes.c_float
+
+    def fwd(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, h0=None,
+                 v0=None, y=0x100000, lh=None, lv=None, Bt=2, L=8, D=4, N=4, beta=0.5, io=0)
+        a.update(kw)
+        return lib.msm_scan_complex_fwd(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
+                                        P(a["Dskip"]), P(a["h0"]), P(a["v0"]), P(a["y"]), P(a["lh"]),
+                                        P(a["lv"]), a["Bt"], a["L"], a["D"], a["N"], F(a["beta"]),
+                                        F(1.0), a["io"], None)
+
+    # x, delta, y: 2*8*4 fp32 = 256 bytes; B, C: 2*8*4 complex = 512 bytes
+    assert fwd(x=None) == INVALID
+    assert fwd(y=None) == INVALID
+    assert fwd(Bt=0) == INVALID
+    assert fwd(N=65) == UNSUPPORTED
+    assert fwd(beta=1.0) == INVALID
+    assert fwd(io=7) == UNSUPPORTED
+    assert fwd(y=0x1000 + 128) == INVALID          # y over x
+    assert fwd(lh=0x4000 + 256) == INVALID         # a final state over B
+    assert fwd(D=1 << 21, N=64) == INVALID         # history rows past 32-bit offsets
+
+    def bwd(ws_bytes=1 << 30, **kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, h0=None,
+                 v0=None, dy=0x6000, dlh=None, dlv=None, dx=0x100000, dd=0x200000, dA=0x300000,
+                 dB=0x400000, dC=0x500000, dDskip=None, dh0=None, dv0=None, ws=0x10000000, Bt=2,
+                 L=8, D=4, N=4)
+        a.update(kw)
+        return lib.msm_scan_complex_bwd(
+            P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]), P(a["Dskip"]), P(a["h0"]),
+            P(a["v0"]), P(a["dy"]), P(a["dlh"]), P(a["dlv"]), P(a["dx"]), P(a["dd"]), P(a["dA"]),
+            P(a["dB"]), P(a["dC"]), P(a["dDskip"]), P(a["dh0"]), P(a["dv0"]), a["Bt"], a["L"],
+            a["D"], a["N"], F(0.5), F(1.0), 0, P(a["ws"]), ws_bytes, None)
+
+    assert bwd(dy=None) == INVALID
+    assert bwd(dC=None) == INVALID
+    assert bwd(Dskip=0x7000) == INVALID            # Dskip without dDskip
+    assert bwd(dDskip=0x7000) == INVALID           # dDskip without Dskip
+    assert bwd(ws_bytes=16) == WORKSPACE
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(dx=0x2000) == INVALID               # dx over delta
+    assert bwd(dB=0x10000000) == INVALID           # dB inside the workspace
+    assert bwd(dh0=0x6000) == INVALID              # dh0 over dy
