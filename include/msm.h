@@ -234,7 +234,8 @@ msm_status msm_scan_step(const void* x, const void* delta, const float* A, const
  * The real part of C h is the readout (a conjugate-pair convention, C h + conj(C h), would be
  * twice this).  h0, v0 (NULL = zero) start the scan; last_h, last_v (may be NULL) receive the
  * final state.  Requirements as msm_scan_fwd, and 17 * N * D * 8 < 2^31 (the kernels address
- * 17 rows of the state history with 32-bit offsets).
+ * 17 rows of the state history with 32-bit offsets); B and C must be aligned to a whole complex
+ * element (8 bytes for MSM_F32, 4 for MSM_BF16), else MSM_ERR_INVALID_ARG.
  * Needs no workspace. */
 msm_status msm_scan_complex_fwd(const void* x, const void* delta, const float* A, const void* B,
                                 const void* C, const float* Dskip, const float* h0,
@@ -253,7 +254,8 @@ size_t msm_scan_complex_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, in
  * dL/dRe + i dL/dIm (the convention of PyTorch's complex autograd for a real loss): dA (summed
  * over batch and time), dB, dC (summed over channels), and dh0, dv0 when non-NULL.  dx, ddelta
  * are real; dDskip is required exactly when Dskip is given.  A forward pass that records every
- * state into the workspace runs first; nothing from an earlier forward call is needed.
+ * state into the workspace runs first; nothing from an earlier forward call is needed.  The
+ * workspace must be 16-byte aligned (MSM_ERR_INVALID_ARG otherwise).
  * Everything else as msm_scan_complex_fwd. */
 msm_status msm_scan_complex_bwd(const void* x, const void* delta, const float* A, const void* B,
                                 const void* C, const float* Dskip, const float* h0,

@@ -229,6 +229,10 @@ CBwdLayout cbwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   return l;
 }
 
+// The complex kernels load B and C as whole (re, im) pairs and read the workspace's partial
+// sums as 16-byte vectors.
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 msm_status check_complex(int64_t Bt, int64_t L, int64_t D, int64_t N, float beta, float alpha,
                          msm_dtype io) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
@@ -614,6 +618,7 @@ msm_status msm_scan_complex_fwd(const void* x, const void* delta, const float* A
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
   const size_t es = io == MSM_BF16 ? 2 : 4;
+  if (!aligned(B, 2 * es) || !aligned(C, 2 * es)) return MSM_ERR_INVALID_ARG;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
   const size_t nst = (size_t)(Bt * D * N) * 8;
   const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),
@@ -663,6 +668,8 @@ msm_status msm_scan_complex_bwd(const void* x, const void* delta, const float* A
   const CBwdLayout lay = cbwd_layout(Bt, L, D, N);
   if (workspace_bytes < lay.total || !workspace) return MSM_ERR_WORKSPACE;
   const size_t es = io == MSM_BF16 ? 2 : 4;
+  if (!aligned(B, 2 * es) || !aligned(C, 2 * es) || !aligned(workspace, 16))
+    return MSM_ERR_INVALID_ARG;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
   const size_t nst = (size_t)(Bt * D * N) * 8;
   const Range ins[] = {rng(x, nxd * es),          rng(delta, nxd * es),

@@ -311,6 +311,8 @@ def test_complex_validation_never_launches(lib):
     assert fwd(y=0x1000 + 128) == INVALID          # y over x
     assert fwd(lh=0x4000 + 256) == INVALID         # a final state over B
     assert fwd(D=1 << 21, N=64) == INVALID         # history rows past 32-bit offsets
+    assert fwd(B=0x4000 + 4) == INVALID            # B not aligned to a complex fp32 pair
+    assert fwd(C=0x5000 + 2, io=1) == INVALID      # C not aligned to a complex bf16 pair
 
     def bwd(ws_bytes=1 << 30, **kw):
         a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, h0=None,
@@ -330,6 +332,7 @@ def test_complex_validation_never_launches(lib):
     assert bwd(dDskip=0x7000) == INVALID           # dDskip without Dskip
     assert bwd(ws_bytes=16) == WORKSPACE
     assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws=0x10000000 + 8) == INVALID       # workspace not 16-byte aligned
     assert bwd(dx=0x2000) == INVALID               # dx over delta
     assert bwd(dB=0x10000000) == INVALID           # dB inside the workspace
     assert bwd(dh0=0x6000) == INVALID              # dh0 over dy
