@@ -21,7 +21,7 @@ constexpr int64_t kMaxWorkgroups = 4096;
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int padded_states(int64_t N) { return N <= 4 ? 4 : (N <= 16 ? 16 : 64); }
+int padded_states(int64_t N) { return N <= 4 ? 4 : (N <= 16 ? 16 : (N <= 32 ? 32 : 64)); }
 
 bool shape_ok(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   if (Bt < 1 || L < 1 || D < 1 || N < 1) return false;
@@ -75,6 +75,7 @@ bool allowed_k(int NP, int K) {
   switch (NP) {
     case 4: return K == 1 || K == 2 || K == 4;
     case 16: return K == 1 || K == 2 || K == 4 || K == 8 || K == 16;
+    case 32: return K == 4 || K == 8;
     case 64: return K == 4 || K == 8 || K == 16;
     default: return false;
   }
@@ -92,12 +93,12 @@ msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int NP = padded_states(N);
   const int64_t chan_blocks = Bt * ceil_div(D, kWave);
   msm_plan pl{0, 1};
-  const int kpref = NP == 4 ? 1 : (NP == 16 ? 2 : 8);
+  const int kpref = NP == 4 ? 1 : (NP == 16 ? 2 : (NP == 32 ? 4 : 8));
   if (chan_blocks * (NP / kpref) >= kTargetWaves) {
     pl.states_per_wave = kpref;
     return pl;
   }
-  const int kchunk = NP == 4 ? 2 : (NP == 16 ? 2 : 8);
+  const int kchunk = NP == 4 ? 2 : (NP == 16 ? 2 : (NP == 32 ? 4 : 8));
   const int64_t waves = chan_blocks * (NP / kchunk);
   const int per_simd = NP == 16 ? 4 : 2;
   int64_t G = ceil_div(per_simd * kTargetWaves, waves);
@@ -134,21 +135,22 @@ bool bwd_allowed_k(int NP, int K) {
   switch (NP) {
     case 4: return K == 1 || K == 2;
     case 16: return K == 1 || K == 2 || K == 4;
+    case 32: return K == 2;  // 8 wavefronts of 2 states per half
     case 64: return K == 4;  // the full-wavefront backward: 16 wavefronts of 4 states
     default: return false;
   }
 }
 
-// For 4 or 16 padded states a backward workgroup holds 2K states of kBwdChans channels per
-// wavefront and NP / (2K) wavefronts.  A wavefront alone on its SIMD stalls on every non-VALU
+// For 4, 16 or 32 padded states a backward workgroup holds 2K states of kBwdChans channels per
+// wavefront and NP / (2K) wavefronts (32 states: always K = 2, 8 wavefronts).  A wavefront alone on its SIMD stalls on every non-VALU
 // instruction and on LDS and fp64 latencies, so the plan asks for two wavefronts per SIMD: the
 // largest K (at most 2: K = 4 needs more registers than two wavefronts leave) that still gives
 // 2 * 1024 wavefronts, else K = 1.  64 padded states always take K = 4 (full-wavefront kernel).
 msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = false) {
   const int NP = padded_states(N);
   msm_plan pl{0, 1};
-  if (NP == 64) {
-    pl.states_per_wave = 4;
+  if (NP == 64 || NP == 32) {
+    pl.states_per_wave = NP == 64 ? 4 : 2;
     return pl;
   }
   const int64_t chan_blocks = Bt * ceil_div(D, msm::kBwdChans);

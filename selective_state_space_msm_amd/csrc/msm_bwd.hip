@@ -35,7 +35,7 @@
 // dx / ddelta, and the bias gradient is summed per channel.  Its zero-order-hold form (EXT = 2)
 // also carries the write coefficient g = delta phi(delta A) and its derivatives (dg/ddelta =
 // e^(delta A), dg/dA = delta^2 psi(delta A)) through dx, ddelta, dA and dB.
-// This kernel serves 4 and 16 padded states; 64 padded states use the full-wavefront
+// This kernel serves 4, 16 and 32 padded states; 64 padded states use the full-wavefront
 // backward in msm_bwd_wide.hip.
 #include <type_traits>
 
@@ -614,6 +614,7 @@ hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
     case 1601: return launch_ks<IO, 1, 8, BETA0, EXT>(a, s);
     case 1602: return launch_ks<IO, 2, 4, BETA0, EXT>(a, s);
     case 1604: return launch_ks<IO, 4, 2, BETA0, EXT>(a, s);
+    case 3202: return launch_ks<IO, 2, 8, BETA0, EXT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

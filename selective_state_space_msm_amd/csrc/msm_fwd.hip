@@ -458,8 +458,8 @@ hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
 
 template <typename IO, bool BETA0, int EXT>
 hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
-  // padded state count NP = K * S is 4, 16 or 64
-  const int NP = a.N <= 4 ? 4 : (a.N <= 16 ? 16 : 64);
+  // padded state count NP = K * S is 4, 16, 32 or 64
+  const int NP = a.N <= 4 ? 4 : (a.N <= 16 ? 16 : (a.N <= 32 ? 32 : 64));
   switch (NP * 100 + K) {
     case 401: return launch_ks<IO, 1, 4, BETA0, EXT>(a, s);
     case 402: return launch_ks<IO, 2, 2, BETA0, EXT>(a, s);
@@ -469,6 +469,8 @@ hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
     case 1604: return launch_ks<IO, 4, 4, BETA0, EXT>(a, s);
     case 1608: return launch_ks<IO, 8, 2, BETA0, EXT>(a, s);
     case 1616: return launch_ks<IO, 16, 1, BETA0, EXT>(a, s);
+    case 3204: return launch_ks<IO, 4, 8, BETA0, EXT>(a, s);
+    case 3208: return launch_ks<IO, 8, 4, BETA0, EXT>(a, s);
     case 6404: return launch_ks<IO, 4, 16, BETA0, EXT>(a, s);
     case 6408: return launch_ks<IO, 8, 8, BETA0, EXT>(a, s);
     case 6416: return launch_ks<IO, 16, 4, BETA0, EXT>(a, s);

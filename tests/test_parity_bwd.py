@@ -62,6 +62,15 @@ def test_many_states(N):
     check_full(inp, plan={"states_per_wave": 4}, tag="N=%d" % N)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N,dskip", [(17, True), (24, False), (32, True)])
+def test_32_states(io, N, dskip):
+    # 17-32 states pad to 32: the half-wavefront backward with 8 wavefronts of 2 states
+    inp = workloads.make_inputs(SMALL.replace(io=io, L=53, D=45, N=N, dskip=dskip),
+                                a_kind="random", seed=60 + N)
+    check_full(inp, tag="N=%d" % N)
+
+
 @pytest.mark.skip(reason="the half-wavefront backward at 64 padded states (N=33, K=2: 16 "
                          "wavefronts per workgroup) stopped with an illegal memory access on "
                          "MI355X; no out-of-bounds index was found on the CPU, so its "

@@ -161,9 +161,10 @@ def test_state_counts(N):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [33, 64])
+@pytest.mark.parametrize("N", [20, 32, 33, 64])
 def test_many_states(io, N):
-    # 64 padded states: the 64-state forward kernels and the full-wavefront backward
+    # 32 padded states (N = 20, 32): the half-wavefront backward with 8 wavefronts; 64 (N = 33,
+    # 64): the 64-state forward kernels and the full-wavefront backward
     w = SMALL.replace(L=40, D=70, N=N, io=io, dskip=True)
     check(fused_inputs(w, 441 + N), tag="N=%d" % N, state=True)
     check(fused_inputs(w.replace(dskip=False, beta=0.0), 442 + N, softplus=False), tag="N=%d" % N)
@@ -258,7 +259,7 @@ def test_zoh_small(io, K):
           state=True, tag="zoh small K=%d" % K)
 
 
-@pytest.mark.parametrize("N", [5, 33])
+@pytest.mark.parametrize("N", [5, 27, 33])
 def test_zoh_state_counts(N):
     w = SMALL.replace(L=40, D=70, N=N, dskip=True)
     check(fused_inputs(w, 500 + N, softplus=False, use_z=False, use_bias=False, zoh=True),

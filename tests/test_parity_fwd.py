@@ -68,7 +68,7 @@ def test_small_ragged_settings(io, beta, alpha, dskip):
     check_full(inp, tag="settings")
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 17, 33, 64])
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 17, 24, 32, 33, 64])
 def test_state_counts(N):
     inp = workloads.make_inputs(SMALL.replace(L=70, D=70, N=N, beta=0.8, dskip=True),
                                 a_kind="random", seed=100 + N)
@@ -184,3 +184,10 @@ def test_rows_beyond_32bit_offsets():
         assert_close(host(y[:, :, dsel]), want, "f32", "y plan %s" % plan)
         assert_close(host(lh[:, dsel]), wh, "f32", "last_h plan %s" % plan)
         del y, lh
+
+
+@pytest.mark.parametrize("K,chunks", [(4, 1), (8, 1), (8, 3)])
+def test_32_state_plans(K, chunks):
+    inp = workloads.make_inputs(SMALL.replace(L=90, D=70, N=29, beta=0.85, dskip=True),
+                                a_kind="random", seed=130 + K + chunks)
+    check_full(inp, plan={"states_per_wave": K, "chunks": chunks}, tag="N=29 K=%d" % K)
