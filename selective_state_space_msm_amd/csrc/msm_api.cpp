@@ -128,15 +128,21 @@ FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
 }
 
 // ---- backward planning ----
-// channels per backward workgroup
-int64_t bwd_chans(int NP) { return NP == 64 ? kWave : msm::kBwdChans; }
+// channels per backward workgroup: 64 for the full-wavefront kernel (64 padded states with
+// K = 4), kBwdChans for the half-wavefront one
+int64_t bwd_chans(int NP, int K) { return (NP == 64 && K == 4) ? kWave : msm::kBwdChans; }
+
+// 64 padded states as two halves of the 32-state plan address a tile of the first half's
+// fp64 sums ([L][2][D] per batch row) with 32-bit offsets: kBwdTile rows of 16 D bytes
+bool bwd_split_ok(int64_t D) { return (int64_t)msm::kBwdTile * 16 * D < ((int64_t)1 << 31); }
 
 bool bwd_allowed_k(int NP, int K) {
   switch (NP) {
     case 4: return K == 1 || K == 2;
     case 16: return K == 1 || K == 2 || K == 4;
     case 32: return K == 2;  // 8 wavefronts of 2 states per half
-    case 64: return K == 4;  // the full-wavefront backward: 16 wavefronts of 4 states
+    // two halves of the 32-state plan (K = 2), or the full-wavefront backward (K = 4)
+    case 64: return K == 2 || K == 4;
     default: return false;
   }
 }
@@ -150,7 +156,9 @@ msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = f
   const int NP = padded_states(N);
   msm_plan pl{0, 1};
   if (NP == 64 || NP == 32) {
-    pl.states_per_wave = NP == 64 ? 4 : 2;
+    // 64 states: two launches of the 32-state plan (measured at Bt=4, L=2048, D=2048, N=64:
+    // the full-wavefront kernel, which spills, takes 12.5 ms)
+    pl.states_per_wave = (NP == 64 && !bwd_split_ok(D)) ? 4 : 2;
     return pl;
   }
   const int64_t chan_blocks = Bt * ceil_div(D, msm::kBwdChans);
@@ -164,7 +172,7 @@ msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = f
 }
 
 struct BwdLayout {
-  size_t off_ckpt, off_dbc, off_dA, off_dD, off_dbias, total;
+  size_t off_ckpt, off_dbc, off_dA, off_dD, off_dbias, off_accq, off_accz, total;
 };
 
 BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
@@ -178,7 +186,14 @@ BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   l.off_dA = l.off_dbc + align_up(sizeof(float) * (size_t)(Bt * ncb * L * 2 * NP));
   l.off_dD = l.off_dA + align_up(sizeof(float) * (size_t)(Bt * N * D));
   l.off_dbias = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
-  l.total = l.off_dbias + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.off_accq = l.off_dbias + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.off_accz = l.off_accq;
+  l.total = l.off_accq;
+  if (NP == 64 && bwd_split_ok(D)) {
+    // the first half's sums when 64 states run as two halves
+    l.off_accz = l.off_accq + align_up(sizeof(double) * 2 * (size_t)(Bt * L * D));
+    l.total = l.off_accz + align_up(sizeof(float) * (size_t)(Bt * L * D));
+  }
   return l;
 }
 
@@ -443,6 +458,7 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   if (plan) {
     if (plan->states_per_wave != 0) {
       if (!bwd_allowed_k(NP, plan->states_per_wave)) return MSM_ERR_UNSUPPORTED;
+      if (NP == 64 && plan->states_per_wave == 2 && !bwd_split_ok(D)) return MSM_ERR_UNSUPPORTED;
       pl.states_per_wave = plan->states_per_wave;
     }
     if (plan->chunks != 0 && plan->chunks != 1) return MSM_ERR_UNSUPPORTED;
@@ -506,12 +522,14 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   a.dA_part = reinterpret_cast<float*>(ws + lay.off_dA);
   a.dD_part = reinterpret_cast<float*>(ws + lay.off_dD);
   a.dbias_part = reinterpret_cast<float*>(ws + lay.off_dbias);
+  a.acc_q = reinterpret_cast<double*>(ws + lay.off_accq);
+  a.acc_dz = reinterpret_cast<float*>(ws + lay.off_accz);
   a.Bt = Bt;
   a.L = L;
   a.D = D;
   a.N = N;
   a.NT = ceil_div(L, msm::kBwdTile);
-  a.ncb = (int32_t)ceil_div(D, bwd_chans(NP));
+  a.ncb = (int32_t)ceil_div(D, bwd_chans(NP, pl.states_per_wave));
   a.NP = NP;
   a.beta = beta;
   a.alpha = alpha;

@@ -46,7 +46,15 @@
 namespace msm {
 namespace {
 
-template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, int EXT>
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// SPLIT: 0 = all states of the channel in one launch; 1 / 2 = the first / second half of 64
+// padded states (states n0 .. n0 + NPB - 1 of the arrays), run as two launches of the 32-state
+// plan.  Every gradient is a sum of per-state terms, so the halves' partial sums add up: the
+// first launch leaves its dx / ddelta (fp64) and dz (fp32) sums in the workspace and writes no
+// bias gradient, the second adds them to its own before storing; the skip term belongs to the
+// first launch (the second runs without Dskip).
+template <typename IO, int K, int S, bool BETA0, bool HAS_DSKIP, int EXT, int SPLIT>
 __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   using T = io<IO>;
   using raw = typename T::raw;
@@ -87,11 +95,13 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const int dl = dvalid ? d : (int)D - 1;
   const float beta = p.beta;
   const double beta64 = p.beta;
+  const int n0 = SPLIT ? p.n0 : 0;      // first state of this launch
+  const int NPD = SPLIT ? p.NP : NPB;   // states per row of the dB / dC partials
 
   float A2[K], Af[K], v[K], h[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int64_t n = (int64_t)gs * K + j;
+    const int64_t n = n0 + (int64_t)gs * K + j;
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     Af[j] = an;
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   for (int r = 0; r < NPE; ++r) {
     const int i = tid + r * NTHR;
     const int ic = i < BCE ? i : BCE - 1;
-    const int n = ic % NPB;
+    const int n = n0 + ic % NPB;
     bc_voff[r] = n < N ? (uint32_t)(((ic / NPB) * N + n) * T::es) : 0x80000000u;
   }
   raw bre[NPE], cre[NPE];
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   uint32_t ck_voff[2][K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int64_t n = (int64_t)gs * K + j;
+    const int64_t n = n0 + (int64_t)gs * K + j;
 #pragma unroll
     for (int w = 0; w < 2; ++w)
       ck_voff[w][j] = (dvalid && n < N) ? (uint32_t)(((w * N + n) * D + d) * 4) : 0x80000000u;
@@ -341,7 +351,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   // (the zero-order-hold variant always runs with the skip term compiled in, a zero weight
   // when no Dskip is given; see launch_ks)
   const float dsk = (HAS_DSKIP && gs == 0 && p.Dskip) ? p.Dskip[dl] : 0.f;
-  const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPB;
+  const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPD;
   char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
   char* ddl0 = static_cast<char*>(p.ddelta) + b * tot_d;
   const uint32_t lane_off = (uint32_t)dl * T::es;
@@ -357,6 +367,12 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   // fused variant: dz of the row comes from lanes 0-31 as well
   char* dz0 = (EXT && p.dz) ? static_cast<char*>(p.dz) + b * tot_d : dx0;
   const uint32_t vo_dz = (dvalid && lane < CB) ? lane_off : 0x80000000u;
+  // split passes: per-lane offsets into the first half's sums
+  const int64_t aq_row_bytes = 2 * D * 8, aq_tot = L * aq_row_bytes;
+  char* aq0 = SPLIT ? reinterpret_cast<char*>(p.acc_q) + b * aq_tot : dx0;
+  char* az0 = SPLIT ? reinterpret_cast<char*>(p.acc_dz) + b * L * D * 4 : dx0;
+  const uint32_t vo_aq = dvalid ? (uint32_t)(((lane >= CB ? 1 : 0) * D + dl) * 8) : 0x80000000u;
+  const uint32_t vo_dz32 = (dvalid && lane < CB) ? (uint32_t)dl * 4u : 0x80000000u;
   // xb: the LDS staging buffer that still holds the tile's inputs
   auto finalize = [&](int64_t tile, int pb, bool valid, int xb) {
     const int64_t ts = tile * TB;
@@ -364,6 +380,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     const auto rdx = valid ? rows_rsrc(dx0, ts, row_bytes, tot_d) : make_rsrc(dx0, 0);
     const auto rdd = valid ? rows_rsrc(ddl0, ts, row_bytes, tot_d) : make_rsrc(ddl0, 0);
     const auto rdz = (valid && has_z) ? rows_rsrc(dz0, ts, row_bytes, tot_d) : make_rsrc(dz0, 0);
+    // split passes: the first half's sums, [L][2][D] fp64 (dx, ddelta) and [L][D] fp32 (dz)
+    const auto raq = (SPLIT && valid) ? rows_rsrc(aq0, ts, aq_row_bytes, aq_tot) : make_rsrc(aq0, 0);
+    const auto raz = (SPLIT && valid && has_z) ? rows_rsrc(az0, ts, D * 4, L * D * 4)
+                                               : make_rsrc(az0, 0);
 #pragma unroll
     for (int tr0 = 0; tr0 < TB; tr0 += S) {
       const int tt = tr0 + g;
@@ -373,20 +393,57 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         for (int w = 1; w < S; ++w) q += (double)spart[pb][w][tt][lane];
         // rows past the end of the sequence are past the extent: dropped
         const uint32_t ro = (uint32_t)(tt * row_bytes);
-        T::bstore(rdx, vo_dx + ro, 0u, (float)q);
-        if (EXT) {
-          // lanes 32-63: the gradient of the raw delta (through softplus); lanes 0-31: dz from
-          // the output before the gate, summed over the S wavefronts in a fixed order
-          const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
-          const double qd = q * (double)e.y;
-          if (valid) dbias64 += qd;
-          T::bstore(rdd, vo_dd + ro, 0u, (float)qd);
-          float yr = ypt[EXT ? pb : 0][0][EXT ? tt : 0][ch];
+        if constexpr (SPLIT == 0) {
+          T::bstore(rdx, vo_dx + ro, 0u, (float)q);
+          if (EXT) {
+            // lanes 32-63: the gradient of the raw delta (through softplus); lanes 0-31: dz from
+            // the output before the gate, summed over the S wavefronts in a fixed order
+            const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
+            const double qd = q * (double)e.y;
+            if (valid) dbias64 += qd;
+            T::bstore(rdd, vo_dd + ro, 0u, (float)qd);
+            float yr = ypt[EXT ? pb : 0][0][EXT ? tt : 0][ch];
 #pragma unroll
-          for (int w = 1; w < S; ++w) yr += ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
-          T::bstore(rdz, vo_dz + ro, 0u, e.x * yr);
+            for (int w = 1; w < S; ++w) yr += ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
+            T::bstore(rdz, vo_dz + ro, 0u, e.x * yr);
+          } else {
+            T::bstore(rdd, vo_dd + ro, 0u, (float)q);
+          }
         } else {
-          T::bstore(rdd, vo_dd + ro, 0u, (float)q);
+          // split passes: lanes 0-31 carry dx, lanes 32-63 ddelta (the raw delta's, through
+          // softplus, when fused); the first pass stores its sums, the second adds them
+          const uint32_t aqo = vo_aq + (uint32_t)(tt * aq_row_bytes);
+          const uint32_t azo = vo_dz32 + (uint32_t)(tt * D * 4);
+          double val = q;
+          float2 e = make_float2(0.f, 0.f);
+          if (EXT) {
+            e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
+            if (lane >= CB) val = q * (double)e.y;
+          }
+          if (SPLIT == 2) {
+            const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(raq, aqo, 0u, 0);
+            val += __longlong_as_double((long long)(((uint64_t)w.y << 32) | w.x));
+          }
+          if (SPLIT == 1) {
+            const uint64_t u = (uint64_t)__double_as_longlong(val);
+            const u32x2_t w = {(uint32_t)u, (uint32_t)(u >> 32)};
+            __builtin_amdgcn_raw_buffer_store_b64(w, raq, aqo, 0u, 0);
+          } else {
+            T::bstore(rdx, vo_dx + ro, 0u, (float)val);
+            T::bstore(rdd, vo_dd + ro, 0u, (float)val);
+            if (EXT && valid && lane >= CB) dbias64 += val;
+          }
+          if (EXT) {
+            float yr = ypt[EXT ? pb : 0][0][EXT ? tt : 0][ch];
+#pragma unroll
+            for (int w = 1; w < S; ++w) yr += ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
+            float zv = e.x * yr;
+            if (SPLIT == 2) zv += io<float>::bload(raz, azo, 0u);
+            if (SPLIT == 1)
+              io<float>::bstore(raz, azo, 0u, zv);
+            else
+              T::bstore(rdz, vo_dz + ro, 0u, zv);
+          }
         }
       }
     }
@@ -394,14 +451,14 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 
   // dB / dC partials of this workgroup, [L][2][NPB] fp32 at dbc: a resource per tile and a
   // constant offset per lane and reduce block (lane l of a half holds value l & 31)
-  const int64_t dbc_row_bytes = 2 * NPB * 4, dbc_tot = L * dbc_row_bytes;
+  const int64_t dbc_row_bytes = 2 * NPD * 4, dbc_tot = L * dbc_row_bytes;
   uint32_t dbc_voff[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int m = lane & 31;
     const int tt = rb * RB + m / (2 * K);
     const int n = gs * K + m % K;
-    dbc_voff[rb] = (uint32_t)((tt * 2 * NPB + ((m / K) & 1) * NPB + n) * 4);
+    dbc_voff[rb] = (uint32_t)((tt * 2 * NPD + ((m / K) & 1) * NPD + n0 + n) * 4);
   }
 
   auto load_ckpt = [&](float(&ov)[K], float(&oh)[K], int64_t tile) {
@@ -430,7 +487,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     double dlh[K], dlv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)gs * K + j;
+      const int64_t n = n0 + (int64_t)gs * K + j;
       const int64_t si = (b * D + dl) * N + n;
       dlh[j] = (FIRST && p.dlast_h && dvalid && n < N) ? (double)p.dlast_h[si] : 0.0;
       dlv[j] = (FIRST && p.dlast_v && dvalid && n < N) ? (double)p.dlast_v[si] : 0.0;
@@ -541,7 +598,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     if (tile == 0 && dvalid) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const int64_t n = (int64_t)gs * K + j;
+        const int64_t n = n0 + (int64_t)gs * K + j;
         const int64_t si = (b * D + d) * N + n;
         if (n < N && p.dh0) p.dh0[si] = (float)ghn[j];
         if (n < N && p.dv0) p.dv0[si] = BETA0 ? 0.f : (float)(beta64 * gvp[j]);
@@ -570,12 +627,12 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)gs * K + j;
+      const int64_t n = n0 + (int64_t)gs * K + j;
       if (n < N) p.dA_part[(b * N + n) * D + d] = (float)dA64[j];
     }
-    if (HAS_DSKIP && gs == 0) p.dD_part[b * D + d] = (float)dD64;
+    if (HAS_DSKIP && gs == 0 && p.Dskip) p.dD_part[b * D + d] = (float)dD64;
   }
-  if (EXT && p.delta_bias) {
+  if (EXT && SPLIT != 1 && p.delta_bias) {
     // the bias gradient of the channel: lanes 32-63 of every wavefront hold their rows' sum
     if (lane >= CB) bred[EXT ? g : 0][ch] = dbias64;
     __syncthreads();
@@ -588,19 +645,19 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S, bool BETA0, int EXT>
+template <typename IO, int K, int S, bool BETA0, int EXT, int SPLIT = 0>
 hipError_t launch_ks(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(S * kWave);
   // The zero-order-hold variant takes the skip-term build even without Dskip (weight zero, its
   // partials left unread): the compiler schedules that build with far fewer spills (measured
   // at Bt=4, L=2048, D=2048, N=16, fp32: 1.16 ms against 2.24 ms without the skip term).
   if constexpr (EXT == 2) {
-    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT, SPLIT>), grid, block, 0, s, a);
   } else {
     if (a.Dskip)
-      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, true, EXT, SPLIT>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false, EXT>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_kernel<IO, K, S, BETA0, false, EXT, SPLIT>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -615,6 +672,10 @@ hipError_t launch_io(const BwdArgs& a, int K, hipStream_t s) {
     case 1602: return launch_ks<IO, 2, 4, BETA0, EXT>(a, s);
     case 1604: return launch_ks<IO, 4, 2, BETA0, EXT>(a, s);
     case 3202: return launch_ks<IO, 2, 8, BETA0, EXT>(a, s);
+    // 64 padded states as two halves of the 32-state plan (a.split_pass 1, then 2)
+    case 6402:
+      return a.split_pass == 1 ? launch_ks<IO, 2, 8, BETA0, EXT, 1>(a, s)
+                               : launch_ks<IO, 2, 8, BETA0, EXT, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -76,6 +76,13 @@ struct BwdArgs {
   float* ckpt;       // [Bt][NT][2][N][D]  (v, h) before each tile of kBwdTile steps
   float* dbc_part;   // [Bt][ncb][L][2][NP] per channel-block (kBwdChans) partial sums
                      // of dB/alpha and dC
+  // 64 padded states in two launches of the 32-state kernel: the launch's first state, which
+  // launch (1, 2), and the first launch's sums for the second ([Bt][L][2][D] fp64 dx, ddelta;
+  // [Bt][L][D] fp32 dz)
+  int32_t n0;
+  int32_t split_pass;
+  double* acc_q;
+  float* acc_dz;
   float* dA_part;    // [Bt][N][D]
   float* dD_part;    // [Bt][D]
   float* dbias_part; // [Bt][D] per batch row partial sums of the delta-bias gradient

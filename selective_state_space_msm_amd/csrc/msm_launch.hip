@@ -72,7 +72,29 @@ hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s) {
   hipError_t e;
-  if (a.NP == 64) {
+  if (a.NP == 64 && K == 2) {
+    // two halves of 32 states through the half-wavefront kernel: the second runs without the
+    // skip term (the first adds it) and adds the first's dx / ddelta / dz sums
+    auto part = [&](const BwdArgs& h) {
+      if (io_bf16)
+        return ext == 2 ? launch_bwd_part_1_2(h, 2, beta0, s)
+               : ext == 1 ? launch_bwd_part_1_1(h, 2, beta0, s)
+                          : launch_bwd_part_1_0(h, 2, beta0, s);
+      return ext == 2 ? launch_bwd_part_0_2(h, 2, beta0, s)
+             : ext == 1 ? launch_bwd_part_0_1(h, 2, beta0, s)
+                        : launch_bwd_part_0_0(h, 2, beta0, s);
+    };
+    BwdArgs h1 = a;
+    h1.n0 = 0;
+    h1.split_pass = 1;
+    e = part(h1);
+    if (e != hipSuccess) return e;
+    BwdArgs h2 = a;
+    h2.n0 = 32;
+    h2.split_pass = 2;
+    h2.Dskip = nullptr;
+    e = part(h2);
+  } else if (a.NP == 64) {
     e = launch_bwd_wide(a, io_bf16, beta0, ext, s);
   } else if (io_bf16) {
     e = ext == 2 ? launch_bwd_part_1_2(a, K, beta0, s)

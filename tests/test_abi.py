@@ -270,8 +270,10 @@ def test_bwd_plan_choice():
     assert msm.msm_scan_bwd_plan(8, 2048, 4096, 16, "f32", 0.9)["states_per_wave"] == 2
     assert msm.msm_scan_bwd_plan(1, 64, 64, 16, "f32", 0.9)["states_per_wave"] == 1
     assert msm.msm_scan_bwd_plan(1, 64, 64, 4, "f32", 0.9)["states_per_wave"] == 1
-    # 64 padded states: the full-wavefront backward, 4 states per lane
-    assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 4
+    # 64 padded states: two halves of the 32-state plan, 2 states per lane (4 selects the
+    # full-wavefront backward)
+    assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 2
+    assert msm.msm_scan_bwd_plan(1, 64, 1 << 23, 64, "f32", 0.9)["states_per_wave"] == 4
     # 17-32 states: the half-wavefront backward with 2 states per lane
     assert msm.msm_scan_bwd_plan(1, 64, 64, 17, "f32", 0.9)["states_per_wave"] == 2
     assert msm.msm_scan_bwd_plan(4, 2048, 2048, 32, "f32", 0.9)["states_per_wave"] == 2

@@ -54,9 +54,19 @@ def test_small_ragged(io, K, beta, alpha, dskip):
     check_full(inp, plan={"states_per_wave": K}, tag="small")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N,dskip", [(33, True), (48, False), (64, True)])
+def test_64_states_in_halves(io, N, dskip):
+    # 33-64 states by default: two launches of the 32-state plan, the second adding the first's
+    # dx / ddelta sums
+    inp = workloads.make_inputs(SMALL.replace(io=io, L=53, D=45, N=N, dskip=dskip),
+                                a_kind="random", seed=70 + N)
+    check_full(inp, tag="N=%d halves" % N)
+
+
 @pytest.mark.parametrize("N", [33, 64])
 def test_many_states(N):
-    # N pads to 64 states: the full-wavefront backward (16 wavefronts of 4 states)
+    # with 4 states per lane N pads to 64 states: the full-wavefront backward (16 wavefronts)
     inp = workloads.make_inputs(SMALL.replace(L=37, D=45, N=N, dskip=True), a_kind="random",
                                 seed=54 + N)
     check_full(inp, plan={"states_per_wave": 4}, tag="N=%d" % N)
