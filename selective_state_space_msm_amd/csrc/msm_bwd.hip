@@ -604,6 +604,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         if (n < N && p.dv0) p.dv0[si] = BETA0 ? 0.f : (float)(beta64 * gvp[j]);
       }
     }
+    // the fused variants' finalize above read xe[buf ^ 1], which x_store refills: every
+    // wavefront must be past those reads first
+    if constexpr (EXT != 0) __syncthreads();
     bc_store(buf ^ 1, true);
     x_store(buf ^ 1, true);
     __syncthreads();
