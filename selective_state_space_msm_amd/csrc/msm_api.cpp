@@ -231,7 +231,7 @@ bool complex_shape_ok(int64_t Bt, int64_t L, int64_t D, int64_t N) {
 }
 
 struct CBwdLayout {
-  size_t off_hist, off_dbc, off_dA, off_dD, total;
+  size_t off_hist, off_dbc, off_dA, off_dD, off_acc, total;
 };
 
 CBwdLayout cbwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
@@ -242,7 +242,10 @@ CBwdLayout cbwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   l.off_dbc = align_up(sizeof(float) * 2 * (size_t)(Bt * (L + 1) * N * D));
   l.off_dA = l.off_dbc + align_up(sizeof(float) * 4 * (size_t)(Bt * ncb * L * NP));
   l.off_dD = l.off_dA + align_up(sizeof(float) * 2 * (size_t)(Bt * D * N));
-  l.total = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.off_acc = l.off_dD + align_up(sizeof(float) * (size_t)(Bt * D));
+  l.total = l.off_acc;
+  // more than 16 states: the backward runs in launches of 16 states that sum dx, ddelta here
+  if (NP > 16) l.total += align_up(sizeof(double) * 2 * (size_t)(Bt * L * D));
   return l;
 }
 
@@ -749,6 +752,8 @@ msm_status msm_scan_complex_bwd(const void* x, const void* delta, const float* A
   a.dbc_part = reinterpret_cast<float*>(ws + lay.off_dbc);
   a.dA_part = reinterpret_cast<float*>(ws + lay.off_dA);
   a.dD_part = reinterpret_cast<float*>(ws + lay.off_dD);
+  a.acc = reinterpret_cast<double*>(ws + lay.off_acc);
+  a.n0 = 0;
   a.Bt = Bt;
   a.L = L;
   a.D = D;

@@ -34,7 +34,12 @@
 namespace msm {
 namespace {
 
-template <typename IO, int K, int S, bool HAS_DSKIP>
+// SPLIT: 0 = all states in one launch; otherwise this launch covers the 16 states n0 .. n0 + 15
+// of 32 or 64 padded states (the 16-state plan runs without spills; wider plans do not), one of
+// several launches: 1 = first, 2 = middle, 3 = last.  dx / ddelta are sums over the states, so
+// the launches add their sums in an fp64 buffer ([Bt][L][2][D]) and the last one stores them;
+// every other gradient comes from disjoint states.  The skip term belongs to the first launch.
+template <typename IO, int K, int S, bool HAS_DSKIP, int SPLIT>
 __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   using T = io<IO>;
   using CT = cio<IO>;
@@ -72,6 +77,8 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   const float beta = p.beta;
   const int64_t hrow_bytes = N * D * 8;
   const float* hist0 = p.hist + b * (L + 1) * N * D * 2;
+  const int n0 = SPLIT ? p.n0 : 0;     // first state of this launch
+  const int NPD = SPLIT ? p.NP : NP;   // states per row of the dB / dC partials
 
   // fp64: the rotation a_t, the adjoints and the sums over n (an fp32 a_t in the adjoint carry,
   // multiplied by |A| in the delta gradient, exceeds the fp32 tolerance); fp32: the history and
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   uint32_t h_voff[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int64_t n = (int64_t)gi * K + j;
+    const int64_t n = n0 + (int64_t)gi * K + j;
     const bool on = n < N;
     const bool live = on && dvalid;
     const int64_t ai = (dl * N + (on ? n : 0)) * 2;
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   const char* C0 = static_cast<const char*>(p.C) + b * L * bc_row_bytes;
   char* dx0 = static_cast<char*>(p.dx) + b * L * row_bytes;
   char* ddl0 = static_cast<char*>(p.ddelta) + b * L * row_bytes;
-  const int64_t part_row_bytes = (int64_t)NP * 16;
+  const int64_t part_row_bytes = (int64_t)NPD * 16;
   char* part0 = reinterpret_cast<char*>(p.dbc_part) + (b * p.ncb + cb) * L * part_row_bytes;
   auto rows = [&](const void* base, int64_t r, int64_t rb, int64_t nrows) {
     return make_rsrc(static_cast<const char*>(base) + r * rb, (nrows - r) * rb);
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
 #pragma unroll
   for (int r = 0; r < NBC; ++r) {
     const int i = tid + r * NTHR;
-    const int n = i % NP;
+    const int n = n0 + i % NP;
     bc_voff[r] = (i < BCE && n < N) ? (uint32_t)((i / NP) * bc_row_bytes + n * CT::es) : 0x80000000u;
   }
   uint32_t x_voff[NX];
@@ -241,12 +248,23 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
       const int q = lane & 31;
       const int r = q / (4 * K), j = (q / 4) % K, comp = q & 3;
       const int tt = TT - 1 - (rb * RB + r);
-      const uint32_t off = (uint32_t)((tt * NP + gi * K + j) * 16 + comp * 4);
+      const uint32_t off = (uint32_t)((tt * NPD + n0 + gi * K + j) * 16 + comp * 4);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vals[0]), rp, off, 0u, 0);
     }
   };
+  // split launches: per-thread offsets into the fp64 sums, [L][2][D] per batch row
+  const int64_t acc_row_bytes = 2 * D * 8;
+  char* acc0 = SPLIT ? reinterpret_cast<char*>(p.acc) + b * L * acc_row_bytes : dx0;
+  uint32_t a_voff[NX];
+#pragma unroll
+  for (int r = 0; r < NX; ++r) {
+    const int i = tid + r * NTHR;
+    const int64_t dch = (int64_t)cb * CB + i % CB;
+    a_voff[r] = (i < XE && dch < D) ? (uint32_t)(((i / CB) * 2 * D + dch) * 8) : 0x80000000u;
+  }
   auto finalize = [&](int buf, int64_t ts) {
     const auto rdx = rows(dx0, ts, row_bytes, L), rdd = rows(ddl0, ts, row_bytes, L);
+    const auto racc = SPLIT ? rows(acc0, ts, acc_row_bytes, L) : make_rsrc(acc0, 0);
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       const int i = tid + r * NTHR;
@@ -258,8 +276,29 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
           sx += v.x;
           sd += v.y;
         }
-        T::bstore(rdx, x_voff[r], 0u, (float)sx);
-        T::bstore(rdd, x_voff[r], 0u, (float)sd);
+        if constexpr (SPLIT == 0) {
+          T::bstore(rdx, x_voff[r], 0u, (float)sx);
+          T::bstore(rdd, x_voff[r], 0u, (float)sd);
+        } else {
+          const uint32_t ox = a_voff[r], od = a_voff[r] + (uint32_t)(D * 8);
+          if (SPLIT != 1) {
+            const u32x2 wx = __builtin_amdgcn_raw_buffer_load_b64(racc, ox, 0u, 0);
+            const u32x2 wd = __builtin_amdgcn_raw_buffer_load_b64(racc, od, 0u, 0);
+            sx += __longlong_as_double((long long)(((uint64_t)wx.y << 32) | wx.x));
+            sd += __longlong_as_double((long long)(((uint64_t)wd.y << 32) | wd.x));
+          }
+          if (SPLIT == 3) {
+            T::bstore(rdx, x_voff[r], 0u, (float)sx);
+            T::bstore(rdd, x_voff[r], 0u, (float)sd);
+          } else {
+            const uint64_t ux = (uint64_t)__double_as_longlong(sx);
+            const uint64_t ud = (uint64_t)__double_as_longlong(sd);
+            const u32x2 wx = {(uint32_t)ux, (uint32_t)(ux >> 32)};
+            const u32x2 wd = {(uint32_t)ud, (uint32_t)(ud >> 32)};
+            __builtin_amdgcn_raw_buffer_store_b64(wx, racc, ox, 0u, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(wd, racc, od, 0u, 0);
+          }
+        }
       }
     }
   };
@@ -292,7 +331,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)gi * K + j;
+      const int64_t n = n0 + (int64_t)gi * K + j;
       if (n < N) {
         const int64_t si = ((b * D + d) * N + n) * 2;
         if (p.dh0) {
@@ -367,29 +406,46 @@ __global__ __launch_bounds__(256) void cbwd_finalize_kernel(const CBwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S>
-hipError_t launch_ks(const CBwdArgs& a, hipStream_t s) {
+template <typename IO, int K, int S, int SPLIT>
+hipError_t launch_sweep(const CBwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.ncb * a.Bt)), block(S * kWave);
   if (a.Dskip)
-    hipLaunchKernelGGL((cbwd_kernel<IO, K, S, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((cbwd_kernel<IO, K, S, true, SPLIT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((cbwd_kernel<IO, K, S, false>), grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = a.Bt * a.L * a.N + a.D * a.N + (a.Dskip ? a.D : 0);
-  hipLaunchKernelGGL((cbwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     s, a);
+    hipLaunchKernelGGL((cbwd_kernel<IO, K, S, false, SPLIT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <typename IO>
 hipError_t launch_io(const CBwdArgs& a, hipStream_t s) {
-  switch (a.NP) {
-    case 4: return launch_ks<IO, 2, 1>(a, s);
-    case 16: return launch_ks<IO, 2, 4>(a, s);
-    case 64: return launch_ks<IO, 4, 8>(a, s);
-    default: return hipErrorInvalidValue;
+  hipError_t e;
+  if (a.NP == 4) {
+    e = launch_sweep<IO, 2, 1, 0>(a, s);
+  } else if (a.NP == 16) {
+    e = launch_sweep<IO, 2, 4, 0>(a, s);
+  } else if (a.NP == 32 || a.NP == 64) {
+    // 16 states per launch (the last launch stores dx / ddelta); the skip term in the first
+    const int parts = a.NP / 16;
+    e = hipSuccess;
+    for (int k = 0; k < parts && e == hipSuccess; ++k) {
+      CBwdArgs h = a;
+      h.n0 = 16 * k;
+      if (k > 0) h.Dskip = nullptr;
+      if (k == 0)
+        e = launch_sweep<IO, 2, 4, 1>(h, s);
+      else if (k == parts - 1)
+        e = launch_sweep<IO, 2, 4, 3>(h, s);
+      else
+        e = launch_sweep<IO, 2, 4, 2>(h, s);
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  const int64_t total = a.Bt * a.L * a.N + a.D * a.N + (a.Dskip ? a.D : 0);
+  hipLaunchKernelGGL((cbwd_finalize_kernel<IO>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -154,6 +154,10 @@ struct CBwdArgs {
   float* dbc_part;       // [Bt][ncb][L][NP][4]: per channel block (dB re, im, dC re, im)
   float* dA_part;        // [Bt][D][N][2]
   float* dD_part;        // [Bt][D]
+  // 32 or 64 padded states run as launches of 16 states: the launch's first state and the
+  // running fp64 sums of dx, ddelta ([Bt][L][2][D])
+  int32_t n0;
+  double* acc;
   int64_t Bt, L, D, N;
   int32_t ncb;
   int32_t NP;            // padded states
@@ -164,8 +168,10 @@ struct CBwdArgs {
 // only, for the backward) and complex backward (its sweep and the partial-sum reduction).
 hipError_t launch_cfwd(const CFwdArgs& a, int io_bf16, bool record, hipStream_t s);
 hipError_t launch_cbwd(const CBwdArgs& a, int io_bf16, hipStream_t s);
-// padded complex states of a plan: 4, 16 or 64
-inline int complex_padded_states(int64_t N) { return N <= 4 ? 4 : (N <= 16 ? 16 : 64); }
+// padded complex states of a plan: 4, 16, 32 or 64
+inline int complex_padded_states(int64_t N) {
+  return N <= 4 ? 4 : (N <= 16 ? 16 : (N <= 32 ? 32 : 64));
+}
 
 // One decode step; vec selects 16-byte state access (N % 4 == 0 and 16-byte aligned states
 // and A).  Returns hipSuccess or the launch error.

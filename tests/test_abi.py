@@ -287,6 +287,11 @@ def test_complex_workspace_query(lib):
     want = (align(8 * Bt * (L + 1) * N * D) + align(16 * Bt * ncb * L * NP) + align(8 * Bt * D * N)
             + align(4 * Bt * D))
     assert msm.msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, "f32") == want
+    # more than 16 states: launches of 16 states add up dx, ddelta in fp64 ([Bt][L][2][D])
+    N2, NP2 = 24, 32
+    want2 = (align(8 * Bt * (L + 1) * N2 * D) + align(16 * Bt * ncb * L * NP2)
+             + align(8 * Bt * D * N2) + align(4 * Bt * D) + align(16 * Bt * L * D))
+    assert msm.msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N2, "f32") == want2
     assert msm.msm_scan_complex_bwd_workspace_bytes(0, L, D, N, "f32") == 0
     assert msm.msm_scan_complex_bwd_workspace_bytes(1, L, D, 65, "f32") == 0
     # 17 history rows of N * D complex fp32 values must stay below 2^31 bytes

@@ -1,6 +1,6 @@
 """The complex-valued scan on the GPU (msm_scan_complex_fwd / msm_scan_complex_bwd through the C
 ABI) against the fp64 oracle: small shapes with ragged tiles, channel blocks and state groups
-for every plan (4, 16 and 64 padded states) and both I/O dtypes, then the full-size workload on
+for every plan (4, 16, 32 and 64 padded states) and both I/O dtypes, then the full-size workload on
 sampled channels, its channel sums on one full batch row, and the degenerate cases."""
 import numpy as np
 import pytest
@@ -108,7 +108,7 @@ def test_fwd_tiny(beta, N):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [3, 16, 40])
+@pytest.mark.parametrize("N", [3, 16, 24, 40])
 @pytest.mark.parametrize("a_kind", ["s4d_lin", "random"])
 def test_fwd_small_ragged(io, N, a_kind):
     w = SMALL.replace(io=io, N=N, dskip=True, beta=0.8, alpha=0.7)
@@ -118,7 +118,7 @@ def test_fwd_small_ragged(io, N, a_kind):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [3, 16, 40])
+@pytest.mark.parametrize("N", [3, 16, 29, 40])
 @pytest.mark.parametrize("dskip", [True, False])
 def test_bwd_small_ragged(io, N, dskip):
     w = SMALL.replace(io=io, N=N, dskip=dskip, beta=0.8, alpha=0.7, direction="bwd")
