@@ -62,10 +62,17 @@ typedef enum {
 typedef enum { MSM_F32 = 0, MSM_BF16 = 1 } msm_dtype;
 
 /* Optional launch plan.  0 in a field means "choose automatically".
- *   states_per_wave : 1, 2, 4, 8 or 16 -- how many of the N states one 64-lane wavefront keeps
- *                     in registers (a workgroup holds ceil(N / states_per_wave) wavefronts).
- *   chunks          : number of time chunks the sequence is cut into (1..64); chunks > 1 adds
- *                     a pass that summarises each chunk as an affine map of its start state.
+ *   states_per_wave : 1, 2, 4, 8 or 16 -- how many of the N states one lane keeps in registers.
+ *                     N pads to 4, 16, 32 or 64 states.  Forward: a 64-lane wavefront serves
+ *                     64 channels and a workgroup holds padded-N / states_per_wave wavefronts
+ *                     (allowed: 1, 2, 4 at 4 states; 1-16 at 16; 4, 8 at 32; 4, 8, 16 at 64).
+ *                     Backward: each 32-lane half of a wavefront holds states_per_wave states of
+ *                     32 channels (allowed: 1, 2 at 4 states; 1, 2, 4 at 16; 2 at 32); at 64
+ *                     states 2 runs two launches of 32 states and 4 the 64-channel kernel.
+ *                     Other values return MSM_ERR_UNSUPPORTED.
+ *   chunks          : number of time chunks the sequence is cut into (1..64, forward only);
+ *                     chunks > 1 adds a pass that summarises each chunk as an affine map of its
+ *                     start state.
  * A plan never changes results beyond fp32 rounding order. */
 typedef struct {
   int32_t states_per_wave;
@@ -85,7 +92,7 @@ size_t msm_scan_bwd_workspace_bytes(int64_t Bt, int64_t L, int64_t D, int64_t N,
 
 /* The plan msm_scan_fwd / msm_scan_bwd would use for this shape (written to *plan).  The fused
  * backward (msm_selective_scan_bwd with any extra) takes two states per wavefront half at 5-16
- * states instead. */
+ * states instead.  At 64 states with D >= 2^23 the backward takes the 64-channel kernel (4). */
 msm_status msm_scan_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
                              float beta, msm_plan* plan);
 msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dtype io,
