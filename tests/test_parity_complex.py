@@ -227,3 +227,54 @@ def test_full_size_bwd(full):
     want0 = oracle_bwd(row)
     for k in ("dB", "dC"):
         assert_close(host(got[k])[:1], ri(want0[k]), "f32", k + " (batch row 0)")
+
+
+# ---- continuation: a sequence in two calls equals one call ----
+
+def _split(inp, t):
+    a = dict(inp, x=inp["x"][:, :t], delta=inp["delta"][:, :t], B=inp["B"][:, :t],
+             C=inp["C"][:, :t])
+    b = dict(inp, x=inp["x"][:, t:], delta=inp["delta"][:, t:], B=inp["B"][:, t:],
+             C=inp["C"][:, t:])
+    if inp.get("dy") is not None:
+        a["dy"], b["dy"] = inp["dy"][:, :t], inp["dy"][:, t:]
+    return a, b
+
+
+@pytest.mark.parametrize("N", [16, 40])
+def test_forward_continuation(N):
+    """Scanning the first 1000 steps and continuing from the returned (last_h, last_v) over the
+    rest gives the outputs and final states of one call over all 2048 steps."""
+    w = CW.replace(Bt=2, L=2048, D=96, N=N, dskip=True)
+    inp = workloads.make_complex_inputs(w, seed=391)
+    y, lh, lv = run_fwd(inp)
+    a, b = _split(inp, 1000)
+    ya, lha, lva = run_fwd(a)
+    yb, lhb, lvb = run_fwd(b, host(lha).astype(np.float32), host(lva).astype(np.float32))
+    assert_close(np.concatenate([host(ya), host(yb)], axis=1), host(y), "f32", "y (continued)")
+    assert_close(host(lhb), host(lh), "f32", "last_h (continued)")
+    assert_close(host(lvb), host(lv), "f32", "last_v (continued)")
+
+
+@pytest.mark.parametrize("N", [16, 40])
+def test_backward_continuation(N):
+    """The backward of a sequence in two parts: the second part first, from the first part's
+    final state, then the first with the second's (dh0, dv0) as its terminal adjoints.  dx,
+    ddelta, dB, dC agree with one backward over the whole sequence; dA is the sum of the parts.
+    The state at the split comes from the fp64 oracle rounded to fp32, as accurate as the state
+    history of the one-call backward: ddelta carries a factor |A| on the states, and the fp32
+    readout forward's state (about 1e-6 relative) moves ddelta past the fp32 bound next to the
+    split."""
+    w = CW.replace(Bt=2, L=2048, D=96, N=N, dskip=False, direction="bwd")
+    inp = workloads.make_complex_inputs(w, seed=397)
+    full = run_bwd(inp)
+    a, b = _split(inp, 1000)
+    _, lha, lva = oracle_fwd(a)
+    h1, v1 = ri(lha).astype(np.float32), ri(lva).astype(np.float32)
+    gb = run_bwd(b, h1, v1)
+    ga = run_bwd(a, dlh=host(gb["dh0"]).astype(np.float32), dlv=host(gb["dv0"]).astype(np.float32))
+    # two GPU results, each held to the fp32 bound elsewhere: compared with the pair bound
+    for k in ("dx", "ddelta", "dB", "dC"):
+        got = np.concatenate([host(ga[k]), host(gb[k])], axis=1)
+        assert_close(got, host(full[k]), "f32_pair", k + " (continued)")
+    assert_close(host(ga["dA"]) + host(gb["dA"]), host(full["dA"]), "f32_pair", "dA (continued)")
