@@ -177,8 +177,8 @@ msm_status msm_scan_bwd_state(const void* x, const void* delta, const float* A, 
  * README's "Discretization Note"; 1 uses the zero-order hold Bbar = (exp(delta_eff A) - 1) A^{-1} B
  * of the glossary and complextorch pages ("The diagonal SSM"), i.e.
  *     v_t = beta v_{t-1} + alpha ((exp(delta_eff A) - 1) / A) B_t x_t   (delta_eff at A = 0).
- * With z, delta_bias NULL and delta_softplus = zero_order_hold = 0 this is msm_scan_fwd_state.  The bias, softplus and gate are applied inside
- * the scan kernels (no extra pass over memory).  Everything else as msm_scan_fwd_state; z and
+ * With z, delta_bias NULL and delta_softplus = zero_order_hold = 0 this is msm_scan_fwd_state.
+ * The bias, softplus and gate are applied inside the scan kernels (no extra pass over memory).  Everything else as msm_scan_fwd_state; z and
  * delta_bias are inputs and must not overlap an output. */
 msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
                                   const void* B, const void* C, const float* Dskip, const void* z,

@@ -148,10 +148,12 @@ bool bwd_allowed_k(int NP, int K) {
 }
 
 // For 4, 16 or 32 padded states a backward workgroup holds 2K states of kBwdChans channels per
-// wavefront and NP / (2K) wavefronts (32 states: always K = 2, 8 wavefronts).  A wavefront alone on its SIMD stalls on every non-VALU
-// instruction and on LDS and fp64 latencies, so the plan asks for two wavefronts per SIMD: the
-// largest K (at most 2: K = 4 needs more registers than two wavefronts leave) that still gives
-// 2 * 1024 wavefronts, else K = 1.  64 padded states always take K = 4 (full-wavefront kernel).
+// wavefront and NP / (2K) wavefronts (32 states: always K = 2, 8 wavefronts).  A wavefront
+// alone on its SIMD stalls on every non-VALU instruction and on LDS and fp64 latencies, so the
+// plan asks for two wavefronts per SIMD: the largest K (at most 2: K = 4 needs more registers
+// than two wavefronts leave) that still gives 2 * 1024 wavefronts, else K = 1.  64 padded states
+// take K = 2, two launches of the 32-state plan, or K = 4, the full-wavefront kernel, when the
+// first half's sums would exceed 32-bit offsets (D >= 2^23).
 msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = false) {
   const int NP = padded_states(N);
   msm_plan pl{0, 1};

@@ -15,8 +15,9 @@
 // fp32 value per (b, t, n, d)): on a 288 GB device trading that buffer for the recompute of the
 // real backward keeps this kernel a single reverse sweep.  The sweep computes a_t, the adjoints
 // and the sums over n in fp64: the delta gradient carries a factor |A| (tens for a rotating
-// state), and an fp32 a_t in the adjoint carry already exceeds the fp32 tolerance there.  Layout as the complex forward: 32
-// channels per workgroup, state group 2 g + l / 32 of K states per lane.  Tiles of TT steps
+// state), and an fp32 a_t in the adjoint carry already exceeds the fp32 tolerance there.
+// Layout as the complex forward: 32 channels per workgroup, state group 2 g + l / 32 of K
+// states per lane.  Tiles of TT steps
 // are swept in reverse; the inputs of the next (earlier) tile -- x, delta, dy, B, C through
 // LDS, its TT history rows straight into registers -- are loaded while the current one is
 // computed.  Reductions in a fixed order:
