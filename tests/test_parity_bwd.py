@@ -81,11 +81,12 @@ def test_32_states(io, N, dskip):
     check_full(inp, tag="N=%d" % N)
 
 
-@pytest.mark.skip(reason="the half-wavefront backward at 64 padded states (N=33, K=2: 16 "
-                         "wavefronts per workgroup) stopped with an illegal memory access on "
-                         "MI355X; no out-of-bounds index was found on the CPU, so its "
-                         "instantiations are compiled out and 64 states run the full-wavefront "
-                         "kernel")
+@pytest.mark.skip(reason="the single-launch half-wavefront backward at 64 padded states (N=33, "
+                         "K=2: 16 wavefronts per workgroup) stopped with an illegal memory access "
+                         "on MI355X; no out-of-bounds index was found on the CPU, so those "
+                         "instantiations are compiled out; 64 states now run as two launches of "
+                         "the 32-state plan (test_64_states_in_halves) or the full-wavefront "
+                         "kernel (test_many_states)")
 @pytest.mark.parametrize("K", [2, 4])
 @pytest.mark.parametrize("N", [33, 64])
 def test_half_wave_64_states(N, K):
