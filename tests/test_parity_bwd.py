@@ -64,6 +64,14 @@ def test_64_states_in_halves(io, N, dskip):
     check_full(inp, tag="N=%d halves" % N)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_64_states_in_halves_beta0(io):
+    # the beta = 0 build of both halves (velocity equals the write), with terminal adjoints
+    inp = workloads.make_inputs(SMALL.replace(io=io, L=61, D=37, N=64, beta=0.0, dskip=True),
+                                a_kind="random", seed=88)
+    check_full(inp, tag="N=64 halves beta=0")
+
+
 @pytest.mark.parametrize("N", [33, 64])
 def test_many_states(N):
     # with 4 states per lane N pads to 64 states: the full-wavefront backward (16 wavefronts)

@@ -128,6 +128,16 @@ def test_bwd_small_ragged(io, N, dskip):
     check_bwd(inp, h0, v0, dlh, dlv, tag="small")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_64_states_beta0(io):
+    # 64 padded states: four launches of 16 states adding their dx / ddelta sums, beta = 0
+    w = SMALL.replace(io=io, N=64, dskip=True, beta=0.0, alpha=1.3, direction="bwd")
+    inp = workloads.make_complex_inputs(w, a_kind="random", seed=327)
+    h0, v0 = workloads.make_complex_state(w, 328)
+    dlh, dlv = workloads.make_complex_state(w, 329)
+    check_bwd(inp, h0, v0, dlh, dlv, tag="N=64 beta=0")
+
+
 @pytest.mark.parametrize("beta", [0.9, 0.0])
 def test_bwd_tiny_no_state(beta):
     w = W["tiny"].replace(beta=beta, N=4, direction="bwd")

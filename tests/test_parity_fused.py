@@ -259,7 +259,7 @@ def test_zoh_small(io, K):
           state=True, tag="zoh small K=%d" % K)
 
 
-@pytest.mark.parametrize("N", [5, 27, 33])
+@pytest.mark.parametrize("N", [5, 27, 33, 64])
 def test_zoh_state_counts(N):
     w = SMALL.replace(L=40, D=70, N=N, dskip=True)
     check(fused_inputs(w, 500 + N, softplus=False, use_z=False, use_bias=False, zoh=True),
