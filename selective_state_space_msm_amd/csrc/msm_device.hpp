@@ -62,6 +62,18 @@ __device__ __forceinline__ float zoh_phi(float u, float a) {
   const float q = (a - 1.f) * rcp_fast(u);
   return fabsf(u) < 0.25f ? p : q;
 }
+// phi alone, for the kernels that never need psi (forward and decode step): the series switches
+// at |u| = 1/8 and stops at u^4 (truncation below 5e-8 relative).  Above the switch a - 1 >= 0.117
+// in magnitude, so its rounding stays below about 1e-6 relative.  psi's (a - phi) / u would lose
+// more than that to cancellation at the lower switch, so the backward keeps zoh_phi.
+__device__ __forceinline__ float zoh_phi_fwd(float u, float a) {
+  float p = fmaf(u, 1.f / 120.f, 1.f / 24.f);
+  p = fmaf(p, u, 1.f / 6.f);
+  p = fmaf(p, u, 0.5f);
+  p = fmaf(p, u, 1.f);
+  const float q = (a - 1.f) * rcp_fast(u);
+  return fabsf(u) < 0.125f ? p : q;
+}
 __device__ __forceinline__ float zoh_psi(float u, float a, float phi) {
   float p = fmaf(u, 1.f / 5760.f, 1.f / 840.f);
   p = fmaf(p, u, 1.f / 144.f);

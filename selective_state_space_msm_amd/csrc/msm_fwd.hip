@@ -267,7 +267,7 @@ void fwd_kernel(const FwdArgs p) {
       const float arg = dv * A2[j];
       const float a = exp2_fast(arg);
       float w = c * bc[j];
-      if (ZOH) w *= zoh_phi(arg * kLn2, a);  // g = delta phi(delta A) instead of delta
+      if (ZOH) w *= zoh_phi_fwd(arg * kLn2, a);  // g = delta phi(delta A) instead of delta
       if (BETA0)
         v[j] = w;
       else

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs p) {
     const float arg = de * (As[j] * kLog2e);
     const float a = exp2_fast(arg);
     float w = c * Bs[j];
-    if (p.zoh) w *= zoh_phi(arg * kLn2, a);  // zero-order hold: g = delta phi(delta A)
+    if (p.zoh) w *= zoh_phi_fwd(arg * kLn2, a);  // zero-order hold: g = delta phi(delta A)
     vs[j] = fmaf(p.beta, vs[j], w);
     hs[j] = fmaf(a, hs[j], vs[j]);
     ys = fmaf(Cs[j], hs[j], ys);  // padding states have C = 0
