@@ -266,6 +266,30 @@ def test_zoh_state_counts(N):
           tag="zoh N=%d" % N)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_zoh_series_switches(io):
+    # decay arguments u = delta A on both sides of the switches between the series and the
+    # quotient forms of phi (|u| = 1/8 in the forward, 1/4 in the backward) and psi (1/4), at
+    # A = 0 exactly (g = delta), and far enough out that e^u underflows (A = -1000).  delta stays
+    # in the softplus range of the workloads: delta near 1 with A near 0 makes dA a sum of terms
+    # of order 1e4, where fp32 states miss the bound by a few units of 1e-5 relative with or
+    # without the hold.
+    w = SMALL.replace(io=io, L=37, D=70, N=16, dskip=True)
+    inp = fused_inputs(w, 541, softplus=False, use_z=False, use_bias=False, zoh=True)
+    cols = np.array([0.0, -1.0, -1.25, -1.5, -2.0, -2.5, -3.0, -4.0, -1000.0, -0.1, -1.1, -1.4,
+                     -2.2, -2.8, -1e-4, -8.0], dtype=np.float32)
+    inp["A"] = np.ascontiguousarray(np.tile(cols, (w.D, 1)))
+    rng = np.random.default_rng(542)
+    inp["delta"] = rng.uniform(0.05, 0.15, size=inp["delta"].shape).astype(np.float32)
+    if io == "bf16":
+        inp["delta"] = workloads.round_to_bf16(inp["delta"])
+    u = np.abs(inp["delta"][..., None] * cols)
+    for edge in (0.125, 0.25):  # both sides of each switch occur
+        assert ((u < edge) & (u > edge / 2)).any() and ((u > edge) & (u < 2 * edge)).any()
+    assert (u > 104).any()  # e^u below the fp32 range
+    check(inp, tag="zoh switches")
+
+
 def test_zoh_full_size():
     """The headline forward shape and the backward shape with the zero-order hold and every
     extra, on sampled outputs."""
