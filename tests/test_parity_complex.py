@@ -154,6 +154,28 @@ def test_single_step_and_channel():
     check_bwd(inp, h0, v0, *workloads.make_complex_state(w, 343), tag="L=D=N=1")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_many_turns_per_step(io):
+    """Rotations of up to about 50 turns per step (|Im A| up to 1000, delta up to 0.3): the
+    quarter-turn reduction of the fp32 readout and of the fp64 training path far from the
+    first turn, both signs of Im A."""
+    w = SMALL.replace(io=io, L=61, N=16, dskip=True, direction="bwd")
+    inp = workloads.make_complex_inputs(w, a_kind="random", seed=361)
+    rng = np.random.default_rng(362)
+    inp["A"] = inp["A"].copy()
+    inp["A"][..., 0] = -0.5
+    inp["A"][..., 1] = rng.uniform(-1000.0, 1000.0, size=inp["A"].shape[:2]).astype(np.float32)
+    inp["delta"] = rng.uniform(0.05, 0.3, size=inp["delta"].shape).astype(np.float32)
+    if io == "bf16":
+        inp["delta"] = workloads.round_to_bf16(inp["delta"])
+    turns = np.abs(inp["delta"][..., None] * inp["A"][None, None, :, :, 1]) / (2 * np.pi)
+    assert turns.max() > 40
+    h0, v0 = workloads.make_complex_state(w, 363)
+    dlh, dlv = workloads.make_complex_state(w, 364)
+    check_fwd(inp, h0, v0, tag="many turns")
+    check_bwd(inp, h0, v0, dlh, dlv, tag="many turns")
+
+
 def test_real_inputs_match_real_scan():
     """Zero imaginary parts: the complex kernels give the real scan's outputs (the real
     kernels' results through the real entry point, to the parity tolerance of each)."""
