@@ -184,6 +184,9 @@ def bench_bwd(w, steps, warmup, stream, fused=False, zoh=False):
            "dA": torch.empty_like(g["A"]), "dB": torch.empty_like(g["B"]),
            "dC": torch.empty_like(g["C"])}
     plan = msm.msm_scan_bwd_plan(w.Bt, w.L, w.D, w.N, w.io, w.beta)
+    if fused and 5 <= w.N <= 16:
+        # the fused backward's documented choice: two states per wavefront half at 5-16 states
+        plan = dict(plan, states_per_wave=2)
 
     if fused:
         out["dz"] = torch.empty_like(g["x"])
