@@ -63,6 +63,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   __shared__ float4 bcs[2][TT][NP];       // alpha B (re, im), C (re, im)
   __shared__ float4 xs[2][TT][CB];        // delta, x, dy, alpha delta x
   __shared__ double2 gpart[2][S][TT][CB];  // (dx, ddelta) partial sums per wavefront
+  __shared__ CTab ctab;                    // fp64 exponential and rotation tables
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -212,8 +213,8 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
           const double ghr = __builtin_fma(dyv, (double)q.z, chr[j]);
           const double ghi = __builtin_fma(-dyv, (double)q.w, chi[j]);
           const double gvr = ghr + cvr[j], gvi = ghi + cvi[j];
-          const double mag = exp_d(dlt * (double)Are[j]);
-          const CisD ee = cis_rev_d(dlt * AiD[j]);
+          const double mag = exp_tab(dlt * (double)Are[j], ctab);
+          const CisD ee = cis_rev_tab(dlt * AiD[j], ctab);
           const double ar = mag * ee.c, ai = mag * ee.s;
           const double Pr = __builtin_fma(ar, hpr, -ai * hpi);  // a h_{t-1}
           const double Pi = __builtin_fma(ar, hpi, ai * hpr);
@@ -320,6 +321,7 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
     __syncthreads();
     finalize(buf, ts);
   };
+  ctab_build(ctab, threadIdx.x, NTHR);
   Set sa, sb;
   load_set(sa, klast * TT);
   store_set(sa, (int)(klast & 1));

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
   __shared__ float2 xdl[2][TT][CB];  // delta, delta * x
   __shared__ float xxl[DSK ? 2 : 1][DSK ? TT : 1][CB];
   __shared__ float ypart[Y ? 2 : 1][Y ? S : 1][TT][CB];
+  __shared__ CTab ctab;  // fp64 exponential and rotation tables (recording pass)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -189,8 +190,8 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const float4 q = bcs[buf][tt][gi * K + j];
-        const double mag = exp_d(dlt * ArD[j]);
-        const CisD e = cis_rev_d(dlt * AiD[j]);
+        const double mag = exp_tab(dlt * ArD[j], ctab);
+        const CisD e = cis_rev_tab(dlt * AiD[j], ctab);
         const double ar = mag * e.c, ai = mag * e.s;
         vdr[j] = __builtin_fma((double)beta, vdr[j], cw * q.x);
         vdi[j] = __builtin_fma((double)beta, vdi[j], cw * q.y);
@@ -262,6 +263,7 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
   const int64_t nfull = L / TT;
   const int nrem = (int)(L - nfull * TT);
   const int64_t ntile = nfull + (nrem > 0 ? 1 : 0);
+  if constexpr (REC) ctab_build(ctab, threadIdx.x, NTHR);
   {
     Set s0;
     load_set(s0, 0);

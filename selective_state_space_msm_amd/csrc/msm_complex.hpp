@@ -110,13 +110,15 @@ __device__ __forceinline__ CisD cis_rev_d(double r) {
   return CisD{((q + 1) & 2) ? -cr : cr, (q & 2) ? -sr : sr};
 }
 
+constexpr double kLn2D = 0.6931471805599453;
+
 // e^x in fp64 for the decay factor (x = delta Re A <= 0 in use): x = k ln 2 + g with
 // k = rint(x log2 e), |g| <= ln(2) / 2 + tiny, e^g from its Taylor series to g^13 (truncated
 // below 5e-18), scaled by 2^k.  The reduction's rounding (k times the error of ln 2 in fp64) is
 // below 1e-13 relative for |x| < 1000; results under the fp64 range flush to zero through
 // ldexp.
 __device__ __forceinline__ double exp_d(double x) {
-  constexpr double kLog2eD = 1.4426950408889634, kLn2D = 0.6931471805599453;
+  constexpr double kLog2eD = 1.4426950408889634;
   const double k = __builtin_rint(x * kLog2eD);
   const double g = __builtin_fma(-k, kLn2D, x);
   double p = __builtin_fma(g, inv_fact(13), inv_fact(12));
@@ -134,6 +136,61 @@ __device__ __forceinline__ double exp_d(double x) {
   p = __builtin_fma(p, g, 1.0);
   const double kc = k < -2000.0 ? -2000.0 : k;  // keeps the int conversion in range
   return ldexp(p, (int)kc);
+}
+
+// Tables for the fp64 exponential and rotation of the training path, built once per workgroup
+// in LDS from exp_d and cis_rev_d: e^(2 pi i m / 64) for m < 64 and 2^(j / 32) for j < 32.  They
+// make the reduced arguments 16 (rotation) and 32 (exponential) times smaller than in the
+// functions above, so shorter series reach fp64 accuracy and the quarter-turn selects go away.
+struct CTab {
+  double2 cis[64];
+  double p2[32];
+};
+__device__ inline void ctab_build(CTab& t, int tid, int nthr) {
+  for (int m = tid; m < 64; m += nthr) {
+    const CisD e = cis_rev_d(m / 64.0);
+    t.cis[m] = make_double2(e.c, e.s);
+  }
+  for (int j = tid; j < 32; j += nthr) t.p2[j] = exp_d(j * (kLn2D / 32.0));
+}
+
+// e^(2 pi i r) with the table: r = k/64 + u, k = rint(64 r), u exact (Sterbenz) with
+// |2 pi u| <= pi/64; sin to the 9th and cos to the 8th power of 2 pi u (truncated below 1e-20),
+// then one complex product with the table entry of k mod 64.
+__device__ __forceinline__ CisD cis_rev_tab(double r, const CTab& t) {
+  const double k = __builtin_rint(64.0 * r);
+  const double u = __builtin_fma(k, -1.0 / 64.0, r);
+  const double z = u * u;
+  double ps = __builtin_fma(z, taylor_2pi(9), -taylor_2pi(7));
+  ps = __builtin_fma(z, ps, taylor_2pi(5));
+  ps = __builtin_fma(z, ps, -taylor_2pi(3));
+  ps = __builtin_fma(z, ps, taylor_2pi(1));
+  const double su = u * ps;
+  double pc = __builtin_fma(z, taylor_2pi(8), -taylor_2pi(6));
+  pc = __builtin_fma(z, pc, taylor_2pi(4));
+  pc = __builtin_fma(z, pc, -taylor_2pi(2));
+  const double cu = __builtin_fma(z, pc, 1.0);
+  const double2 e = t.cis[(int)k & 63];
+  return CisD{__builtin_fma(e.x, cu, -e.y * su), __builtin_fma(e.y, cu, e.x * su)};
+}
+
+// e^x with the table: x = (32 m + j) ln2/32 + g, k = 32 m + j = rint(32 x / ln 2),
+// |g| <= ln2/64 + tiny; e^g from its series to g^6 (truncated below 4e-18), times 2^(j/32) from
+// the table, scaled by 2^m.  The reduction's rounding is k times the error of ln2/32 in fp64,
+// the same bound as exp_d's; results under the fp64 range flush to zero through ldexp.
+__device__ __forceinline__ double exp_tab(double x, const CTab& t) {
+  constexpr double kScale = 32.0 * 1.4426950408889634;  // 32 / ln 2
+  double k = __builtin_rint(x * kScale);
+  k = k < -1073741824.0 ? -1073741824.0 : k;  // keeps the int conversion in range
+  const double g = __builtin_fma(-k, kLn2D / 32.0, x);
+  double p = __builtin_fma(g, inv_fact(6), inv_fact(5));
+  p = __builtin_fma(p, g, inv_fact(4));
+  p = __builtin_fma(p, g, inv_fact(3));
+  p = __builtin_fma(p, g, 0.5);
+  p = __builtin_fma(p, g, 1.0);
+  p = __builtin_fma(p, g, 1.0);
+  const int ki = (int)k;
+  return ldexp(p * t.p2[ki & 31], ki >> 5);
 }
 
 // Adds an fp64 value across the two 32-lane halves (both halves get the same sum).
