@@ -52,6 +52,7 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
   __shared__ float xxl[DSK ? 2 : 1][DSK ? TT : 1][CB];
   __shared__ float ypart[Y ? 2 : 1][Y ? S : 1][TT][CB];
   __shared__ CTab ctab;  // fp64 exponential and rotation tables (recording pass)
+  __shared__ float2 ctabf[64];  // fp32 rotation table (readout pass)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
       const float4 q = bcs[buf][tt][gi * K + j];
       const float mag = exp2_fast(dd.x * Ar[j]);
       float co, si;
-      cis_delta(dd.x, Ai[j], co, si);
+      cis_delta_tab(dd.x, Ai[j], ctabf, co, si);
       const float ar = mag * co, ai = mag * si;
       vr[j] = fmaf(beta, vr[j], dd.y * q.x);
       vi[j] = fmaf(beta, vi[j], dd.y * q.y);
@@ -263,7 +264,10 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
   const int64_t nfull = L / TT;
   const int nrem = (int)(L - nfull * TT);
   const int64_t ntile = nfull + (nrem > 0 ? 1 : 0);
-  if constexpr (REC) ctab_build(ctab, threadIdx.x, NTHR);
+  if constexpr (REC)
+    ctab_build(ctab, threadIdx.x, NTHR);
+  else
+    ctab_build_f32(ctabf, threadIdx.x, NTHR);
   {
     Set s0;
     load_set(s0, 0);

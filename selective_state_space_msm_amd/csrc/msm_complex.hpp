@@ -66,6 +66,29 @@ __device__ __forceinline__ void cis_delta(float delta, RevPair a, float& c, floa
   s = __uint_as_float(__float_as_uint(sr) ^ ((uint32_t)(q & 2) << 30));
 }
 
+// e^(i delta Im A) = (c, s) with a table of e^(2 pi i m / 64), m < 64, in fp32 (each entry
+// rounded from the fp64 rotation): the phase p + lo is formed as in cis_delta, then
+// k = rint(64 p) is split off exactly (Sterbenz) and |2 pi u| <= pi/64 + tiny, where sin to the
+// 3rd and cos to the 4th power of 2 pi u are truncated below 3e-9.  One complex product with
+// the entry of k mod 64 finishes it.
+__device__ __forceinline__ void cis_delta_tab(float delta, RevPair a, const float2* tab, float& c,
+                                              float& s) {
+  constexpr float S1 = (float)kTwoPiD;
+  constexpr float S3 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD / 6.0);
+  constexpr float C2 = (float)(-kTwoPiD * kTwoPiD / 2.0);
+  constexpr float C4 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 24.0);
+  const float p = delta * a.hi;
+  const float lo = fmaf(delta, a.lo, fmaf(delta, a.hi, -p));
+  const float k = __builtin_rintf(64.f * p);
+  const float u = fmaf(k, -1.f / 64.f, p) + lo;
+  const float z = u * u;
+  const float su = u * fmaf(z, S3, S1);
+  const float cu = fmaf(z, fmaf(z, C4, C2), 1.f);
+  const float2 e = tab[(int)k & 63];
+  c = fmaf(e.x, cu, -e.y * su);
+  s = fmaf(e.y, cu, e.x * su);
+}
+
 // (2 pi)^m / m! and 1 / m!, the Taylor coefficients of the fp64 rotation and exponential.
 constexpr double taylor_2pi(int m) {
   double r = 1.0;
@@ -146,6 +169,13 @@ struct CTab {
   double2 cis[64];
   double p2[32];
 };
+// the fp32 rotation table of cis_delta_tab
+__device__ inline void ctab_build_f32(float2* t, int tid, int nthr) {
+  for (int m = tid; m < 64; m += nthr) {
+    const CisD e = cis_rev_d(m / 64.0);
+    t[m] = make_float2((float)e.c, (float)e.s);
+  }
+}
 __device__ inline void ctab_build(CTab& t, int tid, int nthr) {
   for (int m = tid; m < 64; m += nthr) {
     const CisD e = cis_rev_d(m / 64.0);
