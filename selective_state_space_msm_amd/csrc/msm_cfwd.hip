@@ -17,8 +17,9 @@
 //   * the readout sum over n: in-lane over K, across the two halves with v_permlane32_swap,
 //     then across the S wavefronts through LDS in a fixed order (double-buffered partials,
 //     one barrier per tile);
-//   * the rotation e^(i delta Im A) comes from a Taylor series after an exact quarter-turn
-//     reduction of the phase in revolutions (cis_delta), its modulus from v_exp_f32.
+//   * the rotation e^(i delta Im A) comes from a 64-entry LDS table and short Taylor series
+//     after an exact reduction of the phase in revolutions (cis_delta_tab), its modulus from
+//     v_exp_f32.
 // The recording pass (REC) writes h_t for every step to a history buffer laid out
 // [b][t + 1][n][d] (row 0 = the initial state), which the backward reads instead of
 // recomputing the forward; it produces no y.  It runs the recurrence in fp64 (a_t from an fp64

@@ -20,57 +20,15 @@ __device__ __forceinline__ RevPair to_revolutions(float im_a) {
   return RevPair{hi, (float)(r - (double)hi)};
 }
 
-// e^(i delta Im A) = (c, s), to about one unit in the last place.  The phase in revolutions is
-// formed as p + lo with p = fl(delta hi) and lo carrying the rounding error of that product
-// (exact, from an FMA) plus delta lo.  The quarter-turn count k = rint(4 p) is split off
-// exactly (u = p - k/4 needs no rounding, |u| <= 1/8 turn), cos and sin of 2 pi u come from
-// their Taylor series (truncated below 2e-9 for |2 pi u| <= pi/4), and k mod 4 rotates the
-// pair by quarter turns (bit 1 of k and of k + 1 give the signs, two's complement keeps that
-// right for negative k).  The hardware v_sin_f32 / v_cos_f32 are not used: their error (about
-// 1e-6 absolute, judging by the parity errors they caused) is carried into the delta gradient
-// with a factor |A|, beyond the fp32 tolerance.
-__device__ __forceinline__ void cis_delta(float delta, RevPair a, float& c, float& s) {
-  constexpr float S1 = (float)kTwoPiD;
-  constexpr float S3 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD / 6.0);
-  constexpr float S5 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 120.0);
-  constexpr float S7 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD /
-                               5040.0);
-  constexpr float S9 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
-                               kTwoPiD * kTwoPiD / 362880.0);
-  constexpr float C2 = (float)(-kTwoPiD * kTwoPiD / 2.0);
-  constexpr float C4 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 24.0);
-  constexpr float C6 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD / 720.0);
-  constexpr float C8 = (float)(kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
-                               kTwoPiD / 40320.0);
-  constexpr float C10 = (float)(-kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD * kTwoPiD *
-                                kTwoPiD * kTwoPiD * kTwoPiD / 3628800.0);
-  const float p = delta * a.hi;
-  const float lo = fmaf(delta, a.lo, fmaf(delta, a.hi, -p));
-  const float k = __builtin_rintf(4.f * p);
-  const float u = fmaf(k, -0.25f, p) + lo;
-  const float z = u * u;
-  float ps = fmaf(z, S9, S7);
-  ps = fmaf(z, ps, S5);
-  ps = fmaf(z, ps, S3);
-  ps = fmaf(z, ps, S1);
-  const float sn = u * ps;
-  float pc = fmaf(z, C10, C8);
-  pc = fmaf(z, pc, C6);
-  pc = fmaf(z, pc, C4);
-  pc = fmaf(z, pc, C2);
-  const float cs = fmaf(z, pc, 1.f);
-  const int q = (int)k;
-  const bool odd = (q & 1) != 0;
-  const float cr = odd ? sn : cs, sr = odd ? cs : sn;
-  c = __uint_as_float(__float_as_uint(cr) ^ ((uint32_t)((q + 1) & 2) << 30));
-  s = __uint_as_float(__float_as_uint(sr) ^ ((uint32_t)(q & 2) << 30));
-}
-
 // e^(i delta Im A) = (c, s) with a table of e^(2 pi i m / 64), m < 64, in fp32 (each entry
-// rounded from the fp64 rotation): the phase p + lo is formed as in cis_delta, then
-// k = rint(64 p) is split off exactly (Sterbenz) and |2 pi u| <= pi/64 + tiny, where sin to the
-// 3rd and cos to the 4th power of 2 pi u are truncated below 3e-9.  One complex product with
-// the entry of k mod 64 finishes it.
+// rounded from the fp64 rotation).  The phase in revolutions is formed as p + lo with
+// p = fl(delta hi) and lo carrying the rounding error of that product (exact, from an FMA) plus
+// delta lo.  k = rint(64 p) is split off exactly (Sterbenz), leaving |2 pi u| <= pi/64 + tiny,
+// where sin to the 3rd and cos to the 4th power of 2 pi u are truncated below 3e-9.  One complex
+// product with the entry of k mod 64 finishes it: about 1e-7 absolute error in a CPU emulation
+// over phases up to 16 turns.  The hardware v_sin_f32 / v_cos_f32 are not used: their error
+// (about 1e-6 absolute, judging by the parity errors they caused) is carried into the delta
+// gradient with a factor |A|, beyond the fp32 tolerance.
 __device__ __forceinline__ void cis_delta_tab(float delta, RevPair a, const float2* tab, float& c,
                                               float& s) {
   constexpr float S1 = (float)kTwoPiD;
@@ -101,9 +59,10 @@ constexpr double inv_fact(int m) {
   return r;
 }
 
-// e^(2 pi i r) in fp64 for r in revolutions: the same exact quarter-turn split as cis_delta,
-// then the Taylor series of sin to the 15th and of cos to the 16th power of 2 pi u (truncated
-// below 5e-17 for |2 pi u| <= pi/4).
+// e^(2 pi i r) in fp64 for r in revolutions (it builds the rotation tables below): k = rint(4 r)
+// quarter turns are split off exactly, then the Taylor series of sin to the 15th and of cos to
+// the 16th power of 2 pi u (truncated below 5e-17 for |2 pi u| <= pi/4), and k mod 4 rotates
+// the pair by quarter turns (bit 1 of k and of k + 1 give the signs).
 struct CisD {
   double c, s;
 };
@@ -135,7 +94,7 @@ __device__ __forceinline__ CisD cis_rev_d(double r) {
 
 constexpr double kLn2D = 0.6931471805599453;
 
-// e^x in fp64 for the decay factor (x = delta Re A <= 0 in use): x = k ln 2 + g with
+// e^x in fp64 (it builds the table of 2^(j/32) below): x = k ln 2 + g with
 // k = rint(x log2 e), |g| <= ln(2) / 2 + tiny, e^g from its Taylor series to g^13 (truncated
 // below 5e-18), scaled by 2^k.  The reduction's rounding (k times the error of ln 2 in fp64) is
 // below 1e-13 relative for |x| < 1000; results under the fp64 range flush to zero through
