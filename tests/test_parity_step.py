@@ -154,7 +154,7 @@ def test_full_size_decode():
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [4, 16, 33])
+@pytest.mark.parametrize("N", [4, 5, 16, 33, 64])
 def test_zero_order_hold(io, N):
     w = W["decode"].replace(Bt=3, D=70, N=N, io=io)
     check_step(workloads.make_step_inputs(w, seed=560 + N), tag="zoh N=%d" % N, zoh=True)
