@@ -108,7 +108,7 @@ def test_fwd_tiny(beta, N):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [3, 16, 24, 40])
+@pytest.mark.parametrize("N", [3, 16, 24, 40, 64])
 @pytest.mark.parametrize("a_kind", ["s4d_lin", "random"])
 def test_fwd_small_ragged(io, N, a_kind):
     w = SMALL.replace(io=io, N=N, dskip=True, beta=0.8, alpha=0.7)
