@@ -195,12 +195,34 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(nbytes, workspace, device):
+class _Owned:
+    """The tensors the binding allocates for one call (workspace, outputs the caller did not
+    pass).  They are allocated on the current stream; when the call is enqueued on another
+    stream, done() records each of them on that stream (Tensor.record_stream), so the caching
+    allocator hands their memory to no other work until the call's kernels have finished."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.tensors = []
+
+    def empty(self, shape, dtype, device):
+        import torch
+        t = torch.empty(shape, dtype=dtype, device=device)
+        self.tensors.append(t)
+        return t
+
+    def done(self):
+        if self.stream is not None:
+            for t in self.tensors:
+                t.record_stream(self.stream)
+
+
+def _workspace(nbytes, workspace, device, own):
     import torch
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = own.empty(nbytes, torch.uint8, device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise MsmError(3, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
@@ -224,6 +246,7 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
     """
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev = x.device
     Bt, L, D = x.shape
     N = A.shape[1]
@@ -236,18 +259,18 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
     if Dskip is not None:
         _check(Dskip, "Dskip", (D,), torch.float32, dev)
     if y is None:
-        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+        y = own.empty((Bt, L, D), x.dtype, dev)
     _check(y, "y", (Bt, L, D), x.dtype, dev)
     if return_last_state:
         if last_h is None:
-            last_h = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+            last_h = own.empty((Bt, D, N), torch.float32, dev)
         if last_v is None:
-            last_v = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+            last_v = own.empty((Bt, D, N), torch.float32, dev)
     for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
         if t is not None:
             _check(t, nm, (Bt, D, N), torch.float32, dev)
     nbytes = int(lib.msm_scan_fwd_workspace_bytes(Bt, L, D, N, io))
-    ws, wsb = _workspace(nbytes, workspace, dev)
+    ws, wsb = _workspace(nbytes, workspace, dev, own)
     tail = (Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
     if h0 is not None or v0 is not None:
         st = lib.msm_scan_fwd_state(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
@@ -260,6 +283,7 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
             st = lib.msm_scan_fwd(*args)
         else:
             st = lib.msm_scan_fwd_with_plan(*args, _plan_arg(plan))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_scan_fwd")
     if return_last_state:
@@ -279,6 +303,7 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
     """
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev = x.device
     Bt, L, D = x.shape
     N = A.shape[1]
@@ -290,13 +315,19 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
     if Dskip is not None:
         _check(Dskip, "Dskip", (D,), torch.float32, dev)
     o = dict(out or {})
-    o.setdefault("dx", torch.empty((Bt, L, D), dtype=x.dtype, device=dev))
-    o.setdefault("ddelta", torch.empty((Bt, L, D), dtype=x.dtype, device=dev))
-    o.setdefault("dA", torch.empty((D, N), dtype=torch.float32, device=dev))
-    o.setdefault("dB", torch.empty((Bt, L, N), dtype=x.dtype, device=dev))
-    o.setdefault("dC", torch.empty((Bt, L, N), dtype=x.dtype, device=dev))
+    if "dx" not in o:
+        o["dx"] = own.empty((Bt, L, D), x.dtype, dev)
+    if "ddelta" not in o:
+        o["ddelta"] = own.empty((Bt, L, D), x.dtype, dev)
+    if "dA" not in o:
+        o["dA"] = own.empty((D, N), torch.float32, dev)
+    if "dB" not in o:
+        o["dB"] = own.empty((Bt, L, N), x.dtype, dev)
+    if "dC" not in o:
+        o["dC"] = own.empty((Bt, L, N), x.dtype, dev)
     if Dskip is not None:
-        o.setdefault("dDskip", torch.empty((D,), dtype=torch.float32, device=dev))
+        if "dDskip" not in o:
+            o["dDskip"] = own.empty((D,), torch.float32, dev)
     else:
         o["dDskip"] = None
     states = (h0, v0, dlast_h, dlast_v)
@@ -304,10 +335,12 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
         if t is not None:
             _check(t, nm, (Bt, D, N), torch.float32, dev)
     if state_grads:
-        o.setdefault("dh0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
-        o.setdefault("dv0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
+        if "dh0" not in o:
+            o["dh0"] = own.empty((Bt, D, N), torch.float32, dev)
+        if "dv0" not in o:
+            o["dv0"] = own.empty((Bt, D, N), torch.float32, dev)
     nbytes = int(lib.msm_scan_bwd_workspace_bytes(Bt, L, D, N, io))
-    ws, wsb = _workspace(nbytes, workspace, dev)
+    ws, wsb = _workspace(nbytes, workspace, dev, own)
     tail = (Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
     grads = (_ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
              _ptr(o["dDskip"]))
@@ -320,6 +353,7 @@ def msm_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, out=None, wo
         st = lib.msm_scan_bwd(*ins, *grads, *tail)
     else:
         st = lib.msm_scan_bwd_with_plan(*ins, *grads, *tail, _plan_arg(plan))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_scan_bwd")
     return o
@@ -344,6 +378,7 @@ def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None
     msm_scan_fwd.  Returns y, or (y, last_h, last_v)."""
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev = x.device
     Bt, L, D = x.shape
     N = A.shape[1]
@@ -356,24 +391,25 @@ def msm_selective_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, z=None
         _check(Dskip, "Dskip", (D,), torch.float32, dev)
     _check_extras(x, z, delta_bias, dev)
     if y is None:
-        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+        y = own.empty((Bt, L, D), x.dtype, dev)
     _check(y, "y", (Bt, L, D), x.dtype, dev)
     if return_last_state:
         if last_h is None:
-            last_h = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+            last_h = own.empty((Bt, D, N), torch.float32, dev)
         if last_v is None:
-            last_v = torch.empty((Bt, D, N), dtype=torch.float32, device=dev)
+            last_v = own.empty((Bt, D, N), torch.float32, dev)
     for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
         if t is not None:
             _check(t, nm, (Bt, D, N), torch.float32, dev)
     nbytes = int(lib.msm_scan_fwd_workspace_bytes(Bt, L, D, N, io))
-    ws, wsb = _workspace(nbytes, workspace, dev)
+    ws, wsb = _workspace(nbytes, workspace, dev, own)
     st = lib.msm_selective_scan_fwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
         int(bool(delta_softplus)), int(bool(zero_order_hold)), _ptr(h0), _ptr(v0), _ptr(y),
         _ptr(last_h), _ptr(last_v), Bt,
         L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
         _plan_arg(plan))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_selective_scan_fwd")
     if return_last_state:
@@ -391,6 +427,7 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
     dv0."""
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev = x.device
     Bt, L, D = x.shape
     N = A.shape[1]
@@ -410,18 +447,22 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
     for k, shp, dt in (("dx", (Bt, L, D), x.dtype), ("ddelta", (Bt, L, D), x.dtype),
                        ("dA", (D, N), torch.float32), ("dB", (Bt, L, N), x.dtype),
                        ("dC", (Bt, L, N), x.dtype)):
-        o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+        if k not in o:
+            o[k] = own.empty(shp, dt, dev)
     for k, given, shp, dt in (("dDskip", Dskip, (D,), torch.float32), ("dz", z, (Bt, L, D), x.dtype),
                               ("ddelta_bias", delta_bias, (D,), torch.float32)):
         if given is not None:
-            o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+            if k not in o:
+                o[k] = own.empty(shp, dt, dev)
         else:
             o[k] = None
     if state_grads:
-        o.setdefault("dh0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
-        o.setdefault("dv0", torch.empty((Bt, D, N), dtype=torch.float32, device=dev))
+        if "dh0" not in o:
+            o["dh0"] = own.empty((Bt, D, N), torch.float32, dev)
+        if "dv0" not in o:
+            o["dv0"] = own.empty((Bt, D, N), torch.float32, dev)
     nbytes = int(lib.msm_scan_bwd_workspace_bytes(Bt, L, D, N, io))
-    ws, wsb = _workspace(nbytes, workspace, dev)
+    ws, wsb = _workspace(nbytes, workspace, dev, own)
     st = lib.msm_selective_scan_bwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
         int(bool(delta_softplus)), int(bool(zero_order_hold)), _ptr(dy),
@@ -430,6 +471,7 @@ def msm_selective_scan_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, z=
         _ptr(o["dz"]), _ptr(o["ddelta_bias"]), _ptr(o.get("dh0")), _ptr(o.get("dv0")), Bt, L, D,
         N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev),
         _plan_arg(plan))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_selective_scan_bwd")
     return o
@@ -441,6 +483,7 @@ def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, d
     h, v (Bt, D, N) fp32 states, updated in place.  Returns y (Bt, D)."""
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev = x.device
     Bt, D = x.shape
     N = A.shape[1]
@@ -458,12 +501,13 @@ def msm_scan_step(x, delta, A, B, C, h, v, beta, alpha, Dskip=None, *, z=None, d
     if delta_bias is not None:
         _check(delta_bias, "delta_bias", (D,), torch.float32, dev)
     if y is None:
-        y = torch.empty((Bt, D), dtype=x.dtype, device=dev)
+        y = own.empty((Bt, D), x.dtype, dev)
     _check(y, "y", (Bt, D), x.dtype, dev)
     st = lib.msm_scan_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
                            _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zero_order_hold)),
                            _ptr(h), _ptr(v), _ptr(y),
                            Bt, D, N, float(beta), float(alpha), io, _stream_handle(stream, dev))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_scan_step")
     return y
@@ -499,21 +543,23 @@ def msm_scan_complex_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, h0=None,
     (Bt, L, D), or (y, last_h, last_v)."""
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev, Bt, L, D, N, io = _complex_inputs(x, delta, A, B, C, Dskip)
     if y is None:
-        y = torch.empty((Bt, L, D), dtype=x.dtype, device=dev)
+        y = own.empty((Bt, L, D), x.dtype, dev)
     _check(y, "y", (Bt, L, D), x.dtype, dev)
     if return_last_state:
         if last_h is None:
-            last_h = torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev)
+            last_h = own.empty((Bt, D, N, 2), torch.float32, dev)
         if last_v is None:
-            last_v = torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev)
+            last_v = own.empty((Bt, D, N, 2), torch.float32, dev)
     for t, nm in ((last_h, "last_h"), (last_v, "last_v"), (h0, "h0"), (v0, "v0")):
         if t is not None:
             _check(t, nm, (Bt, D, N, 2), torch.float32, dev)
     st = lib.msm_scan_complex_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
                                   _ptr(h0), _ptr(v0), _ptr(y), _ptr(last_h), _ptr(last_v), Bt, L,
                                   D, N, float(beta), float(alpha), io, _stream_handle(stream, dev))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_scan_complex_fwd")
     if return_last_state:
@@ -530,6 +576,7 @@ def msm_scan_complex_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, h0=N
     gradients hold dL/dRe and dL/dIm in their last dimension."""
     import torch
     lib = load_library()
+    own = _Owned(stream)
     dev, Bt, L, D, N, io = _complex_inputs(x, delta, A, B, C, Dskip)
     _check(dy, "dy", (Bt, L, D), x.dtype, dev)
     for t, nm in ((h0, "h0"), (v0, "v0"), (dlast_h, "dlast_h"), (dlast_v, "dlast_v")):
@@ -539,21 +586,26 @@ def msm_scan_complex_bwd(x, delta, A, B, C, dy, beta, alpha, Dskip=None, *, h0=N
     for k, shp, dt in (("dx", (Bt, L, D), x.dtype), ("ddelta", (Bt, L, D), x.dtype),
                        ("dA", (D, N, 2), torch.float32), ("dB", (Bt, L, N, 2), x.dtype),
                        ("dC", (Bt, L, N, 2), x.dtype)):
-        o.setdefault(k, torch.empty(shp, dtype=dt, device=dev))
+        if k not in o:
+            o[k] = own.empty(shp, dt, dev)
     if Dskip is not None:
-        o.setdefault("dDskip", torch.empty((D,), dtype=torch.float32, device=dev))
+        if "dDskip" not in o:
+            o["dDskip"] = own.empty((D,), torch.float32, dev)
     else:
         o["dDskip"] = None
     if state_grads:
-        o.setdefault("dh0", torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev))
-        o.setdefault("dv0", torch.empty((Bt, D, N, 2), dtype=torch.float32, device=dev))
+        if "dh0" not in o:
+            o["dh0"] = own.empty((Bt, D, N, 2), torch.float32, dev)
+        if "dv0" not in o:
+            o["dv0"] = own.empty((Bt, D, N, 2), torch.float32, dev)
     nbytes = int(lib.msm_scan_complex_bwd_workspace_bytes(Bt, L, D, N, io))
-    ws, wsb = _workspace(nbytes, workspace, dev)
+    ws, wsb = _workspace(nbytes, workspace, dev, own)
     st = lib.msm_scan_complex_bwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(h0), _ptr(v0), _ptr(dy),
         _ptr(dlast_h), _ptr(dlast_v), _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]),
         _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dDskip"]), _ptr(o.get("dh0")), _ptr(o.get("dv0")),
         Bt, L, D, N, float(beta), float(alpha), io, _ptr(ws), wsb, _stream_handle(stream, dev))
+    own.done()
     if st != 0:
         raise MsmError(st, "msm_scan_complex_bwd")
     return o

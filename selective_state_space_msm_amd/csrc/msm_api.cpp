@@ -132,9 +132,16 @@ FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
 // K = 4), kBwdChans for the half-wavefront one
 int64_t bwd_chans(int NP, int K) { return (NP == 64 && K == 4) ? kWave : msm::kBwdChans; }
 
+// The half-wavefront backward addresses one tile's checkpoints ([2][N][D] fp32) through one
+// buffer resource, whose extent is at most 2^31 - 1 bytes: 8 N D must stay below 2^31.
+bool bwd_ckpt_ok(int64_t N, int64_t D) { return 8 * N * D < ((int64_t)1 << 31); }
+
 // 64 padded states as two halves of the 32-state plan address a tile of the first half's
-// fp64 sums ([L][2][D] per batch row) with 32-bit offsets: kBwdTile rows of 16 D bytes
-bool bwd_split_ok(int64_t D) { return (int64_t)msm::kBwdTile * 16 * D < ((int64_t)1 << 31); }
+// fp64 sums ([L][2][D] per batch row) with 32-bit offsets: kBwdTile rows of 16 D bytes; the
+// checkpoints keep their N-state layout
+bool bwd_split_ok(int64_t N, int64_t D) {
+  return (int64_t)msm::kBwdTile * 16 * D < ((int64_t)1 << 31) && bwd_ckpt_ok(N, D);
+}
 
 bool bwd_allowed_k(int NP, int K) {
   switch (NP) {
@@ -160,7 +167,7 @@ msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = f
   if (NP == 64 || NP == 32) {
     // 64 states: two launches of the 32-state plan (measured at Bt=4, L=2048, D=2048, N=64:
     // the full-wavefront kernel, which spills, takes 12.5 ms)
-    pl.states_per_wave = (NP == 64 && !bwd_split_ok(D)) ? 4 : 2;
+    pl.states_per_wave = (NP == 64 && !bwd_split_ok(N, D)) ? 4 : 2;
     return pl;
   }
   const int64_t chan_blocks = Bt * ceil_div(D, msm::kBwdChans);
@@ -191,7 +198,7 @@ BwdLayout bwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   l.off_accq = l.off_dbias + align_up(sizeof(float) * (size_t)(Bt * D));
   l.off_accz = l.off_accq;
   l.total = l.off_accq;
-  if (NP == 64 && bwd_split_ok(D)) {
+  if (NP == 64 && bwd_split_ok(N, D)) {
     // the first half's sums when 64 states run as two halves
     l.off_accz = l.off_accq + align_up(sizeof(double) * 2 * (size_t)(Bt * L * D));
     l.total = l.off_accz + align_up(sizeof(float) * (size_t)(Bt * L * D));
@@ -463,11 +470,14 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   if (plan) {
     if (plan->states_per_wave != 0) {
       if (!bwd_allowed_k(NP, plan->states_per_wave)) return MSM_ERR_UNSUPPORTED;
-      if (NP == 64 && plan->states_per_wave == 2 && !bwd_split_ok(D)) return MSM_ERR_UNSUPPORTED;
+      if (NP == 64 && plan->states_per_wave == 2 && !bwd_split_ok(N, D)) return MSM_ERR_UNSUPPORTED;
       pl.states_per_wave = plan->states_per_wave;
     }
     if (plan->chunks != 0 && plan->chunks != 1) return MSM_ERR_UNSUPPORTED;
   }
+  // up to 32 states the backward runs only in the half-wavefront kernel (64 states take the
+  // full-wavefront one when the checkpoints are too large, see auto_bwd_plan)
+  if (NP <= 32 && !bwd_ckpt_ok(N, D)) return MSM_ERR_UNSUPPORTED;
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);

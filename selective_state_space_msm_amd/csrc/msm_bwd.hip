@@ -35,8 +35,9 @@
 // dx / ddelta, and the bias gradient is summed per channel.  Its zero-order-hold form (EXT = 2)
 // also carries the write coefficient g = delta phi(delta A) and its derivatives (dg/ddelta =
 // e^(delta A), dg/dA = delta^2 psi(delta A)) through dx, ddelta, dA and dB.
-// This kernel serves 4, 16 and 32 padded states; 64 padded states use the full-wavefront
-// backward in msm_bwd_wide.hip.
+// This kernel serves 4, 16 and 32 padded states, and 64 padded states as two launches of its
+// 32-state plan (SPLIT below); the full-wavefront backward in msm_bwd_wide.hip takes 64 padded
+// states only when those halves would exceed 32-bit offsets.
 #include <type_traits>
 
 #include "msm_device.hpp"

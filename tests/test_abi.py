@@ -138,6 +138,13 @@ def test_bwd_argument_validation_never_launches(lib):
     assert call(plan=msm._Plan(4, 1)) == UNSUPPORTED
     assert call(plan=msm._Plan(3, 1)) == UNSUPPORTED
     assert call(plan=msm._Plan(2, 2)) == UNSUPPORTED  # the backward is never chunked
+    # one tile's checkpoints ([2][N][D] fp32) sit behind one buffer resource of at most
+    # 2^31 - 1 bytes: larger shapes are refused up to 32 states instead of losing their high
+    # states' checkpoints
+    assert call(N=32, D=1 << 23) == UNSUPPORTED
+    assert call(N=17, D=(1 << 31) // (8 * 17) + 1) == UNSUPPORTED
+    assert call(N=16, D=1 << 24) == UNSUPPORTED
+    assert call(N=32, D=(1 << 23) - 64, plan=msm._Plan(2, 1)) == WORKSPACE  # within the limit
 
 
 def test_state_entry_points_validation_never_launches(lib):
@@ -274,6 +281,10 @@ def test_bwd_plan_choice():
     # full-wavefront backward)
     assert msm.msm_scan_bwd_plan(1, 64, 64, 64, "f32", 0.9)["states_per_wave"] == 2
     assert msm.msm_scan_bwd_plan(1, 64, 1 << 23, 64, "f32", 0.9)["states_per_wave"] == 4
+    # the split halves keep the 64-state checkpoint layout: 8 N D must stay below 2^31 bytes
+    assert msm.msm_scan_bwd_plan(1, 64, (1 << 22) - 64, 64, "f32", 0.9)["states_per_wave"] == 2
+    assert msm.msm_scan_bwd_plan(1, 64, 1 << 22, 64, "f32", 0.9)["states_per_wave"] == 4
+    assert msm.msm_scan_bwd_plan(1, 64, (1 << 22) + 64, 48, "f32", 0.9)["states_per_wave"] == 2
     # 17-32 states: the half-wavefront backward with 2 states per lane
     assert msm.msm_scan_bwd_plan(1, 64, 64, 17, "f32", 0.9)["states_per_wave"] == 2
     assert msm.msm_scan_bwd_plan(4, 2048, 2048, 32, "f32", 0.9)["states_per_wave"] == 2
@@ -347,3 +358,23 @@ def test_complex_validation_never_launches(lib):
     assert bwd(dx=0x2000) == INVALID               # dx over delta
     assert bwd(dB=0x10000000) == INVALID           # dB inside the workspace
     assert bwd(dh0=0x6000) == INVALID              # dh0 over dy
+
+
+def test_binding_records_owned_tensors_on_the_launch_stream():
+    # tensors the binding allocates are recorded on the stream the call is enqueued on, so the
+    # caching allocator cannot reuse their memory while the kernels still run
+    calls = []
+
+    class FakeTensor:
+        def record_stream(self, s):
+            calls.append(s)
+
+    own = msm._Owned("side-stream")
+    own.tensors = [FakeTensor(), FakeTensor()]
+    own.done()
+    assert calls == ["side-stream", "side-stream"]
+    calls.clear()
+    own = msm._Owned(None)  # the current stream: nothing to record
+    own.tensors = [FakeTensor()]
+    own.done()
+    assert calls == []

@@ -191,3 +191,30 @@ def test_32_state_plans(K, chunks):
     inp = workloads.make_inputs(SMALL.replace(L=90, D=70, N=29, beta=0.85, dskip=True),
                                 a_kind="random", seed=130 + K + chunks)
     check_full(inp, plan={"states_per_wave": K, "chunks": chunks}, tag="N=29 K=%d" % K)
+
+
+def test_side_stream_calls_match_current_stream():
+    """Calls enqueued on a side stream: the binding's own workspace and outputs are recorded on
+    that stream; results equal the current-stream results."""
+    import torch
+    import selective_state_space_msm_amd as msm
+    inp = workloads.make_inputs(SMALL.replace(L=300, beta=0.9, dskip=True), seed=14, with_dy=True)
+    g = inputs_to_device(inp)
+    dy = torch.from_numpy(inp["dy"]).to("cuda")
+    ref_y = msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], 0.9, 1.0, g["Dskip"],
+                             plan={"states_per_wave": 2, "chunks": 3})
+    ref_g = msm.msm_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy, 0.9, 1.0, g["Dskip"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y = msm.msm_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], 0.9, 1.0, g["Dskip"],
+                         stream=side, plan={"states_per_wave": 2, "chunks": 3})
+    gr = msm.msm_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy, 0.9, 1.0, g["Dskip"],
+                          stream=side)
+    # memory allocated on the current stream meanwhile must not land on the side stream's buffers
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+    side.synchronize()
+    assert np.array_equal(host(y), host(ref_y))
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dDskip"):
+        assert np.array_equal(host(gr[k]), host(ref_g[k])), k
+    del junk
