@@ -128,6 +128,23 @@ msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, 
                               msm_dtype io, void* workspace, size_t workspace_bytes, void* stream,
                               const msm_plan* plan);
 
+/* Allocation-free forward scan, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, checks
+ * and results as msm_scan_fwd, without the workspace: the chunk summaries of a chunked plan
+ * live in a static device array owned by the library, MSM_NOALLOC_SCRATCH_BYTES (32 MiB) per
+ * GPU, held until the process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the first call on a device looks up that device's copy of the array.  A shape
+ * whose summaries exceed the array returns MSM_ERR_WORKSPACE before anything is enqueued (use
+ * msm_scan_fwd with a workspace for it).  Every call on one GPU shares that GPU's array: two
+ * calls in flight on one GPU at the same time (different streams, or host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs to start at zero: every summary is
+ * written before it is read within the call. */
+#define MSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+msm_status msm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, void* y, float* last_h,
+                                float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                float beta, float alpha, msm_dtype io, void* stream);
+
 /* Backward scan: gradients of sum(dy * y).  dx, ddelta, dB, dC, dA are overwritten (not
  * accumulated).  dDskip is required exactly when Dskip is non-NULL.  The forward is recomputed
  * inside; no saved activations are needed.  Same requirements as msm_scan_fwd. */

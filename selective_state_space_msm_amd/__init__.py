@@ -26,7 +26,7 @@ __all__ = [
     "msm_scan_bwd_workspace_bytes", "msm_scan_fwd_plan", "msm_scan_bwd_plan", "msm_scan_fwd",
     "msm_scan_bwd", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
     "msm_scan_complex_fwd", "msm_scan_complex_bwd", "msm_scan_complex_bwd_workspace_bytes",
-    "EXPORTED_SYMBOLS",
+    "msm_scan_fwd_noalloc", "EXPORTED_SYMBOLS",
 ]
 
 MSM_F32 = 0
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = [
     "msm_scan_fwd_with_plan", "msm_scan_bwd", "msm_scan_bwd_with_plan", "msm_scan_fwd_state",
     "msm_scan_bwd_state", "msm_selective_scan_fwd", "msm_selective_scan_bwd", "msm_scan_step",
     "msm_scan_complex_fwd", "msm_scan_complex_bwd_workspace_bytes", "msm_scan_complex_bwd",
+    "msm_scan_fwd_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +96,8 @@ def load_library():
     lib.msm_scan_fwd.restype = ctypes.c_int
     lib.msm_scan_fwd_with_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
     lib.msm_scan_fwd_with_plan.restype = ctypes.c_int
+    lib.msm_scan_fwd_noalloc.argtypes = [P] * 9 + [I64, I64, I64, I64, F, F, ctypes.c_int, P]
+    lib.msm_scan_fwd_noalloc.restype = ctypes.c_int
     bwd = [P, P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, F, ctypes.c_int, P, SZ, P]
     lib.msm_scan_bwd.argtypes = bwd
     lib.msm_scan_bwd.restype = ctypes.c_int
@@ -288,6 +291,35 @@ def msm_scan_fwd(x, delta, A, B, C, beta, alpha, Dskip=None, *, y=None, last_h=N
         raise MsmError(st, "msm_scan_fwd")
     if return_last_state:
         return y, last_h, last_v
+    return y
+
+
+def msm_scan_fwd_noalloc(x, delta, A, B, C, beta, alpha, Dskip=None, *, y, last_h=None,
+                         last_v=None, stream=None):
+    """Allocation-free forward (msm_scan_fwd_noalloc): msm_scan_fwd without a workspace, for
+    callers that cannot allocate.  Every output is passed by the caller (y, and last_h / last_v
+    when wanted); neither this function nor the library allocates.  Calls on one GPU share the
+    library's static scratch and must not overlap.  Returns y."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bt, L, D = x.shape
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for t, nm, shp in ((x, "x", (Bt, L, D)), (delta, "delta", (Bt, L, D)), (B, "B", (Bt, L, N)),
+                       (C, "C", (Bt, L, N)), (y, "y", (Bt, L, D))):
+        _check(t, nm, shp, x.dtype, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    if Dskip is not None:
+        _check(Dskip, "Dskip", (D,), torch.float32, dev)
+    for t, nm in ((last_h, "last_h"), (last_v, "last_v")):
+        if t is not None:
+            _check(t, nm, (Bt, D, N), torch.float32, dev)
+    st = lib.msm_scan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
+                                  _ptr(y), _ptr(last_h), _ptr(last_v), Bt, L, D, N, float(beta),
+                                  float(alpha), io, _stream_handle(stream, dev))
+    if st != 0:
+        raise MsmError(st, "msm_scan_fwd_noalloc")
     return y
 
 

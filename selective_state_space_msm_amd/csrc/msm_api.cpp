@@ -114,8 +114,8 @@ struct FwdLayout {
   size_t off_bv, off_bh, off_q, off_sd, total;
 };
 
-FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
-  const int64_t G = fwd_max_chunks(Bt, L, D, es);
+// Chunk summaries for G chunks: (bv, bh, q) [Bt][G][N][D] and the delta sums [Bt][G][D], fp32.
+FwdLayout fwd_layout_g(int64_t Bt, int64_t G, int64_t D, int64_t N) {
   FwdLayout l{};
   if (G <= 1) return l;
   const size_t per = align_up(sizeof(float) * (size_t)(Bt * G * N * D));
@@ -125,6 +125,11 @@ FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
   l.off_sd = 3 * per;
   l.total = 3 * per + align_up(sizeof(float) * (size_t)(Bt * G * D));
   return l;
+}
+
+// The workspace a caller passes is sized for the most chunks any plan can use.
+FwdLayout fwd_layout(int64_t Bt, int64_t L, int64_t D, int64_t N, int64_t es) {
+  return fwd_layout_g(Bt, fwd_max_chunks(Bt, L, D, es), D, N);
 }
 
 // ---- backward planning ----
@@ -316,14 +321,20 @@ msm_status msm_scan_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, msm_dt
   return MSM_OK;
 }
 
-msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
-                                  const void* B, const void* C, const float* Dskip, const void* z,
-                                  const float* delta_bias, int32_t delta_softplus,
-                                  int32_t zero_order_hold, const float* h0, const float* v0,
-                                  void* y, float* last_h,
-                                  float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
-                                  float beta, float alpha, msm_dtype io, void* workspace,
-                                  size_t workspace_bytes, void* stream, const msm_plan* plan) {
+}  // extern "C"
+
+namespace {
+
+// The forward behind every forward entry point.  noalloc: ignore workspace / workspace_bytes
+// and place the chunk summaries of this call's plan in the library's static device scratch
+// (msm_scan_fwd_noalloc).
+msm_status fwd_impl(const void* x, const void* delta, const float* A, const void* B,
+                    const void* C, const float* Dskip, const void* z, const float* delta_bias,
+                    int32_t delta_softplus, int32_t zero_order_hold, const float* h0,
+                    const float* v0, void* y, float* last_h, float* last_v, int64_t Bt,
+                    int64_t L, int64_t D, int64_t N, float beta, float alpha, msm_dtype io,
+                    void* workspace, size_t workspace_bytes, void* stream, const msm_plan* plan,
+                    bool noalloc) {
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!x || !delta || !A || !B || !C || !y) return MSM_ERR_INVALID_ARG;
@@ -348,17 +359,6 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);
   // a batch row's array may span at most kMaxChunks chunks of 2 GiB
   if (fwd_min_chunks(L, D, (int64_t)es) > kMaxChunks) return MSM_ERR_INVALID_ARG;
-  const FwdLayout lay = fwd_layout(Bt, L, D, N, (int64_t)es);
-  if (workspace_bytes < lay.total || (lay.total > 0 && !workspace)) return MSM_ERR_WORKSPACE;
-  const size_t nst = (size_t)(Bt * D * N) * 4;
-  const Range ins[] = {rng(x, nxd * es),        rng(delta, nxd * es),
-                       rng(A, (size_t)(D * N) * 4), rng(B, nbc * es),
-                       rng(C, nbc * es),        rng(Dskip, Dskip ? (size_t)D * 4 : 0),
-                       rng(h0, h0 ? nst : 0),   rng(v0, v0 ? nst : 0),
-                       rng(z, z ? nxd * es : 0), rng(delta_bias, delta_bias ? (size_t)D * 4 : 0)};
-  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? nst : 0),
-                        rng(last_v, last_v ? nst : 0), rng(workspace, lay.total)};
-  if (any_overlap(outs, 4, ins, 10)) return MSM_ERR_INVALID_ARG;
 
   // chunk length: a multiple of the tile, so only the final chunk can end mid-tile.  The
   // kernels address a chunk with 32-bit byte offsets: keep every chunk of every (Bt,L,D)
@@ -366,8 +366,33 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   int64_t G = pl.chunks;
   const int64_t gmin = fwd_min_chunks(L, D, (int64_t)es);
   if (G < gmin) G = gmin;  // within the workspace: fwd_layout is sized for it
-  int64_t Tc = ceil_div(ceil_div(L, G), kTile) * kTile;
+  const int64_t Tc = ceil_div(ceil_div(L, G), kTile) * kTile;
   G = ceil_div(L, Tc);  // rounding Tc up can leave fewer non-empty chunks
+
+  FwdLayout lay{};
+  if (noalloc) {
+    // the summaries of exactly this call's chunks, in the static scratch
+    lay = fwd_layout_g(Bt, G, D, N);
+    if (G > 1 && lay.total > msm::kNoAllocScratchBytes) return MSM_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else {
+    lay = fwd_layout(Bt, L, D, N, (int64_t)es);
+    if (workspace_bytes < lay.total || (lay.total > 0 && !workspace)) return MSM_ERR_WORKSPACE;
+  }
+  const size_t nst = (size_t)(Bt * D * N) * 4;
+  const Range ins[] = {rng(x, nxd * es),        rng(delta, nxd * es),
+                       rng(A, (size_t)(D * N) * 4), rng(B, nbc * es),
+                       rng(C, nbc * es),        rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                       rng(h0, h0 ? nst : 0),   rng(v0, v0 ? nst : 0),
+                       rng(z, z ? nxd * es : 0), rng(delta_bias, delta_bias ? (size_t)D * 4 : 0)};
+  const Range outs[] = {rng(y, nxd * es), rng(last_h, last_h ? nst : 0),
+                        rng(last_v, last_v ? nst : 0), rng(workspace, noalloc ? 0 : lay.total)};
+  if (any_overlap(outs, 4, ins, 10)) return MSM_ERR_INVALID_ARG;
+  if (noalloc && G > 1) {
+    // the scratch's device address on the current device (no allocation)
+    if (msm::noalloc_scratch(&workspace) != hipSuccess) return MSM_ERR_LAUNCH;
+  }
 
   msm::FwdArgs a{};
   a.x = x;
@@ -411,6 +436,31 @@ msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float*
   hipError_t e = msm::launch_fwd(a, io == MSM_BF16, pl.states_per_wave, beta == 0.0f, ext,
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSM_OK : MSM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+msm_status msm_selective_scan_fwd(const void* x, const void* delta, const float* A,
+                                  const void* B, const void* C, const float* Dskip, const void* z,
+                                  const float* delta_bias, int32_t delta_softplus,
+                                  int32_t zero_order_hold, const float* h0, const float* v0,
+                                  void* y, float* last_h,
+                                  float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                  float beta, float alpha, msm_dtype io, void* workspace,
+                                  size_t workspace_bytes, void* stream, const msm_plan* plan) {
+  return fwd_impl(x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, zero_order_hold, h0,
+                  v0, y, last_h, last_v, Bt, L, D, N, beta, alpha, io, workspace,
+                  workspace_bytes, stream, plan, false);
+}
+
+msm_status msm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* Dskip, void* y, float* last_h,
+                                float* last_v, int64_t Bt, int64_t L, int64_t D, int64_t N,
+                                float beta, float alpha, msm_dtype io, void* stream) {
+  return fwd_impl(x, delta, A, B, C, Dskip, nullptr, nullptr, 0, 0, nullptr, nullptr, y, last_h,
+                  last_v, Bt, L, D, N, beta, alpha, io, nullptr, 0, stream, nullptr, true);
 }
 
 msm_status msm_scan_fwd_state(const void* x, const void* delta, const float* A, const void* B,

@@ -203,4 +203,9 @@ hipError_t launch_bwd_part_1_2(const BwdArgs& a, int K, bool beta0, hipStream_t 
 // The 64-state backward (channel blocks of 64, K = 4); launch_bwd calls it for NP == 64.
 hipError_t launch_bwd_wide(const BwdArgs& a, int io_bf16, bool beta0, int ext, hipStream_t s);
 
+// Size of the static device scratch behind msm_scan_fwd_noalloc (the chunk summaries of one
+// call), and its device address on the current device (looked up on first use per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace msm

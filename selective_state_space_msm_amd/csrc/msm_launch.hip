@@ -1,6 +1,8 @@
 // Launchers: the forward and backward recurrence kernels (one build of msm_fwd.hip /
 // msm_bwd.hip per I/O dtype and variant; the full-wave backward for 64 padded states), and
 // the kernel that finishes the backward by summing its per-block partials.
+#include <mutex>
+
 #include "msm_device.hpp"
 #include "msm_internal.h"
 
@@ -107,6 +109,36 @@ hipError_t launch_bwd(const BwdArgs& a, int io_bf16, int K, bool beta0, int ext,
   }
   if (e != hipSuccess) return e;
   return io_bf16 ? launch_finalize<bf16_storage>(a, s) : launch_finalize<float>(a, s);
+}
+
+// Scratch of the allocation-free forward (msm_scan_fwd_noalloc): a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code never uses the
+// array's name as an address: the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept in `scratch_dev`.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *ptr = scratch_dev[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int io_bf16, int K, bool beta0, int ext, hipStream_t s) {

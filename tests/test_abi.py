@@ -360,6 +360,31 @@ def test_complex_validation_never_launches(lib):
     assert bwd(dh0=0x6000) == INVALID              # dh0 over dy
 
 
+def test_noalloc_forward_validation_never_launches(lib):
+    # the allocation-free forward checks its arguments like msm_scan_fwd, and refuses shapes whose
+    # chunk summaries exceed its static scratch before touching the device
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, Dskip=None, y=0x100000,
+                 lh=None, lv=None, Bt=1, L=8, D=4, N=4, beta=0.5, alpha=1.0, io=0)
+        a.update(kw)
+        return lib.msm_scan_fwd_noalloc(P(a["x"]), P(a["delta"]), P(a["A"]), P(a["B"]), P(a["C"]),
+                                        P(a["Dskip"]), P(a["y"]), P(a["lh"]), P(a["lv"]), a["Bt"],
+                                        a["L"], a["D"], a["N"], ctypes.c_float(a["beta"]),
+                                        ctypes.c_float(a["alpha"]), a["io"], None)
+
+    assert call(x=None) == INVALID
+    assert call(beta=1.0) == INVALID
+    assert call(N=65) == UNSUPPORTED
+    assert call(y=0x1000 + 16) == INVALID
+    # two batch rows of 2^20 steps x 4096 fp32 channels at 64 states: 9 chunks of < 2 GiB per
+    # row, whose summaries (about 57 MB) exceed the 32 MiB scratch
+    big = dict(x=1 << 44, delta=2 << 44, A=3 << 44, B=4 << 44, C=5 << 44, y=6 << 44, Bt=2,
+               L=1 << 20, D=4096, N=64)
+    assert call(**big) == WORKSPACE
+
+
 def test_binding_records_owned_tensors_on_the_launch_stream():
     # tensors the binding allocates are recorded on the stream the call is enqueued on, so the
     # caching allocator cannot reuse their memory while the kernels still run
