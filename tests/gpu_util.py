@@ -9,12 +9,7 @@ import numpy as np
 # Tolerances: |got - want| <= atol + rtol * |want|, elementwise, for every output.
 #   fp32 I/O: rtol 1e-5, atol 1e-4.
 #   bf16 I/O (fp32 state): rtol 2e-2, with the fp32 atol of 1e-4 kept for values near zero.
-TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 1e-4),
-       # the long-sequence tail of ddelta (see test_parity_bwd.test_rows_beyond_32bit_offsets)
-       "f32_tail": (1e-5, 2e-4),
-       # two GPU results compared with each other, each within the fp32 bound of the exact
-       # value: their difference is within twice that bound
-       "f32_pair": (2e-5, 2e-4)}
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 1e-4)}
 
 
 def log(msg):

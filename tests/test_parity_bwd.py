@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 import workloads
+from conditioning import assert_close_cond, spread
 from gpu_util import (assert_close, host, inputs_to_device, log, run_bwd, run_fwd,
                       sample_channels, sub_problem)
 
@@ -24,14 +25,21 @@ def check_full(inp, plan=None, tag=""):
     log("bwd %s shape=%s io=%s beta=%g alpha=%g plan=%s" % (tag, inp["x"].shape, io, inp["beta"],
                                                            inp["alpha"], plan))
     got = run_bwd(inp, plan=plan)
-    want = oracle_bwd(inp)
+    # gradients are differences of large per-state terms: each is held to the fp32 bound plus the
+    # oracle's own spread under one fp32 rounding of the inputs (tests/conditioning.py), which
+    # is far below the bound except for the rare ill-conditioned element
+    outs = tuple(k for k in NAMES if not (k == "dDskip" and inp["Dskip"] is None))
+    want, sp = spread(oracle_bwd, inp, ("x", "delta", "B", "C", "dy"), outs)
     for k in NAMES:
-        if want[k] is None:
+        if k not in outs:
             assert got[k] is None
             continue
         # dA and dDskip are fp32 outputs in every I/O mode
-        assert_close(host(got[k]), want[k], "f32" if k in ("dA", "dDskip") and io == "f32" else io,
-                     "%s %s" % (k, tag))
+        n = assert_close_cond(host(got[k]), want[k], sp[k],
+                              "f32" if k in ("dA", "dDskip") and io == "f32" else io,
+                              "%s %s" % (k, tag))
+        if n:
+            log("  %s %s: %d elements needed the conditioning term" % (k, tag, n))
 
 
 @pytest.mark.parametrize("beta", [0.9, 0.0])
@@ -126,26 +134,46 @@ def test_deterministic_across_runs():
         assert np.array_equal(host(a[k]), host(b[k])), k
 
 
+def test_long_memory_large_delta():
+    """delta ~ U[0.4, 1.3] with A in {0, -1e-4, -0.06, -0.11}: states with memories as long as
+    the sequence, where dA and ddelta are ill-conditioned (one fp32 rounding of the inputs moves
+    the exact dA past the fp32 bound, tests/test_conditioning.py).  Every output against the
+    oracle with the bound plus the oracle's own spread under such perturbations."""
+    for io in ("f32", "bf16"):
+        w = SMALL.replace(io=io, L=37, D=70, N=16)
+        inp = workloads.make_inputs(w, a_kind="random", seed=541, with_dy=True)
+        cols = np.array([0.0, -1e-4, -0.06, -0.11] * 4, dtype=np.float32)
+        inp["A"] = np.ascontiguousarray(np.tile(cols, (w.D, 1)))
+        rng = np.random.default_rng(542)
+        dl = rng.uniform(0.4, 1.3, size=inp["delta"].shape).astype(np.float32)
+        inp["delta"] = dl if io == "f32" else workloads.round_to_bf16(dl)
+        got = run_bwd(inp)
+        want, sp = spread(oracle_bwd, inp, ("x", "delta", "B", "C", "dy"), NAMES[:5])
+        for k in NAMES[:5]:
+            tol = "f32" if k == "dA" and io == "f32" else io
+            n = assert_close_cond(host(got[k]), want[k], sp[k], tol, "%s %s" % (k, io))
+            log("  %s %s: %d of %d elements needed the conditioning term"
+                % (k, io, n, want[k].size))
+
+
 def test_full_size_backward():
     w = W["bwd"]
     log("full-size bwd: drawing inputs")
     inp = workloads.make_inputs(w)
     g = inputs_to_device(inp)
     got = {k: (None if v is None else host(v)) for k, v in run_bwd(inp, g).items()}
-    # (1) batch row 0 in full: every output of that row, including dB and dC (sums over all d)
-    log("  oracle on batch row 0 (all channels)")
-    sub0 = sub_problem(inp, bsel=slice(0, 1))
-    o0 = oracle_bwd(sub0)
-    for k in ("dx", "ddelta", "dB", "dC"):
-        assert_close(got[k][0:1], o0[k], w.io, "%s row 0" % k)
-    # (2) sampled channels over every batch row: dx, ddelta and dA (dA sums over b and t)
-    dsel = sample_channels(w.D, 16, seed=w.seed)
-    log("  oracle on %d sampled channels x all rows" % len(dsel))
-    od = oracle_bwd(sub_problem(inp, dsel=dsel))
-    assert_close(got["dx"][:, :, dsel], od["dx"], w.io, "dx sampled")
-    assert_close(got["ddelta"][:, :, dsel], od["ddelta"], w.io, "ddelta sampled")
-    assert_close(got["dA"][dsel], od["dA"], w.io, "dA sampled")
-    # (3) scaling identities on the whole output (fp64 inner products on the host):
+    # (1) every output of every batch row and channel against the oracle on the whole workload.
+    #     Its steps are in the well-conditioned regime (tests/test_conditioning.py), yet among
+    #     16.7M ddelta elements a few cancel far enough that one fp32 rounding of the inputs
+    #     moves them by about the bound: the bound adds the oracle's own spread (two perturbed
+    #     runs), and the test logs how many elements needed it.
+    log("  oracle on the whole workload (and two perturbed runs)")
+    want, sp = spread(oracle_bwd, inp, ("x", "delta", "B", "C", "dy"), NAMES[:5], trials=2)
+    for k in ("dx", "ddelta", "dA", "dB", "dC"):
+        n = assert_close_cond(got[k], want[k], sp[k], w.io, "%s full" % k)
+        log("  %s: %d of %d elements needed the conditioning term" % (k, n, want[k].size))
+    del want, sp
+    # (2) scaling identities on the whole output (fp64 inner products on the host):
     #     <dB,B> = <dC,C> = <dx,x> = <ddelta,delta> - <dA,A> = <dy,y>  (no skip term here)
     y = host(run_fwd(inp, g)[0])
     ip = lambda a, b: float(np.sum(np.asarray(a, np.float64) * np.asarray(b, np.float64)))
@@ -173,22 +201,17 @@ def test_rows_beyond_32bit_offsets():
     got = msm.msm_scan_bwd(x, delta, A, B, C, dy, 0.9, 1.0)
     torch.cuda.synchronize()
     dsel = sample_channels(D, 6, seed=83)
-    od = oracle.bwd(host(x[:, :, dsel]), host(delta[:, :, dsel]), host(A[dsel]), host(B),
-                    host(C), host(dy[:, :, dsel]), 0.9, 1.0)
-    assert_close(host(got["dx"][:, :, dsel]), od["dx"], "f32", "dx sampled")
-    assert_close(host(got["dA"][dsel]), od["dA"], "f32", "dA sampled")
-    # ddelta is a difference of per-state terms that reach ~5e2 for states with a long memory
-    # (small delta |A|, with momentum); the fp32 decay factors exp(delta A) compounding over
-    # such memories leave a tail of elements (a few in 1e7 at this length) slightly past the
-    # fp32 bound.  Checked: the bound holds for all but at most 1e-6 of the elements, and every
-    # element is within twice the absolute bound (the README reports CUDA-vs-CPU gradient
-    # agreement up to 3.1e-4 for its own kernel).
-    gd, wd = host(got["ddelta"][:, :, dsel]), od["ddelta"]
-    err = np.abs(gd - wd)
-    over = err > 1e-4 + 1e-5 * np.abs(wd)
-    log("  ddelta: %d of %d past the fp32 bound, max err %.3g" % (over.sum(), err.size, err.max()))
-    assert over.sum() <= max(1, int(1e-6 * err.size)), over.sum()
-    assert_close(gd, wd, "f32_tail", "ddelta sampled")
+    sub = dict(x=host(x[:, :, dsel]), delta=host(delta[:, :, dsel]), A=host(A[dsel]), B=host(B),
+               C=host(C), dy=host(dy[:, :, dsel]), beta=0.9, alpha=1.0, Dskip=None)
+    # over 2^19 steps a few states keep memories of thousands of steps, and ddelta, a difference
+    # of per-state terms of order 1e2, is ill-conditioned for a few elements in 1e7: the bound
+    # adds the oracle's own spread under one fp32 rounding of the inputs (tests/conditioning.py)
+    od, sp = spread(oracle_bwd, sub, ("x", "delta", "B", "C", "dy"), ("dx", "ddelta", "dA"),
+                    trials=2)
+    for k in ("dx", "ddelta"):
+        n = assert_close_cond(host(got[k][:, :, dsel]), od[k], sp[k], "f32", k + " sampled")
+        log("  %s: %d elements needed the conditioning term" % (k, n))
+    assert_close_cond(host(got["dA"][dsel]), od["dA"], sp["dA"], "f32", "dA sampled")
     y = msm.msm_scan_fwd(x, delta, A, B, C, 0.9, 1.0)
     ip = lambda a, b: float(torch.sum(a.double() * b.double()))
     ref = ip(dy, y)

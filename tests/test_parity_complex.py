@@ -1,13 +1,14 @@
 """The complex-valued scan on the GPU (msm_scan_complex_fwd / msm_scan_complex_bwd through the C
 ABI) against the fp64 oracle: small shapes with ragged tiles, channel blocks and state groups
-for every plan (4, 16, 32 and 64 padded states) and both I/O dtypes, then the full-size workload on
-sampled channels, its channel sums on one full batch row, and the degenerate cases."""
+for every plan (4, 16, 32 and 64 padded states) and both I/O dtypes, then every output of the
+full-size workload, continuation across calls, and the degenerate cases."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gpu_util import assert_close, dev, host, log, sample_channels
+from conditioning import assert_close_cond, spread
+from gpu_util import assert_close, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -90,12 +91,20 @@ def check_bwd(inp, h0=None, v0=None, dlh=None, dlv=None, tag=""):
     io = inp["io"]
     log("complex bwd %s shape=%s N=%d io=%s" % (tag, inp["x"].shape, inp["A"].shape[1], io))
     got = run_bwd(inp, h0, v0, dlh, dlv)
-    want = oracle_bwd(inp, h0, v0, dlh, dlv)
-    for k in ("dx", "ddelta", "dDskip"):
-        if want[k] is not None:
-            assert_close(host(got[k]), want[k], io, "%s %s" % (k, tag))
-    for k in ("dA", "dB", "dC", "dh0", "dv0"):
-        assert_close(host(got[k]), ri(want[k]), io, "%s %s" % (k, tag))
+    outs = ("dx", "ddelta", "dA", "dB", "dC", "dh0", "dv0") + (("dDskip",) if inp["Dskip"] is not None
+                                                               else ())
+
+    def fn(q):
+        o = oracle_bwd(q, h0, v0, dlh, dlv)
+        return {k: (o[k] if k in ("dx", "ddelta", "dDskip") else ri(o[k])) for k in outs}
+
+    # gradients held to the bound plus the oracle's own spread under one fp32 rounding of the
+    # inputs (tests/conditioning.py)
+    want, sp = spread(fn, inp, ("x", "delta", "B", "C", "dy"), outs)
+    for k in outs:
+        n = assert_close_cond(host(got[k]), want[k], sp[k], io, "%s %s" % (k, tag))
+        if n:
+            log("  %s %s: %d elements needed the conditioning term" % (k, tag, n))
 
 
 # ---- small shapes: every plan, ragged tiles / channel blocks / states, both dtypes ----
@@ -226,39 +235,40 @@ def full():
     return inp, to_dev(inp)
 
 
-def test_full_size_fwd_sampled_channels(full):
+def test_full_size_fwd(full):
     import torch
     import selective_state_space_msm_amd as msm
     inp, g = full
     log("complex fwd full size %s" % (inp["x"].shape,))
-    y, lh, _ = msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"],
-                                        inp["alpha"], g["Dskip"], return_last_state=True)
+    y, lh, lv = msm.msm_scan_complex_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"],
+                                         inp["alpha"], g["Dskip"], return_last_state=True)
     torch.cuda.synchronize()
-    ds = sample_channels(inp["x"].shape[2], 24, 371)
-    sub = dict(inp, x=inp["x"][:, :, ds], delta=inp["delta"][:, :, ds], A=inp["A"][ds])
-    oy, olh, _ = oracle_fwd(sub)
-    assert_close(host(y)[:, :, ds], oy, "f32", "y (sampled channels)")
-    assert_close(host(lh)[:, ds], ri(olh), "f32", "last_h (sampled channels)")
+    oy, olh, olv = oracle_fwd(inp)
+    assert_close(host(y), oy, "f32", "y")
+    assert_close(host(lh), ri(olh), "f32", "last_h")
+    assert_close(host(lv), ri(olv), "f32", "last_v")
 
 
 def test_full_size_bwd(full):
-    """Per-channel gradients (dx, ddelta, dA) on sampled channels of every batch row; the channel
-    sums dB, dC on batch row 0 with all its channels."""
+    """Every gradient of every batch row and channel against the oracle on the whole workload.
+    ddelta holds Re(conj(gh) A a h) terms a factor |A| (up to 47) above the states, which cancel:
+    among its 16.7M elements a few move by about the fp32 bound under one fp32 rounding of the
+    inputs, so the bound adds the oracle's own spread (two perturbed runs,
+    tests/conditioning.py) and the test logs how many elements needed it."""
     inp, g = full
     log("complex bwd full size %s" % (inp["x"].shape,))
     got = run_bwd(inp)
-    ds = sample_channels(inp["x"].shape[2], 16, 381)
-    sub = dict(inp, x=inp["x"][:, :, ds], delta=inp["delta"][:, :, ds], dy=inp["dy"][:, :, ds],
-               A=inp["A"][ds])
-    want = oracle_bwd(sub)
-    for k in ("dx", "ddelta"):
-        assert_close(host(got[k])[:, :, ds], want[k], "f32", k + " (sampled channels)")
-    assert_close(host(got["dA"])[ds], ri(want["dA"]), "f32", "dA (sampled channels)")
-    row = dict(inp, x=inp["x"][:1], delta=inp["delta"][:1], dy=inp["dy"][:1], B=inp["B"][:1],
-               C=inp["C"][:1])
-    want0 = oracle_bwd(row)
-    for k in ("dB", "dC"):
-        assert_close(host(got[k])[:1], ri(want0[k]), "f32", k + " (batch row 0)")
+
+    def fn(q):
+        o = oracle_bwd(q)
+        return {k: (ri(v) if k in ("dA", "dB", "dC") else v) for k, v in o.items()
+                if k in ("dx", "ddelta", "dA", "dB", "dC")}
+
+    want, sp = spread(fn, inp, ("x", "delta", "B", "C", "dy"), ("dx", "ddelta", "dA", "dB", "dC"),
+                      trials=2)
+    for k in ("dx", "ddelta", "dA", "dB", "dC"):
+        n = assert_close_cond(host(got[k]), want[k], sp[k], "f32", k)
+        log("  %s: %d of %d elements needed the conditioning term" % (k, n, want[k].size))
 
 
 # ---- continuation: a sequence in two calls equals one call ----
@@ -276,37 +286,47 @@ def _split(inp, t):
 @pytest.mark.parametrize("N", [16, 40])
 def test_forward_continuation(N):
     """Scanning the first 1000 steps and continuing from the returned (last_h, last_v) over the
-    rest gives the outputs and final states of one call over all 2048 steps."""
+    rest gives the outputs and final states of one scan over all 2048 steps (the oracle's)."""
     w = CW.replace(Bt=2, L=2048, D=96, N=N, dskip=True)
     inp = workloads.make_complex_inputs(w, seed=391)
-    y, lh, lv = run_fwd(inp)
+    oy, olh, olv = oracle_fwd(inp)
     a, b = _split(inp, 1000)
     ya, lha, lva = run_fwd(a)
     yb, lhb, lvb = run_fwd(b, host(lha).astype(np.float32), host(lva).astype(np.float32))
-    assert_close(np.concatenate([host(ya), host(yb)], axis=1), host(y), "f32", "y (continued)")
-    assert_close(host(lhb), host(lh), "f32", "last_h (continued)")
-    assert_close(host(lvb), host(lv), "f32", "last_v (continued)")
+    assert_close(np.concatenate([host(ya), host(yb)], axis=1), oy, "f32", "y (continued)")
+    assert_close(host(lhb), ri(olh), "f32", "last_h (continued)")
+    assert_close(host(lvb), ri(olv), "f32", "last_v (continued)")
 
 
 @pytest.mark.parametrize("N", [16, 40])
 def test_backward_continuation(N):
     """The backward of a sequence in two parts: the second part first, from the first part's
-    final state, then the first with the second's (dh0, dv0) as its terminal adjoints.  dx,
-    ddelta, dB, dC agree with one backward over the whole sequence; dA is the sum of the parts.
-    The state at the split comes from the fp64 oracle rounded to fp32, as accurate as the state
-    history of the one-call backward: ddelta carries a factor |A| on the states, and the fp32
-    readout forward's state (about 1e-6 relative) moves ddelta past the fp32 bound next to the
-    split."""
+    final state, then the first with the second's (dh0, dv0) as its terminal adjoints.  Each
+    part runs on the GPU and in the oracle from the same inputs: the state at the split is the
+    oracle's forward over the first part rounded to fp32, and the first part's terminal adjoints
+    are the oracle's (dh0, dv0) of the second part rounded to fp32.  Every output of both parts,
+    including the adjoints of the initial state, is held to the fp32 bound plus the oracle's own
+    spread under one fp32 rounding of the inputs (ddelta's terms carry |A| up to 47 and cancel;
+    tests/conditioning.py)."""
     w = CW.replace(Bt=2, L=2048, D=96, N=N, dskip=False, direction="bwd")
     inp = workloads.make_complex_inputs(w, seed=397)
-    full = run_bwd(inp)
     a, b = _split(inp, 1000)
     _, lha, lva = oracle_fwd(a)
     h1, v1 = ri(lha).astype(np.float32), ri(lva).astype(np.float32)
+    outs = ("dx", "ddelta", "dA", "dB", "dC", "dh0", "dv0")
+
+    def as_ri(o):
+        return {k: (o[k] if k in ("dx", "ddelta") else ri(o[k])) for k in outs}
+
     gb = run_bwd(b, h1, v1)
-    ga = run_bwd(a, dlh=host(gb["dh0"]).astype(np.float32), dlv=host(gb["dv0"]).astype(np.float32))
-    # two GPU results, each held to the fp32 bound elsewhere: compared with the pair bound
-    for k in ("dx", "ddelta", "dB", "dC"):
-        got = np.concatenate([host(ga[k]), host(gb[k])], axis=1)
-        assert_close(got, host(full[k]), "f32_pair", k + " (continued)")
-    assert_close(host(ga["dA"]) + host(gb["dA"]), host(full["dA"]), "f32_pair", "dA (continued)")
+    ob, spb = spread(lambda q: as_ri(oracle_bwd(q, h1, v1)), b, ("x", "delta", "B", "C", "dy"),
+                     outs)
+    dlh, dlv = ob["dh0"].astype(np.float32), ob["dv0"].astype(np.float32)
+    ga = run_bwd(a, dlh=dlh, dlv=dlv)
+    oa, spa = spread(lambda q: as_ri(oracle_bwd(q, dlh=dlh, dlv=dlv)), a,
+                     ("x", "delta", "B", "C", "dy"), outs)
+    for tag, got, want, sp in (("second part", gb, ob, spb), ("first part", ga, oa, spa)):
+        for k in outs:
+            n = assert_close_cond(host(got[k]), want[k], sp[k], "f32", "%s %s" % (k, tag))
+            if n:
+                log("  %s %s: %d elements needed the conditioning term" % (k, tag, n))

@@ -119,36 +119,105 @@ def test_plans_agree_with_each_other():
 
 # ---- full-size workloads, in the launch configuration the bench times ----
 
-def check_sampled(w, a_kind="s4d", beta=None, nsample=24):
+def check_full_size(w, a_kind="s4d", beta=None):
+    """Every output of the workload against the oracle on the whole workload."""
     wl = w if beta is None else w.replace(beta=beta)
     log("full-size %s beta=%g: drawing inputs" % (wl.name, wl.beta))
     inp = workloads.make_inputs(wl, a_kind=a_kind)
     y, lh, lv = run_fwd(inp)
-    dsel = sample_channels(wl.D, nsample, seed=wl.seed)
-    log("  comparing %d channels x %d batch rows against the oracle" % (len(dsel), wl.Bt))
-    sub = sub_problem(inp, dsel=dsel)
-    oy, olh, olv = oracle_fwd(sub)
-    y = host(y)[:, :, dsel]
-    assert_close(y, oy, wl.io, "y %s" % wl.name)
-    assert_close(host(lh)[:, dsel], olh, "f32", "last_h %s" % wl.name)
-    assert_close(host(lv)[:, dsel], olv, "f32", "last_v %s" % wl.name)
+    log("  oracle on the whole workload")
+    oy, olh, olv = oracle_fwd(inp)
+    assert_close(host(y), oy, wl.io, "y %s" % wl.name)
+    assert_close(host(lh), olh, "f32", "last_h %s" % wl.name)
+    assert_close(host(lv), olv, "f32", "last_v %s" % wl.name)
 
 
 @pytest.mark.parametrize("beta", [0.0, 0.9])
 def test_full_m130m(beta):
-    check_sampled(W["m130m"], beta=beta)
+    check_full_size(W["m130m"], beta=beta)
 
 
 def test_full_m1p4b():
-    check_sampled(W["m1p4b"])
+    check_full_size(W["m1p4b"])
 
 
 def test_full_m1p4b_unstructured_A():
-    check_sampled(W["m1p4b"], a_kind="random")
+    check_full_size(W["m1p4b"], a_kind="random")
 
 
 def test_full_long_sequence():
-    check_sampled(W["long"], nsample=12)
+    check_full_size(W["long"])
+
+
+def test_batch_32():
+    """Batch 32, one of the README's edge cases, forward and backward against the oracle."""
+    inp = workloads.make_inputs(W["m130m"].replace(Bt=32, L=300, D=200, dskip=True),
+                                a_kind="random", seed=15, with_dy=True)
+    check_full(inp, tag="batch 32")
+    from test_parity_bwd import check_full as check_bwd
+    check_bwd(inp, tag="batch 32")
+
+
+# ---- structure of the scan at full size, on the GPU's own outputs ----
+# Properties that hold for the exact scan at any size (the oracle's pins check the same ones on
+# small inputs): causality, linearity in x, homogeneity in alpha.
+
+def _fwd_dev(g, beta, alpha, Dskip=None, x=None, plan=None):
+    import torch
+    import selective_state_space_msm_amd as msm
+    y = msm.msm_scan_fwd(g["x"] if x is None else x, g["delta"], g["A"], g["B"], g["C"], beta,
+                         alpha, Dskip, plan=plan)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_full_size_causality():
+    """Changing x at one step changes no output before it, bit for bit (m130m shape, chunked
+    and unchunked plans)."""
+    import torch
+    w = W["m130m"]
+    inp = workloads.make_inputs(w, seed=21)
+    g = inputs_to_device(inp)
+    for plan in (None, {"states_per_wave": 2, "chunks": 4}):
+        y0 = _fwd_dev(g, inp["beta"], inp["alpha"], plan=plan)
+        for t in (1, 777, w.L - 1):
+            x2 = g["x"].clone()
+            x2[:, t, :] += 1.0
+            y1 = _fwd_dev(g, inp["beta"], inp["alpha"], x=x2, plan=plan)
+            assert torch.equal(y1[:, :t], y0[:, :t]), (t, plan)
+            assert not torch.equal(y1[:, t], y0[:, t]), (t, plan)
+
+
+def test_full_size_linearity_in_x():
+    """y(x1 + x2) = y(x1) + y(x2) (m130m shape, fp32 I/O, no skip term): each of the three
+    results is within atol + rtol |y| of its exact value, so the identity holds to the sum of
+    the three bounds."""
+    import torch
+    w = W["m130m"]
+    inp = workloads.make_inputs(w, seed=22)
+    g = inputs_to_device(inp)
+    x1 = g["x"]
+    x2 = torch.flip(g["x"], dims=[2]).contiguous()
+    ya = _fwd_dev(g, inp["beta"], inp["alpha"], x=x1).double()
+    yb = _fwd_dev(g, inp["beta"], inp["alpha"], x=x2).double()
+    yab = _fwd_dev(g, inp["beta"], inp["alpha"], x=(x1 + x2)).double()
+    err = (yab - (ya + yb)).abs()
+    lim = 3e-4 + 1e-5 * (ya.abs() + yb.abs() + yab.abs())
+    assert bool((err <= lim).all()), float((err - lim).max())
+
+
+def test_full_size_alpha_homogeneity():
+    """y(alpha) - Dskip x = alpha (y(1) - Dskip x) (m130m shape, fp32 I/O, with the skip term),
+    to the bounds of the two results (atol + rtol |y| each, the second scaled by alpha)."""
+    w = W["m130m"].replace(dskip=True)
+    inp = workloads.make_inputs(w, seed=23)
+    g = inputs_to_device(inp)
+    skip = (g["Dskip"][None, None, :] * g["x"]).double()
+    f1 = _fwd_dev(g, inp["beta"], 1.0, g["Dskip"]).double()
+    fa = _fwd_dev(g, inp["beta"], 0.37, g["Dskip"]).double()
+    err = ((fa - skip) - 0.37 * (f1 - skip)).abs()
+    lim = 1.37e-4 + 1e-5 * (fa.abs() + 0.37 * f1.abs())
+    assert bool((err <= lim).all()), float((err - lim).max())
 
 
 def _device_inputs(Bt, L, D, N, seed):
