@@ -2,10 +2,13 @@
 
 One step = one msm_scan_fwd call over the Mamba-1.4B layer shape (Bt=4, L=4096, D=4096, N=16,
 bf16 I/O with fp32 state, beta=0.9, alpha=1) with inputs already resident in HBM.  The line
-also reports the backward on its own workload (Bt=4, L=2048, D=2048, N=16, fp32) timed the
-same way, one decode step (msm_scan_step, Bt=1024 sequences of the same layer shape) with its
-HBM roofline, the ALU roofline of the forward's single kernel, the algorithmic HBM rate, and the
-fp64 oracle timed on the host cores on a bounded sample of the same workload.
+reports its HBM roofline (algorithmic bytes over the kernel's time against 8 TB/s) and, as a
+second figure, its VALU issue share; the median and minimum over 50 calls with the last-level
+cache warm and flushed; the backward on its own workload (Bt=4, L=2048, D=2048, N=16, fp32);
+one decode step (msm_scan_step, Bt=1024 sequences of the same layer shape) with its HBM
+roofline; the tiny workload's latency; every other configuration of the measurement plan with
+its workspace and device memory; and the fp64 oracle timed on the host cores (all of them, and
+one) on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload m1p4b] [--no-cpu-baseline]
 """
@@ -29,8 +32,11 @@ import workloads  # noqa: E402
 
 METRIC = "fwd/bwd selective-scan state-updates/sec (Bt·L·D·N) + achieved HBM GB/s"
 HBM_PEAK_GBS = 8000.0
-# VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (packed FP32 is not used)
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# VALU issue slots per second from the published fp32 vector peak, 157.3 TFLOP/s: halved because
+# packed FP32 is not used, halved again because an FMA counts two flops (= 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz)
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+VALU_PEAK_TSLOTS = FP32_VECTOR_PEAK_TFLOPS / 2 / 2
 # Issue slots the recurrence needs per state update: exp2 (v_exp_f32, half rate: 2 slots) plus
 # delta*A, the write c*B, the velocity FMA, the hidden-state FMA and the readout FMA; the
 # velocity FMA disappears when beta = 0.
@@ -120,6 +126,51 @@ def timed(fn, stream, steps, warmup):
     return total / steps, per
 
 
+def per_call_ms(fn, stream, calls, flush=None):
+    """Duration of each of `calls` calls of fn, from HIP events recorded on `stream` right
+    before and after it.  flush: a function run before each call, outside the timed interval
+    (it evicts the inputs from the last-level cache)."""
+    import torch
+    out = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    with torch.cuda.stream(stream):
+        for a, b in ev:
+            if flush is not None:
+                flush()
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+_flush_buf = None
+
+
+def cache_flush():
+    """Write 1 GiB on the device: more than the 256 MB last-level cache holds."""
+    import torch
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    _flush_buf.fill_(1.0)
+
+
+def timing_record(fn, stream, calls=50):
+    """Median and minimum per-call time over `calls` calls, warm (back to back) and with the
+    last-level cache flushed before each call."""
+    warm = per_call_ms(fn, stream, calls)
+    cold = per_call_ms(fn, stream, calls, flush=cache_flush)
+    return {"calls": calls,
+            "warm": {"median_ms": float(np.median(warm)), "min_ms": float(np.min(warm))},
+            "flushed": {"median_ms": float(np.median(cold)), "min_ms": float(np.min(cold))}}
+
+
+def nbytes_of(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def to_dev(inp):
     import torch
     dt = torch.float32 if inp["io"] == "f32" else torch.bfloat16
@@ -162,7 +213,9 @@ def bench_fwd(w, steps, warmup, stream, a_kind="s4d", fused=False, zoh=False):
                              g["Dskip"], y=y, workspace=ws, stream=stream)
 
     ms, per = timed(step, stream, steps, warmup)
-    return ms, per, plan
+    mem = {"workspace_bytes": int(nbytes),
+           "device_bytes": int(sum(nbytes_of(t) for t in list(g.values()) + [y]) + nbytes)}
+    return ms, per, plan, step, mem
 
 
 def bench_bwd(w, steps, warmup, stream, fused=False, zoh=False):
@@ -203,7 +256,10 @@ def bench_bwd(w, steps, warmup, stream, fused=False, zoh=False):
                              w.alpha, g["Dskip"], out=out, workspace=ws, stream=stream)
 
     ms, per = timed(step, stream, steps, warmup)
-    return ms, per, plan
+    mem = {"workspace_bytes": int(nbytes),
+           "device_bytes": int(sum(nbytes_of(t) for t in list(g.values()) + list(out.values()))
+                               + nbytes)}
+    return ms, per, plan, step, mem
 
 
 def bench_step(w, steps, warmup, stream):
@@ -298,16 +354,18 @@ def bench_configs(steps, warmup, stream, only=None):
             continue
         w = W[name].replace(**kw)
         if direction == "fwd":
-            ms, per, plan = bench_fwd(w, steps, warmup, stream, a_kind=a_kind, fused=fused, zoh=zoh)
+            ms, per, plan, fn, mem = bench_fwd(w, steps, warmup, stream, a_kind=a_kind,
+                                               fused=fused, zoh=zoh)
             nb = alg_bytes_fwd(w)
         else:
-            ms, per, plan = bench_bwd(w, steps, warmup, stream, fused=fused, zoh=zoh)
+            ms, per, plan, fn, mem = bench_bwd(w, steps, warmup, stream, fused=fused, zoh=zoh)
             nb = alg_bytes_bwd(w)
         out.append({"workload": name, "direction": direction, "beta": w.beta, "A": a_kind,
                     "fused_extras": fused, "zero_order_hold": zoh, "Bt": w.Bt, "L": w.L,
                     "D": w.D, "N": w.N, "io": w.io,
                     "ms": ms, "ms_min": min(per), "state_updates_per_s": w.updates / (ms / 1e3),
-                    "algorithmic_GBs": nb / (ms / 1e3) / 1e9, "plan": plan})
+                    "algorithmic_GBs": nb / (ms / 1e3) / 1e9, "hbm_frac":
+                    nb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": plan, "memory": mem})
         import torch
         torch.cuda.empty_cache()
     return out
@@ -331,11 +389,22 @@ def cpu_baseline(w, target_s=12.0):
     oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], w.beta, w.alpha,
                Dskip=inp["Dskip"], threads=threads)
     dt = time.perf_counter() - t0
+    # one thread on the first batch row, a few channels sized for about a fifth of target_s
+    ch1 = int(max(1, min(w.D, target_s / 5 * probe_rate / threads / (w.L * w.N))))
+    w1 = w.replace(Bt=1, D=ch1)
+    inp1 = workloads.make_inputs(w1, seed=w.seed + 9)
+    t0 = time.perf_counter()
+    oracle.fwd(inp1["x"], inp1["delta"], inp1["A"], inp1["B"], inp1["C"], w.beta, w.alpha,
+               Dskip=inp1["Dskip"], threads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": sw.updates / dt, "unit": "state-updates/s", "cores": threads,
             "kind": "oracle",
             "sample": "fp64 C oracle forward, Bt=%d L=%d N=%d over %d of the %d channels "
                       "(%.3g state updates in %.1f s, OpenMP over channels)"
-                      % (sw.Bt, sw.L, sw.N, dsel, w.D, sw.updates, dt)}
+                      % (sw.Bt, sw.L, sw.N, dsel, w.D, sw.updates, dt),
+            "one_thread": {"value": w1.updates / dt1, "unit": "state-updates/s", "cores": 1,
+                           "sample": "batch row 0, L=%d N=%d, %d channels (%.3g state updates "
+                                     "in %.1f s)" % (w1.L, w1.N, ch1, w1.updates, dt1)}}
 
 
 def pmc_summary(fetch_csv, write_csv, kernel_substr, name, command):
@@ -412,7 +481,7 @@ def main(argv=None):
     w = workloads.WORKLOADS[args.workload]
     if w.direction != "fwd":
         raise SystemExit("--workload must be a forward workload")
-    ms, per, plan = bench_fwd(w, args.steps, args.warmup, stream)
+    ms, per, plan, fwd_fn, fwd_mem = bench_fwd(w, args.steps, args.warmup, stream)
     fwd_warmup_run = last_warmup
     sec = ms / 1e3
     beta0 = w.beta == 0.0
@@ -432,30 +501,47 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic the path computes in; the I/O dtype is config.io
         "dtype": "f32",
         "data": "synthetic (seeded; distributions of the workload recipe)",
         "config": {"workload": "%s: forward scan, Mamba-1.4B layer shape" % w.name if w.name == "m1p4b"
                    else "%s: forward scan" % w.name,
-                   "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io, "beta": w.beta,
-                   "alpha": w.alpha, "dskip": w.dskip, "plan": plan},
-        "roofline": {"bound": "alu", "achieved": achieved_slots, "peak": VALU_PEAK_TSLOTS,
-                     "unit": "T VALU slots/s", "frac": achieved_slots / VALU_PEAK_TSLOTS,
-                     "traffic": measured_traffic(kname),
-                     "slots_per_update": SLOTS_PER_UPDATE[beta0],
+                   "Bt": w.Bt, "L": w.L, "D": w.D, "N": w.N, "io": w.io, "state": "f32",
+                   "beta": w.beta, "alpha": w.alpha, "dskip": w.dskip, "plan": plan},
+        # the forward is one kernel at this shape: the call's time on its stream is the kernel's
+        "roofline": {"bound": "hbm", "achieved": abytes / sec / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": abytes / sec / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kname), "algorithmic_bytes": abytes,
                      "kernel_ms_mean": ms, "kernel_ms_min": min(per)},
-        "hbm": {"algorithmic_bytes": abytes, "achieved_GBs": abytes / sec / 1e9,
-                "peak_GBs": HBM_PEAK_GBS, "frac": abytes / sec / 1e9 / HBM_PEAK_GBS},
+        "alu": {"achieved": achieved_slots, "peak": VALU_PEAK_TSLOTS,
+                "unit": "T VALU lane-slots/s", "frac": achieved_slots / VALU_PEAK_TSLOTS,
+                "slots_per_update": SLOTS_PER_UPDATE[beta0],
+                "peak_from": "157.3 TFLOP/s fp32 vector / 2 (no packed FP32) / 2 (FMA)"},
+        "memory": fwd_mem,
     }
+    rec["timing"] = timing_record(fwd_fn, stream)
     if args.bwd_workload != "none":
         wb = workloads.WORKLOADS[args.bwd_workload]
-        bms, bper, bplan = bench_bwd(wb, max(3, args.steps // 2), max(1, args.warmup // 2), stream)
+        bms, bper, bplan, bwd_fn, bwd_mem = bench_bwd(wb, max(3, args.steps // 2),
+                                                      max(1, args.warmup // 2), stream)
         bbytes = alg_bytes_bwd(wb)
         rec["bwd"] = {"workload": "%s: backward, Bt=%d L=%d D=%d N=%d io=%s beta=%g"
                                   % (wb.name, wb.Bt, wb.L, wb.D, wb.N, wb.io, wb.beta),
                       "ms_per_call": bms, "state_updates_per_s": wb.updates / (bms / 1e3),
                       "algorithmic_GBs": bbytes / (bms / 1e3) / 1e9,
                       "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "plan": bplan,
-                      "traffic": measured_traffic("bwd_%s" % wb.name)}
+                      "traffic": measured_traffic("bwd_%s" % wb.name), "memory": bwd_mem,
+                      "timing": timing_record(bwd_fn, stream)}
+        del bwd_fn
+        import torch
+        torch.cuda.empty_cache()
+    # latency of the smallest workload (launch-bound): median and minimum over 50 calls
+    wt = workloads.WORKLOADS["tiny"]
+    _, tper, tplan, tiny_fn, tiny_mem = bench_fwd(wt, 10, 10, stream)
+    tt = per_call_ms(tiny_fn, stream, 50)
+    rec["latency_tiny"] = {"workload": "tiny: forward, Bt=1 L=64 D=4 N=4 io=f32 beta=0.9",
+                           "median_ms": float(np.median(tt)), "min_ms": float(np.min(tt)),
+                           "calls": 50, "plan": tplan, "memory": tiny_mem}
     if args.step_workload != "none":
         ws_ = workloads.WORKLOADS[args.step_workload]
         sms, sper = bench_step(ws_, max(5, args.steps), max(2, args.warmup // 2), stream)
@@ -475,7 +561,7 @@ def main(argv=None):
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         cms, _ = timed(lambda: dst.copy_(src), stream, 10, 3)
-        rec["hbm"]["copy_probe_GBs"] = 2 * src.numel() / (cms / 1e3) / 1e9
+        rec["roofline"]["copy_probe_GBs"] = 2 * src.numel() / (cms / 1e3) / 1e9
         del src, dst
         torch.cuda.empty_cache()
     if not args.no_configs:

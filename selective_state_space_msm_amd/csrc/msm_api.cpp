@@ -424,6 +424,9 @@ msm_status fwd_impl(const void* x, const void* delta, const float* A, const void
   a.beta = beta;
   a.alpha = alpha;
   a.beta_pow_tc = (float)pow((double)beta, (double)Tc);
+  // rows after which the velocity's share beta^rows is below 2^-kWinLog2 (beta = 0: none)
+  a.win_rows = beta > 0.f ? (int64_t)ceil(msm::kWinLog2 / -log2((double)beta)) : 0;
+  if (a.win_rows < 0 || a.win_rows > L) a.win_rows = L;
   a.cus = 256;  // MI355X; replaced by the current device's count when the runtime reports it
   {
     int dev = 0, cus = 0;

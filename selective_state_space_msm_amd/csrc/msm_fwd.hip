@@ -71,7 +71,7 @@ void fwd_kernel(const FwdArgs p) {
   const int64_t b = blk % (uint32_t)p.Bt;
   const int k = (int)(blk / (uint32_t)p.Bt);
   const int64_t L = p.L, D = p.D, N = p.N;
-  const int64_t t0 = (int64_t)k * p.Tc;
+  int64_t t0 = (int64_t)k * p.Tc;
   const int64_t t1 = (t0 + p.Tc < L) ? t0 + p.Tc : L;
   const int d = cb * kWave + lane;
   const bool dvalid = d < D;
@@ -117,6 +117,54 @@ void fwd_kernel(const FwdArgs p) {
           }
           h[j] = hn;
         }
+      }
+    }
+  }
+
+  // ---- summaries: the window of the chunk that decides its end state ----
+  // A chunk's end state is its map applied to the start state plus the part written inside
+  // it.  The start state's share shrinks by prod a_t = 2^(A2 sum delta) for h and beta^rows for
+  // v, so once both fall below 2^-kWinLog2 over the chunk's last rows, those rows alone give the
+  // end state: everything written before them, and the start state, reach the end scaled by
+  // less than 2^-kWinLog2 (relative to their size there).  The window is found by summing
+  // delta backwards from the chunk end, a tile at a time, until every channel of the workgroup
+  // meets the bound for its slowest state (and at least win_rows rows for beta).  A truncated
+  // summary then maps any start state to zero: q = 0 and sum delta = +inf (r = 0).
+  bool trunc = false;
+  if (SUMMARY && p.win_rows < t1 - t0) {
+    float amin = INFINITY;  // slowest decay of this lane's channel, |A| log2 e
+    for (int64_t n = 0; n < N; ++n) amin = fminf(amin, -p.A[dl * N + n] * kLog2e);
+    // channels past D only repeat channel D - 1
+    const uint32_t rb = (uint32_t)(D * T::es);
+    const auto rdw = make_rsrc(static_cast<const char*>(p.delta) + (b * L + t0) * D * T::es,
+                               (t1 - t0) * D * T::es);
+    float acc = 0.f;
+    // a state that does not decay (A >= 0) needs the whole chunk: no search
+    int64_t w0 = __syncthreads_and(amin > 0.f) ? t1 : t0;
+    while (w0 > t0) {
+      // rows 2g, 2g + 1 of the tile ending at w0, channel dl, summed over the S wavefronts
+      const int64_t tb = w0 - kTile;
+      float part = 0.f;
+      for (int r = 2 * g; r < kTile; r += 2 * S) {
+        const uint32_t o0 = (uint32_t)((tb - t0 + r) * rb + (int64_t)dl * T::es);
+        float d0 = T::widen(T::bload(rdw, o0, 0u)), d1 = T::widen(T::bload(rdw, o0 + rb, 0u));
+        if (EXT) {
+          const float u0 = d0 + dbias, u1 = d1 + dbias;
+          d0 = softplus ? softplus_f(u0) : u0;
+          d1 = softplus ? softplus_f(u1) : u1;
+        }
+        part += d0 + d1;
+      }
+      xdl[0][g][lane].x = part;
+      __syncthreads();
+      for (int gg = 0; gg < S; ++gg) acc += xdl[0][gg][lane].x;
+      w0 = tb;
+      const bool mine = amin * acc >= kWinLog2 && t1 - w0 >= p.win_rows;
+      __syncthreads();  // every wavefront has read the partial sums before they are rewritten
+      if (__syncthreads_and(mine)) {
+        trunc = w0 > t0;
+        t0 = w0;
+        break;
       }
     }
   }
@@ -407,11 +455,11 @@ void fwd_kernel(const FwdArgs p) {
           p.s_bh[idx] = h[j];
           if (!BETA0) {
             p.s_bv[idx] = v[j];
-            p.s_q[idx] = q[j];
+            p.s_q[idx] = trunc ? 0.f : q[j];
           }
         }
       }
-      if (g == 0) p.s_sd[base * D + d] = sd;
+      if (g == 0) p.s_sd[base * D + d] = trunc ? INFINITY : sd;
     }
   } else if (k == p.G - 1 && dvalid) {
 #pragma unroll

@@ -13,6 +13,8 @@ constexpr int kMaxChunks = 64;   // upper bound on time chunks (sizes the worksp
 constexpr int kMaxN = 64;        // states supported per channel
 constexpr int kBwdTile = 16;     // time steps recomputed per register tile in the backward
 constexpr int kBwdChans = 32;    // channels per workgroup in the backward (half a wavefront)
+// A chunk summary ignores rows whose share of the chunk's end state is below 2^-kWinLog2.
+constexpr float kWinLog2 = 32.f;
 
 struct FwdArgs {
   const void* x;
@@ -42,6 +44,7 @@ struct FwdArgs {
   int32_t ncb;       // channel blocks of 64
   float beta, alpha;
   float beta_pow_tc;  // beta^Tc, the velocity decay across one full chunk
+  int64_t win_rows;   // rows over which beta^rows < 2^-kWinLog2 (a summary window's minimum)
   int32_t cus;        // compute units of the device (picks the LDS layout of the y partials)
 };
 

@@ -83,3 +83,10 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_valu_peak_follows_the_published_fp32_peak():
+    # 157.3 TFLOP/s fp32 vector, halved for unpacked FP32 and halved for the two flops of an FMA:
+    # the issue rate of 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz
+    assert abs(bench.VALU_PEAK_TSLOTS - 157.3 / 4) < 1e-9
+    assert abs(bench.VALU_PEAK_TSLOTS - 256 * 4 * 16 * 2.4e9 / 1e12) < 0.01

@@ -287,3 +287,42 @@ def test_side_stream_calls_match_current_stream():
     for k in ("dx", "ddelta", "dA", "dB", "dC", "dDskip"):
         assert np.array_equal(host(gr[k]), host(ref_g[k])), k
     del junk
+
+
+# ---- chunk summaries over a window of the chunk ----
+
+@pytest.mark.parametrize("case", ["window", "long-memory", "slow-velocity", "zoh-window"])
+def test_chunk_summary_windows(case):
+    """Chunked plans whose summaries may cover only the chunk's last rows (the rows after which
+    the start state's share is below 2^-32): steps large enough that a window is found
+    (delta = softplus(N(-2, 1)), about 150 rows), steps so small that the whole chunk is needed
+    (delta in [1e-5, 1e-4], the long-memory case), a velocity memory longer than a chunk
+    (beta = 0.99: 2207 rows for 2^-32), and the fused zero-order-hold build with windows.
+    Every output against the oracle."""
+    import selective_state_space_msm_amd as msm
+    w = W["m130m"].replace(Bt=2, L=8000, D=130, N=16, beta=0.99 if case == "slow-velocity" else 0.9,
+                           dskip=True)
+    inp = workloads.make_inputs(w, a_kind="random", seed=160)
+    rng = np.random.default_rng(161)
+    if case == "long-memory":
+        inp["delta"] = np.exp(rng.uniform(np.log(1e-5), np.log(1e-4),
+                                          size=inp["delta"].shape)).astype(np.float32)
+    else:
+        u = rng.normal(-2.0, 1.0, size=inp["delta"].shape)
+        inp["delta"] = np.log1p(np.exp(u)).astype(np.float32)
+    if case != "zoh-window":
+        for plan in ({"states_per_wave": 2, "chunks": 4}, {"states_per_wave": 4, "chunks": 7}):
+            check_full(inp, plan=plan, tag=case)
+        return
+    import torch
+    g = inputs_to_device(inp)
+    y, lh, lv = msm.msm_selective_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], inp["beta"],
+                                           inp["alpha"], g["Dskip"], zero_order_hold=True,
+                                           return_last_state=True,
+                                           plan={"states_per_wave": 2, "chunks": 5})
+    torch.cuda.synchronize()
+    oy, _, oh, ov = oracle.fused_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                     inp["beta"], inp["alpha"], Dskip=inp["Dskip"], zoh=True)
+    assert_close(host(y), oy, "f32", "zoh y windows")
+    assert_close(host(lh), oh, "f32", "zoh last_h windows")
+    assert_close(host(lv), ov, "f32", "zoh last_v windows")
