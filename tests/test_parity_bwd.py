@@ -97,12 +97,13 @@ def test_32_states(io, N, dskip):
     check_full(inp, tag="N=%d" % N)
 
 
-@pytest.mark.skip(reason="the single-launch half-wavefront backward at 64 padded states (N=33, "
-                         "K=2: 16 wavefronts per workgroup) stopped with an illegal memory access "
-                         "on MI355X; no out-of-bounds index was found on the CPU, so those "
-                         "instantiations are compiled out; 64 states now run as two launches of "
-                         "the 32-state plan (test_64_states_in_halves) or the full-wavefront "
-                         "kernel (test_many_states)")
+@pytest.mark.skip(reason="64 padded states in one half-wavefront launch (K=2: 16 wavefronts) "
+                         "need 172 KB of LDS, above the 160 KB of an MI355X workgroup, so the "
+                         "build has no such instantiation; a build of it once stopped with an "
+                         "illegal memory access (uncommitted, no out-of-bounds index found in the "
+                         "nearest committed form). 64 states run as two launches of the 32-state "
+                         "plan (test_64_states_in_halves) or in the full-wavefront kernel "
+                         "(test_many_states)")
 @pytest.mark.parametrize("K", [2, 4])
 @pytest.mark.parametrize("N", [33, 64])
 def test_half_wave_64_states(N, K):
