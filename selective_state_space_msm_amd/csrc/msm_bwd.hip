@@ -81,6 +81,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   __shared__ float2 xe[EXT ? 2 : 1][EXT ? TB : 1][CB];
   __shared__ float ypt[EXT ? 2 : 1][EXT ? S : 1][EXT ? TB : 1][CB];
   __shared__ double bred[EXT ? S : 1][CB];
+  // the forward pass of phase 1: (delta, delta x) per channel and step, alpha B per state group
+  // and step (rows padded to keep 16-byte reads aligned and spread over the banks)
+  __shared__ __attribute__((aligned(16))) float2 xd1[2][CB][TB + 2];
+  __shared__ __attribute__((aligned(16))) float b1[2][GS][TB * K + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -283,20 +287,27 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
       for (int r = 0; r < NPE; ++r) st.b[r] = T::bload(rb, bc_voff[r], 0u);
     };
+    // The forward here reads only (delta, delta x) and alpha B, so it stages them in their own
+    // layout: a channel's steps contiguous ((delta, delta x) of two steps per 16-byte read) and
+    // a state group's steps contiguous (alpha B of 4 / K steps per 16-byte read).  That is 12
+    // bytes per lane and step against 20 through the sweep's layout, which kept this loop
+    // waiting on LDS bandwidth.
     auto store1 = [&](const Set& st, int buf) {
 #pragma unroll
       for (int r = 0; r < NX; ++r) {
         const int i = tid + r * NTHR;
         if (NX * NTHR == XE || i < XE) {
           const float xv = T::widen(st.x[r]), dv = delta_eff(T::widen(st.d[r]));
-          xs[buf][i / CB][i % CB] = make_float4(xv, dv, 0.f, dv * xv);
+          xd1[buf][i % CB][i / CB] = make_float2(dv, dv * xv);
         }
       }
 #pragma unroll
       for (int r = 0; r < NPE; ++r) {
         const int i = tid + r * NTHR;
-        if (NPE * NTHR == BCE || i < BCE)
-          bs[buf][i / NPB][(i % NPB) / K][(i % NPB) % K] = T::widen(st.b[r]) * p.alpha;
+        if (NPE * NTHR == BCE || i < BCE) {
+          const int n = i % NPB;
+          b1[buf][n / K][(i / NPB) * K + n % K] = T::widen(st.b[r]) * p.alpha;
+        }
       }
     };
     // one step: checkpoint and compute `tile` (if it exists), refill `mine` with tile + 4,
@@ -317,10 +328,16 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
       load1(mine, tile + 4);
       if (live) {
         const int buf = (int)(tile & 1);
+        float4 dd[TB / 2], bq[TB * K / 4];
+#pragma unroll
+        for (int q = 0; q < TB / 2; ++q) dd[q] = *reinterpret_cast<const float4*>(&xd1[buf][ch][2 * q]);
+#pragma unroll
+        for (int q = 0; q < TB * K / 4; ++q) bq[q] = *reinterpret_cast<const float4*>(&b1[buf][gs][4 * q]);
+        const float* bf = reinterpret_cast<const float*>(bq);
 #pragma unroll
         for (int tt = 0; tt < TB; ++tt) {
-          const float4 r = xs[buf][tt][ch];
-          fstep(r.y, r.w, &bs[buf][tt][gs][0], nullptr, nullptr);
+          const float4 r = dd[tt / 2];
+          fstep((tt & 1) ? r.z : r.x, (tt & 1) ? r.w : r.y, bf + tt * K, nullptr, nullptr);
         }
       }
       store1(next, (int)((tile + 1) & 1));
