@@ -139,6 +139,8 @@ int64_t bwd_chans(int NP, int K) { return (NP == 64 && K == 4) ? kWave : msm::kB
 
 // The half-wavefront backward addresses one tile's checkpoints ([2][N][D] fp32) through one
 // buffer resource, whose extent is at most 2^31 - 1 bytes: 8 N D must stay below 2^31.
+constexpr int64_t kBwdMaxL = (int64_t)1 << 30;
+
 bool bwd_ckpt_ok(int64_t N, int64_t D) { return 8 * N * D < ((int64_t)1 << 31); }
 
 // 64 padded states as two halves of the 32-state plan address a tile of the first half's
@@ -531,6 +533,8 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   // up to 32 states the backward runs only in the half-wavefront kernel (64 states take the
   // full-wavefront one when the checkpoints are too large, see auto_bwd_plan)
   if (NP <= 32 && !bwd_ckpt_ok(N, D)) return MSM_ERR_UNSUPPORTED;
+  // the backward kernels index rows and tiles of a sequence in 32 bits
+  if (L >= kBwdMaxL) return MSM_ERR_UNSUPPORTED;
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);

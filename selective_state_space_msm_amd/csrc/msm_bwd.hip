@@ -134,6 +134,15 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const char* B0 = static_cast<const char*>(p.B) + b * tot_n;
   const char* C0 = static_cast<const char*>(p.C) + b * tot_n;
   const char* z0 = has_z ? static_cast<const char*>(p.z) + b * tot_d : x0;
+  // per-tile resources (tile_rsrc) span one tile's rows: 32-bit row indices and extents (the
+  // host keeps L below 2^30)
+  const int32_t L32 = (int32_t)L;
+  // (the clamp compiles to a vector med3: read back as a scalar, or every resource built from it
+  // would leave the scalar registers and each buffer access would loop over its lanes' values)
+  auto rows_at = [&](int64_t ts) {
+    return __builtin_amdgcn_readfirstlane(min(max(L32 - (int32_t)ts, 0), TB));
+  };
+  const uint32_t rb_d = (uint32_t)row_bytes, rb_n = (uint32_t)bc_row_bytes;
 
   // x, delta, dy of channels past D are staged as zeros (their offset is past every extent),
   // so those lanes carry zero gradients without further masking
@@ -149,21 +158,22 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
   raw xr[NX], dr[NX], gr[NX], zr[EXT ? NX : 1];
   auto x_load = [&](int64_t ts, bool with_dy) {
-    const auto rx = rows_rsrc(x0, ts, row_bytes, tot_d);
-    const auto rd = rows_rsrc(dl0, ts, row_bytes, tot_d);
+    const int32_t t32 = (int32_t)ts, nr = rows_at(ts);
+    const auto rx = tile_rsrc(x0, t32, nr, rb_d);
+    const auto rd = tile_rsrc(dl0, t32, nr, rb_d);
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       xr[r] = T::bload(rx, x_voff[r], 0u);
       dr[r] = T::bload(rd, x_voff[r], 0u);
     }
     if (with_dy) {
-      const auto rg = rows_rsrc(dy0, ts, row_bytes, tot_d);
+      const auto rg = tile_rsrc(dy0, t32, nr, rb_d);
 #pragma unroll
       for (int r = 0; r < NX; ++r) gr[r] = T::bload(rg, x_voff[r], 0u);
     }
     if (EXT) {
       // without a gate the loads read zeros through an empty resource
-      const auto rz = has_z ? rows_rsrc(z0, ts, row_bytes, tot_d) : make_rsrc(x0, 0);
+      const auto rz = tile_rsrc(z0, t32, has_z ? nr : 0, rb_d);
 #pragma unroll
       for (int r = 0; r < NX; ++r) zr[r] = T::bload(rz, x_voff[r], 0u);
     }
@@ -203,11 +213,12 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
   raw bre[NPE], cre[NPE];
   auto bc_load = [&](int64_t ts, bool with_c) {
-    const auto rb = rows_rsrc(B0, ts, bc_row_bytes, tot_n);
+    const int32_t t32 = (int32_t)ts, nr = rows_at(ts);
+    const auto rb = tile_rsrc(B0, t32, nr, rb_n);
 #pragma unroll
     for (int r = 0; r < NPE; ++r) bre[r] = T::bload(rb, bc_voff[r], 0u);
     if (with_c) {
-      const auto rc = rows_rsrc(C0, ts, bc_row_bytes, tot_n);
+      const auto rc = tile_rsrc(C0, t32, nr, rb_n);
 #pragma unroll
       for (int r = 0; r < NPE; ++r) cre[r] = T::bload(rc, bc_voff[r], 0u);
     }
@@ -235,9 +246,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     for (int w = 0; w < 2; ++w)
       ck_voff[w][j] = (dvalid && n < N) ? (uint32_t)(((w * N + n) * D + d) * 4) : 0x80000000u;
   }
+  const char* ck_b = reinterpret_cast<const char*>(p.ckpt) + b * NT * ck_tile_bytes;
+  const uint32_t ck_tb = (uint32_t)ck_tile_bytes;
   auto ck_rsrc = [&](int64_t tile) {
-    return make_rsrc(reinterpret_cast<const char*>(p.ckpt) + (b * NT + tile) * ck_tile_bytes,
-                     ck_tile_bytes);
+    return make_rsrc_u32(ck_b + (uint64_t)(uint32_t)tile * ck_tb, ck_tb);
   };
 
   // one forward step of the K states (recurrence only); c = delta * x.  The zero-order hold
@@ -276,9 +288,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     Set s0{}, s1{}, s2{}, s3{};
     auto load1 = [&](Set& st, int64_t tile) {
       const int64_t ts = tile * TB;
-      const auto rx = rows_rsrc(x0, ts, row_bytes, tot_d);
-      const auto rd = rows_rsrc(dl0, ts, row_bytes, tot_d);
-      const auto rb = rows_rsrc(B0, ts, bc_row_bytes, tot_n);
+      const int32_t t32 = (int32_t)ts, nr = rows_at(ts);
+      const auto rx = tile_rsrc(x0, t32, nr, rb_d);
+      const auto rd = tile_rsrc(dl0, t32, nr, rb_d);
+      const auto rb = tile_rsrc(B0, t32, nr, rb_n);
 #pragma unroll
       for (int r = 0; r < NX; ++r) {
         st.x[r] = T::bload(rx, x_voff[r], 0u);
@@ -392,23 +405,34 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const uint32_t vo_aq = dvalid ? (uint32_t)(((lane >= CB ? 1 : 0) * D + dl) * 8) : 0x80000000u;
   const uint32_t vo_dz32 = (dvalid && lane < CB) ? (uint32_t)dl * 4u : 0x80000000u;
   // xb: the LDS staging buffer that still holds the tile's inputs
-  auto finalize = [&](int64_t tile, int pb, bool valid, int xb) {
+  auto finalize = [&](int64_t tile, int pb, bool valid, int xb) __attribute__((always_inline)) {
     const int64_t ts = tile * TB;
     // an invalid tile gets empty resources: every store below is then dropped
-    const auto rdx = valid ? rows_rsrc(dx0, ts, row_bytes, tot_d) : make_rsrc(dx0, 0);
-    const auto rdd = valid ? rows_rsrc(ddl0, ts, row_bytes, tot_d) : make_rsrc(ddl0, 0);
-    const auto rdz = (valid && has_z) ? rows_rsrc(dz0, ts, row_bytes, tot_d) : make_rsrc(dz0, 0);
+    const int32_t t32 = valid ? (int32_t)ts : 0, nr = valid ? rows_at(ts) : 0;
+    const auto rdx = tile_rsrc(dx0, t32, nr, rb_d);
+    const auto rdd = tile_rsrc(ddl0, t32, nr, rb_d);
+    const auto rdz = tile_rsrc(dz0, t32, has_z ? nr : 0, rb_d);
     // split passes: the first half's sums, [L][2][D] fp64 (dx, ddelta) and [L][D] fp32 (dz)
-    const auto raq = (SPLIT && valid) ? rows_rsrc(aq0, ts, aq_row_bytes, aq_tot) : make_rsrc(aq0, 0);
-    const auto raz = (SPLIT && valid && has_z) ? rows_rsrc(az0, ts, D * 4, L * D * 4)
-                                               : make_rsrc(az0, 0);
+    const auto raq = tile_rsrc(aq0, t32, SPLIT ? nr : 0, (uint32_t)aq_row_bytes);
+    const auto raz = tile_rsrc(az0, t32, (SPLIT && has_z) ? nr : 0, (uint32_t)(D * 4));
+    // every partial of the wavefront's rows is read before the first sum, so the reads share
+    // one LDS round trip (summed as they arrive, the compiler waits on each in turn)
+    constexpr int FR = (TB + S - 1) / S;  // rows finished by this wavefront
+    float sp[FR][S];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) {
+      const int tt = r * S + g < TB ? r * S + g : TB - 1;
+#pragma unroll
+      for (int w = 0; w < S; ++w) sp[r][w] = spart[pb][w][tt][lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tr0 = 0; tr0 < TB; tr0 += S) {
       const int tt = tr0 + g;
       if (tr0 + S <= TB || tt < TB) {
-        double q = (double)spart[pb][0][tt][lane];
+        double q = (double)sp[tr0 / S][0];
 #pragma unroll
-        for (int w = 1; w < S; ++w) q += (double)spart[pb][w][tt][lane];
+        for (int w = 1; w < S; ++w) q += (double)sp[tr0 / S][w];
         // rows past the end of the sequence are past the extent: dropped
         const uint32_t ro = (uint32_t)(tt * row_bytes);
         if constexpr (SPLIT == 0) {
@@ -469,7 +493,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 
   // dB / dC partials of this workgroup, [L][2][NPB] fp32 at dbc: a resource per tile and a
   // constant offset per lane and reduce block (lane l of a half holds value l & 31)
-  const int64_t dbc_row_bytes = 2 * NPD * 4, dbc_tot = L * dbc_row_bytes;
+  const int64_t dbc_row_bytes = 2 * NPD * 4;
   uint32_t dbc_voff[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -523,7 +547,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     // dropped through an empty resource and its sums are not kept.  No memory operation
     // depends on a branch, so the compiler can count the loads still in flight exactly.
     const int64_t ts = tile * TB;
-    const auto rdbc = live ? rows_rsrc(dbc, ts, dbc_row_bytes, dbc_tot) : make_rsrc(dbc, 0);
+    const auto rdbc = tile_rsrc(dbc, live ? (int32_t)ts : 0, live ? rows_at(ts) : 0,
+                                (uint32_t)dbc_row_bytes);
     // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt} (and for
     // the zero-order hold phi and psi of each step)
     float hs[TB + 1][K], av[TB][K];

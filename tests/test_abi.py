@@ -145,6 +145,9 @@ def test_bwd_argument_validation_never_launches(lib):
     assert call(N=17, D=(1 << 31) // (8 * 17) + 1) == UNSUPPORTED
     assert call(N=16, D=1 << 24) == UNSUPPORTED
     assert call(N=32, D=(1 << 23) - 64, plan=msm._Plan(2, 1)) == WORKSPACE  # within the limit
+    # rows and tiles of a sequence are indexed in 32 bits: L below 2^30
+    assert call(L=1 << 30) == UNSUPPORTED
+    assert call(L=(1 << 30) - 1, wsb=16) == WORKSPACE
 
 
 def test_state_entry_points_validation_never_launches(lib):
