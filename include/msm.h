@@ -148,7 +148,8 @@ msm_status msm_scan_fwd_noalloc(const void* x, const void* delta, const float* A
 /* Backward scan: gradients of sum(dy * y).  dx, ddelta, dB, dC, dA are overwritten (not
  * accumulated).  dDskip is required exactly when Dskip is non-NULL.  The forward is recomputed
  * inside; no saved activations are needed.  Same requirements as msm_scan_fwd, and L < 2^30
- * (a longer sequence returns MSM_ERR_UNSUPPORTED: split it with msm_scan_bwd_state). */
+ * (a longer sequence returns MSM_ERR_UNSUPPORTED: split it with msm_scan_bwd_state) and
+ * 64 * D * (element size) < 2^31 (D < 2^23 channels with fp32 I/O). */
 msm_status msm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
                         const void* C, const float* Dskip, const void* dy, void* dx,
                         void* ddelta, float* dA, void* dB, void* dC, float* dDskip, int64_t Bt,

@@ -533,8 +533,11 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   // up to 32 states the backward runs only in the half-wavefront kernel (64 states take the
   // full-wavefront one when the checkpoints are too large, see auto_bwd_plan)
   if (NP <= 32 && !bwd_ckpt_ok(N, D)) return MSM_ERR_UNSUPPORTED;
-  // the backward kernels index rows and tiles of a sequence in 32 bits
+  // the backward kernels index rows and tiles of a sequence in 32 bits, and address a step of
+  // their forward pass (4 tiles of (Bt, L, D) rows) with 32-bit offsets
   if (L >= kBwdMaxL) return MSM_ERR_UNSUPPORTED;
+  if ((int64_t)4 * msm::kBwdTile * D * (io == MSM_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+    return MSM_ERR_UNSUPPORTED;
 
   const size_t es = io == MSM_BF16 ? 2 : 4;
   const size_t nxd = (size_t)(Bt * L * D), nbc = (size_t)(Bt * L * N);

@@ -75,16 +75,30 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   __shared__ float4 xs[2][TB][CB];          // x, delta, dy, delta * x
   __shared__ float bs[2][TB][GS][K];        // alpha B
   __shared__ double cs64[2][TB][GS][K];     // C, widened for the adjoint recurrence
-  __shared__ float spart[2][S][TB][kWave];  // per wavefront: dx (lanes < 32) | ddelta partials
   // fused variant: (dy silu'(z), logistic(delta + bias)) per staged element, the per-wavefront
   // partials of the output before the gate, and the bias-gradient partials
   __shared__ float2 xe[EXT ? 2 : 1][EXT ? TB : 1][CB];
   __shared__ float ypt[EXT ? 2 : 1][EXT ? S : 1][EXT ? TB : 1][CB];
   __shared__ double bred[EXT ? S : 1][CB];
-  // the forward pass of phase 1: (delta, delta x) per channel and step, alpha B per state group
-  // and step (rows padded to keep 16-byte reads aligned and spread over the banks)
-  __shared__ __attribute__((aligned(16))) float2 xd1[2][CB][TB + 2];
-  __shared__ __attribute__((aligned(16))) float b1[2][GS][TB * K + 4];
+  // Phase 1 stages R1 rows at a time: (delta, delta x) per channel and alpha B per state group,
+  // each with its rows contiguous (padded to keep 16-byte reads aligned and spread over the
+  // banks).  The sweep's per-wavefront dx (lanes < 32) | ddelta partials reuse that LDS: phase 1
+  // ends with a barrier.
+  constexpr int TP = S >= 4 ? 4 : 1;  // checkpoint tiles per phase-1 step
+  constexpr int R1 = TP * TB;
+  struct Ph1 {
+    float2 xd1[2][CB][R1 + 2];
+    float b1[2][GS][R1 * K + 4];
+  };
+  struct Ph2 {
+    float spart[2][S][TB][kWave];
+  };
+  union Ph12 {
+    Ph1 f;
+    Ph2 r;
+  };
+  __shared__ __attribute__((aligned(16))) Ph12 ph;
+  auto& spart = ph.r.spart;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -139,9 +153,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const int32_t L32 = (int32_t)L;
   // (the clamp compiles to a vector med3: read back as a scalar, or every resource built from it
   // would leave the scalar registers and each buffer access would loop over its lanes' values)
-  auto rows_at = [&](int64_t ts) {
-    return __builtin_amdgcn_readfirstlane(min(max(L32 - (int32_t)ts, 0), TB));
+  auto rows_in = [&](int64_t ts, int rmax) {
+    return __builtin_amdgcn_readfirstlane(min(max(L32 - (int32_t)ts, 0), rmax));
   };
+  auto rows_at = [&](int64_t ts) { return rows_in(ts, TB); };
   const uint32_t rb_d = (uint32_t)row_bytes, rb_n = (uint32_t)bc_row_bytes;
 
   // x, delta, dy of channels past D are staged as zeros (their offset is past every extent),
@@ -277,28 +292,48 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   };
 
   // ---------------- phase 1: forward over the whole sequence, checkpoint every tile ----
-  // A tile's arithmetic here is short next to the latency of its loads, so the loads run four
-  // tiles ahead through a ring of register sets: tile k is loaded into set k % 4 during tile
-  // k - 4 and staged into LDS at the end of tile k - 1.  The loop starts at tile -4 (steps
-  // with a negative tile only load and stage), so every step has the same memory pattern.
+  // Steps of R1 rows (TP checkpoint tiles): one barrier and one set of resources per step.
+  // The loads of step k + 2 are issued at the start of step k into one of two register sets
+  // (the one step k's data was staged from) and staged into LDS at the end of step k + 1.  The
+  // first step is staged before the loop, and every step of the loop computes: steps past the
+  // end read zeros, advance a state nothing reads afterwards and drop their checkpoint stores
+  // (no memory operation depends on a branch, so the compiler counts the loads in flight
+  // exactly).
   {
+    constexpr int XE1 = R1 * CB, NX1 = (XE1 + NTHR - 1) / NTHR;
+    constexpr int BE1 = R1 * NPB, NB1 = (BE1 + NTHR - 1) / NTHR;
+    uint32_t x1_voff[NX1], b1_voff[NB1];
+#pragma unroll
+    for (int r = 0; r < NX1; ++r) {
+      const int i = tid + r * NTHR;
+      const int ic = i < XE1 ? i : XE1 - 1;
+      const int dch = cb * CB + ic % CB;
+      x1_voff[r] = dch < D ? (uint32_t)((ic / CB) * row_bytes + dch * T::es) : 0x80000000u;
+    }
+#pragma unroll
+    for (int r = 0; r < NB1; ++r) {
+      const int i = tid + r * NTHR;
+      const int ic = i < BE1 ? i : BE1 - 1;
+      const int n = n0 + ic % NPB;
+      b1_voff[r] = n < N ? (uint32_t)(((ic / NPB) * N + n) * T::es) : 0x80000000u;
+    }
     struct Set {
-      raw x[NX], d[NX], b[NPE];
+      raw x[NX1], d[NX1], b[NB1];
     };
-    Set s0{}, s1{}, s2{}, s3{};
-    auto load1 = [&](Set& st, int64_t tile) {
-      const int64_t ts = tile * TB;
-      const int32_t t32 = (int32_t)ts, nr = rows_at(ts);
+    Set s0{}, s1{};
+    auto load1 = [&](Set& st, int64_t k) {
+      const int64_t ts = k * R1;
+      const int32_t t32 = (int32_t)ts, nr = rows_in(ts, R1);
       const auto rx = tile_rsrc(x0, t32, nr, rb_d);
       const auto rd = tile_rsrc(dl0, t32, nr, rb_d);
       const auto rb = tile_rsrc(B0, t32, nr, rb_n);
 #pragma unroll
-      for (int r = 0; r < NX; ++r) {
-        st.x[r] = T::bload(rx, x_voff[r], 0u);
-        st.d[r] = T::bload(rd, x_voff[r], 0u);
+      for (int r = 0; r < NX1; ++r) {
+        st.x[r] = T::bload(rx, x1_voff[r], 0u);
+        st.d[r] = T::bload(rd, x1_voff[r], 0u);
       }
 #pragma unroll
-      for (int r = 0; r < NPE; ++r) st.b[r] = T::bload(rb, bc_voff[r], 0u);
+      for (int r = 0; r < NB1; ++r) st.b[r] = T::bload(rb, b1_voff[r], 0u);
     };
     // The forward here reads only (delta, delta x) and alpha B, so it stages them in their own
     // layout: a channel's steps contiguous ((delta, delta x) of two steps per 16-byte read) and
@@ -307,45 +342,46 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     // waiting on LDS bandwidth.
     auto store1 = [&](const Set& st, int buf) {
 #pragma unroll
-      for (int r = 0; r < NX; ++r) {
+      for (int r = 0; r < NX1; ++r) {
         const int i = tid + r * NTHR;
-        if (NX * NTHR == XE || i < XE) {
+        if (NX1 * NTHR == XE1 || i < XE1) {
           const float xv = T::widen(st.x[r]), dv = delta_eff(T::widen(st.d[r]));
-          xd1[buf][i % CB][i / CB] = make_float2(dv, dv * xv);
+          ph.f.xd1[buf][i % CB][i / CB] = make_float2(dv, dv * xv);
         }
       }
 #pragma unroll
-      for (int r = 0; r < NPE; ++r) {
+      for (int r = 0; r < NB1; ++r) {
         const int i = tid + r * NTHR;
-        if (NPE * NTHR == BCE || i < BCE) {
+        if (NB1 * NTHR == BE1 || i < BE1) {
           const int n = i % NPB;
-          b1[buf][n / K][(i / NPB) * K + n % K] = T::widen(st.b[r]) * p.alpha;
+          ph.f.b1[buf][n / K][(i / NPB) * K + n % K] = T::widen(st.b[r]) * p.alpha;
         }
       }
     };
-    // one step: checkpoint and compute `tile` (if it exists), refill `mine` with tile + 4,
-    // stage `next` (tile + 1) into the other LDS buffer.  Loads and stores are unconditional
-    // (past the end the resources read zeros and the staged buffer goes unused).
-    auto step1 = [&](int64_t tile, Set& mine, const Set& next) {
-      const bool live = tile >= 0 && tile < NT;
-      {
-        // a step without a tile stores through an empty resource (dropped): a store under a
-        // branch would not be counted in the wait for this step's loads, three steps later
-        const auto rc = live ? ck_rsrc(tile) : make_rsrc(p.ckpt, 0);
+    // step k: refill `ld` with step k + 2, checkpoint and compute the TP tiles of step k, stage
+    // step k + 1 from `st` into the other LDS buffer
+    auto step1 = [&](int64_t k, Set& ld, const Set& st) {
+      load1(ld, k + 2);
+      const int buf = (int)(k & 1);
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-          io<float>::bstore(rc, ck_voff[0][j], 0u, v[j]);
-          io<float>::bstore(rc, ck_voff[1][j], 0u, h[j]);
+      for (int q = 0; q < TP; ++q) {
+        const int64_t tile = k * TP + q;
+        {
+          // tiles past the last one store through an empty resource (dropped)
+          const auto rc = tile < NT ? ck_rsrc(tile) : make_rsrc(p.ckpt, 0);
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            io<float>::bstore(rc, ck_voff[0][j], 0u, v[j]);
+            io<float>::bstore(rc, ck_voff[1][j], 0u, h[j]);
+          }
         }
-      }
-      load1(mine, tile + 4);
-      if (live) {
-        const int buf = (int)(tile & 1);
         float4 dd[TB / 2], bq[TB * K / 4];
 #pragma unroll
-        for (int q = 0; q < TB / 2; ++q) dd[q] = *reinterpret_cast<const float4*>(&xd1[buf][ch][2 * q]);
+        for (int i = 0; i < TB / 2; ++i)
+          dd[i] = *reinterpret_cast<const float4*>(&ph.f.xd1[buf][ch][q * TB + 2 * i]);
 #pragma unroll
-        for (int q = 0; q < TB * K / 4; ++q) bq[q] = *reinterpret_cast<const float4*>(&b1[buf][gs][4 * q]);
+        for (int i = 0; i < TB * K / 4; ++i)
+          bq[i] = *reinterpret_cast<const float4*>(&ph.f.b1[buf][gs][q * TB * K + 4 * i]);
         const float* bf = reinterpret_cast<const float*>(bq);
 #pragma unroll
         for (int tt = 0; tt < TB; ++tt) {
@@ -353,16 +389,18 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           fstep((tt & 1) ? r.z : r.x, (tt & 1) ? r.w : r.y, bf + tt * K, nullptr, nullptr);
         }
       }
-      store1(next, (int)((tile + 1) & 1));
+      store1(st, (int)((k + 1) & 1));
       __syncthreads();
     };
-    // whole groups of four steps (up to three idle steps at the end): a single loop exit
-    // keeps the compiler's count of loads in flight exact at the loop head
-    for (int64_t t0 = -4; t0 < NT; t0 += 4) {
-      step1(t0, s0, s1);
-      step1(t0 + 1, s1, s2);
-      step1(t0 + 2, s2, s3);
-      step1(t0 + 3, s3, s0);
+    const int64_t NS = (NT + TP - 1) / TP;  // phase-1 steps
+    load1(s0, 0);
+    load1(s1, 1);
+    store1(s0, 0);
+    __syncthreads();
+    // pairs of steps so the two register sets alternate without copies; one loop exit
+    for (int64_t k = 0; k < NS; k += 2) {
+      step1(k, s0, s1);
+      step1(k + 1, s1, s0);
     }
   }
 

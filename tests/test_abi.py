@@ -148,6 +148,9 @@ def test_bwd_argument_validation_never_launches(lib):
     # rows and tiles of a sequence are indexed in 32 bits: L below 2^30
     assert call(L=1 << 30) == UNSUPPORTED
     assert call(L=(1 << 30) - 1, wsb=16) == WORKSPACE
+    # its forward pass addresses 64 rows of (Bt, L, D) arrays with 32-bit offsets
+    assert call(N=4, D=1 << 23) == UNSUPPORTED
+    assert call(N=4, D=1 << 23, io=1, wsb=16) == WORKSPACE
 
 
 def test_state_entry_points_validation_never_launches(lib):
