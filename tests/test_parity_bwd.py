@@ -62,6 +62,17 @@ def test_small_ragged(io, K, beta, alpha, dskip):
     check_full(inp, plan={"states_per_wave": K}, tag="small")
 
 
+@pytest.mark.parametrize("K", [1, 2])
+@pytest.mark.parametrize("L", [64, 65, 193, 320])
+def test_forward_pass_step_boundaries(K, L):
+    # the backward's forward pass stages 64 rows (four checkpoint tiles) per step when a
+    # workgroup has four or more wavefronts: sequences of whole steps, one row past a step, a
+    # ragged last tile in a fourth step, and an odd number of whole steps
+    inp = workloads.make_inputs(SMALL.replace(L=L, D=40, dskip=True), a_kind="random",
+                                seed=90 + L)
+    check_full(inp, plan={"states_per_wave": K}, tag="L=%d" % L)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N,dskip", [(33, True), (48, False), (64, True)])
 def test_64_states_in_halves(io, N, dskip):
