@@ -74,6 +74,19 @@ __device__ __forceinline__ float zoh_phi_fwd(float u, float a) {
   const float q = (a - 1.f) * rcp_fast(u);
   return fabsf(u) < 0.125f ? p : q;
 }
+// The forward's write coefficient g = delta phi(delta A) = (e^(delta A) - 1) / A itself, from
+// arg = delta A log2 e, a = 2^arg and invA = 1 / A (0 for A = 0).  Below |delta A| = 1/8 it is
+// delta times the same degree-4 series, evaluated in arg (coefficient k is ln 2^k / (k + 1)!);
+// above, (a - 1) / A = a invA - invA in one FMA, with the same rounding as (a - 1) / u above:
+// no reciprocal per update.
+__device__ __forceinline__ float zoh_g_fwd(float arg, float a, float delta, float invA) {
+  float p = fmaf(arg, 0.0019236258215256953f, 0.013876027166205394f);
+  p = fmaf(p, arg, 0.08007550231970023f);
+  p = fmaf(p, arg, 0.34657359027997264f);
+  p = fmaf(p, arg, 1.f);
+  const float q = fmaf(a, invA, -invA);
+  return fabsf(arg) < 0.18033688f ? delta * p : q;
+}
 __device__ __forceinline__ float zoh_psi(float u, float a, float phi) {
   float p = fmaf(u, 1.f / 5760.f, 1.f / 840.f);
   p = fmaf(p, u, 1.f / 144.f);

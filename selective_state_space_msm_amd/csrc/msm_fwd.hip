@@ -79,10 +79,13 @@ void fwd_kernel(const FwdArgs p) {
   const float beta = p.beta;
 
   float A2[K], v[K], h[K], q[K];
+  float invA[EXT == 2 ? K : 1];  // zero-order hold: 1 / A (0 for A = 0 and padded states)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int64_t n = (int64_t)g * K + j;
-    A2[j] = n < N ? p.A[dl * N + n] * kLog2e : 0.f;
+    const float an = n < N ? p.A[dl * N + n] : 0.f;
+    A2[j] = an * kLog2e;
+    if (EXT == 2) invA[EXT == 2 ? j : 0] = an != 0.f ? 1.f / an : 0.f;
     // the scan starts at the given state; chunk summaries are maps from a zero start
     const int64_t si = (b * D + dl) * N + n;
     v[j] = (!SUMMARY && p.v0 && n < N) ? p.v0[si] : 0.f;
@@ -289,7 +292,7 @@ void fwd_kernel(const FwdArgs p) {
         if (EXT) {
           const float u = dv + dbias;
           const float de = softplus ? softplus_f(u) : u;
-          xdl[buf][i / kWave][i % kWave] = make_float2(de, de * xv);
+          xdl[buf][i / kWave][i % kWave] = make_float2(de, ZOH ? xv : de * xv);
         } else {
           xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
         }
@@ -314,8 +317,10 @@ void fwd_kernel(const FwdArgs p) {
     for (int j = 0; j < K; ++j) {
       const float arg = dv * A2[j];
       const float a = exp2_fast(arg);
+      // the write: c B with c = delta x, or with the zero-order hold x B g (c = x staged) for
+      // g = delta phi(delta A)
       float w = c * bc[j];
-      if (ZOH) w *= zoh_phi_fwd(arg * kLn2, a);  // g = delta phi(delta A) instead of delta
+      if (ZOH) w *= zoh_g_fwd(arg, a, dv, invA[ZOH ? j : 0]);
       if (BETA0)
         v[j] = w;
       else
