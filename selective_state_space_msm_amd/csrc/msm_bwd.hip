@@ -118,12 +118,14 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const int NPD = SPLIT ? p.NP : NPB;   // states per row of the dB / dC partials
 
   float A2[K], Af[K], v[K], h[K];
+  float invA[EXT == 2 ? K : 1];  // zero-order hold: 1 / A (0 for A = 0 and padded states)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int64_t n = n0 + (int64_t)gs * K + j;
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     Af[j] = an;
+    if (EXT == 2) invA[EXT == 2 ? j : 0] = an != 0.f ? 1.f / an : 0.f;
     // the forward starts at the given initial state
     const int64_t si = (b * D + dl) * N + n;
     v[j] = (p.v0 && dvalid && n < N) ? p.v0[si] : 0.f;
@@ -267,21 +269,22 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     return make_rsrc_u32(ck_b + (uint64_t)(uint32_t)tile * ck_tb, ck_tb);
   };
 
-  // one forward step of the K states (recurrence only); c = delta * x.  The zero-order hold
-  // also hands out phi and psi of the step for the reverse sweep (ph_out / ps_out).
+  // one forward step of the K states (recurrence only); c = delta * x, or x with the
+  // zero-order hold, whose write is x B g.  That variant also hands out g = delta phi(delta A)
+  // and dg/dA of the step for the reverse sweep (g_out / gA_out).
   auto fstep = [&](float dv, float c, const float* bb, float* a_out, float* h_out,
-                   float* ph_out = nullptr, float* ps_out = nullptr) {
+                   float* g_out = nullptr, float* gA_out = nullptr) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float arg = dv * A2[j];
       const float a = exp2_fast(arg);
       float w = c * bb[j];
       if (ZOH) {
-        const float ph = zoh_phi(arg * kLn2, a);
-        w *= ph;
-        if (ph_out) {
-          ph_out[j] = ph;
-          ps_out[j] = zoh_psi(arg * kLn2, a, ph);
+        const float gz = zoh_g_bwd(arg, a, dv, invA[ZOH ? j : 0]);
+        w *= gz;
+        if (g_out) {
+          g_out[j] = gz;
+          gA_out[j] = zoh_gA_bwd(arg, a, dv, invA[ZOH ? j : 0], gz);
         }
       }
       v[j] = BETA0 ? w : fmaf(beta, v[j], w);
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         const int i = tid + r * NTHR;
         if (NX1 * NTHR == XE1 || i < XE1) {
           const float xv = T::widen(st.x[r]), dv = delta_eff(T::widen(st.d[r]));
-          ph.f.xd1[buf][i % CB][i / CB] = make_float2(dv, dv * xv);
+          ph.f.xd1[buf][i % CB][i / CB] = make_float2(dv, ZOH ? xv : dv * xv);
         }
       }
 #pragma unroll
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     const auto rdbc = tile_rsrc(dbc, live ? (int32_t)ts : 0, live ? rows_at(ts) : 0,
                                 (uint32_t)dbc_row_bytes);
     // recompute the tile from its checkpoint: hs[tt] = h_{ts+tt-1}, av[tt] = a_{ts+tt} (and for
-    // the zero-order hold phi and psi of each step)
+    // the zero-order hold g and dg/dA of each step in phs, pss)
     float hs[TB + 1][K], av[TB][K];
     float phs[ZOH ? TB : 1][K], pss[ZOH ? TB : 1][K];
 #pragma unroll
@@ -600,8 +603,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       const float4 r = xs[buf][tt][ch];
-      fstep(r.y, r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1], ZOH ? phs[ZOH ? tt : 0] : nullptr,
-            ZOH ? pss[ZOH ? tt : 0] : nullptr);
+      fstep(r.y, ZOH ? r.x : r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1],
+            ZOH ? phs[ZOH ? tt : 0] : nullptr, ZOH ? pss[ZOH ? tt : 0] : nullptr);
     }
 
     float dAt[K];
@@ -635,19 +638,19 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
             p1 = j == 0 ? bs[buf][tt][gs][j] * gvf : fmaf(bs[buf][tt][gs][j], gvf, p1);
             vals[(tb * 2 + 0) * K + j] = c * gvf;             // dB / alpha
           } else {
-            // g = delta phi: dx and dB take phi, ddelta's write part dg/ddelta = a, and dA
-            // gains alpha B x gv delta^2 psi
+            // write x B g: dx and dB take g, ddelta's write part dg/ddelta = a, and dA gains
+            // alpha B x gv dg/dA (phs: g, pss: dg/dA of the step)
             const float a = av[tt][j];
-            const float ph = phs[ZOH ? tt : 0][j];
+            const float gz = phs[ZOH ? tt : 0][j];
             const float bg = bs[buf][tt][gs][j] * gvf;  // alpha B gv
-            p1 = j == 0 ? bg * ph : fmaf(bg, ph, p1);
+            p1 = j == 0 ? bg * gz : fmaf(bg, gz, p1);
             p1d = j == 0 ? bg * a : fmaf(bg, a, p1d);
-            dAt[j] = fmaf(bg * (xv * dv * dv), pss[ZOH ? tt : 0][j], dAt[j]);
-            vals[(tb * 2 + 0) * K + j] = c * ph * gvf;        // dB / alpha
+            dAt[j] = fmaf(bg * xv, pss[ZOH ? tt : 0][j], dAt[j]);
+            vals[(tb * 2 + 0) * K + j] = xv * gz * gvf;       // dB / alpha
           }
           vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
         }
-        float qx = dv * p1;
+        float qx = ZOH ? p1 : dv * p1;  // (g already carries delta)
         if (HAS_DSKIP) {
           qx = fmaf(dsk, gy, qx);
           dDt = fmaf(gy, xv, dDt);

@@ -98,6 +98,34 @@ __device__ __forceinline__ float zoh_psi(float u, float a, float phi) {
   return fabsf(u) < 0.25f ? p : q;
 }
 
+// The backward's zero-order-hold quantities from arg = delta A log2 e, a = 2^arg, delta and
+// invA = 1 / A (0 for A = 0): the write coefficient g = delta phi(delta A) and its derivative
+// dg/dA = delta^2 psi(delta A).  Below |delta A| = 1/4 they come from the degree-6 series of
+// zoh_phi and zoh_psi, evaluated in arg (coefficient k carries ln 2^k); above it from
+// g = (a - 1) / A and dg/dA = (delta a - g) / A, with no reciprocal per update.
+constexpr float kZohSwitchArg = 0.36067376f;  // |delta A| = 1/4 in units of log2 e
+__device__ __forceinline__ float zoh_g_bwd(float arg, float a, float delta, float invA) {
+  float p = fmaf(arg, 2.2005043419116583e-05f, 0.0002222259691071407f);
+  p = fmaf(p, arg, 0.0019236258215256953f);
+  p = fmaf(p, arg, 0.013876027166205394f);
+  p = fmaf(p, arg, 0.08007550231970023f);
+  p = fmaf(p, arg, 0.34657359027997264f);
+  p = fmaf(p, arg, 1.f);
+  const float q = fmaf(a, invA, -invA);
+  return fabsf(arg) < kZohSwitchArg ? delta * p : q;
+}
+// g as zoh_g_bwd returned it
+__device__ __forceinline__ float zoh_gA_bwd(float arg, float a, float delta, float invA, float g) {
+  float p = fmaf(arg, 1.9254412991727008e-05f, 0.0001904794020918349f);
+  p = fmaf(p, arg, 0.0016030215179380794f);
+  p = fmaf(p, arg, 0.011100821732964315f);
+  p = fmaf(p, arg, 0.06005662673977517f);
+  p = fmaf(p, arg, 0.23104906018664842f);
+  p = fmaf(p, arg, 0.5f);
+  const float q = fmaf(delta, a, -g) * invA;
+  return fabsf(arg) < kZohSwitchArg ? (delta * delta) * p : q;
+}
+
 struct bf16_storage {
   uint16_t bits;
 };
