@@ -87,8 +87,10 @@ bool allowed_k(int NP, int K) {
 // one wavefront per SIMD.  Otherwise the sequence is cut into chunks until there are a few
 // wavefronts per SIMD: shorter chunks shorten the sequential path of every wavefront, and the
 // extra summary work is small.  Measured on MI355X (Bt=1): L=65536 D=2048 N=16, 2 states per
-// wavefront: 16 chunks 1.34 ms, 8 chunks 1.49 ms (4 states, 16 chunks: 1.47 ms); L=16384
-// D=1024 N=16: 32 chunks best; N=4 and N=64 are best at about two wavefronts per SIMD.
+// wavefront: 16 chunks 0.804 ms, 8 chunks 0.886 ms, 24 chunks 0.906 ms, 32 chunks 0.956 ms
+// (4 states, 16 chunks: 0.840 ms; chunk counts that leave the workgroups unevenly spread over
+// the CUs, 12 or 20, are slower still); L=16384 D=1024 N=16: 32 chunks best; N=4 and N=64 are
+// best at about two wavefronts per SIMD.
 msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   const int NP = padded_states(N);
   const int64_t chan_blocks = Bt * ceil_div(D, kWave);
@@ -104,6 +106,12 @@ msm_plan auto_fwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N) {
   int64_t G = ceil_div(per_simd * kTargetWaves, waves);
   const int64_t gmax = fwd_plan_chunks(Bt, L, D);
   if (G > gmax) G = gmax;
+  // Chunk k composes the maps of the k chunks before it in its prologue, so chunks are kept at
+  // least 2G rows long (README shape, Bt=2 L=512 D=256 N=16: 16 chunks 20.0 us, 32 chunks
+  // 24.2 us).  Below about a million state updates the summary pass's launch costs more than
+  // its parallelism gains (Bt=1 L=64 D=4 N=4: one chunk 14.9 us, four chunks 16.9 us).
+  while (G > 1 && ceil_div(L, G) < 2 * G) --G;
+  if (Bt * L * D * N < ((int64_t)1 << 20)) G = 1;
   if (G < 1) G = 1;
   pl.states_per_wave = kchunk;
   pl.chunks = (int32_t)G;

@@ -407,9 +407,9 @@ void fwd_kernel(const FwdArgs p) {
 #pragma unroll
     for (int r = 0; r < TT / S; ++r) {
       const int tt = r * S + g;
-      float s = 0.f;
+      float s = ypart[YPART && YB == 2 ? buf : 0][0][tt][lane];
 #pragma unroll
-      for (int gg = 0; gg < S; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][lane];
+      for (int gg = 1; gg < S; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][lane];
       T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, gate(s, cur.z[ZG ? r : 0]));
     }
   };
