@@ -36,7 +36,7 @@ def _noalloc(g, inp, y, lh, lv):
 def test_noalloc_matches_workspace_forward(io):
     import torch
     import selective_state_space_msm_amd as msm
-    shapes = [dict(Bt=2, L=3000, D=200, N=16), dict(Bt=1, L=1000, D=70, N=13)]
+    shapes = [dict(Bt=2, L=3000, D=200, N=16), dict(Bt=1, L=2000, D=70, N=13)]
     for i, shp in enumerate(shapes):
         w = W["m130m"].replace(io=io, beta=0.9, alpha=0.8, dskip=True, **shp)
         inp = workloads.make_inputs(w, a_kind="random", seed=900 + i)
