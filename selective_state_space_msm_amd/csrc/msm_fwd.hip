@@ -133,10 +133,22 @@ void fwd_kernel(const FwdArgs p) {
   // delta backwards from the chunk end, a tile at a time, until every channel of the workgroup
   // meets the bound for its slowest state (and at least win_rows rows for beta).  A truncated
   // summary then maps any start state to zero: q = 0 and sum delta = +inf (r = 0).
+  // Each wavefront also finds the window of its own K states (their slowest decay): before it
+  // the wavefront only adds up delta (the chunk's decay sum), so fast-decaying states cost less
+  // than the workgroup's slowest one.  A wavefront whose window starts after the chunk start
+  // reports its states' maps as truncated (q = 0); their decay over the whole chunk is below
+  // 2^-kWinLog2 as well.
   bool trunc = false;
+  const int64_t tc0 = t0;  // the chunk's first row
+  int64_t wg0 = t0;        // this wavefront's window start
   if (SUMMARY && p.win_rows < t1 - t0) {
     float amin = INFINITY;  // slowest decay of this lane's channel, |A| log2 e
     for (int64_t n = 0; n < N; ++n) amin = fminf(amin, -p.A[dl * N + n] * kLog2e);
+    float amin_w = INFINITY;  // the same over this wavefront's states
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if ((int64_t)g * K + j < N) amin_w = fminf(amin_w, -A2[j]);
+    bool wdone = false;
     // channels past D only repeat channel D - 1
     const uint32_t rb = (uint32_t)(D * T::es);
     const auto rdw = make_rsrc(static_cast<const char*>(p.delta) + (b * L + t0) * D * T::es,
@@ -162,6 +174,10 @@ void fwd_kernel(const FwdArgs p) {
       __syncthreads();
       for (int gg = 0; gg < S; ++gg) acc += xdl[0][gg][lane].x;
       w0 = tb;
+      if (!wdone && __all(amin_w * acc >= kWinLog2 && t1 - w0 >= p.win_rows)) {
+        wdone = true;
+        wg0 = w0;
+      }
       const bool mine = amin * acc >= kWinLog2 && t1 - w0 >= p.win_rows;
       __syncthreads();  // every wavefront has read the partial sums before they are rewritten
       if (__syncthreads_and(mine)) {
@@ -170,6 +186,8 @@ void fwd_kernel(const FwdArgs p) {
         break;
       }
     }
+    // (when the workgroup's bound holds, every wavefront's does: amin <= amin_w)
+    if (!wdone) wg0 = t0;
   }
 
   // ---- addressing ----
@@ -359,6 +377,12 @@ void fwd_kernel(const FwdArgs p) {
   constexpr int RB = (32 / K) < 4 ? (32 / K) : 4;
   constexpr int NB = TT / RB;
   auto compute_tile = [&](int buf, int64_t ts, const Set& cur) {
+    if (SUMMARY && ts < wg0) {
+      // before this wavefront's window: only the chunk's delta sum
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) sd += xdl[buf][tt][lane].x;
+      return;
+    }
     const auto ry = rs_d(y0, (uint32_t)(ts - t0));
     float bcv[2][RB][BCW];
     float2 dcv[2][RB];
@@ -460,7 +484,7 @@ void fwd_kernel(const FwdArgs p) {
           p.s_bh[idx] = h[j];
           if (!BETA0) {
             p.s_bv[idx] = v[j];
-            p.s_q[idx] = trunc ? 0.f : q[j];
+            p.s_q[idx] = wg0 > tc0 ? 0.f : q[j];
           }
         }
       }
