@@ -326,3 +326,26 @@ def test_chunk_summary_windows(case):
     assert_close(host(y), oy, "f32", "zoh y windows")
     assert_close(host(lh), oh, "f32", "zoh last_h windows")
     assert_close(host(lv), ov, "f32", "zoh last_v windows")
+
+
+@pytest.mark.parametrize("beta", [0.9, 0.0])
+@pytest.mark.parametrize("N", [16, 13])
+def test_chunk_summary_windows_per_wavefront(beta, N):
+    """Summary windows that differ between the wavefronts of a workgroup: state 0 decays so
+    slowly in half the channels (A = -0.05: the 2^-32 bound needs about 3400 rows, more than a
+    chunk) that its wavefront maps the whole chunk, while the other states (A = -(n + 1)) stop
+    at the velocity's bound (about 220 rows), so the workgroup's map is exact and some of its
+    wavefronts' maps are truncated; with N = 13 the last wavefronts hold padded states.  (A much
+    slower state, A = -1e-3 with a memory of about 7700 rows, is outside what an fp32 state can
+    hold to the fp32 bound: a sequential fp32 scan of the same input misses it by 5.9x.)  Every
+    output against the oracle."""
+    w = W["m130m"].replace(Bt=2, L=6000, D=130, N=N, beta=beta, dskip=True)
+    inp = workloads.make_inputs(w, seed=170 + N)
+    rng = np.random.default_rng(171)
+    u = rng.normal(-2.0, 1.0, size=inp["delta"].shape)
+    inp["delta"] = np.log1p(np.exp(u)).astype(np.float32)
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float32), (w.D, 1))
+    A[::2, 0] = -0.05
+    inp["A"] = np.ascontiguousarray(A)
+    for plan in ({"states_per_wave": 2, "chunks": 4}, {"states_per_wave": 4, "chunks": 7}):
+        check_full(inp, plan=plan, tag="windows per wavefront N=%d beta=%g" % (N, beta))
