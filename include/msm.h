@@ -259,8 +259,9 @@ msm_status msm_scan_step(const void* x, const void* delta, const float* A, const
  *   of a complex64 array); h0, v0, last_h, last_v, dlast_h, dlast_v, dh0, dv0: (Bt, D, N, 2) fp32.
  * The real part of C h is the readout (a conjugate-pair convention, C h + conj(C h), would be
  * twice this).  h0, v0 (NULL = zero) start the scan; last_h, last_v (may be NULL) receive the
- * final state.  Requirements as msm_scan_fwd, and 17 * N * D * 8 < 2^31 (the kernels address
- * 17 rows of the state history with 32-bit offsets); B and C must be aligned to a whole complex
+ * final state.  Requirements as msm_scan_fwd, L < 2^30 (else MSM_ERR_UNSUPPORTED), and
+ * 17 * N * D * 8 < 2^31 (the kernels address 17 rows of the state history with 32-bit
+ * offsets); B and C must be aligned to a whole complex
  * element (8 bytes for MSM_F32, 4 for MSM_BF16), else MSM_ERR_INVALID_ARG.
  * Needs no workspace. */
 msm_status msm_scan_complex_fwd(const void* x, const void* delta, const float* A, const void* B,

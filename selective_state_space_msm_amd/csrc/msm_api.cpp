@@ -282,6 +282,8 @@ msm_status check_complex(int64_t Bt, int64_t L, int64_t D, int64_t N, float beta
   msm_status st = check_common(Bt, L, D, N, beta, alpha, io);
   if (st != MSM_OK) return st;
   if (!complex_shape_ok(Bt, L, D, N)) return MSM_ERR_INVALID_ARG;
+  // the complex kernels index rows and tiles of a sequence in 32 bits
+  if (L >= kBwdMaxL) return MSM_ERR_UNSUPPORTED;
   return MSM_OK;
 }
 

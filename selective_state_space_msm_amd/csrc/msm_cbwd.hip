@@ -122,8 +122,13 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
   char* ddl0 = static_cast<char*>(p.ddelta) + b * L * row_bytes;
   const int64_t part_row_bytes = (int64_t)NPD * 16;
   char* part0 = reinterpret_cast<char*>(p.dbc_part) + (b * p.ncb + cb) * L * part_row_bytes;
+  // Resource for the TT rows of a (nrows, rb) slab from row r on (rows past nrows are out of
+  // range): the tile's own rows only, so extent and offset are 32-bit (tile_rsrc; the host keeps
+  // L below 2^30).  The clamped row count is read back as a scalar (the compiler forms it with a
+  // vector med3, and a resource built from a vector value loops over the lanes' values).
   auto rows = [&](const void* base, int64_t r, int64_t rb, int64_t nrows) {
-    return make_rsrc(static_cast<const char*>(base) + r * rb, (nrows - r) * rb);
+    const int32_t nr = __builtin_amdgcn_readfirstlane(min(max((int32_t)nrows - (int32_t)r, 0), TT));
+    return tile_rsrc(base, (int32_t)r, nr, (uint32_t)rb);
   };
 
   uint32_t bc_voff[NBC];
@@ -271,12 +276,15 @@ __global__ __launch_bounds__(S* kWave) void cbwd_kernel(const CBwdArgs p) {
     for (int r = 0; r < NX; ++r) {
       const int i = tid + r * NTHR;
       if (NX * NTHR == XE || i < XE) {
-        double sx = 0.0, sd = 0.0;
+        // every partial read before the first sum: one LDS round trip
+        double2 pv[S];
 #pragma unroll
-        for (int gg = 0; gg < S; ++gg) {
-          const double2 v = gpart[buf][gg][i / CB][i % CB];
-          sx += v.x;
-          sd += v.y;
+        for (int gg = 0; gg < S; ++gg) pv[gg] = gpart[buf][gg][i / CB][i % CB];
+        double sx = pv[0].x, sd = pv[0].y;
+#pragma unroll
+        for (int gg = 1; gg < S; ++gg) {
+          sx += pv[gg].x;
+          sd += pv[gg].y;
         }
         if constexpr (SPLIT == 0) {
           T::bstore(rdx, x_voff[r], 0u, (float)sx);

@@ -104,12 +104,19 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
   const char* B0 = static_cast<const char*>(p.B) + b * L * bc_row_bytes;
   const char* C0 = static_cast<const char*>(p.C) + b * L * bc_row_bytes;
   char* y0 = Y ? static_cast<char*>(p.y) + b * L * row_bytes : nullptr;
+  // resource for the TT rows from row r on (rows past L are out of range): the tile's own rows
+  // only, so extent and offset are 32-bit (tile_rsrc; the host keeps L below 2^30), with the
+  // clamped row count read back as a scalar so that the resource stays scalar
+  auto tile_rows = [&](int64_t r) {
+    return __builtin_amdgcn_readfirstlane(min(max((int32_t)L - (int32_t)r, 0), TT));
+  };
   auto rows = [&](const void* base, int64_t r, int64_t rb) {
-    return make_rsrc(static_cast<const char*>(base) + r * rb, (L - r) * rb);
+    return tile_rsrc(base, (int32_t)r, tile_rows(r), (uint32_t)rb);
   };
   // history rows (REC): row ts + 1 + tt holds h after step ts + tt
   const int64_t hrow_bytes = N * D * 8;
   float* hist0 = REC ? p.hist + b * (L + 1) * N * D * 2 : nullptr;
+  float* hist1 = REC ? hist0 + N * D * 2 : nullptr;  // row 1: h after step 0
   uint32_t h_voff[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -232,15 +239,13 @@ __global__ __launch_bounds__(S* kWave) void cfwd_kernel(const CFwdArgs p) {
     }
   };
   auto compute_full = [&](int buf, int64_t ts) {
-    const auto rh = REC ? make_rsrc(hist0 + (ts + 1) * N * D * 2, (L - ts) * hrow_bytes)
-                        : make_rsrc(nullptr, 0);
+    const auto rh = REC ? rows(hist1, ts, hrow_bytes) : make_rsrc(nullptr, 0);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) emit(buf, tt, step(buf, tt, rh));
   };
   // the ragged last tile: rows past L must leave the states alone (uniform branch per row)
   auto compute_tail = [&](int buf, int64_t ts, int nv) {
-    const auto rh = REC ? make_rsrc(hist0 + (ts + 1) * N * D * 2, (L - ts) * hrow_bytes)
-                        : make_rsrc(nullptr, 0);
+    const auto rh = REC ? rows(hist1, ts, hrow_bytes) : make_rsrc(nullptr, 0);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
       if (tt < nv) emit(buf, tt, step(buf, tt, rh));

@@ -141,6 +141,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
+// Buffer resource for the `rows` rows of a slab that start at row r (0 <= r < 2^31; rows <= 0
+// gives an empty resource).  The resource spans that tile alone, so its extent and the row
+// offset need 32-bit arithmetic only, whatever the slab's size, as long as the tile's bytes fit
+// in 31 bits; accesses at or past `rows` rows are dropped (stores) or read zero (loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int32_t r,
+                                                             int32_t rows, uint32_t row_bytes) {
+  const uint64_t off = (uint64_t)(uint32_t)r * row_bytes;
+  return make_rsrc_u32(static_cast<const char*>(base) + off,
+                       rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+}
 
 // I/O element access.  "raw" is what sits in a register between the load and its first use.
 template <typename IO>

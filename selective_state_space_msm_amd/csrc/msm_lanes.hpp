@@ -60,15 +60,4 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return make_rsrc(static_cast<const char*>(base) + off, total - off);
 }
 
-// Buffer resource for the `rows` rows of a slab that start at row r (0 <= r < 2^31; rows <= 0
-// gives an empty resource).  The resource spans that tile alone, so its extent and the row
-// offset need 32-bit arithmetic only, whatever the slab's size, as long as the tile's bytes fit
-// in 31 bits; accesses at or past `rows` rows are dropped (stores) or read zero (loads).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int32_t r,
-                                                             int32_t rows, uint32_t row_bytes) {
-  const uint64_t off = (uint64_t)(uint32_t)r * row_bytes;
-  return make_rsrc_u32(static_cast<const char*>(base) + off,
-                       rows > 0 ? (uint32_t)rows * row_bytes : 0u);
-}
-
 }  // namespace msm

@@ -339,6 +339,7 @@ def test_complex_validation_never_launches(lib):
     assert fwd(y=0x1000 + 128) == INVALID          # y over x
     assert fwd(lh=0x4000 + 256) == INVALID         # a final state over B
     assert fwd(D=1 << 21, N=64) == INVALID         # history rows past 32-bit offsets
+    assert fwd(L=1 << 30) == UNSUPPORTED           # rows and tiles indexed in 32 bits
     assert fwd(B=0x4000 + 4) == INVALID            # B not aligned to a complex fp32 pair
     assert fwd(C=0x5000 + 2, io=1) == INVALID      # C not aligned to a complex bf16 pair
 
