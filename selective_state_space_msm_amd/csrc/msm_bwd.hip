@@ -70,16 +70,26 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   constexpr int NRB = TB / RB;
   static_assert(P == 2, "the lane pairing below assumes two 32-lane halves");
   constexpr bool ZOH = EXT == 2;  // zero-order-hold write coefficient g = delta phi(delta A)
+  // DEF: the sweep keeps per-state sums without the factors every state shares (delta for dx, x
+  // for ddelta's write term); the finalize applies them once per (row, channel).  The
+  // zero-order hold's sums already carry g and dg/ddelta per state, so it keeps the finished
+  // per-lane products.
+  constexpr bool DEF = !ZOH;
   static_assert(RB >= 1 && TB % RB == 0, "tile must split into reduce blocks");
 
-  __shared__ float4 xs[2][TB][CB];          // x, delta, dy, delta * x
+  // (delta, delta x) and (dy, x) of each staged element, in two arrays so the sweep reads 8 and 4
+  // bytes per lane (a 12-byte read of a 16-byte element waited longer); odd rows have their
+  // channel halves swapped (position ch ^ 16), so the finalize's rows 2g and 2g + 1 read
+  // different banks
+  __shared__ float2 xs[2][TB][CB];
+  __shared__ float2 xg[2][TB][CB];
   __shared__ float bs[2][TB][GS][K];        // alpha B
   __shared__ double cs64[2][TB][GS][K];     // C, widened for the adjoint recurrence
   // fused variant: (dy silu'(z), logistic(delta + bias)) per staged element, the per-wavefront
   // partials of the output before the gate, and the bias-gradient partials
   __shared__ float2 xe[EXT ? 2 : 1][EXT ? TB : 1][CB];
   __shared__ float ypt[EXT ? 2 : 1][EXT ? S : 1][EXT ? TB : 1][CB];
-  __shared__ double bred[EXT ? S : 1][CB];
+  __shared__ double bred[EXT ? S : 1][EXT ? 2 : 1][CB];
   // Phase 1 stages R1 rows at a time: (delta, delta x) per channel and alpha B per state group,
   // each with its rows contiguous (padded to keep 16-byte reads aligned and spread over the
   // banks).  The sweep's per-wavefront dx (lanes < 32) | ddelta partials reuse that LDS: phase 1
@@ -105,6 +115,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int ch = lane & (CB - 1);
   const int gs = g * P + lane / CB;  // state group of this lane
+  // position of channel c of staged row t in xs, xg and xe (odd rows: halves swapped)
+  auto swz = [](int t, int c) { return c ^ ((t & 1) * (CB / 2)); };
   const uint32_t bq = blockIdx.x / (uint32_t)p.ncb;
   const int cb = (int)(blockIdx.x - bq * (uint32_t)p.ncb);
   const int64_t b = bq;
@@ -202,6 +214,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
       if (NX * NTHR == XE || i < XE) {
         const float xv = T::widen(xr[r]), draw = T::widen(dr[r]);
         const float dv = delta_eff(draw);
+        const int xc = swz(i / CB, i % CB);
         float gy = with_dy ? T::widen(gr[r]) : 0.f;
         if (EXT) {
           const float dsp = softplus ? logistic_f(draw + dbias).s : 1.f;
@@ -211,9 +224,10 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
             gz = gy * silu_grad_f(zv);
             gy *= silu_f(zv);
           }
-          xe[EXT ? buf : 0][EXT ? i / CB : 0][i % CB] = make_float2(gz, dsp);
+          xe[EXT ? buf : 0][EXT ? i / CB : 0][xc] = make_float2(gz, dsp);
         }
-        xs[buf][i / CB][i % CB] = make_float4(xv, dv, gy, dv * xv);
+        xs[buf][i / CB][xc] = make_float2(dv, dv * xv);
+        xg[buf][i / CB][xc] = make_float2(gy, xv);
       }
     }
   };
@@ -422,7 +436,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   double dbias64 = 0.0;  // fused variant: this lane's rows of the bias gradient (lanes >= 32)
   // (the zero-order-hold variant always runs with the skip term compiled in, a zero weight
   // when no Dskip is given; see launch_ks)
-  const float dsk = (HAS_DSKIP && gs == 0 && p.Dskip) ? p.Dskip[dl] : 0.f;
+  // (added in the finalize, by every lane, or in the sweep by state group 0)
+  const float dsk = (HAS_DSKIP && (DEF || gs == 0) && p.Dskip) ? p.Dskip[dl] : 0.f;
   const float* dbc = p.dbc_part + (b * p.ncb + cb) * L * 2 * NPD;
   char* dx0 = static_cast<char*>(p.dx) + b * tot_d;
   char* ddl0 = static_cast<char*>(p.ddelta) + b * tot_d;
@@ -445,6 +460,12 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   char* az0 = SPLIT ? reinterpret_cast<char*>(p.acc_dz) + b * L * D * 4 : dx0;
   const uint32_t vo_aq = dvalid ? (uint32_t)(((lane >= CB ? 1 : 0) * D + dl) * 8) : 0x80000000u;
   const uint32_t vo_dz32 = (dvalid && lane < CB) ? (uint32_t)dl * 4u : 0x80000000u;
+  // DEF finalize: every lane stores both outputs of its element (dx, ddelta, dz; and in the
+  // split passes its fp64 sums at [row][0][d] and [row][1][d], and dz at [row][d])
+  const uint32_t vo_c = dvalid ? lane_off : 0x80000000u;
+  const uint32_t vo_q = dvalid ? (uint32_t)dl * 8u : 0x80000000u;
+  const uint32_t q_dd = (uint32_t)(D * 8);
+  const uint32_t vo_z = dvalid ? (uint32_t)dl * 4u : 0x80000000u;
   // xb: the LDS staging buffer that still holds the tile's inputs
   auto finalize = [&](int64_t tile, int pb, bool valid, int xb) __attribute__((always_inline)) {
     const int64_t ts = tile * TB;
@@ -456,8 +477,87 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     // split passes: the first half's sums, [L][2][D] fp64 (dx, ddelta) and [L][D] fp32 (dz)
     const auto raq = tile_rsrc(aq0, t32, SPLIT ? nr : 0, (uint32_t)aq_row_bytes);
     const auto raz = tile_rsrc(az0, t32, (SPLIT && has_z) ? nr : 0, (uint32_t)(D * 4));
-    // every partial of the wavefront's rows is read before the first sum, so the reads share
-    // one LDS round trip (summed as they arrive, the compiler waits on each in turn)
+    if constexpr (DEF) {
+      // Lane l finishes channel l % 32 of row tt = r 2S + 2g + l / 32: from the S wavefronts'
+      // sums S1 = sum(B gv) and S2 = sum(A a h gh) (written by lanes l % 32 and l % 32 + 32,
+      // at positions l and l ^ 32 of the row, as odd rows are stored with the halves swapped)
+      // it forms dx = delta S1 + Dskip dy and ddelta = x S1 + S2 in fp64, and stores both.
+      // Every partial is read before the first sum, so the reads share one LDS round trip.
+      constexpr int FR2 = TB / (2 * S);
+      const int hf = lane / CB;
+      float sp[FR2][2][S];
+      float yp[EXT ? FR2 : 1][EXT ? S : 1];
+#pragma unroll
+      for (int r = 0; r < FR2; ++r) {
+        const int tt = r * 2 * S + 2 * g + hf;
+#pragma unroll
+        for (int w = 0; w < S; ++w) {
+          sp[r][0][w] = spart[pb][w][tt][lane];
+          sp[r][1][w] = spart[pb][w][tt][lane ^ CB];
+          if (EXT) yp[EXT ? r : 0][EXT ? w : 0] = ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < FR2; ++r) {
+        const int tt = r * 2 * S + 2 * g + hf;
+        double s1 = (double)sp[r][0][0], s2 = (double)sp[r][1][0];
+#pragma unroll
+        for (int w = 1; w < S; ++w) {
+          s1 += (double)sp[r][0][w];
+          s2 += (double)sp[r][1][w];
+        }
+        const int xc = swz(tt, ch);
+        const float dv = xs[xb][tt][xc].x;
+        const float2 gx = xg[xb][tt][xc];  // dy, x
+        double qdx = (double)dv * s1;
+        double qdd = fma((double)gx.y, s1, s2);
+        if (HAS_DSKIP) qdx = fma((double)dsk, (double)gx.x, qdx);
+        float zv = 0.f;
+        if (EXT) {
+          // the raw delta's gradient (through softplus) and dz from the output before the gate
+          const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][xc];
+          qdd *= (double)e.y;
+          float yr = yp[EXT ? r : 0][0];
+#pragma unroll
+          for (int w = 1; w < S; ++w) yr += yp[EXT ? r : 0][EXT ? w : 0];
+          if (HAS_DSKIP) yr = fmaf(dsk, gx.y, yr);
+          zv = e.x * yr;
+        }
+        // rows past the end of the sequence are past the extent: dropped
+        const uint32_t ro = vo_c + (uint32_t)(tt * row_bytes);
+        if constexpr (SPLIT != 0) {
+          // split passes: the first stores its fp64 sums, the second adds them
+          const uint32_t aqo = vo_q + (uint32_t)(tt * aq_row_bytes);
+          const uint32_t azo = vo_z + (uint32_t)(tt * D * 4);
+          if constexpr (SPLIT == 1) {
+            const uint64_t ux = (uint64_t)__double_as_longlong(qdx);
+            const uint64_t ud = (uint64_t)__double_as_longlong(qdd);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)ux, (uint32_t)(ux >> 32)},
+                                                  raq, aqo, 0u, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)ud, (uint32_t)(ud >> 32)},
+                                                  raq, aqo + q_dd, 0u, 0);
+            if (EXT) io<float>::bstore(raz, azo, 0u, zv);
+            continue;
+          } else {
+            const u32x2_t wx = __builtin_amdgcn_raw_buffer_load_b64(raq, aqo, 0u, 0);
+            const u32x2_t wd = __builtin_amdgcn_raw_buffer_load_b64(raq, aqo + q_dd, 0u, 0);
+            qdx += __longlong_as_double((long long)(((uint64_t)wx.y << 32) | wx.x));
+            qdd += __longlong_as_double((long long)(((uint64_t)wd.y << 32) | wd.x));
+            if (EXT) zv += io<float>::bload(raz, azo, 0u);
+          }
+        }
+        T::bstore(rdx, ro, 0u, (float)qdx);
+        T::bstore(rdd, ro, 0u, (float)qdd);
+        if (EXT) {
+          if (valid) dbias64 += qdd;
+          T::bstore(rdz, ro, 0u, zv);
+        }
+      }
+    } else {
+    // zero-order hold: lanes 0-31 finish dx and lanes 32-63 ddelta of every S-th row.  Every
+    // partial of the wavefront's rows is read before the first sum, so the reads share one LDS
+    // round trip (summed as they arrive, the compiler waits on each in turn)
     constexpr int FR = (TB + S - 1) / S;  // rows finished by this wavefront
     float sp[FR][S];
 #pragma unroll
@@ -481,7 +581,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           if (EXT) {
             // lanes 32-63: the gradient of the raw delta (through softplus); lanes 0-31: dz from
             // the output before the gate, summed over the S wavefronts in a fixed order
-            const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
+            const float2 e = xe[EXT ? xb : 0][EXT ? tt : 0][swz(tt, ch)];
             const double qd = q * (double)e.y;
             if (valid) dbias64 += qd;
             T::bstore(rdd, vo_dd + ro, 0u, (float)qd);
@@ -500,7 +600,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           double val = q;
           float2 e = make_float2(0.f, 0.f);
           if (EXT) {
-            e = xe[EXT ? xb : 0][EXT ? tt : 0][ch];
+            e = xe[EXT ? xb : 0][EXT ? tt : 0][swz(tt, ch)];
             if (lane >= CB) val = q * (double)e.y;
           }
           if (SPLIT == 2) {
@@ -529,6 +629,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           }
         }
       }
+    }
     }
   };
 
@@ -602,8 +703,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     }
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
-      const float4 r = xs[buf][tt][ch];
-      fstep(r.y, ZOH ? r.x : r.w, &bs[buf][tt][gs][0], av[tt], hs[tt + 1],
+      const int xc = swz(tt, ch);
+      const float2 r = xs[buf][tt][xc];
+      fstep(r.x, ZOH ? xg[buf][tt][xc].y : r.y, &bs[buf][tt][gs][0], av[tt], hs[tt + 1],
             ZOH ? phs[ZOH ? tt : 0] : nullptr, ZOH ? pss[ZOH ? tt : 0] : nullptr);
     }
 
@@ -617,8 +719,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
 #pragma unroll
       for (int tb = RB - 1; tb >= 0; --tb) {
         const int tt = rb * RB + tb;
-        const float4 r = xs[buf][tt][ch];
-        const float xv = r.x, dv = r.y, gy = r.z, c = r.w;
+        const int xc = swz(tt, ch);
+        const float2 r0 = xs[buf][tt][xc], r1 = xg[buf][tt][xc];
+        const float dv = r0.x, c = r0.y, gy = r1.x, xv = r1.y;
         const double gy64 = gy;
         float p1 = 0.f, p2 = 0.f, yq = 0.f, p1d = 0.f;
 #pragma unroll
@@ -650,17 +753,20 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           }
           vals[(tb * 2 + 1) * K + j] = gy * hs[tt + 1][j];  // dC
         }
-        float qx = ZOH ? p1 : dv * p1;  // (g already carries delta)
-        if (HAS_DSKIP) {
-          qx = fmaf(dsk, gy, qx);
-          dDt = fmaf(gy, xv, dDt);
+        float qx = p1, qd = p2;  // DEF: sums over the lane's states, finished in the finalize
+        if (HAS_DSKIP) dDt = fmaf(gy, xv, dDt);
+        if constexpr (!DEF) {
+          // zero-order hold: g already carries delta; the skip term on state group 0
+          if (HAS_DSKIP) qx = fmaf(dsk, gy, qx);
+          qd = fmaf(xv, p1d, p2);
         }
-        const float qd = fmaf(xv, ZOH ? p1d : p1, p2);
-        spart[pb][g][tt][lane] = swap_add32(qx, qd);
+        // (DEF: odd rows with the halves swapped, so the finalize's two rows per wavefront
+        // fall in different LDS banks)
+        spart[pb][g][tt][DEF ? (lane ^ ((tt & 1) * CB)) : lane] = swap_add32(qx, qd);
         if (EXT) {
-          // the output before the gate: this lane's states (+ the skip term on group 0), then
-          // both halves of the wavefront
-          if (HAS_DSKIP) yq = fmaf(dsk, xv, yq);
+          // the output before the gate: this lane's states (+ the skip term on group 0 with
+          // the zero-order hold; the finalize adds it otherwise), then both halves
+          if (!DEF && HAS_DSKIP) yq = fmaf(dsk, xv, yq);
           const float ys = swap_add32(yq, yq);
           if (lane < CB) ypt[EXT ? pb : 0][EXT ? g : 0][EXT ? tt : 0][lane] = ys;
         }
@@ -721,12 +827,20 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   }
   if (EXT && SPLIT != 1 && p.delta_bias) {
     // the bias gradient of the channel: lanes 32-63 of every wavefront hold their rows' sum
-    if (lane >= CB) bred[EXT ? g : 0][ch] = dbias64;
+    // (DEF: both halves hold rows of the channel; otherwise lanes 32-63 hold them all)
+    if (DEF)
+      bred[EXT ? g : 0][EXT ? lane / CB : 0][ch] = dbias64;
+    else if (lane >= CB)
+      bred[EXT ? g : 0][0][ch] = dbias64;
     __syncthreads();
     if (g == 0 && lane < CB && dvalid) {
-      double t = bred[0][ch];
+      double t = bred[0][0][ch];
+      if (DEF) t += bred[0][EXT ? 1 : 0][ch];
 #pragma unroll
-      for (int w = 1; w < S; ++w) t += bred[EXT ? w : 0][ch];
+      for (int w = 1; w < S; ++w) {
+        t += bred[EXT ? w : 0][0][ch];
+        if (DEF) t += bred[EXT ? w : 0][EXT ? 1 : 0][ch];
+      }
       p.dbias_part[b * D + d] = (float)t;
     }
   }
