@@ -40,40 +40,62 @@ namespace {
 
 // Occupancy hint: the launch plans put one or two wavefronts on a SIMD, so the scheduler may
 // spend registers on hiding LDS and transcendental latency instead of on more wavefronts.
-template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, int EXT, int YBP>
+// HW (half-wavefront layout, main pass only): a workgroup owns 32 channels; lane l serves
+// channel l % 32 and the two 32-lane halves of a wavefront hold different state groups, so a
+// workgroup of S wavefronts covers 2 S K states with half the wavefronts of the full layout.
+// The grid then has twice the workgroups, two of them share a CU, and each keeps its own
+// barrier schedule: while one workgroup stages its next tile and finishes y, the other one's
+// wavefronts on the same SIMDs are still computing.
+template <typename IO, int K, int S, bool BETA0, bool SUMMARY, bool HAS_DSKIP, int EXT, int YBP,
+          bool HW>
 __global__ __launch_bounds__(S* kWave) __attribute__((amdgpu_waves_per_eu(1, K >= 8 ? 1 : 2)))
 void fwd_kernel(const FwdArgs p) {
+  static_assert(!(HW && SUMMARY), "the summaries keep the full-wavefront layout");
   using T = io<IO>;
   using raw = typename T::raw;
   constexpr int TT = kTile;
-  constexpr int BCW = 2 * K;                    // floats per (tile row, wave): B then C
+  constexpr int BCW = 2 * K;                    // floats per (tile row, state group): B then C
   constexpr int NTHR = S * kWave;
-  constexpr bool YPART = !SUMMARY && S > 1;
+  constexpr int CW = HW ? kWave / 2 : kWave;    // channels per workgroup
+  constexpr int PG = kWave / CW;                // state groups per wavefront
+  constexpr int GS = S * PG;                    // state groups per workgroup
+  constexpr int RPF = NTHR / CW;                // rows one finalize round covers
+  static_assert(TT % RPF == 0, "the finalize rounds must tile the LDS tile");
+  constexpr bool YPART = !SUMMARY && GS > 1;
   // y partials are double-buffered (one barrier per tile) when one workgroup per CU is all
   // the grid provides (YBP = 2).  With more workgroups than CUs (YBP = 1), and always with 16
   // wavefronts, they are single-buffered and take a second barrier: the smaller LDS lets two
   // workgroups share a CU (measured at Bt=1, L=65536, D=2048, N=16 in 16 chunks: 1.13 ms
   // single-buffered, 1.27 ms double-buffered; at Bt=4, L=4096, D=4096: 0.366 ms double,
   // 0.388 ms single)
-  constexpr int YB = (S >= 16 || YBP == 1) ? 1 : 2;
+  // (the half-wavefront layout's workgroups are small: two share a CU with both buffers)
+  constexpr int YB = HW ? 2 : ((S >= 16 || YBP == 1) ? 1 : 2);
 
-  __shared__ float bcs[2][TT][S][BCW];
-  __shared__ float ypart[YPART ? YB : 1][YPART ? S : 1][TT][kWave];
+  __shared__ float bcs[2][TT][GS][BCW];
+  __shared__ float ypart[YPART ? YB : 1][YPART ? GS : 1][TT][CW];
   // (delta, delta * x) of the tile, widened once per workgroup: the S wavefronts share them
-  __shared__ float2 xdl[2][TT][kWave];
-  __shared__ float xxl[HAS_DSKIP ? 2 : 1][HAS_DSKIP ? TT : 1][kWave];  // x, for the skip term
+  __shared__ float2 xdl[2][TT][CW];
+  __shared__ float xxl[HAS_DSKIP ? 2 : 1][HAS_DSKIP ? TT : 1][CW];  // x, for the skip term
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int g = tid / kWave;
-  const uint32_t blk = blockIdx.x / (uint32_t)p.ncb;
-  const int cb = (int)(blockIdx.x - blk * (uint32_t)p.ncb);
+  const int ch = lane & (CW - 1);          // channel within the workgroup's block
+  const int gs = g * PG + lane / CW;       // state group of this lane
+  // Half-wavefront layout: workgroups dispatch to the eight XCDs in turn, so within each
+  // group of 16 the two halves of a 64-channel block are given indices 8 apart (one XCD, one
+  // L2 for their shared cache lines).
+  const uint32_t ncbk = HW ? (uint32_t)p.ncb_hw : (uint32_t)p.ncb;
+  uint32_t bid = blockIdx.x;
+  if (HW && bid < (gridDim.x & ~15u)) bid = (bid & ~15u) | ((bid & 7u) << 1) | ((bid >> 3) & 1u);
+  const uint32_t blk = bid / ncbk;
+  const int cb = (int)(bid - blk * ncbk);
   const int64_t b = blk % (uint32_t)p.Bt;
   const int k = (int)(blk / (uint32_t)p.Bt);
   const int64_t L = p.L, D = p.D, N = p.N;
   int64_t t0 = (int64_t)k * p.Tc;
   const int64_t t1 = (t0 + p.Tc < L) ? t0 + p.Tc : L;
-  const int d = cb * kWave + lane;
+  const int d = cb * CW + ch;
   const bool dvalid = d < D;
   const int dl = dvalid ? d : (int)D - 1;
   const float beta = p.beta;
@@ -82,7 +104,7 @@ void fwd_kernel(const FwdArgs p) {
   float invA[EXT == 2 ? K : 1];  // zero-order hold: 1 / A (0 for A = 0 and padded states)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int64_t n = (int64_t)g * K + j;
+    const int64_t n = (int64_t)gs * K + j;
     const float an = n < N ? p.A[dl * N + n] : 0.f;
     A2[j] = an * kLog2e;
     if (EXT == 2) invA[EXT == 2 ? j : 0] = an != 0.f ? 1.f / an : 0.f;
@@ -93,7 +115,7 @@ void fwd_kernel(const FwdArgs p) {
     q[j] = 0.f;
   }
   float sd = 0.f, bpow = 1.f;
-  const float dsk = (HAS_DSKIP && g == 0) ? p.Dskip[dl] : 0.f;
+  const float dsk = (HAS_DSKIP && gs == 0) ? p.Dskip[dl] : 0.f;
   // fused extras: every x / delta element a thread stages belongs to its lane's channel
   constexpr bool ZG = EXT && !SUMMARY;  // the gate is loaded (the summaries produce no y)
   constexpr bool ZOH = EXT == 2;        // zero-order-hold write coefficient
@@ -109,7 +131,7 @@ void fwd_kernel(const FwdArgs p) {
       const float sdv = p.s_sd[base * D + dl];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const int64_t n = (int64_t)g * K + j;
+        const int64_t n = (int64_t)gs * K + j;
         if (n < N) {
           const int64_t idx = (base * N + n) * D + dl;
           const float r = exp2_fast(A2[j] * sdv);     // product of a_t over the chunk
@@ -147,7 +169,7 @@ void fwd_kernel(const FwdArgs p) {
     float amin_w = INFINITY;  // the same over this wavefront's states
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      if ((int64_t)g * K + j < N) amin_w = fminf(amin_w, -A2[j]);
+      if ((int64_t)gs * K + j < N) amin_w = fminf(amin_w, -A2[j]);
     bool wdone = false;
     // channels past D only repeat channel D - 1
     const uint32_t rb = (uint32_t)(D * T::es);
@@ -170,9 +192,9 @@ void fwd_kernel(const FwdArgs p) {
         }
         part += d0 + d1;
       }
-      xdl[0][g][lane].x = part;
+      xdl[0][g][ch].x = part;
       __syncthreads();
-      for (int gg = 0; gg < S; ++gg) acc += xdl[0][gg][lane].x;
+      for (int gg = 0; gg < S; ++gg) acc += xdl[0][gg][ch].x;
       w0 = tb;
       if (!wdone && __all(amin_w * acc >= kWinLog2 && t1 - w0 >= p.win_rows)) {
         wdone = true;
@@ -191,14 +213,14 @@ void fwd_kernel(const FwdArgs p) {
   }
 
   // ---- addressing ----
-  // Every global access of a tile goes through a buffer resource whose base is the tile's first
-  // row and whose extent ends at the last row of this chunk.  Offsets are per-lane constants
-  // (row * row_bytes + lane_bytes), so the loads need no address arithmetic, and rows past the
-  // chunk end fall outside the resource: they read as zero and touch no memory.  That is what
-  // makes the prefetch unconditional (an uneven number of loads on different paths would make
-  // the in-order vmcnt waits of the current tile drain the prefetch of the next one).
-  // Resource bases and extents are carried as byte offsets from the chunk start; the host keeps
-  // every chunk below 2^31 bytes per array.
+  // Every global access goes through a buffer resource whose base is this chunk's first row
+  // and whose extent ends at its last row; a tile adds its row offset to constant per-lane
+  // offsets (one vector add per offset register), clamped so that a tile past the chunk end
+  // starts at the extent.  Rows past the chunk end therefore read as zero and touch no memory.
+  // That is what makes the prefetch unconditional (an uneven number of loads on different
+  // paths would make the in-order vmcnt waits of the current tile drain the prefetch of the
+  // next one).  Offsets are 32-bit: the host keeps every chunk below 2^31 bytes per array and
+  // rows below 2^26 bytes, so a clamped tile's offsets stay below 2^32.
   const uint32_t lane_off = (uint32_t)dl * T::es;
   const uint32_t row_bytes = (uint32_t)(D * T::es);
   const uint32_t bc_row_bytes = (uint32_t)(N * T::es);
@@ -212,28 +234,20 @@ void fwd_kernel(const FwdArgs p) {
   // without a gate its loads go through an empty resource (they read zeros, touch no memory)
   const char* z0 = has_z ? static_cast<const char*>(p.z) + (b * L + t0) * D * T::es : x0;
   const uint32_t ext_z = has_z ? ext_d : 0u;
-  // resource for the rows starting at chunk row r (r may lie past the chunk end)
-  // (extents in signed 64-bit so that they stay scalar: an unsigned saturating subtract is
-  // lowered to a vector instruction, which turns every load into a waterfall loop)
-  auto rs_d = [&](const char* base, uint32_t r) {
-    const uint32_t off = r * row_bytes;
-    const int64_t e = (int64_t)ext_d - (int64_t)off;
-    return make_rsrc_u32(base + off, e > 0 ? (uint32_t)e : 0u);
+  const auto rsx = make_rsrc_u32(x0, ext_d), rsdl = make_rsrc_u32(dl0, ext_d);
+  const auto rsy = make_rsrc_u32(y0, ext_d), rsz = make_rsrc_u32(z0, ext_z);
+  const auto rsb = make_rsrc_u32(B0, ext_n), rsc = make_rsrc_u32(C0, ext_n);
+  // first row of the tile starting at ts, relative to the chunk, clamped to the chunk end
+  auto trow = [&](int64_t ts) -> uint32_t {
+    const int64_t r = ts - t0;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(r < (int64_t)chunk_rows ? r : chunk_rows));
   };
-  auto rs_z = [&](uint32_t r) {
-    const uint32_t off = r * row_bytes;
-    const int64_t e = (int64_t)ext_z - (int64_t)off;
-    return make_rsrc_u32(z0 + off, e > 0 ? (uint32_t)e : 0u);
-  };
-  auto rs_n = [&](const char* base, uint32_t r) {
-    const uint32_t off = r * bc_row_bytes;
-    const int64_t e = (int64_t)ext_n - (int64_t)off;
-    return make_rsrc_u32(base + off, e > 0 ? (uint32_t)e : 0u);
-  };
+  // y offsets: channels past D store at an offset past every extent (dropped)
+  constexpr uint32_t kDrop = 0xFFFFFF00u;
 
   // ---- B/C staging: global (I/O dtype) -> registers -> LDS (fp32) ----
   // Element (tt, n) of a tile; both B and C are loaded for it.
-  constexpr int BCE = TT * S * K;                       // (tt, n) elements per tile
+  constexpr int BCE = TT * GS * K;                      // (tt, n) elements per tile
   constexpr int NPE = (BCE + NTHR - 1) / NTHR;
   uint32_t bc_voff[NPE];
   bool bc_nok[NPE];
@@ -241,26 +255,25 @@ void fwd_kernel(const FwdArgs p) {
   for (int r = 0; r < NPE; ++r) {
     const int i = tid + r * NTHR;
     const int ic = i < BCE ? i : BCE - 1;
-    const int n = ic % (S * K);
+    const int n = ic % (GS * K);
     bc_nok[r] = n < N;
-    bc_voff[r] = (uint32_t)(((ic / (S * K)) * N + (n < N ? n : 0)) * T::es);
+    bc_voff[r] = (uint32_t)(((ic / (GS * K)) * N + (n < N ? n : 0)) * T::es);
   }
   // The inputs of one tile as this thread stages them (a few elements of B, C, x and delta).
   // Loads run two tiles ahead of the arithmetic through a ring of three such sets.
-  constexpr int XE = TT * kWave;
+  constexpr int XE = TT * CW;
   constexpr int NX = (XE + NTHR - 1) / NTHR;
-  // z[r] is the gate of row r * S + g, channel `lane` of the tile: the same (row, channel) this
-  // thread stores y for, so the gate never goes through LDS
+  // z[r] is the gate of row r * RPF + tid / CW, channel tid % CW of the tile: the same
+  // (row, channel) this thread stores y for, so the gate never goes through LDS
   struct Set {
     raw b[NPE], c[NPE], x[NX], d[NX], z[ZG ? NX : 1];
   };
   auto stage_load = [&](Set& st, int64_t ts) {
-    const auto rb = rs_n(B0, (uint32_t)(ts - t0));
-    const auto rc = rs_n(C0, (uint32_t)(ts - t0));
+    const uint32_t ob = trow(ts) * bc_row_bytes;
 #pragma unroll
     for (int r = 0; r < NPE; ++r) {
-      st.b[r] = T::bload(rb, bc_voff[r], 0u);
-      st.c[r] = T::bload(rc, bc_voff[r], 0u);
+      st.b[r] = T::bload(rsb, bc_voff[r] + ob, 0u);
+      st.c[r] = T::bload(rsc, bc_voff[r] + ob, 0u);
     }
   };
   auto stage_store = [&](const Set& st, int buf) {
@@ -268,8 +281,8 @@ void fwd_kernel(const FwdArgs p) {
     for (int r = 0; r < NPE; ++r) {
       const int i = tid + r * NTHR;
       if (i < BCE) {
-        const int tt = i / (S * K);
-        const int n = i % (S * K);
+        const int tt = i / (GS * K);
+        const int n = i % (GS * K);
         float* dst = &bcs[buf][tt][n / K][0];
         dst[n % K] = bc_nok[r] ? T::widen(st.b[r]) * p.alpha : 0.f;
         dst[K + n % K] = bc_nok[r] ? T::widen(st.c[r]) : 0.f;
@@ -278,27 +291,25 @@ void fwd_kernel(const FwdArgs p) {
   };
   // x / delta staging: element (row, channel) i of a tile goes through thread i mod NTHR; the
   // values are widened and delta * x formed once here, then every wavefront reads them from
-  // LDS.  Channels past D carry an offset past every extent and read as zero.
+  // LDS.  Channels past D read channel D - 1 (their lanes' results are never stored).
   uint32_t x_voff[NX];
 #pragma unroll
   for (int r = 0; r < NX; ++r) {
     const int i = tid + r * NTHR;
     const int ic = i < XE ? i : XE - 1;
-    const int dch = cb * kWave + ic % kWave;
-    x_voff[r] = dch < D ? (uint32_t)((ic / kWave) * row_bytes + dch * T::es) : 0x80000000u;
+    const int dch = cb * CW + ic % CW;
+    x_voff[r] = (uint32_t)((ic / CW) * row_bytes + (dch < D ? dch : (int)D - 1) * T::es);
   }
   auto load_xd = [&](Set& st, int64_t ts) {
-    const auto rx = rs_d(x0, (uint32_t)(ts - t0));
-    const auto rd = rs_d(dl0, (uint32_t)(ts - t0));
+    const uint32_t od = trow(ts) * row_bytes;
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
-      st.x[r] = T::bload(rx, x_voff[r], 0u);
-      st.d[r] = T::bload(rd, x_voff[r], 0u);
+      st.x[r] = T::bload(rsx, x_voff[r] + od, 0u);
+      st.d[r] = T::bload(rsdl, x_voff[r] + od, 0u);
     }
     if (ZG) {
-      const auto rz = rs_z((uint32_t)(ts - t0));
 #pragma unroll
-      for (int r = 0; r < NX; ++r) st.z[r] = T::bload(rz, x_voff[r], 0u);
+      for (int r = 0; r < NX; ++r) st.z[r] = T::bload(rsz, x_voff[r] + od, 0u);
     }
   };
   auto store_xd = [&](const Set& st, int buf) {
@@ -310,11 +321,11 @@ void fwd_kernel(const FwdArgs p) {
         if (EXT) {
           const float u = dv + dbias;
           const float de = softplus ? softplus_f(u) : u;
-          xdl[buf][i / kWave][i % kWave] = make_float2(de, ZOH ? xv : de * xv);
+          xdl[buf][i / CW][i % CW] = make_float2(de, ZOH ? xv : de * xv);
         } else {
-          xdl[buf][i / kWave][i % kWave] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
+          xdl[buf][i / CW][i % CW] = make_float2(dv, T::mul_raw(st.d[r], st.x[r]));
         }
-        if (HAS_DSKIP) xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? i / kWave : 0][i % kWave] = xv;
+        if (HAS_DSKIP) xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? i / CW : 0][i % CW] = xv;
       }
     }
   };
@@ -355,17 +366,19 @@ void fwd_kernel(const FwdArgs p) {
   };
   // y stores are never under a branch (a store the compiler cannot count makes its waits for
   // the prefetched inputs drain more than they need): channels past D carry an offset past
-  // every extent, and rows past the chunk end lie past the tile resource's extent, so the
-  // buffer unit drops both.
-  const uint32_t lane_off_y = dvalid ? lane_off : 0x80000000u;
+  // every extent, and rows past the chunk end lie past the resource's extent, so the buffer
+  // unit drops both.
+  auto yoff = [&](uint32_t tr, int tt) -> uint32_t {
+    return dvalid ? (tr + (uint32_t)tt) * row_bytes + lane_off : kDrop;
+  };
   auto gate = [&](float y, raw zr) { return (ZG && has_z) ? y * silu_f(T::widen(zr)) : y; };
-  // ry: resource of the tile being computed; cur: its inputs (only used when S == 1)
-  auto emit = [&](int buf, int tt, __amdgpu_buffer_rsrc_t ry, float ysum, const Set& cur) {
+  // tr: first row of the tile being computed; cur: its inputs (only used when GS == 1)
+  auto emit = [&](int buf, int tt, uint32_t tr, float ysum, const Set& cur) {
     if (SUMMARY) return;
-    if (S == 1) {
-      T::bstore(ry, (uint32_t)tt * row_bytes + lane_off_y, 0u, gate(ysum, cur.z[ZG ? tt : 0]));
+    if (GS == 1) {
+      T::bstore(rsy, yoff(tr, tt), 0u, gate(ysum, cur.z[ZG ? tt : 0]));
     } else {
-      ypart[YPART && YB == 2 ? buf : 0][YPART ? g : 0][tt][lane] = ysum;
+      ypart[YPART && YB == 2 ? buf : 0][YPART ? gs : 0][tt][ch] = ysum;
     }
   };
   // Full tile.  The B/C broadcasts of the next batch of RB steps are read from LDS into
@@ -380,19 +393,19 @@ void fwd_kernel(const FwdArgs p) {
     if (SUMMARY && ts < wg0) {
       // before this wavefront's window: only the chunk's delta sum
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) sd += xdl[buf][tt][lane].x;
+      for (int tt = 0; tt < TT; ++tt) sd += xdl[buf][tt][ch].x;
       return;
     }
-    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
+    const uint32_t ry = trow(ts);
     float bcv[2][RB][BCW];
     float2 dcv[2][RB];
     auto read_batch = [&](float(&dst)[RB][BCW], float2(&dd)[RB], int jb) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        const float* src = &bcs[buf][jb * RB + i][g][0];
+        const float* src = &bcs[buf][jb * RB + i][gs][0];
 #pragma unroll
         for (int e = 0; e < BCW; ++e) dst[i][e] = src[e];
-        dd[i] = xdl[buf][jb * RB + i][lane];
+        dd[i] = xdl[buf][jb * RB + i][ch];
       }
     };
     read_batch(bcv[0], dcv[0], 0);
@@ -403,7 +416,7 @@ void fwd_kernel(const FwdArgs p) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int tt = jb * RB + i;
-        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
+        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][ch] : 0.f;
         const float ysum = step(xv, dcv[jb & 1][i].x, dcv[jb & 1][i].y, bcv[jb & 1][i]);
         emit(buf, tt, ry, ysum, cur);
       }
@@ -412,29 +425,30 @@ void fwd_kernel(const FwdArgs p) {
   // The ragged last tile of a chunk (nv < TT rows), once per chunk after the main loop: rows
   // past nv must leave the state alone, so each row is guarded (a uniform branch).
   auto compute_tail = [&](int buf, int64_t ts, int nv, const Set& cur) {
-    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
+    const uint32_t ry = trow(ts);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       if (tt < nv) {
-        const float2 dc = xdl[buf][tt][lane];
-        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][lane] : 0.f;
-        const float ysum = step(xv, dc.x, dc.y, &bcs[buf][tt][g][0]);
+        const float2 dc = xdl[buf][tt][ch];
+        const float xv = HAS_DSKIP ? xxl[HAS_DSKIP ? buf : 0][HAS_DSKIP ? tt : 0][ch] : 0.f;
+        const float ysum = step(xv, dc.x, dc.y, &bcs[buf][tt][gs][0]);
         emit(buf, tt, ry, ysum, cur);
       }
     }
   };
-  // y of the tile whose partials are in ypart[buf]: each wavefront takes rows g, g + S, ...,
-  // adds the S partials in a fixed order and stores, a fixed number of stores per wavefront.
+  // y of the tile whose partials are in ypart[buf]: thread tid takes rows tid / CW, + RPF, ...
+  // of channel tid % CW (its own lane's channel), adds the GS partials in a fixed order and
+  // stores, a fixed number of stores per wavefront.
   auto finalize = [&](int buf, int64_t ts, const Set& cur) {
     if (!YPART) return;
-    const auto ry = rs_d(y0, (uint32_t)(ts - t0));
+    const uint32_t ry = trow(ts);
 #pragma unroll
-    for (int r = 0; r < TT / S; ++r) {
-      const int tt = r * S + g;
-      float s = ypart[YPART && YB == 2 ? buf : 0][0][tt][lane];
+    for (int r = 0; r < TT / RPF; ++r) {
+      const int tt = r * RPF + tid / CW;
+      float s = ypart[YPART && YB == 2 ? buf : 0][0][tt][ch];
 #pragma unroll
-      for (int gg = 1; gg < S; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][lane];
-      T::bstore(ry, (uint32_t)(tt * row_bytes) + lane_off_y, 0u, gate(s, cur.z[ZG ? r : 0]));
+      for (int gg = 1; gg < GS; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][ch];
+      T::bstore(rsy, yoff(ry, tt), 0u, gate(s, cur.z[ZG ? r : 0]));
     }
   };
 
@@ -478,7 +492,7 @@ void fwd_kernel(const FwdArgs p) {
       const int64_t base = b * p.G + k;
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const int64_t n = (int64_t)g * K + j;
+        const int64_t n = (int64_t)gs * K + j;
         if (n < N) {
           const int64_t idx = (base * N + n) * D + d;
           p.s_bh[idx] = h[j];
@@ -493,7 +507,7 @@ void fwd_kernel(const FwdArgs p) {
   } else if (k == p.G - 1 && dvalid) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t n = (int64_t)g * K + j;
+      const int64_t n = (int64_t)gs * K + j;
       if (n < N) {
         if (p.last_h) p.last_h[(b * D + d) * N + n] = h[j];
         if (p.last_v) p.last_v[(b * D + d) * N + n] = v[j];
@@ -502,33 +516,43 @@ void fwd_kernel(const FwdArgs p) {
   }
 }
 
-template <typename IO, int K, int S, bool BETA0, int EXT, int YBP>
+template <typename IO, int K, int S, bool BETA0, int EXT, int YBP, bool HW>
 void launch_main(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   if (a.Dskip)
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true, EXT, YBP>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, true, EXT, YBP, HW>), grid, block, 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false, EXT, YBP>), grid, block, 0, s,
-                       a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, false, false, EXT, YBP, HW>), grid, block, 0,
+                       s, a);
 }
 
-template <typename IO, int K, int S, bool BETA0, int EXT>
+// SH: wavefronts per workgroup of the half-wavefront layout for this (NP, K), 0 if it has none
+template <typename IO, int K, int S, bool BETA0, int EXT, int SH = 0>
 hipError_t launch_ks(const FwdArgs& a, hipStream_t s) {
   const dim3 block(S * kWave);
   if (a.G > 1) {
     const dim3 grid((unsigned)(a.ncb * a.Bt * (a.G - 1)));
-    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false, EXT, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, K, S, BETA0, true, false, EXT, 1, false>), grid, block, 0,
+                       s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if constexpr (SH > 0) {
+    if (a.half_wave) {
+      const dim3 grid((unsigned)(a.ncb_hw * a.Bt * a.G));
+      launch_main<IO, K, SH, BETA0, EXT, 2, true>(a, grid, dim3(SH * kWave), s);
+      return hipGetLastError();
+    }
   }
   const dim3 grid((unsigned)(a.ncb * a.Bt * a.G));
   // single-buffered y partials when the grid has more workgroups than the GPU has CUs
   if constexpr (S >= 16) {
-    launch_main<IO, K, S, BETA0, EXT, 1>(a, grid, block, s);
+    launch_main<IO, K, S, BETA0, EXT, 1, false>(a, grid, block, s);
   } else {
     if ((int64_t)grid.x > a.cus)
-      launch_main<IO, K, S, BETA0, EXT, 1>(a, grid, block, s);
+      launch_main<IO, K, S, BETA0, EXT, 1, false>(a, grid, block, s);
     else
-      launch_main<IO, K, S, BETA0, EXT, 2>(a, grid, block, s);
+      launch_main<IO, K, S, BETA0, EXT, 2, false>(a, grid, block, s);
   }
   return hipGetLastError();
 }
@@ -542,8 +566,8 @@ hipError_t launch_io(const FwdArgs& a, int K, hipStream_t s) {
     case 402: return launch_ks<IO, 2, 2, BETA0, EXT>(a, s);
     case 404: return launch_ks<IO, 4, 1, BETA0, EXT>(a, s);
     case 1601: return launch_ks<IO, 1, 16, BETA0, EXT>(a, s);
-    case 1602: return launch_ks<IO, 2, 8, BETA0, EXT>(a, s);
-    case 1604: return launch_ks<IO, 4, 4, BETA0, EXT>(a, s);
+    case 1602: return launch_ks<IO, 2, 8, BETA0, EXT, 4>(a, s);
+    case 1604: return launch_ks<IO, 4, 4, BETA0, EXT, 2>(a, s);
     case 1608: return launch_ks<IO, 8, 2, BETA0, EXT>(a, s);
     case 1616: return launch_ks<IO, 16, 1, BETA0, EXT>(a, s);
     case 3204: return launch_ks<IO, 4, 8, BETA0, EXT>(a, s);

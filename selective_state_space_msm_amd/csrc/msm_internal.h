@@ -46,6 +46,10 @@ struct FwdArgs {
   float beta_pow_tc;  // beta^Tc, the velocity decay across one full chunk
   int64_t win_rows;   // rows over which beta^rows < 2^-kWinLog2 (a summary window's minimum)
   int32_t cus;        // compute units of the device (picks the LDS layout of the y partials)
+  // main pass in the half-wavefront layout (32-channel workgroups, 2 state groups per
+  // wavefront) when the plan has one; ncb_hw = its channel blocks, 2 ceil(D / 64)
+  int32_t half_wave;
+  int32_t ncb_hw;
 };
 
 struct BwdArgs {
