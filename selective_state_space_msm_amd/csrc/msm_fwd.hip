@@ -15,7 +15,9 @@
 //   * B_t and C_t are the same for all channels, so each workgroup stages a tile of kTile steps
 //     of them in LDS (fp32, B pre-multiplied by alpha) and every lane reads them as broadcasts;
 //   * the per-wavefront partial sums of y_t = C_t . h_t are added across the S wavefronts in
-//     LDS in a fixed order (deterministic), one barrier per tile, double-buffered;
+//     LDS in a fixed order (deterministic), one barrier per tile when double-buffered;
+//   * unchunked plans use a half-wavefront layout instead (HW below): 32 channels per
+//     workgroup, the two lane halves on different state groups, 32-row tiles;
 //   * time runs sequentially inside a lane.  When the channel count alone cannot fill the
 //     GPU the sequence is cut into G chunks: a summary pass maps every chunk but the last to
 //     its affine map from a zero start (bv, bh, q and the sum of delta), and the main pass
@@ -53,7 +55,10 @@ void fwd_kernel(const FwdArgs p) {
   static_assert(!(HW && SUMMARY), "the summaries keep the full-wavefront layout");
   using T = io<IO>;
   using raw = typename T::raw;
-  constexpr int TT = kTile;
+  // rows per LDS tile: 32 in the half-wavefront layout, whose workgroups have LDS to spare
+  // (Bt=4 L=4096 D=4096 bf16: 0.319 ms against 0.336 ms with 16-row tiles, both with
+  // 4-row read batches)
+  constexpr int TT = HW ? 2 * kTile : kTile;
   constexpr int BCW = 2 * K;                    // floats per (tile row, state group): B then C
   constexpr int NTHR = S * kWave;
   constexpr int CW = HW ? kWave / 2 : kWave;    // channels per workgroup
@@ -68,8 +73,9 @@ void fwd_kernel(const FwdArgs p) {
   // workgroups share a CU (measured at Bt=1, L=65536, D=2048, N=16 in 16 chunks: 1.13 ms
   // single-buffered, 1.27 ms double-buffered; at Bt=4, L=4096, D=4096: 0.366 ms double,
   // 0.388 ms single)
-  // (the half-wavefront layout's workgroups are small: two share a CU with both buffers)
-  constexpr int YB = HW ? 2 : ((S >= 16 || YBP == 1) ? 1 : 2);
+  // (the half-wavefront layout single-buffers its 32-row tiles: 56 KB of LDS per workgroup,
+  // so two share a CU)
+  constexpr int YB = HW ? 1 : ((S >= 16 || YBP == 1) ? 1 : 2);
 
   __shared__ float bcs[2][TT][GS][BCW];
   __shared__ float ypart[YPART ? YB : 1][YPART ? GS : 1][TT][CW];
@@ -384,10 +390,11 @@ void fwd_kernel(const FwdArgs p) {
   // Full tile.  The B/C broadcasts of the next batch of RB steps are read from LDS into
   // registers before the current batch is computed; the scheduling barrier keeps the compiler
   // from sinking those reads next to their uses, where their latency would be exposed.
-  // Batches of 4 steps (2 for 16 states per wavefront) keep the double buffer small (measured
-  // at Bt=4, L=4096, D=4096, N=16, 2 states per wavefront: 0.366 ms against 0.399 ms with the
-  // whole tile as one batch).
-  constexpr int RB = (32 / K) < 4 ? (32 / K) : 4;
+  // Batches of 2 steps: measured at N=16, 2 states per wavefront, Bt=4 L=4096 D=4096 bf16
+  // (half-wavefront layout, 32-row tiles): 0.301 ms, against 0.305 ms with 1 step, 0.319 ms
+  // with 4 and 0.357 ms with 8; Bt=1 L=65536 D=2048 in 16 chunks (full layout): 0.719 ms
+  // against 0.772 ms with 4.
+  constexpr int RB = 2;
   constexpr int NB = TT / RB;
   auto compute_tile = [&](int buf, int64_t ts, const Set& cur) {
     if (SUMMARY && ts < wg0) {
