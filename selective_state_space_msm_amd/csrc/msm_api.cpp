@@ -623,7 +623,8 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   a.L = L;
   a.D = D;
   a.N = N;
-  a.NT = ceil_div(L, msm::kBwdTile);
+  // (the split passes of 64 states and the full-wavefront kernel take kBwdTile rows)
+  a.NT = ceil_div(L, NP == 64 ? msm::kBwdTile : msm::bwd_tile_rows(ext, pl.states_per_wave, 0));
   a.ncb = (int32_t)ceil_div(D, bwd_chans(NP, pl.states_per_wave));
   a.NP = NP;
   a.beta = beta;

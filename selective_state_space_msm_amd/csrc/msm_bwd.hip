@@ -13,8 +13,9 @@
 // (padded) states.  Half-width channel blocks double the number of workgroups, which is what
 // fills the 256 CUs at the usual training shapes (Bt * D / 32 workgroups).
 //   phase 1: forward over the whole sequence, writing the (v, h) state before every tile of
-//            kBwdTile steps to a checkpoint buffer (the recompute strategy of the README's
-//            backward notes: reconstruct the forward instead of storing it);
+//            TB steps (32 for the plain variant at one state per lane, else 16) to a
+//            checkpoint buffer (the recompute strategy of the README's backward notes:
+//            reconstruct the forward instead of storing it);
 //   phase 2: tiles in reverse order; each tile is recomputed from its checkpoint into
 //            registers (h_t and a_t for every step), then swept backwards.
 // x, delta, dy and B, C are staged once per workgroup into LDS, one tile ahead (the loads for
@@ -61,7 +62,14 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   using raw = typename T::raw;
   constexpr int CB = kBwdChans;          // channels per workgroup
   constexpr int P = kWave / CB;          // state groups per wavefront (2)
-  constexpr int TB = kBwdTile;
+  // rows per tile: 32 for the plain variant at one state per lane (its registers and LDS have
+  // room: a tile's states, decays and partials), 16 otherwise; the host sizes NT to match.
+  // Measured at Bt=4 L=2048 D=2048 N=16 fp32: 0.366 ms against 0.370 ms with 16-row tiles,
+  // and half the checkpoint traffic.
+  constexpr int TB = bwd_tile_rows(EXT, K, SPLIT);
+  // the dx / ddelta partials of 32-row tiles are single-buffered (64 KB at 8 wavefronts), with
+  // a barrier between the finalize that reads them and the sweep that rewrites them
+  constexpr int SPB = TB > kBwdTile ? 1 : 2;
   constexpr int NTHR = S * kWave;
   constexpr int NPB = S * P * K;         // padded states of the workgroup
   constexpr int GS = S * P;              // state groups of the workgroup
@@ -94,14 +102,14 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   // each with its rows contiguous (padded to keep 16-byte reads aligned and spread over the
   // banks).  The sweep's per-wavefront dx (lanes < 32) | ddelta partials reuse that LDS: phase 1
   // ends with a barrier.
-  constexpr int TP = S >= 4 ? 4 : 1;  // checkpoint tiles per phase-1 step
+  constexpr int TP = (S >= 4 ? 4 * kBwdTile / TB : 1);  // checkpoint tiles per phase-1 step
   constexpr int R1 = TP * TB;
   struct Ph1 {
     float2 xd1[2][CB][R1 + 2];
     float b1[2][GS][R1 * K + 4];
   };
   struct Ph2 {
-    float spart[2][S][TB][kWave];
+    float spart[SPB][S][TB][kWave];
   };
   union Ph12 {
     Ph1 f;
@@ -492,8 +500,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         const int tt = r * 2 * S + 2 * g + hf;
 #pragma unroll
         for (int w = 0; w < S; ++w) {
-          sp[r][0][w] = spart[pb][w][tt][lane];
-          sp[r][1][w] = spart[pb][w][tt][lane ^ CB];
+          sp[r][0][w] = spart[SPB == 2 ? pb : 0][w][tt][lane];
+          sp[r][1][w] = spart[SPB == 2 ? pb : 0][w][tt][lane ^ CB];
           if (EXT) yp[EXT ? r : 0][EXT ? w : 0] = ypt[EXT ? pb : 0][EXT ? w : 0][EXT ? tt : 0][ch];
         }
       }
@@ -564,7 +572,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     for (int r = 0; r < FR; ++r) {
       const int tt = r * S + g < TB ? r * S + g : TB - 1;
 #pragma unroll
-      for (int w = 0; w < S; ++w) sp[r][w] = spart[pb][w][tt][lane];
+      for (int w = 0; w < S; ++w) sp[r][w] = spart[SPB == 2 ? pb : 0][w][tt][lane];
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -684,6 +692,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     x_load(tp * TB, true);
     // tile + 1's partials were completed before the last barrier
     finalize(tile + 1, pb ^ 1, tile + 1 < NT && tile + 1 >= 0, buf ^ 1);
+    // single-buffered partials: every wavefront has read them before the sweep rewrites them
+    // (this also orders the finalize's reads of the staging buffer before its refill below)
+    if constexpr (SPB == 1) __syncthreads();
 
     // The sweep runs in every step (a step past tile 0 sweeps stale LDS data): its stores are
     // dropped through an empty resource and its sums are not kept.  No memory operation
@@ -762,7 +773,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         }
         // (DEF: odd rows with the halves swapped, so the finalize's two rows per wavefront
         // fall in different LDS banks)
-        spart[pb][g][tt][DEF ? (lane ^ ((tt & 1) * CB)) : lane] = swap_add32(qx, qd);
+        spart[SPB == 2 ? pb : 0][g][tt][DEF ? (lane ^ ((tt & 1) * CB)) : lane] = swap_add32(qx, qd);
         if (EXT) {
           // the output before the gate: this lane's states (+ the skip term on group 0 with
           // the zero-order hold; the finalize adds it otherwise), then both halves
@@ -794,9 +805,9 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         if (n < N && p.dv0) p.dv0[si] = BETA0 ? 0.f : (float)(beta64 * gvp[j]);
       }
     }
-    // the fused variants' finalize above read xe[buf ^ 1], which x_store refills: every
-    // wavefront must be past those reads first
-    if constexpr (EXT != 0) __syncthreads();
+    // the finalize above read xs, xg (and in the fused variants xe) [buf ^ 1], which the
+    // staging below refills: every wavefront must be past those reads first
+    if constexpr (SPB == 2) __syncthreads();
     bc_store(buf ^ 1, true);
     x_store(buf ^ 1, true);
     __syncthreads();

@@ -13,6 +13,11 @@ constexpr int kMaxChunks = 64;   // upper bound on time chunks (sizes the worksp
 constexpr int kMaxN = 64;        // states supported per channel
 constexpr int kBwdTile = 16;     // time steps recomputed per register tile in the backward
 constexpr int kBwdChans = 32;    // channels per workgroup in the backward (half a wavefront)
+// Rows per tile of the half-wavefront backward: 2 kBwdTile for the plain variant (EXT 0) at
+// one state per lane in one launch, kBwdTile otherwise.  NT (and the checkpoint count) follow.
+constexpr int bwd_tile_rows(int ext, int K, int split) {
+  return (ext == 0 && K == 1 && split == 0) ? 2 * kBwdTile : kBwdTile;
+}
 // A chunk summary ignores rows whose share of the chunk's end state is below 2^-kWinLog2.
 constexpr float kWinLog2 = 32.f;
 
