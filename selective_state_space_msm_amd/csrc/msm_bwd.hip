@@ -85,12 +85,15 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   constexpr bool DEF = !ZOH;
   static_assert(RB >= 1 && TB % RB == 0, "tile must split into reduce blocks");
 
-  // (delta, delta x) and (dy, x) of each staged element, in two arrays so the sweep reads 8 and 4
-  // bytes per lane (a 12-byte read of a 16-byte element waited longer); odd rows have their
-  // channel halves swapped (position ch ^ 16), so the finalize's rows 2g and 2g + 1 read
-  // different banks
+  // (delta, delta x), dy and x of each staged element, in three arrays: the recompute reads 8
+  // bytes per lane, and the sweep, which reuses those, reads dy alone from a contiguous array
+  // (dy read as one half of an 8-byte element touched every other bank, and those reads
+  // conflicted: 0.041 conflict cycles per state update against 0.005 with the old 16-byte
+  // element).  Odd rows have their channel halves swapped (position ch ^ 16), so the
+  // finalize's rows 2g and 2g + 1 read different banks
   __shared__ float2 xs[2][TB][CB];
-  __shared__ float2 xg[2][TB][CB];
+  __shared__ float gys[2][TB][CB];
+  __shared__ float xvs[2][TB][CB];
   __shared__ float bs[2][TB][GS][K];        // alpha B
   __shared__ double cs64[2][TB][GS][K];     // C, widened for the adjoint recurrence
   // fused variant: (dy silu'(z), logistic(delta + bias)) per staged element, the per-wavefront
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
   const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int ch = lane & (CB - 1);
   const int gs = g * P + lane / CB;  // state group of this lane
-  // position of channel c of staged row t in xs, xg and xe (odd rows: halves swapped)
+  // position of channel c of staged row t in xs, gys, xvs and xe (odd rows: halves swapped)
   auto swz = [](int t, int c) { return c ^ ((t & 1) * (CB / 2)); };
   const uint32_t bq = blockIdx.x / (uint32_t)p.ncb;
   const int cb = (int)(blockIdx.x - bq * (uint32_t)p.ncb);
@@ -235,7 +238,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
           xe[EXT ? buf : 0][EXT ? i / CB : 0][xc] = make_float2(gz, dsp);
         }
         xs[buf][i / CB][xc] = make_float2(dv, dv * xv);
-        xg[buf][i / CB][xc] = make_float2(gy, xv);
+        gys[buf][i / CB][xc] = gy;
+        xvs[buf][i / CB][xc] = xv;
       }
     }
   };
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         }
         const int xc = swz(tt, ch);
         const float dv = xs[xb][tt][xc].x;
-        const float2 gx = xg[xb][tt][xc];  // dy, x
+        const float2 gx = make_float2(gys[xb][tt][xc], xvs[xb][tt][xc]);  // dy, x
         double qdx = (double)dv * s1;
         double qdd = fma((double)gx.y, s1, s2);
         if (HAS_DSKIP) qdx = fma((double)dsk, (double)gx.x, qdx);
@@ -716,7 +720,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
     for (int tt = 0; tt < TB; ++tt) {
       const int xc = swz(tt, ch);
       const float2 r = xs[buf][tt][xc];
-      fstep(r.x, ZOH ? xg[buf][tt][xc].y : r.y, &bs[buf][tt][gs][0], av[tt], hs[tt + 1],
+      fstep(r.x, ZOH ? xvs[buf][tt][xc] : r.y, &bs[buf][tt][gs][0], av[tt], hs[tt + 1],
             ZOH ? phs[ZOH ? tt : 0] : nullptr, ZOH ? pss[ZOH ? tt : 0] : nullptr);
     }
 
@@ -731,8 +735,8 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
       for (int tb = RB - 1; tb >= 0; --tb) {
         const int tt = rb * RB + tb;
         const int xc = swz(tt, ch);
-        const float2 r0 = xs[buf][tt][xc], r1 = xg[buf][tt][xc];
-        const float dv = r0.x, c = r0.y, gy = r1.x, xv = r1.y;
+        const float2 r0 = xs[buf][tt][xc];
+        const float dv = r0.x, c = r0.y, gy = gys[buf][tt][xc], xv = xvs[buf][tt][xc];
         const double gy64 = gy;
         float p1 = 0.f, p2 = 0.f, yq = 0.f, p1d = 0.f;
 #pragma unroll
@@ -805,7 +809,7 @@ __global__ __launch_bounds__(S* kWave) void bwd_kernel(const BwdArgs p) {
         if (n < N && p.dv0) p.dv0[si] = BETA0 ? 0.f : (float)(beta64 * gvp[j]);
       }
     }
-    // the finalize above read xs, xg (and in the fused variants xe) [buf ^ 1], which the
+    // the finalize above read xs, gys, xvs (and in the fused variants xe) [buf ^ 1], which the
     // staging below refills: every wavefront must be past those reads first
     if constexpr (SPB == 2) __syncthreads();
     bc_store(buf ^ 1, true);

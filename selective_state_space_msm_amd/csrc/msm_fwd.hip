@@ -377,6 +377,13 @@ void fwd_kernel(const FwdArgs p) {
   auto yoff = [&](uint32_t tr, int tt) -> uint32_t {
     return dvalid ? (tr + (uint32_t)tt) * row_bytes + lane_off : kDrop;
   };
+  // the finalize's rows of this thread (tid / CW + r RPF): their offsets within a tile are
+  // constants, so a tile adds its scalar row offset (one add and one select per store)
+  constexpr int FR = TT / RPF;
+  uint32_t fin_off[YPART ? FR : 1];
+#pragma unroll
+  for (int r = 0; r < (YPART ? FR : 1); ++r)
+    fin_off[r] = (uint32_t)(r * RPF + tid / CW) * row_bytes + lane_off;
   auto gate = [&](float y, raw zr) { return (ZG && has_z) ? y * silu_f(T::widen(zr)) : y; };
   // tr: first row of the tile being computed; cur: its inputs (only used when GS == 1)
   auto emit = [&](int buf, int tt, uint32_t tr, float ysum, const Set& cur) {
@@ -448,14 +455,15 @@ void fwd_kernel(const FwdArgs p) {
   // stores, a fixed number of stores per wavefront.
   auto finalize = [&](int buf, int64_t ts, const Set& cur) {
     if (!YPART) return;
-    const uint32_t ry = trow(ts);
+    const uint32_t rbytes = __builtin_amdgcn_readfirstlane(trow(ts) * row_bytes);
 #pragma unroll
-    for (int r = 0; r < TT / RPF; ++r) {
+    for (int r = 0; r < FR; ++r) {
       const int tt = r * RPF + tid / CW;
       float s = ypart[YPART && YB == 2 ? buf : 0][0][tt][ch];
 #pragma unroll
       for (int gg = 1; gg < GS; ++gg) s += ypart[YPART && YB == 2 ? buf : 0][YPART ? gg : 0][tt][ch];
-      T::bstore(rsy, yoff(ry, tt), 0u, gate(s, cur.z[ZG ? r : 0]));
+      const uint32_t o = dvalid ? rbytes + fin_off[YPART ? r : 0] : kDrop;
+      T::bstore(rsy, o, 0u, gate(s, cur.z[ZG ? r : 0]));
     }
   };
 
