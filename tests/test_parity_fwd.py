@@ -45,6 +45,21 @@ def test_tiny_workload_auto_plan():
         check_full(workloads.make_inputs(W["tiny"].replace(beta=beta)), tag="tiny-auto")
 
 
+# ---- the half-wavefront layout of unchunked 16-state plans: workgroup order and edges ----
+# 32-channel workgroups whose indices are permuted within each group of 16 (the two halves of a
+# 64-channel block 8 apart); grids of 18 leave a tail of 2 unpermuted; D = 160 and D = 30
+# leave a workgroup with no valid channel; 64 workgroups are all permuted.
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 70, 160), (9, 40, 30), (8, 100, 256)])
+def test_half_wave_workgroup_order(io, shape):
+    Bt, L, D = shape
+    inp = workloads.make_inputs(W["m130m"].replace(Bt=Bt, L=L, D=D, N=16, io=io, beta=0.9,
+                                                   alpha=0.7, dskip=True),
+                                a_kind="random", seed=91)
+    check_full(inp, plan={"states_per_wave": 2, "chunks": 1}, tag="half-wave %s" % (shape,))
+
+
 # ---- several tiles, ragged time and channel tails, every state split and chunking ----
 
 SMALL = W["m130m"].replace(Bt=2, L=200, D=100, N=16)
