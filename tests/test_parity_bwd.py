@@ -62,15 +62,18 @@ def test_small_ragged(io, K, beta, alpha, dskip):
     check_full(inp, plan={"states_per_wave": K}, tag="small")
 
 
+@pytest.mark.parametrize("N", [16, 4])
 @pytest.mark.parametrize("K", [1, 2])
-@pytest.mark.parametrize("L", [64, 65, 193, 320])
-def test_forward_pass_step_boundaries(K, L):
-    # the backward's forward pass stages 64 rows (four checkpoint tiles) per step when a
-    # workgroup has four or more wavefronts: sequences of whole steps, one row past a step, a
-    # ragged last tile in a fourth step, and an odd number of whole steps
-    inp = workloads.make_inputs(SMALL.replace(L=L, D=40, dskip=True), a_kind="random",
+@pytest.mark.parametrize("L", [31, 32, 33, 64, 65, 96, 97, 193, 320])
+def test_forward_pass_step_boundaries(N, K, L):
+    # the backward's forward pass stages 64 rows (two 32-row checkpoint tiles at one state per
+    # lane, four 16-row tiles at two) per step when a workgroup has four or more wavefronts:
+    # one tile short of, at and one row past a 32-row tile, whole steps, one row past a step,
+    # an odd tile count, a ragged last tile in a fourth step, and an odd number of whole steps
+    # (4 states: one checkpoint tile per step, the workgroup has one or two wavefronts)
+    inp = workloads.make_inputs(SMALL.replace(L=L, D=40, N=N, dskip=True), a_kind="random",
                                 seed=90 + L)
-    check_full(inp, plan={"states_per_wave": K}, tag="L=%d" % L)
+    check_full(inp, plan={"states_per_wave": K}, tag="N=%d L=%d" % (N, L))
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
