@@ -184,7 +184,7 @@ bool bwd_allowed_k(int NP, int K) {
 // than two wavefronts leave) that still gives 2 * 1024 wavefronts, else K = 1.  64 padded states
 // take K = 2, two launches of the 32-state plan, or K = 4, the full-wavefront kernel, when the
 // first half's sums would exceed 32-bit offsets (D >= 2^23).
-msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = false) {
+msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int ext = 0) {
   const int NP = padded_states(N);
   msm_plan pl{0, 1};
   if (NP == 64 || NP == 32) {
@@ -196,10 +196,11 @@ msm_plan auto_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, bool ext = f
   const int64_t chan_blocks = Bt * ceil_div(D, msm::kBwdChans);
   pl.states_per_wave = 1;
   if (bwd_allowed_k(NP, 2) && chan_blocks * (NP / 4) >= 2 * kTargetWaves) pl.states_per_wave = 2;
-  // the fused variants carry more registers per state: at 16 padded states they run best with
-  // two states per lane (measured at Bt=4, L=2048, D=2048: fused 0.73 ms against 0.79 ms with
-  // one; with the zero-order hold 1.17 ms against 3.09 ms, where one state per lane spills)
-  if (ext && NP == 16) pl.states_per_wave = 2;
+  // the zero-order hold carries more registers per state: at 16 padded states it runs with two
+  // states per lane (measured at Bt=4, L=2048, D=2048: 0.99 ms against 2.52 ms with one, which
+  // spills); the fused variant without it takes the default (0.504 ms with one state per lane
+  // against 0.577 ms with two)
+  if (ext == 2 && NP == 16) pl.states_per_wave = 2;
   return pl;
 }
 
@@ -540,7 +541,7 @@ msm_status msm_selective_scan_bwd(const void* x, const void* delta, const float*
   if (zero_order_hold != 0 && zero_order_hold != 1) return MSM_ERR_INVALID_ARG;
   const int ext = zero_order_hold ? 2 : (z || delta_bias || delta_softplus ? 1 : 0);
 
-  msm_plan pl = auto_bwd_plan(Bt, L, D, N, ext != 0);
+  msm_plan pl = auto_bwd_plan(Bt, L, D, N, ext);
   const int NP = padded_states(N);
   if (plan) {
     if (plan->states_per_wave != 0) {
