@@ -490,10 +490,11 @@ void fwd_kernel(const FwdArgs p) {
       compute_tile(buf, ts, cur);
     else if (k == nfull && nrem > 0)
       compute_tail(buf, ts, nrem, cur);
-    // staging and the y finalize run at a raised wave priority: where two workgroups share a
+    // staging and the y finalize run at the highest wave priority: where two workgroups share a
     // SIMD, the one nearing its barriers gets the issue slots first (Bt=4 L=4096 D=4096 bf16:
-    // 0.294 ms against 0.299 ms; Bt=1 L=65536 D=2048 in 16 chunks: 0.720 against 0.732 ms)
-    __builtin_amdgcn_s_setprio(2);
+    // 0.292 ms against 0.299 ms at priority 0 and 0.294 ms at 2; Bt=1 L=65536 D=2048 in 16
+    // chunks: 0.720 against 0.732 ms)
+    __builtin_amdgcn_s_setprio(3);
     store_set(st, buf ^ 1);
     __syncthreads();
     finalize(buf, ts, cur);
